@@ -1,0 +1,179 @@
+/*
+ * oracle.c -- reference GEMM in double precision.
+ *
+ * TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library; the product path (the
+ * HIP library and its Python binding) never does, and this file shares no
+ * code, header or table with it.
+ *
+ * What it computes. C = A*B for compact row-major A[M,K] and B[K,N], with no
+ * scale on the product and nothing taken from the old contents of C (page
+ * "Scale coverage exposes a remaining GEMM gap", section "Measurement contract
+ * and evidence": the GEMM there has alpha one, beta zero, no transpose and no
+ * prepacked operand). Operands are FP32, or bfloat16 / IEEE binary16 bit
+ * patterns (the 16-bit operand port of page "Measured data point on fixed-tile
+ * vs shape-adaptive GEMM", section "One more result that surprised us").
+ *
+ * How. Each operand value is decoded exactly to double. Each product a*b is
+ * then exact in double (two significands of at most 24 bits make at most 48
+ * bits), and the products of one output element are added in double in
+ * ascending k, starting from +0.0. The loop order is i, then k, then j with
+ * a double row accumulator: for every element the additions still happen in
+ * ascending k, so the bits equal those of the i-j-k dot-product order. No
+ * blocking and no reassociation; build with -O2 -fno-fast-math
+ * -ffp-contract=off.
+ *
+ * The double result is handed back as is; rounding it (for a bit-exact
+ * comparison) is the caller's business.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. It is
+ * the upper half of an IEEE binary32, so the value follows binary32's rules:
+ * exponent field 0 is zero/subnormal with scale 2^-126, field 255 is inf/NaN. */
+double oracle_decode_bf16(uint16_t bits)
+{
+    int sign = bits >> 15;
+    int e = (bits >> 7) & 0xFF;
+    int f = bits & 0x7F;
+    double v;
+    if (e == 0xFF)
+        v = f ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)f, -126 - 7);          /* 0.f * 2^-126 */
+    else
+        v = ldexp((double)(0x80 | f), e - 127 - 7); /* 1.f * 2^(e-127) */
+    return sign ? -v : v;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits;
+ * field 0 is zero/subnormal with scale 2^-14, field 31 is inf/NaN. */
+double oracle_decode_f16(uint16_t bits)
+{
+    int sign = bits >> 15;
+    int e = (bits >> 10) & 0x1F;
+    int f = bits & 0x3FF;
+    double v;
+    if (e == 0x1F)
+        v = f ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)f, -14 - 10);
+    else
+        v = ldexp((double)(0x400 | f), e - 15 - 10);
+    return sign ? -v : v;
+}
+
+static double load_val(int dtype, const void* p, int64_t idx)
+{
+    switch (dtype) {
+    case ORACLE_F32:  return (double)((const float*)p)[idx];
+    case ORACLE_BF16: return oracle_decode_bf16(((const uint16_t*)p)[idx]);
+    default:          return oracle_decode_f16(((const uint16_t*)p)[idx]);
+    }
+}
+
+static int check_args(int dtype, const void* A, const void* B, int64_t M,
+                      int64_t N, int64_t K)
+{
+    if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
+    if (M < 0 || N < 0 || K < 0) return -1;
+    if (K > 0 && ((M > 0 && !A) || (N > 0 && !B))) return -1;
+    return 0;
+}
+
+static void set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/* Number of threads an OpenMP region would use now (1 without OpenMP). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Rows [row0, row0+nrows) of C into Cslab[nrows][N].  Returns 0 or -1. */
+int oracle_gemm_rows(int dtype, const void* A, const void* B, int64_t M,
+                     int64_t N, int64_t K, int64_t row0, int64_t nrows,
+                     double* Cslab, int nthreads)
+{
+    if (check_args(dtype, A, B, M, N, K)) return -1;
+    if (row0 < 0 || nrows < 0 || row0 + nrows > M) return -1;
+    if (nrows == 0 || N == 0) return 0;
+    if (!Cslab) return -1;
+
+    /* B decoded once into double; the conversion is exact, and it is the
+     * same value load_val would give inside the loop. */
+    double* Bd = NULL;
+    if (K > 0) {
+        Bd = (double*)malloc((size_t)K * (size_t)N * sizeof(double));
+        if (!Bd) return -1;
+        set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+        for (int64_t k = 0; k < K; ++k)
+            for (int64_t j = 0; j < N; ++j)
+                Bd[k * N + j] = load_val(dtype, B, k * N + j);
+    }
+
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = row0 + r;
+        double* acc = Cslab + r * N;
+        for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = load_val(dtype, A, i * K + k);
+            const double* brow = Bd + k * N;
+            for (int64_t j = 0; j < N; ++j) acc[j] = acc[j] + a * brow[j];
+        }
+    }
+    free(Bd);
+    return 0;
+}
+
+/* The whole of C into C[M][N]. */
+int oracle_gemm(int dtype, const void* A, const void* B, int64_t M, int64_t N,
+                int64_t K, double* C, int nthreads)
+{
+    return oracle_gemm_rows(dtype, A, B, M, N, K, 0, M, C, nthreads);
+}
+
+/* Single elements: out[p] = C[rows[p]][cols[p]], each one its own
+ * ascending-k sum. */
+int oracle_gemm_points(int dtype, const void* A, const void* B, int64_t M,
+                       int64_t N, int64_t K, const int64_t* rows,
+                       const int64_t* cols, int64_t npts, double* out,
+                       int nthreads)
+{
+    if (check_args(dtype, A, B, M, N, K)) return -1;
+    if (npts < 0 || (npts > 0 && (!rows || !cols || !out))) return -1;
+    for (int64_t p = 0; p < npts; ++p)
+        if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N)
+            return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npts; ++p) {
+        const int64_t i = rows[p], j = cols[p];
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s = s + load_val(dtype, A, i * K + k) * load_val(dtype, B, k * N + j);
+        out[p] = s;
+    }
+    return 0;
+}

@@ -1,0 +1,137 @@
+"""Seeded synthetic operands for the GEMM workloads.
+
+Shared by the tests, the benchmark and the smoke check. It holds no GEMM
+arithmetic: only random draws, the rounding of a draw to a 16-bit storage
+format (part of the input's definition: normal(0,1) values stored as bfloat16
+or binary16), and the workload table.
+
+Recipes:
+  * ``uniform``: FP32 uniform on [-1, 1). Drawn directly as float32 (24 random
+    bits, so multiples of 2^-24 on [0, 1)), then x*2-1, which is exact in FP32
+    and never reaches +1.
+  * ``ints``: integers uniform on the closed range [lo, hi], stored as FP32.
+    Small integers make every FP32 partial sum exact (dyadic inputs).
+  * ``normal16``: float32 standard normal, rounded to nearest-even to bfloat16
+    or binary16; the 16-bit bit patterns are returned as uint16.
+A is always drawn before B from one ``numpy.random.default_rng(seed)``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "by_name", "uniform_pm1", "small_ints",
+           "normal16", "make_operands", "sample_points", "bf16_rne_bits"]
+
+
+def uniform_pm1(rng: np.random.Generator, shape) -> np.ndarray:
+    x = rng.random(shape, dtype=np.float32)
+    return x * np.float32(2.0) - np.float32(1.0)
+
+
+def small_ints(rng: np.random.Generator, shape, lo: int, hi: int) -> np.ndarray:
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even.
+
+    Finite inputs only (normal draws never produce NaN or Inf)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def normal16(rng: np.random.Generator, shape, kind: str) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if kind == "bf16":
+        return bf16_rne_bits(x)
+    if kind == "f16":
+        return x.astype(np.float16).view(np.uint16)  # numpy rounds to nearest-even
+    raise ValueError(kind)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "f32" | "bf16" | "f16"
+    M: int
+    N: int
+    K: int
+    dist: str           # "uniform" | "ints" | "normal16"
+    seed: int
+    lo: int = 0         # integer range for "ints"
+    hi: int = 0
+    check: str = "rel_rms"   # "bitexact" | "rel_rms"
+    tol: float = 1e-5
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def in_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def alg_bytes(self) -> int:
+        """Operands read once, C written once (beta = 0, C is never read)."""
+        return self.in_bytes * (self.M * self.K + self.K * self.N) + 4 * self.M * self.N
+
+
+def _u(name, M, N, K, seed):
+    return Workload(name, "f32", M, N, K, "uniform", seed)
+
+
+WORKLOADS = [
+    Workload("f32_256_ints", "f32", 256, 256, 256, "ints", 1, -4, 4, "bitexact", 0.0),
+    _u("f32_2048", 2048, 2048, 2048, 2),
+    Workload("f32_2048_ints", "f32", 2048, 2048, 2048, "ints", 3, -2, 2, "bitexact", 0.0),
+    _u("f32_4096", 4096, 4096, 4096, 4),
+    _u("f32_8192", 8192, 8192, 8192, 5),
+    Workload("bf16_4096", "bf16", 4096, 4096, 4096, "normal16", 6, tol=1e-2),
+    Workload("bf16_8192", "bf16", 8192, 8192, 8192, "normal16", 7, tol=1e-2),
+    Workload("f16_4096", "f16", 4096, 4096, 4096, "normal16", 8, tol=1e-2),
+    Workload("f16_8192", "f16", 8192, 8192, 8192, "normal16", 9, tol=1e-2),
+    _u("f32_768", 768, 768, 768, 10),
+    _u("f32_4097x3071x8191", 4097, 3071, 8191, 11),
+    _u("f32_8191x8193x4096", 8191, 8193, 4096, 12),
+    _u("f32_16x8192x8192", 16, 8192, 8192, 13),
+    _u("f32_8192x16x8192", 8192, 16, 8192, 14),
+    _u("f32_8192x8192x64", 8192, 8192, 64, 15),
+]
+
+_BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def by_name(name: str) -> Workload:
+    return _BY_NAME[name]
+
+
+def make_operands(w: Workload, seed: int | None = None):
+    """(A, B) as numpy arrays: float32 for f32, uint16 bit patterns otherwise."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    sa, sb = (w.M, w.K), (w.K, w.N)
+    if w.dist == "uniform":
+        return uniform_pm1(rng, sa), uniform_pm1(rng, sb)
+    if w.dist == "ints":
+        return small_ints(rng, sa, w.lo, w.hi), small_ints(rng, sb, w.lo, w.hi)
+    if w.dist == "normal16":
+        return normal16(rng, sa, w.dtype), normal16(rng, sb, w.dtype)
+    raise ValueError(w.dist)
+
+
+def sample_points(M: int, N: int, count: int, seed: int):
+    """Distinct output positions for a spot check: ``count`` seeded random ones
+    plus the four corners and samples of the last row and last column (the
+    elements next to the M and N tails). Returns (rows, cols) int64 arrays."""
+    rng = np.random.default_rng(seed)
+    total = M * N
+    flat = rng.choice(total, size=min(count, total), replace=False).astype(np.int64)
+    extra = [0, N - 1, (M - 1) * N, M * N - 1]
+    extra += [(M - 1) * N + j for j in np.linspace(0, N - 1, 16, dtype=np.int64)]
+    extra += [i * N + (N - 1) for i in np.linspace(0, M - 1, 16, dtype=np.int64)]
+    flat = np.unique(np.concatenate([flat, np.asarray(extra, dtype=np.int64)]))
+    return flat // N, flat % N

@@ -1,0 +1,266 @@
+"""Checks that tie the oracle to facts outside itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with brute force, a closed form, an invariant, a hand-worked
+fixture, a library routine or the FP64 error bound. ``test_oracle_pins.py``
+runs them on the real oracle; ``test_oracle_mutants.py`` runs them on copies of
+the oracle with planted mistakes and requires that some pin fails for each.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+# -- fixtures ---------------------------------------------------------------
+def _parse_value(tok: str) -> float:
+    if tok in ("inf", "-inf"):
+        return float(tok)
+    neg = tok.startswith("-")
+    t = tok[1:] if neg else tok
+    if t.startswith("2^"):
+        v = 2.0 ** int(t[2:])
+    elif "*2^" in t:
+        a, e = t.split("*2^")
+        v = float(int(a)) * 2.0 ** int(e)
+    elif "/" in t:
+        v = float(Fraction(t))
+    else:
+        v = float(t)
+    return -v if neg else v
+
+
+def decode_table():
+    rows = []
+    for line in (GOLDEN / "decode_16bit.txt").read_text().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        fmt, bits, val = line.split()[:3]
+        rows.append((fmt, int(bits, 16), _parse_value(val)))
+    return rows
+
+
+def small_gemm_cases():
+    lines = [l for l in (GOLDEN / "small_gemms.txt").read_text().splitlines()
+             if l.strip() and not l.startswith("#")]
+    cases, i = [], 0
+    while i < len(lines):
+        _, name, M, N, K = lines[i].split()
+        M, N, K = int(M), int(N), int(K)
+        i += 1
+        rd = lambda n: [[float(x) for x in lines[i + r].split()] for r in range(n)]
+        A = rd(M); i += M
+        B = rd(K); i += K
+        C = rd(M); i += M
+        cases.append((name, np.array(A, np.float32), np.array(B, np.float32),
+                      np.array(C, np.float64)))
+    return cases
+
+
+# -- helpers ------------------------------------------------------------------
+def _bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float64).view(np.uint64)
+
+
+def _bruteforce_int(A, B):
+    A = [[int(v) for v in row] for row in A.tolist()]
+    B = [[int(v) for v in row] for row in B.tolist()]
+    M, K, N = len(A), len(B), len(B[0]) if B else 0
+    return [[sum(A[i][k] * B[k][j] for k in range(K)) for j in range(N)]
+            for i in range(M)]
+
+
+# -- pins ---------------------------------------------------------------------
+def pin_golden_small(o):
+    """Hand-worked products from the definition match exactly."""
+    for name, A, B, C in small_gemm_cases():
+        got = o.gemm("f32", A, B)
+        assert np.array_equal(got, C), (name, got, C)
+        assert not np.signbit(got[C == 0]).any(), (name, "negative zero")
+
+
+def pin_decode_table(o):
+    """16-bit decoding matches the hand-worked format table bit for bit."""
+    for fmt, bits, val in decode_table():
+        got = o.decode(fmt, bits)
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), \
+            (fmt, hex(bits), got, val)
+    for fmt in ("bf16", "f16"):   # NaN patterns
+        nan_bits = 0x7FC0 if fmt == "bf16" else 0x7E00
+        assert math.isnan(o.decode(fmt, nan_bits))
+
+
+def pin_decode_library(o):
+    """Every finite 16-bit pattern decodes to what numpy's own routines give:
+    binary16 through numpy.float16, bfloat16 as the top half of a float32."""
+    allbits = np.arange(1 << 16, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        f16 = allbits.astype(np.uint16).view(np.float16).astype(np.float64)
+        bf = (allbits << 16).view(np.float32).astype(np.float64)
+    step = 97  # a spread subset keeps the ctypes loop short
+    for b in range(0, 1 << 16, step):
+        for fmt, ref in (("f16", f16[b]), ("bf16", bf[b])):
+            got = o.decode(fmt, b)
+            if math.isnan(ref):
+                assert math.isnan(got), (fmt, hex(b))
+            else:
+                assert got == ref and math.copysign(1, got) == math.copysign(1, ref), \
+                    (fmt, hex(b), got, ref)
+
+
+def pin_bruteforce_ints(o):
+    """Integer operands on tiny shapes equal a pure-Python integer triple sum."""
+    rng = np.random.default_rng(101)
+    sizes = [1, 2, 3, 4, 5, 7, 13, 17]
+    for M in sizes:
+        for N in sizes:
+            for K in (1, 2, 3, 5, 17):
+                A = rng.integers(-9, 10, size=(M, K)).astype(np.float32)
+                B = rng.integers(-9, 10, size=(K, N)).astype(np.float32)
+                ref = np.array(_bruteforce_int(A, B), dtype=np.float64)
+                got = o.gemm("f32", A, B)
+                assert np.array_equal(got, ref), (M, N, K)
+
+
+def pin_bruteforce_16bit(o):
+    """16-bit operands: the oracle equals exact rational arithmetic on values
+    decoded by numpy (float16, and bfloat16 as the top half of a float32)."""
+    rng = np.random.default_rng(102)
+    for fmt in ("bf16", "f16"):
+        for (M, N, K) in [(3, 5, 7), (4, 4, 16), (1, 9, 33)]:
+            x = rng.standard_normal((M * K + K * N,)).astype(np.float32)
+            if fmt == "f16":
+                bits = x.astype(np.float16).view(np.uint16)
+                vals = bits.view(np.float16).astype(np.float64)
+            else:
+                bits = (x.view(np.uint32) >> 16).astype(np.uint16)  # truncation is fine here
+                vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            A, B = bits[:M * K].reshape(M, K), bits[M * K:].reshape(K, N)
+            Av, Bv = vals[:M * K].reshape(M, K), vals[M * K:].reshape(K, N)
+            got = o.gemm(fmt, A, B)
+            for i in range(M):
+                for j in range(N):
+                    exact = sum(Fraction(Av[i, k]) * Fraction(Bv[k, j]) for k in range(K))
+                    bound = (K - 1) * 2.0 ** -53 * float(sum(abs(Fraction(Av[i, k]) * Fraction(Bv[k, j])) for k in range(K)))
+                    assert abs(Fraction(got[i, j]) - exact) <= Fraction(bound), (fmt, i, j)
+
+
+def pin_fsum_bound(o):
+    """Random FP32: each element is within the recursive-summation bound
+    (K-1)*u*sum|a_k b_k| of the exact sum (math.fsum of exact double products)."""
+    rng = np.random.default_rng(103)
+    for (M, N, K) in [(9, 11, 64), (5, 3, 257), (16, 16, 16)]:
+        A = (rng.random((M, K), dtype=np.float32) * 2 - 1).astype(np.float32)
+        B = (rng.random((K, N), dtype=np.float32) * 2 - 1).astype(np.float32)
+        got = o.gemm("f32", A, B)
+        A64, B64 = A.astype(np.float64), B.astype(np.float64)
+        for i in range(M):
+            for j in range(N):
+                prods = A64[i, :] * B64[:, j]
+                exact = math.fsum(prods)
+                bound = (K - 1) * 2.0 ** -53 * math.fsum(np.abs(prods))
+                assert abs(got[i, j] - exact) <= bound, (M, N, K, i, j)
+
+
+def pin_closed_forms(o):
+    """ones*ones = K; A=1, B[k][j]=k gives K(K-1)/2; A[i][k]=i, B[k][j]=j
+    gives K*i*j."""
+    for (M, N, K) in [(3, 4, 5), (8, 1, 100), (1, 7, 1000), (6, 6, 1)]:
+        A = np.ones((M, K), np.float32)
+        B = np.ones((K, N), np.float32)
+        assert np.array_equal(o.gemm("f32", A, B), np.full((M, N), float(K)))
+        Bk = np.repeat(np.arange(K, dtype=np.float32)[:, None], N, axis=1)
+        assert np.array_equal(o.gemm("f32", A, Bk), np.full((M, N), K * (K - 1) / 2))
+        Ai = np.repeat(np.arange(M, dtype=np.float32)[:, None], K, axis=1)
+        Bj = np.repeat(np.arange(N, dtype=np.float32)[None, :], K, axis=0)
+        ref = K * np.outer(np.arange(M), np.arange(N)).astype(np.float64)
+        assert np.array_equal(o.gemm("f32", Ai, Bj), ref)
+
+
+def pin_identity_permutation(o):
+    """A*I = A and I*B = B bitwise; row/column permutations commute with the
+    product bitwise (same dot products in the same order); (A*B)^T = B^T*A^T
+    bitwise."""
+    rng = np.random.default_rng(104)
+    M, N, K = 13, 11, 17
+    A = (rng.random((M, K), dtype=np.float32) * 2 - 1).astype(np.float32)
+    B = (rng.random((K, N), dtype=np.float32) * 2 - 1).astype(np.float32)
+    assert np.array_equal(o.gemm("f32", A, np.eye(K, dtype=np.float32)), A.astype(np.float64))
+    assert np.array_equal(o.gemm("f32", np.eye(K, dtype=np.float32), B), B.astype(np.float64))
+    C = o.gemm("f32", A, B)
+    p = rng.permutation(M)
+    q = rng.permutation(N)
+    assert np.array_equal(_bits(o.gemm("f32", A[p], B)), _bits(C[p]))
+    assert np.array_equal(_bits(o.gemm("f32", A, B[:, q])), _bits(C[:, q]))
+    Ct = o.gemm("f32", np.ascontiguousarray(B.T), np.ascontiguousarray(A.T))
+    assert np.array_equal(_bits(Ct), _bits(np.ascontiguousarray(C.T)))
+    # Permuting the summation index: exact on integers, within the bound otherwise.
+    r = rng.permutation(K)
+    Ai = rng.integers(-7, 8, (M, K)).astype(np.float32)
+    Bi = rng.integers(-7, 8, (K, N)).astype(np.float32)
+    assert np.array_equal(o.gemm("f32", Ai[:, r], Bi[r, :]), o.gemm("f32", Ai, Bi))
+    Cr = o.gemm("f32", np.ascontiguousarray(A[:, r]), np.ascontiguousarray(B[r, :]))
+    assert np.max(np.abs(Cr - C)) <= 2 * K * 2.0 ** -53 * K
+
+
+def pin_associativity_linearity(o):
+    """Small integers keep every intermediate exact: (AB)C = A(BC) and
+    A(B1+B2) = AB1 + AB2 exactly."""
+    rng = np.random.default_rng(105)
+    A = rng.integers(-5, 6, (7, 9)).astype(np.float32)
+    B = rng.integers(-5, 6, (9, 6)).astype(np.float32)
+    Cm = rng.integers(-5, 6, (6, 8)).astype(np.float32)
+    AB = o.gemm("f32", A, B).astype(np.float32)
+    BC = o.gemm("f32", B, Cm).astype(np.float32)
+    assert np.array_equal(o.gemm("f32", AB, Cm), o.gemm("f32", A, BC))
+    B2 = rng.integers(-5, 6, (9, 6)).astype(np.float32)
+    lhs = o.gemm("f32", A, (B + B2).astype(np.float32))
+    assert np.array_equal(lhs, o.gemm("f32", A, B) + o.gemm("f32", A, B2))
+
+
+def pin_numpy_matmul(o):
+    """numpy's float64 BLAS product agrees within the FP64 error bound."""
+    rng = np.random.default_rng(106)
+    for (M, N, K) in [(64, 48, 200), (128, 128, 128), (1, 300, 77)]:
+        A = (rng.random((M, K), dtype=np.float32) * 2 - 1).astype(np.float32)
+        B = (rng.random((K, N), dtype=np.float32) * 2 - 1).astype(np.float32)
+        A64, B64 = A.astype(np.float64), B.astype(np.float64)
+        ref = A64 @ B64
+        bound = 2 * K * 2.0 ** -53 * (np.abs(A64) @ np.abs(B64))
+        assert np.all(np.abs(o.gemm("f32", A, B) - ref) <= bound)
+
+
+def pin_rows_points_consistent(o):
+    """Row slabs and single points are the same sums as the full product,
+    bit for bit, and independent of the thread count."""
+    rng = np.random.default_rng(107)
+    M, N, K = 37, 29, 71
+    A = (rng.random((M, K), dtype=np.float32) * 2 - 1).astype(np.float32)
+    B = (rng.random((K, N), dtype=np.float32) * 2 - 1).astype(np.float32)
+    C1 = o.gemm("f32", A, B, nthreads=1)
+    C8 = o.gemm("f32", A, B, nthreads=8)
+    assert np.array_equal(_bits(C1), _bits(C8))
+    assert np.array_equal(_bits(o.gemm_rows("f32", A, B, 5, 20)), _bits(C1[5:25]))
+    rows = rng.integers(0, M, 200)
+    cols = rng.integers(0, N, 200)
+    assert np.array_equal(_bits(o.gemm_points("f32", A, B, rows, cols)), _bits(C1[rows, cols]))
+
+
+def pin_degenerate(o):
+    """K = 0 gives +0 everywhere; M = 0 or N = 0 gives an empty result."""
+    z = o.gemm("f32", np.zeros((3, 0), np.float32), np.zeros((0, 4), np.float32))
+    assert z.shape == (3, 4) and np.array_equal(_bits(z), np.zeros((3, 4), np.uint64))
+    assert o.gemm("f32", np.zeros((0, 5), np.float32), np.ones((5, 4), np.float32)).shape == (0, 4)
+    assert o.gemm("f32", np.ones((2, 5), np.float32), np.ones((5, 0), np.float32)).shape == (2, 0)
+
+
+ALL_PINS = [pin_golden_small, pin_decode_table, pin_decode_library,
+            pin_bruteforce_ints, pin_bruteforce_16bit, pin_fsum_bound,
+            pin_closed_forms, pin_identity_permutation,
+            pin_associativity_linearity, pin_numpy_matmul,
+            pin_rows_points_consistent, pin_degenerate]

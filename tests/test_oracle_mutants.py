@@ -1,0 +1,48 @@
+"""Planted mistakes in copies of the oracle must each fail some pin (CPU only).
+
+Each mutant is a one-line textual change to a copy of ``oracle/oracle.c`` (a
+dropped term, a sign error, a wrong index, a wrong format constant, a wrong
+zero, a narrower accumulator), built into its own library under a temporary
+directory. The real oracle is never modified.
+"""
+import pytest
+
+import oracle
+from tests import pins
+
+MUTANTS = {
+    "drop_last_k": ("for (int64_t k = 0; k < K; ++k) {\n            const double a",
+                    "for (int64_t k = 0; k < K - 1; ++k) {\n            const double a"),
+    "sign_flip": ("acc[j] = acc[j] + a * brow[j]", "acc[j] = acc[j] - a * brow[j]"),
+    "reversed_k_in_A": ("const double a = load_val(dtype, A, i * K + k);",
+                        "const double a = load_val(dtype, A, i * K + (K - 1 - k));"),
+    "transposed_B_decode": ("Bd[k * N + j] = load_val(dtype, B, k * N + j);",
+                            "Bd[k * N + j] = load_val(dtype, B, (k * N + j) % K * N + (k * N + j) / K);"),
+    "bf16_bias": ("v = ldexp((double)(0x80 | f), e - 127 - 7);",
+                  "v = ldexp((double)(0x80 | f), e - 126 - 7);"),
+    "f16_subnormal_scale": ("v = ldexp((double)f, -14 - 10);", "v = ldexp((double)f, -15 - 10);"),
+    "f16_hidden_bit": ("v = ldexp((double)(0x400 | f), e - 15 - 10);",
+                       "v = ldexp((double)f, e - 15 - 10);"),
+    "negative_zero_start": ("acc[j] = 0.0;", "acc[j] = -0.0;"),
+    "float_point_accumulator": ("double s = 0.0;", "float s = 0.0f;"),
+    "points_column_reversed": ("load_val(dtype, B, k * N + j);\n        out[p]",
+                               "load_val(dtype, B, k * N + (N - 1 - j));\n        out[p]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = oracle.SRC.read_text()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    msrc = tmp_path / "oracle_mutant.c"
+    msrc.write_text(src.replace(old, new))
+    lib = oracle.build(src=msrc, out=tmp_path / "liboracle_mutant.so")
+    o = oracle.Oracle(lib)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught mutant {name}"
