@@ -1,0 +1,147 @@
+/*
+ * sam.h -- C ABI of the shape-adaptive GEMM library for MI355X (gfx950).
+ *
+ * Operation (page "Scale coverage exposes a remaining GEMM gap", section
+ * "Measurement contract and evidence"): C = A*B with compact row-major
+ * A[M][K], B[K][N], C[M][N] (leading dimensions K, N, N), alpha one, beta
+ * zero: C is write-only and its old contents are never read. Operands are
+ * FP32, or bfloat16 / IEEE binary16 passed as raw 16-bit patterns; products
+ * are accumulated in FP32 and C is always FP32 (the 16-bit operand runs of
+ * page "Measured data point on fixed-tile vs shape-adaptive GEMM", section
+ * "One more result that surprised us", there on other hardware).
+ *
+ * Shape adaptivity (same page, sections "The wall, and why we think it's
+ * structural" and "The actual question"; page "Post-mortem: a GPU stack
+ * without nvcc, cuBLAS, or LLVM", section 2.1): a dispatcher picks one of
+ * several macro-tile / schedule variants from (M, N, K, dtype) alone, through
+ * a frozen, source-controlled table. No timing happens at run time.
+ *
+ * Determinism (page "Measured data point ...", question 2; page
+ * "Post-mortem ...", section 7): no atomics anywhere; the K sum of every
+ * output runs in a fixed order per variant, and split-K partials are added
+ * in split order 0, 1, ..., S-1 by a separate kernel. The same (M, N, K,
+ * dtype) on the same library build gives the same plan and the same bits.
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers to operands, C and workspace are DEVICE pointers of the
+ *     current HIP device; `stream` is a hipStream_t (NULL = default stream).
+ *   - Calls are asynchronous: work is enqueued on `stream` and the call
+ *     returns. The library never synchronises the host and keeps no pointer
+ *     after returning; buffers must live until the stream work completes.
+ *   - The caller owns and allocates everything (A, B, C, workspace). The
+ *     library never allocates device memory on these paths.
+ *   - Errors found before enqueueing (arguments, workspace size, device,
+ *     launch) are returned as a negative sam_status; detail text is in
+ *     sam_last_error() (per thread). Faults inside kernels surface at the
+ *     caller's next synchronisation. No C++ exception crosses this ABI.
+ *   - Sizes: M, N, K >= 0. M == 0 or N == 0 is a no-op returning SAM_OK.
+ *     K == 0 writes +0.0f to every element of C. M*N, M*K and K*N must fit
+ *     in int64 and every index below 2^31 elements per operand.
+ *   - A, B, C, workspace base addresses must be 16-byte aligned, else
+ *     SAM_ERR_MISALIGNED. Odd K or N are fine: such shapes take load paths
+ *     that never form an unaligned vector address.
+ *   - C must not overlap A, B or the workspace (SAM_ERR_INVALID_ARG).
+ *   - Thread-safe: the variant table is immutable and module state is
+ *     initialised once.
+ */
+#ifndef SAM_H
+#define SAM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SAM_F32 = 0, SAM_BF16 = 1, SAM_F16 = 2 } sam_dtype;
+
+typedef enum {
+    SAM_OK = 0,
+    SAM_ERR_INVALID_ARG = -1,        /* bad size, null or overlapping pointer */
+    SAM_ERR_MISALIGNED = -2,         /* a base pointer not 16-byte aligned   */
+    SAM_ERR_WORKSPACE = -3,          /* workspace smaller than the plan needs */
+    SAM_ERR_UNSUPPORTED = -4,        /* forced variant cannot take this case  */
+    SAM_ERR_UNSUPPORTED_DEVICE = -5, /* no gfx950 device / kernels not loadable */
+    SAM_ERR_LAUNCH = -6,             /* the HIP runtime refused a launch      */
+    SAM_ERR_INTERNAL = -7
+} sam_status;
+
+/* One dispatch decision. Plain old data; struct_size is set by the library
+ * to sizeof(sam_plan) for ABI versioning. */
+typedef struct {
+    uint32_t struct_size;
+    int32_t variant_id;        /* stable index into the variant table        */
+    char name[64];             /* e.g. "f32_t256x256_w2x2_b32" + "_s4" ...    */
+    int32_t dtype;             /* sam_dtype                                   */
+    int32_t tile_m, tile_n, tile_k; /* macro tile; tile_k = K per LDS stage  */
+    int32_t waves_m, waves_n;  /* wave grid inside a workgroup               */
+    int32_t mfma_m;            /* MFMA block edge: 32 or 16                   */
+    int32_t split_k;           /* 1 = single pass; >1 = partials + ordered sum */
+    int32_t group_m;           /* grouped-raster height in tiles             */
+    int32_t xcd_remap;         /* 1 = workgroup ids remapped per XCD          */
+    int32_t a_vector, b_vector;/* 1 = 16-byte loads of A / B rows            */
+    int64_t grid_wgs;          /* workgroups of the main kernel              */
+    uint64_t workspace_bytes;  /* device workspace the call needs (0 if none) */
+    double est_us;             /* the dispatcher's cost estimate, microseconds */
+} sam_plan;
+
+/* The plan sam_gemm_<dtype> would run for this shape. Host only: touches no
+ * device state and needs no GPU. Returns SAM_ERR_INVALID_ARG for negative
+ * sizes or a null `out`. */
+sam_status sam_gemm_plan(int64_t M, int64_t N, int64_t K, sam_dtype dtype,
+                         sam_plan* out);
+
+/* C = A*B, FP32 operands. `workspace` may be NULL when the plan's
+ * workspace_bytes is 0; otherwise it must hold at least that many bytes
+ * (else SAM_ERR_WORKSPACE: the call never falls back to another plan). */
+sam_status sam_gemm_f32(const float* A, const float* B, float* C, int64_t M,
+                        int64_t N, int64_t K, void* workspace,
+                        uint64_t workspace_bytes, void* stream);
+
+/* C = A*B, bfloat16 operands as raw bit patterns, FP32 accumulate/output. */
+sam_status sam_gemm_bf16(const uint16_t* A, const uint16_t* B, float* C,
+                         int64_t M, int64_t N, int64_t K, void* workspace,
+                         uint64_t workspace_bytes, void* stream);
+
+/* C = A*B, IEEE binary16 operands as raw bit patterns, FP32 accumulate/out. */
+sam_status sam_gemm_f16(const uint16_t* A, const uint16_t* B, float* C,
+                        int64_t M, int64_t N, int64_t K, void* workspace,
+                        uint64_t workspace_bytes, void* stream);
+
+/* Number of entries in the variant table (ids 0 .. count-1). */
+int32_t sam_variant_count(void);
+
+/* Static description of variant `id` (no shape: split_k = 1, grid 0). */
+sam_status sam_variant_info(int32_t id, sam_plan* out);
+
+/* The plan for a forced variant and split. split_k = 0 lets the dispatcher
+ * pick the split for that variant. SAM_ERR_UNSUPPORTED if the variant does
+ * not take `dtype` or the split is not admissible for K. */
+sam_status sam_variant_plan(int32_t id, int64_t M, int64_t N, int64_t K,
+                            sam_dtype dtype, int32_t split_k, sam_plan* out);
+
+/* Run a forced variant (tests, profiling and calibration). Operands as for
+ * sam_gemm_<dtype> (16-bit ones as uint16_t patterns). */
+sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k,
+                            const void* A, const void* B, float* C, int64_t M,
+                            int64_t N, int64_t K, void* workspace,
+                            uint64_t workspace_bytes, void* stream);
+
+/* Checks once per process that the current device is gfx950 and that the
+ * library's kernels are loadable on it. SAM_ERR_UNSUPPORTED_DEVICE if not. */
+sam_status sam_device_check(void);
+
+/* Static text for a status code. */
+const char* sam_status_string(sam_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* sam_last_error(void);
+
+/* Build stamp: library version, git revision, ROCm/HIP version, target. */
+const char* sam_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAM_H */

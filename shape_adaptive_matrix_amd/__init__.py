@@ -1,0 +1,217 @@
+"""Python binding of the shape-adaptive GEMM library (``libsam.so``).
+
+Argument marshalling only: every step of C = A·B runs in the library's HIP
+kernels. PyTorch supplies device memory and the current stream; nothing here
+computes a product, and there is no CPU fallback — if the library is missing
+or the device is not gfx950 the call raises.
+
+The C ABI is declared in ``include/sam.h``; the names here follow it without
+the ``sam_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libsam.so"
+HEADER = PKG.parent / "include" / "sam.h"
+
+F32, BF16, F16 = 0, 1, 2
+DTYPES = {"f32": F32, "bf16": BF16, "f16": F16}
+DTYPE_NAMES = {v: k for k, v in DTYPES.items()}
+
+STATUS = {
+    0: "SAM_OK", -1: "SAM_ERR_INVALID_ARG", -2: "SAM_ERR_MISALIGNED",
+    -3: "SAM_ERR_WORKSPACE", -4: "SAM_ERR_UNSUPPORTED",
+    -5: "SAM_ERR_UNSUPPORTED_DEVICE", -6: "SAM_ERR_LAUNCH", -7: "SAM_ERR_INTERNAL",
+}
+
+
+class SamError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+class SamPlan(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("variant_id", ctypes.c_int32),
+        ("name", ctypes.c_char * 64), ("dtype", ctypes.c_int32),
+        ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+        ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32), ("mfma_m", ctypes.c_int32),
+        ("split_k", ctypes.c_int32), ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
+        ("a_vector", ctypes.c_int32), ("b_vector", ctypes.c_int32),
+        ("grid_wgs", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
+        ("est_us", ctypes.c_double),
+    ]
+
+    def as_dict(self) -> dict:
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["name"] = self.name.decode()
+        return d
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise ImportError(f"{LIB_PATH} is missing: run `python -m shape_adaptive_matrix_amd.build`")
+    L = ctypes.CDLL(str(LIB_PATH))
+    i64, u64, vp, i32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32
+    P = ctypes.POINTER(SamPlan)
+    sig = {
+        "sam_gemm_plan": ([i64, i64, i64, ctypes.c_int, P], ctypes.c_int),
+        "sam_gemm_f32": ([vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
+        "sam_gemm_bf16": ([vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
+        "sam_gemm_f16": ([vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
+        "sam_variant_count": ([], i32),
+        "sam_variant_info": ([i32, P], ctypes.c_int),
+        "sam_variant_plan": ([i32, i64, i64, i64, ctypes.c_int, i32, P], ctypes.c_int),
+        "sam_gemm_variant": ([i32, ctypes.c_int, i32, vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
+        "sam_device_check": ([], ctypes.c_int),
+        "sam_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "sam_last_error": ([], ctypes.c_char_p),
+        "sam_build_info": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def header_symbols() -> list[str]:
+    """Function names declared in include/sam.h."""
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sam_\w+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != 0:
+        raise SamError(status, lib().sam_last_error().decode())
+
+
+def _dt(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    return DTYPES[dtype]
+
+
+# -- host-only queries ---------------------------------------------------------
+def plan(M: int, N: int, K: int, dtype="f32") -> dict:
+    p = SamPlan()
+    _check(lib().sam_gemm_plan(M, N, K, _dt(dtype), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def variant_count() -> int:
+    return lib().sam_variant_count()
+
+
+def variant_info(vid: int) -> dict:
+    p = SamPlan()
+    _check(lib().sam_variant_info(vid, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def variant_plan(vid: int, M: int, N: int, K: int, dtype="f32", split_k: int = 0) -> dict:
+    p = SamPlan()
+    _check(lib().sam_variant_plan(vid, M, N, K, _dt(dtype), split_k, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def build_info() -> str:
+    return lib().sam_build_info().decode()
+
+
+def device_check() -> None:
+    _check(lib().sam_device_check())
+
+
+def last_error() -> str:
+    return lib().sam_last_error().decode()
+
+
+# -- device calls (torch tensors for memory and streams) ------------------------
+def _torch_dtype_code(t, dtype):
+    import torch
+    if dtype is not None:
+        return _dt(dtype)
+    m = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+    if t.dtype not in m:
+        raise TypeError(f"pass dtype= for operands of type {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else None
+
+
+def _operands(A, B, dtype):
+    code = _torch_dtype_code(A, dtype)
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"bad shapes {tuple(A.shape)} x {tuple(B.shape)}")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous row-major")
+    want = 4 if code == F32 else 2
+    if A.element_size() != want or B.element_size() != want:
+        raise TypeError("operand element size does not match the dtype")
+    return code
+
+
+def workspace_for(plan_dict: dict, device):
+    import torch
+    n = int(plan_dict["workspace_bytes"])
+    if n == 0:
+        return None
+    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
+
+
+def gemm(A, B, C=None, dtype=None, workspace=None, stream=None):
+    """C = A·B on the tensors' device through the dispatcher; returns C (FP32)."""
+    import torch
+    code = _operands(A, B, dtype)
+    M, K = A.shape
+    N = B.shape[1]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    p = plan(M, N, K, code)
+    if workspace is None:
+        workspace = workspace_for(p, A.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    fn = {F32: lib().sam_gemm_f32, BF16: lib().sam_gemm_bf16, F16: lib().sam_gemm_f16}[code]
+    _check(fn(_ptr(A), _ptr(B), _ptr(C), M, N, K, _ptr(workspace), ws_bytes, _stream_ptr(stream)))
+    return C
+
+
+def gemm_variant(vid: int, A, B, C=None, split_k: int = 0, dtype=None, workspace=None, stream=None):
+    """C = A·B with a forced variant (and split; 0 = the variant's own pick)."""
+    import torch
+    code = _operands(A, B, dtype)
+    M, K = A.shape
+    N = B.shape[1]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    p = variant_plan(vid, M, N, K, code, split_k)
+    if workspace is None:
+        workspace = workspace_for(p, A.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sam_gemm_variant(vid, code, p["split_k"], _ptr(A), _ptr(B), _ptr(C), M, N, K,
+                                  _ptr(workspace), ws_bytes, _stream_ptr(stream)))
+    return C

@@ -1,0 +1,88 @@
+// Internal declarations shared by the dispatcher, the kernels and the C ABI.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace sam {
+
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// Fixed facts of one MI355X (gfx950) used by the cost model. They are frozen
+// here rather than queried so that a plan is a pure function of the shape.
+struct DeviceModel {
+    int cus = 256;                 // 8 XCDs x 32 CUs
+    int xcds = 8;
+    int lds_bytes = 160 * 1024;    // LDS per CU
+    double clock_ghz = 2.4;
+    double f32_flop_per_clk_cu = 256.0;    // 4 SIMDs x 64 (32x32x2 f32 in 64 clk)
+    double h16_flop_per_clk_cu = 4096.0;   // 4 SIMDs x 1024
+    double hbm_gbs = 8000.0;
+    double l2_gbs = 20000.0;       // aggregate L2/MALL delivery, rough
+    double launch_us = 4.0;        // per kernel launch, rough
+};
+
+// Static description of a tile/schedule variant.
+struct Variant {
+    int id;
+    const char* name;
+    int dtype_mask;      // bit (1 << Dt)
+    int bm, bn;          // macro tile
+    int wm, wn;          // wave grid
+    int blk;             // MFMA block edge (32 or 16)
+    int group_m;         // grouped raster height (tiles)
+    int xcd_remap;       // 1: remap workgroup ids so each XCD gets a contiguous range
+    int max_split;       // largest split-K the variant is planned with
+    double eff;          // calibrated fraction of MFMA peak it sustains in steady state
+};
+
+int variant_count();
+const Variant* variant_get(int id);
+
+// Arguments of one main-kernel launch.
+struct GemmArgs {
+    const void* A;
+    const void* B;
+    float* out;          // C when split == 1, else workspace partials [split][M][N]
+    int M, N, K;
+    int k_chunk;         // K range per split, a multiple of the LDS K-stage
+    int split;
+    int tiles_m, tiles_n;
+    int group_m;
+    int xcd_remap;
+    long long part_stride;  // M*N (elements between consecutive partials)
+};
+
+// Fully resolved plan (internal form of sam_plan).
+struct Plan {
+    int variant_id;
+    int dtype;
+    int bm, bn, bk;
+    int wm, wn, blk;
+    int split;
+    int k_chunk;
+    int group_m;
+    int xcd_remap;
+    int a_vec, b_vec;
+    int tiles_m, tiles_n;
+    long long grid;
+    unsigned long long ws_bytes;
+    double est_us;
+};
+
+// Dispatcher (sam_plan.cpp). Host only, pure.
+bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
+                      int split_req, Plan* out);
+bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out);
+void plan_name(const Plan& p, char* buf, int n);
+int k_stage(int dtype);   // K per LDS stage: 128 bytes of one row
+
+// Kernel launchers (sam_kernels.hip). Return hipSuccess or the launch error.
+hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_reduce(const float* parts, int split, long long part_stride,
+                         float* C, long long count, hipStream_t s);
+hipError_t launch_zero(float* C, long long count, hipStream_t s);
+// A representative kernel symbol for loadability checks.
+const void* probe_kernel();
+
+}  // namespace sam

@@ -1,0 +1,194 @@
+// Dispatcher: (M, N, K, dtype) -> variant, split-K and launch geometry.
+//
+// The point of the pages (page "Measured data point on fixed-tile vs
+// shape-adaptive GEMM", section "The wall, and why we think it's
+// structural"; page "Post-mortem: a GPU stack without nvcc, cuBLAS, or
+// LLVM", section 2.1): one fixed tile reaches parity in one shape band and
+// loses elsewhere, so the library carries several tiles/schedules and a
+// selector. This selector is a pure function over a frozen table:
+//
+//  * Admission (page "Scale coverage exposes a remaining GEMM gap", section
+//    "Why the fixed view request rejects tails": candidates are admitted only
+//    within the target's local-memory limits, and a tail never silently
+//    swaps in another block): a variant is admitted for a dtype when its
+//    double-buffered LDS stages fit the CU's 160 KB, and a split is admitted
+//    only when every split owns at least one K stage. Tails are handled
+//    inside every variant, so no shape is rejected.
+//  * Score = estimated time. Tiles are counted in waves of workgroups over
+//    the 256 CUs (wave quantisation, the tile-count argument of page
+//    "fix(fp4_gemm autotune) SM107 kernel family excluded...", section "Swap
+//    microbenchmarks across M, N, and K"), each workgroup costing its MFMA
+//    work at the variant's calibrated efficiency; the estimate is the larger
+//    of that and the HBM / L2 transfer time, plus the split-K reduce pass.
+//  * Ties go to the lowest variant id, so list order can never leak into the
+//    choice through an unstable sort (the tie-break problem raised in the
+//    review of that same page).
+// No timing at run time: the same shape always gets the same plan.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sam_internal.h"
+#include "sam_variants.h"
+
+namespace sam {
+
+#define SAM_VARIANT_ROW(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16) \
+    {id, name, 7, BM, BN, WM, WN, BLK, gm, xr, ms, 0.0},
+
+static const Variant kVariants[] = {SAM_VARIANT_LIST(SAM_VARIANT_ROW)};
+
+#define SAM_VARIANT_EFF(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16) {e32, e16},
+static const double kEff[][2] = {SAM_VARIANT_LIST(SAM_VARIANT_EFF)};
+
+static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+
+int variant_count() { return kVariantCount; }
+
+const Variant* variant_get(int id)
+{
+    return (id >= 0 && id < kVariantCount) ? &kVariants[id] : nullptr;
+}
+
+int k_stage(int dtype) { return dtype == DT_F32 ? 32 : 64; }
+
+static int vec_elems(int dtype) { return dtype == DT_F32 ? 4 : 8; }
+
+static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+static const DeviceModel kDev;
+
+static double estimate_us(const Variant& v, long long M, long long N, long long K, int dtype,
+                          int split, int a_vec, int b_vec)
+{
+    const int bk = k_stage(dtype);
+    const long long nkb = cdiv(K, bk);
+    const long long kc = cdiv(nkb, split) * bk;               // K per split, padded
+    const long long tiles_m = cdiv(M, v.bm), tiles_n = cdiv(N, v.bn);
+    const long long wgs = tiles_m * tiles_n * split;
+    const double in_b = dtype == DT_F32 ? 4.0 : 2.0;
+
+    double eff = kEff[v.id][dtype == DT_F32 ? 0 : 1];
+    if (!a_vec) eff *= 0.85;
+    if (!b_vec) eff *= 0.85;
+    const double peak_cu = (dtype == DT_F32 ? kDev.f32_flop_per_clk_cu : kDev.h16_flop_per_clk_cu) *
+                           kDev.clock_ghz * 1e3;              // FLOP per microsecond
+    const double t_wg = 2.0 * v.bm * v.bn * (double)kc / (peak_cu * eff);
+    const double rounds = (double)cdiv(wgs, kDev.cus);
+    const double t_mfma = rounds * t_wg;
+
+    const double mb = 1e-6;                                   // bytes -> MB; GB/s = MB/ms
+    const double alg = in_b * (double)(M * K + K * N) + 4.0 * (double)(M * N);
+    const double part = split > 1 ? 4.0 * (double)(M * N) * split : 0.0;
+    const double t_hbm = (alg + part) * mb / kDev.hbm_gbs * 1e3;
+    const double tile_traffic = in_b * ((double)M * K * tiles_n + (double)K * N * tiles_m);
+    const double t_l2 = tile_traffic * mb / kDev.l2_gbs * 1e3;
+
+    double t = fmax(t_mfma, fmax(t_hbm, t_l2)) + kDev.launch_us;
+    if (split > 1) t += (part + 4.0 * M * N) * mb / kDev.hbm_gbs * 1e3 + kDev.launch_us;
+    return t;
+}
+
+static bool split_admissible(long long K, int dtype, int split)
+{
+    if (split < 1) return false;
+    if (split == 1) return true;
+    const long long nkb = cdiv(K, k_stage(dtype));
+    if (split > nkb) return false;
+    const long long per = cdiv(nkb, split);
+    return cdiv(nkb, per) == split;                           // no empty split
+}
+
+static void fill_plan(const Variant& v, long long M, long long N, long long K, int dtype, int split,
+                      Plan* p)
+{
+    const int bk = k_stage(dtype);
+    const int ve = vec_elems(dtype);
+    p->variant_id = v.id;
+    p->dtype = dtype;
+    p->bm = v.bm;
+    p->bn = v.bn;
+    p->bk = bk;
+    p->wm = v.wm;
+    p->wn = v.wn;
+    p->blk = v.blk;
+    p->split = split;
+    p->k_chunk = (int)(cdiv(cdiv(K, bk), split) * bk);
+    p->group_m = v.group_m;
+    p->xcd_remap = v.xcd_remap;
+    p->a_vec = (K % ve) == 0;
+    p->b_vec = (N % ve) == 0;
+    p->tiles_m = (int)cdiv(M, v.bm);
+    p->tiles_n = (int)cdiv(N, v.bn);
+    p->grid = (long long)p->tiles_m * p->tiles_n * split;
+    p->ws_bytes = split > 1 ? (unsigned long long)split * (unsigned long long)(M * N) * 4ull : 0ull;
+    p->est_us = estimate_us(v, M, N, K, dtype, split, p->a_vec, p->b_vec);
+}
+
+static const int kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+
+// Split-K is for filling the machine when there are fewer output tiles than
+// CUs, not for smoothing wave quantisation of large grids; and its partials
+// must stay a modest multiple of C.
+static const unsigned long long kMaxWorkspace = 512ull << 20;
+
+static bool split_wanted(const Plan& p)
+{
+    if (p.split == 1) return true;
+    return (long long)p.tiles_m * p.tiles_n < kDev.cus && p.ws_bytes <= kMaxWorkspace;
+}
+
+bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype, int split_req,
+                      Plan* out)
+{
+    const Variant* v = variant_get(vid);
+    if (!v || dtype < DT_F32 || dtype > DT_F16 || !(v->dtype_mask & (1 << dtype))) return false;
+    if (2 * (v->bm + v->bn) * 128 > kDev.lds_bytes) return false;
+    if (M < 0 || N < 0 || K < 0) return false;
+    if (split_req > 0) {
+        if (split_req > 1 && (K == 0 || !split_admissible(K, dtype, split_req))) return false;
+        fill_plan(*v, M, N, K, dtype, split_req, out);
+        return out->grid < (1ll << 31);
+    }
+    bool found = false;
+    Plan best{};
+    for (int s : kSplits) {
+        if (s > v->max_split) break;
+        if (s > 1 && (K == 0 || !split_admissible(K, dtype, s))) continue;
+        Plan p{};
+        fill_plan(*v, M, N, K, dtype, s, &p);
+        if (p.grid >= (1ll << 31) || !split_wanted(p)) continue;
+        if (!found || p.est_us < best.est_us) {
+            best = p;
+            found = true;
+        }
+    }
+    if (found) *out = best;
+    return found;
+}
+
+bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out)
+{
+    bool found = false;
+    Plan best{};
+    for (int id = 0; id < kVariantCount; ++id) {
+        Plan p{};
+        if (!plan_for_variant(id, M, N, K, dtype, 0, &p)) continue;
+        if (!found || p.est_us < best.est_us) {   // strict: ties keep the lower id
+            best = p;
+            found = true;
+        }
+    }
+    if (found) *out = best;
+    return found;
+}
+
+void plan_name(const Plan& p, char* buf, int n)
+{
+    static const char* dt[] = {"f32", "bf16", "f16"};
+    const Variant* v = variant_get(p.variant_id);
+    snprintf(buf, n, "%s_%s_s%d%s%s", dt[p.dtype], v ? v->name : "?", p.split,
+             p.a_vec ? "" : "_ua", p.b_vec ? "" : "_ub");
+}
+
+}  // namespace sam

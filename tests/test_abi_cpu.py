@@ -1,0 +1,158 @@
+"""The C ABI and the dispatcher without a GPU: the library loads, exports
+every symbol the header declares, plans are pure and deterministic, the
+automatic choice is the audited minimum, and bad calls are rejected before
+any device work."""
+import ctypes
+import subprocess
+
+import pytest
+
+import shape_adaptive_matrix_amd as sam
+
+L = sam.lib()
+
+
+def test_exports_every_header_symbol():
+    names = sam.header_symbols()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", str(sam.LIB_PATH)],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(L, n)
+
+
+def test_plan_struct_abi():
+    p = sam.SamPlan()
+    assert L.sam_gemm_plan(64, 64, 64, sam.F32, ctypes.byref(p)) == 0
+    assert p.struct_size == ctypes.sizeof(sam.SamPlan)
+
+
+def test_build_stamp_names_target():
+    info = sam.build_info()
+    assert "gfx950" in info and "git=" in info
+
+
+def test_status_strings():
+    for code, name in sam.STATUS.items():
+        assert L.sam_status_string(code).decode() == name
+
+
+SHAPES = [(256, 256, 256), (2048, 2048, 2048), (4096, 4096, 4096), (8192, 8192, 8192),
+          (768, 768, 768), (4097, 3071, 8191), (8191, 8193, 4096), (16, 8192, 8192),
+          (8192, 16, 8192), (8192, 8192, 64), (1, 1, 1), (3, 5, 7)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=str)
+def test_plan_is_audited_argmin(shape, dtype):
+    """The automatic plan is the minimum estimate over every admissible
+    variant, ties to the lowest id, and asking twice gives the same plan."""
+    M, N, K = shape
+    p = sam.plan(M, N, K, dtype)
+    assert p == sam.plan(M, N, K, dtype)
+    best = None
+    for vid in range(sam.variant_count()):
+        try:
+            q = sam.variant_plan(vid, M, N, K, dtype, 0)
+        except sam.SamError:
+            continue
+        if best is None or q["est_us"] < best["est_us"]:
+            best = q
+    assert best is not None
+    assert p["variant_id"] == best["variant_id"]
+    assert p["split_k"] == best["split_k"]
+    assert p["grid_wgs"] == -(-M // p["tile_m"]) * -(-N // p["tile_n"]) * p["split_k"]
+    if p["split_k"] > 1:
+        assert p["workspace_bytes"] == p["split_k"] * M * N * 4
+    else:
+        assert p["workspace_bytes"] == 0
+
+
+def test_large_d_picks_other_tile_than_2048():
+    """Wave quantisation on 256 CUs makes the 2048 and 4096/8192 choices differ."""
+    p2 = sam.plan(2048, 2048, 2048, "f32")
+    for d in (4096, 8192):
+        pd = sam.plan(d, d, d, "f32")
+        assert (pd["variant_id"], pd["split_k"]) != (p2["variant_id"], p2["split_k"])
+
+
+def test_alignment_routes():
+    assert sam.plan(4097, 3071, 8191, "f32")["a_vector"] == 0
+    assert sam.plan(4097, 3071, 8191, "f32")["b_vector"] == 0
+    p = sam.plan(8191, 8193, 4096, "f32")
+    assert p["a_vector"] == 1 and p["b_vector"] == 0
+    p = sam.plan(64, 64, 68, "bf16")
+    assert p["a_vector"] == 0 and p["b_vector"] == 1
+
+
+def test_variant_table():
+    n = sam.variant_count()
+    assert n >= 5
+    seen = set()
+    for vid in range(n):
+        v = sam.variant_info(vid)
+        assert v["variant_id"] == vid and v["name"] not in seen
+        seen.add(v["name"])
+        assert v["tile_m"] % v["mfma_m"] == 0 and v["tile_n"] % v["mfma_m"] == 0
+    with pytest.raises(sam.SamError) as e:
+        sam.variant_info(n)
+    assert e.value.status == -1
+
+
+def test_forced_split_admission():
+    # K = 64 FP32 is two stages of 32: split 2 is fine, split 3 would leave one empty.
+    assert sam.variant_plan(1, 256, 256, 64, "f32", 2)["split_k"] == 2
+    with pytest.raises(sam.SamError) as e:
+        sam.variant_plan(1, 256, 256, 64, "f32", 3)
+    assert e.value.status == -4
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4), -1), ((4, -1, 4), -1), ((4, 4, -1), -1), ((1 << 31, 4, 4), -1),
+])
+def test_plan_rejects_bad_sizes(args, code):
+    p = sam.SamPlan()
+    assert L.sam_gemm_plan(*args, sam.F32, ctypes.byref(p)) == code
+    assert L.sam_gemm_plan(4, 4, 4, 7, ctypes.byref(p)) == -1
+    assert L.sam_gemm_plan(4, 4, 4, sam.F32, None) == -1
+
+
+# Fake, never dereferenced device addresses: every call below must be
+# rejected by the host checks before any HIP call.
+A_, B_, C_, W_ = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def _call(A, B, C, M, N, K, ws=None, wsb=0, fn="sam_gemm_f32"):
+    return getattr(L, fn)(A, B, C, M, N, K, ws, wsb, None)
+
+
+def test_rejects_before_device():
+    assert _call(A_, B_, C_, -1, 4, 4) == -1
+    assert _call(A_, B_, None, 4, 4, 4) == -1                  # null C
+    assert _call(None, B_, C_, 4, 4, 4) == -1                  # null A with K > 0
+    assert _call(A_ + 4, B_, C_, 4, 4, 4) == -2                # misaligned A
+    assert _call(A_, B_, C_ + 8, 4, 4, 4, fn="sam_gemm_bf16") == -2
+    assert _call(A_, B_, A_ + 16, 4, 4, 4) == -1               # C overlaps A
+    assert "overlap" in sam.last_error()
+    # 16 x 8192 x 8192 plans a split: workspace missing or short
+    p = sam.plan(16, 8192, 8192, "f32")
+    assert p["workspace_bytes"] > 0
+    assert _call(A_, B_, C_, 16, 8192, 8192) == -3
+    assert _call(A_, B_, C_, 16, 8192, 8192, W_, p["workspace_bytes"] - 4) == -3
+
+
+def test_empty_outputs_are_noops():
+    # M == 0 or N == 0: nothing to do, nothing touched, even with null pointers.
+    assert _call(None, None, None, 0, 5, 5) == 0
+    assert _call(None, None, None, 5, 0, 5) == 0
+
+
+def test_no_gpu_is_reported_not_hidden():
+    """Without a usable gfx950 device a well-formed call fails loudly."""
+    if L.sam_device_check() == 0:
+        pytest.skip("a gfx950 device is present")
+    assert _call(A_, B_, C_, 64, 64, 64) == -5
+    assert sam.last_error()

@@ -1,0 +1,173 @@
+"""Parity of the HIP path with the oracle on an MI355X (gfx950).
+
+Every call goes through the C ABI (the ctypes binding). Dyadic inputs must
+match bit for bit; random inputs must meet the rel_rms bound of the
+workload; repeated runs must be bitwise identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sam_inputs as si
+import shape_adaptive_matrix_amd as sam
+from tests.compare import bitexact_mismatches, rel_rms
+from tests.gpu_util import ints_operands, run, to_dev
+
+pytestmark = pytest.mark.gpu
+
+ORC = None
+
+
+def orc():
+    global ORC
+    if ORC is None:
+        ORC = oracle.get()
+    return ORC
+
+
+def test_device_is_gfx950():
+    sam.device_check()
+    assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+
+
+RAGGED = [(1, 1, 1), (17, 33, 45), (64, 64, 64), (70, 130, 100), (129, 257, 200), (16, 300, 96),
+          (300, 16, 96), (256, 256, 256)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("vid", range(7))
+def test_every_variant_dyadic_ragged(vid, dtype):
+    """Each variant, forced, on ragged shapes with small integers: the sums
+    are exact, so the bits must equal the oracle's."""
+    for (M, N, K) in RAGGED:
+        A, B = ints_operands(M, N, K, dtype, seed=M * 7 + N * 3 + K)
+        ref = orc().gemm(dtype, A, B)
+        splits = [0, 1] + [s for s in (2, 3) if s * sam.variant_plan(vid, M, N, K, dtype, 1)["tile_k"] <= K]
+        for s in splits:
+            try:
+                sam.variant_plan(vid, M, N, K, dtype, s)
+            except sam.SamError:
+                continue
+            C = run(A, B, dtype, variant=vid, split=s)
+            bad = bitexact_mismatches(C, ref)
+            assert bad == 0, f"variant {vid} {dtype} {(M, N, K)} split {s}: {bad} mismatches"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("vid", range(7))
+def test_every_variant_random(vid, dtype):
+    M, N, K = 150, 170, 333
+    rng = np.random.default_rng(vid + 40)
+    if dtype == "f32":
+        A, B = si.uniform_pm1(rng, (M, K)), si.uniform_pm1(rng, (K, N))
+        tol = 1e-5
+    else:
+        A, B = si.normal16(rng, (M, K), dtype), si.normal16(rng, (K, N), dtype)
+        tol = 1e-5   # exact products, FP32 accumulation: far below the 1e-2 gate
+    ref = orc().gemm(dtype, A, B)
+    C = run(A, B, dtype, variant=vid)
+    assert rel_rms(C, ref) <= tol
+
+
+def test_c_is_write_only_and_fully_written():
+    """NaN-prefilled C: every element written; guard band after C untouched."""
+    M, N, K = 99, 77, 55
+    A, B = ints_operands(M, N, K, "f32", seed=3)
+    ref = orc().gemm("f32", A, B)
+    guard = 4096
+    buf = torch.full((M * N + guard,), float("nan"), dtype=torch.float32, device="cuda")
+    buf[M * N:] = 12345.0
+    C = buf[:M * N].view(M, N)
+    for vid in range(sam.variant_count()):
+        buf[:M * N] = float("nan")
+        sam.gemm_variant(vid, to_dev(A, "f32"), to_dev(B, "f32"), C)
+        torch.cuda.synchronize()
+        out = buf.cpu().numpy()
+        assert bitexact_mismatches(out[:M * N].reshape(M, N), ref) == 0, vid
+        assert np.all(out[M * N:] == 12345.0), vid
+
+
+def test_k_zero_writes_positive_zero():
+    C = torch.full((33, 65), float("nan"), device="cuda")
+    A = torch.empty((33, 0), device="cuda")
+    B = torch.empty((0, 65), device="cuda")
+    sam.gemm(A, B, C)
+    torch.cuda.synchronize()
+    assert np.all(C.cpu().numpy().view(np.uint32) == 0)
+
+
+def test_inf_beyond_k_tail_is_not_read():
+    """An Inf just past row i's K range in memory must not leak into C: the K
+    tail is zero-filled on both operands."""
+    M, N, K = 64, 64, 37
+    store = np.zeros((M * K + 64,), np.float32)
+    A = store[:M * K].reshape(M, K)
+    A[:] = 1.0
+    store[M * K:] = np.inf
+    B = np.ones((K, N), np.float32)
+    dstore = torch.from_numpy(store).cuda()
+    dA = dstore[:M * K].view(M, K)
+    for vid in range(sam.variant_count()):
+        C = sam.gemm_variant(vid, dA, to_dev(B, "f32"))
+        torch.cuda.synchronize()
+        assert np.all(C.cpu().numpy() == K), vid
+
+
+# -- the workloads at their real sizes ------------------------------------------------
+def _check_workload(w, C):
+    A, B = si.make_operands(w)
+    M, N = w.M, w.N
+    o = orc()
+    if w.M * w.N * w.K <= 2048 ** 3:
+        ref = o.gemm(w.dtype, A, B)
+        got = C
+    else:
+        # A slab of leading and trailing rows plus sampled points (corners and
+        # tail-adjacent elements included).
+        rows = min(32, M)
+        top = o.gemm_rows(w.dtype, A, B, 0, rows)
+        bot = o.gemm_rows(w.dtype, A, B, M - rows, rows)
+        r, c = si.sample_points(M, N, 4096, seed=w.seed + 7)
+        pts = o.gemm_points(w.dtype, A, B, r, c)
+        ref = np.concatenate([top.ravel(), bot.ravel(), pts])
+        got = np.concatenate([C[:rows].ravel(), C[M - rows:].ravel(), C[r, c]])
+    if w.check == "bitexact":
+        assert bitexact_mismatches(got, ref) == 0
+    else:
+        e = rel_rms(got, ref)
+        assert e <= w.tol, e
+        if w.dtype != "f32":
+            # FP32 accumulation of exact products: anything near the 1e-2 gate
+            # would mean a reduced-precision output or accumulator.
+            assert e <= 1e-4, e
+
+
+@pytest.mark.parametrize("name", [w.name for w in si.WORKLOADS])
+def test_workload_parity(name):
+    w = si.by_name(name)
+    A, B = si.make_operands(w)
+    print(f"[parity] {name} plan={sam.plan(w.M, w.N, w.K, w.dtype)['name']}", flush=True)
+    C = run(A, B, w.dtype)
+    _check_workload(w, C)
+
+
+@pytest.mark.parametrize("name", ["f32_2048", "bf16_4096", "f32_16x8192x8192", "f32_768"])
+def test_run_to_run_bitwise(name):
+    """Five runs give identical bytes; a different seed gives different bytes
+    (so the equality is not vacuous)."""
+    w = si.by_name(name)
+    A, B = si.make_operands(w)
+    dA, dB = to_dev(A, w.dtype), to_dev(B, w.dtype)
+    outs = []
+    for _ in range(5):
+        C = torch.full((w.M, w.N), float("nan"), device="cuda")
+        sam.gemm(dA, dB, C)
+        torch.cuda.synchronize()
+        outs.append(C.cpu().numpy().view(np.uint32).copy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    A2, B2 = si.make_operands(w, seed=w.seed + 1000)
+    C2 = sam.gemm(to_dev(A2, w.dtype), to_dev(B2, w.dtype))
+    torch.cuda.synchronize()
+    assert not np.array_equal(C2.cpu().numpy().view(np.uint32), outs[0])
