@@ -45,22 +45,24 @@ template <> struct Acc<32> { typedef v16f T; static constexpr int N = 16; };
 template <> struct Acc<16> { typedef v4f T; static constexpr int N = 4; };
 
 // One MFMA on element e of a 16-byte chunk (FP32: four steps per chunk;
-// 16-bit: the chunk is the whole 8-element operand).
+// 16-bit: the chunk is the whole 8-element operand). FP32 elements are taken
+// with __uint_as_float: this compiler turned __builtin_bit_cast of a vector
+// element into element 0 for every E.
 template <int DT, int BLK> struct Mfma;
 template <> struct Mfma<DT_F32, 32> {
     static constexpr int PER_CHUNK = 4;
     template <int E>
     static __device__ __forceinline__ void run(v16f& c, const u4& a, const u4& b) {
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[E]),
-                                                 __builtin_bit_cast(float, b[E]), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[E]),
+                                                 __uint_as_float(b[E]), c, 0, 0, 0);
     }
 };
 template <> struct Mfma<DT_F32, 16> {
     static constexpr int PER_CHUNK = 4;
     template <int E>
     static __device__ __forceinline__ void run(v4f& c, const u4& a, const u4& b) {
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a[E]),
-                                                 __builtin_bit_cast(float, b[E]), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[E]),
+                                                 __uint_as_float(b[E]), c, 0, 0, 0);
     }
 };
 template <> struct Mfma<DT_BF16, 32> {
