@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Throughput of C = A·B on one MI355X through the library's C ABI.
+
+One step = one GEMM call (dispatcher, main kernel, and the split-K reduce
+when the plan has one) on resident device operands. The headline workload is
+FP32 M = N = K = 2048 (uniform [-1, 1) from seed 2); ``--workload`` picks
+another from the table in ``sam_inputs``. After the headline line's timing,
+``--sweep`` (default on) times every workload with the batch protocol of
+page "Scale coverage exposes a remaining GEMM gap" (section "GEMM: frozen
+schedules at larger dimensions": warmup, several rounds of batched launches,
+median of round medians), plus a cold-cache single-launch time for the
+HBM-bound skinny shapes.
+
+Prints one JSON line (rank 0, N = 1 only: this path runs on one GPU).
+
+The CPU baseline leg times the oracle (test infrastructure, double precision,
+as it stands) on a bounded slab of rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense MFMA, 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+
+def src_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "shape_adaptive_matrix_amd" / "csrc").iterdir()):
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def prepare(w, torch, sam, si, variant=None, split=0):
+    A, B = si.make_operands(w)
+    if w.dtype == "f32":
+        dA = torch.from_numpy(A).cuda()
+        dB = torch.from_numpy(B).cuda()
+    else:
+        t = {"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+        dA = torch.from_numpy(A.view("int16")).cuda().view(t)
+        dB = torch.from_numpy(B.view("int16")).cuda().view(t)
+    del A, B
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    if variant is None:
+        plan = sam.plan(w.M, w.N, w.K, w.dtype)
+    else:
+        plan = sam.variant_plan(variant, w.M, w.N, w.K, w.dtype, split)
+    ws = sam.workspace_for(plan, dA.device)
+    L = sam.lib()
+    stream = torch.cuda.current_stream()
+    args = (ctypes.c_void_p(dA.data_ptr()), ctypes.c_void_p(dB.data_ptr()), ctypes.c_void_p(C.data_ptr()),
+            w.M, w.N, w.K, ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
+            ws.numel() * 4 if ws is not None else 0, ctypes.c_void_p(stream.cuda_stream))
+    if variant is None:
+        fn = {"f32": L.sam_gemm_f32, "bf16": L.sam_gemm_bf16, "f16": L.sam_gemm_f16}[w.dtype]
+    else:
+        forced = L.sam_gemm_variant
+        code = sam.DTYPES[w.dtype]
+
+        def fn(*a):
+            return forced(variant, code, plan["split_k"], *a)
+
+    def step():
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"{sam.STATUS.get(rc, rc)}: {sam.last_error()}")
+
+    return {"step": step, "plan": plan, "keep": (dA, dB, C, ws), "stream": stream}
+
+
+def time_steps(torch, step, steps: int) -> float:
+    """Milliseconds for `steps` back-to-back calls, HIP events on the stream the
+    kernels run on (torch's current stream, which the calls are given)."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        step()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e)
+
+
+def sweep(torch, sam, si, rounds: int = 5):
+    """Every workload: median over rounds of the per-launch time of a batch
+    lasting >= 20 ms; cold-cache single launches for the skinny shapes."""
+    out = []
+    flush = None
+    for w in si.WORKLOADS:
+        g = prepare(w, torch, sam, si)
+        step = g["step"]
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        one = time_steps(torch, step, 3) / 3
+        n = max(3, math.ceil(20.0 / max(one, 1e-3)))
+        meds = []
+        for _ in range(rounds):
+            samples = [time_steps(torch, step, n) / n for _ in range(5)]
+            meds.append(statistics.median(samples))
+        t_ms = statistics.median(meds)
+        rec = {
+            "workload": w.name, "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
+            "plan": g["plan"]["name"], "ms": round(t_ms, 5),
+            "ms_range": [round(min(meds), 5), round(max(meds), 5)],
+            "tflops": round(w.flops / t_ms / 1e9, 2),
+            "pct_mfma_peak": round(100 * w.flops / t_ms / 1e9 / PEAK_TFLOPS[w.dtype], 1),
+            "alg_gbs": round(w.alg_bytes / t_ms / 1e6, 1),
+        }
+        if min(w.M, w.N) <= 16:
+            if flush is None:
+                flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+            cold = []
+            for _ in range(20):
+                flush.fill_(1.0)
+                cold.append(time_steps(torch, step, 1))
+            c_ms = statistics.median(cold)
+            rec["cold_ms"] = round(c_ms, 5)
+            rec["cold_alg_gbs"] = round(w.alg_bytes / c_ms / 1e6, 1)
+            rec["cold_pct_hbm"] = round(100 * w.alg_bytes / c_ms / 1e6 / PEAK_HBM_GBS, 1)
+        out.append(rec)
+        del g
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w, si, seconds: float):
+    """The oracle (as it stands) on a bounded sample of the workload: a slab of
+    rows sized to take about `seconds` on the host cores, or the whole product
+    repeated until that long when the whole product is quicker."""
+    import oracle
+    o = oracle.get()
+    A, B = si.make_operands(w)
+    threads = o.max_threads()
+    rows = max(1, min(w.M, 16))
+    t0 = time.perf_counter()
+    o.gemm_rows(w.dtype, A, B, 0, rows)
+    t = time.perf_counter() - t0
+    target = max(1, min(w.M, int(rows * seconds / max(t, 1e-6))))
+    reps, elapsed = 0, 0.0
+    while elapsed < 0.8 * seconds or reps == 0:
+        t0 = time.perf_counter()
+        o.gemm_rows(w.dtype, A, B, 0, target)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    flops = 2.0 * target * w.N * w.K * reps
+    what = (f"rows 0..{target - 1}" if target < w.M else "all rows") + f" of {w.name}"
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what} (N={w.N}, K={w.K}) x{reps}, {elapsed:.1f} s, double-precision i-k-j loop"}
+
+
+def load_traffic(workload: str, digest: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    p = ROOT / "profiles" / f"traffic_{workload}.json"
+    if not p.exists():
+        return None
+    d = json.loads(p.read_text())
+    if d.get("src_digest") != digest:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="f32_2048")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--shape", default=None,
+                    help="M,N,K[,dtype]: time an ad-hoc shape (uniform / normal inputs) instead of a named workload")
+    ap.add_argument("--variant", type=int, default=None,
+                    help="force this variant id (calibration); default: the dispatcher's plan")
+    ap.add_argument("--split", type=int, default=0, help="split-K for --variant (0: the variant's pick)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also run the MFMA-loop / HBM-copy ceiling probe and report its figures")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this GEMM path runs on one GPU; --gpus {args.gpus} / WORLD_SIZE {world} "
+              "is not supported (the single-GPU kernel is the unit that would be sharded).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sam_inputs as si
+    import shape_adaptive_matrix_amd as sam
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "launches": 5}))
+        return
+
+    sam.device_check()
+    if args.shape:
+        parts = args.shape.split(",")
+        M, N, K = (int(x) for x in parts[:3])
+        dt = parts[3] if len(parts) > 3 else "f32"
+        w = si.Workload(f"{dt}_{M}x{N}x{K}", dt, M, N, K, "uniform" if dt == "f32" else "normal16", 99)
+    else:
+        w = si.by_name(args.workload)
+    g = prepare(w, torch, sam, si, args.variant, args.split)
+    step = g["step"]
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_steps(torch, step, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ms / args.steps
+    tflops = w.flops / ms_step / 1e9
+
+    digest = src_digest()
+    split = g["plan"]["split_k"] > 1
+    line = {
+        "metric": "GEMM TFLOP/s and % of MFMA peak on 1 MI355X, fp32 and bf16, D=2048-8192",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: C=A*B, M={w.M} N={w.N} K={w.K}, {w.dtype} operands, "
+                               f"FP32 accumulate/output, {w.dist} inputs seed {w.seed}",
+                   "M": w.M, "N": w.N, "K": w.K, "plan": g["plan"]["name"]},
+        "pct_mfma_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2),
+        "wall_s": round(wall, 4),
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_TFLOPS[w.dtype],
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS[w.dtype], 4),
+            "traffic": None if split else load_traffic(w.name, digest),
+            "kernel": "sam::gemm_kernel" + (" + splitk_reduce_kernel" if split else ""),
+            "per_launch_flops": w.flops, "src_digest": digest,
+        },
+        "build": sam.build_info(),
+    }
+    del g
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        line["sweep"] = sweep(torch, sam, si)
+    if args.ceilings:
+        import subprocess
+        exe = ROOT / "shape_adaptive_matrix_amd" / "microbench" / "sam_ceilings"
+        r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+        line["ceilings"] = json.loads(r.stdout) if r.returncode == 0 else {"error": r.stderr[-500:]}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, si, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

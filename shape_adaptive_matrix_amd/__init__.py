@@ -14,8 +14,11 @@ import ctypes
 import re
 from pathlib import Path
 
+import os
+
 PKG = Path(__file__).resolve().parent
-LIB_PATH = PKG / "libsam.so"
+# SAM_LIBRARY may point at another build of the same library (A/B timing).
+LIB_PATH = Path(os.environ.get("SAM_LIBRARY", PKG / "libsam.so"))
 HEADER = PKG.parent / "include" / "sam.h"
 
 F32, BF16, F16 = 0, 1, 2

@@ -27,7 +27,7 @@ BUILD_DIR = ROOT / "_build" / "sam"
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sam_kernels.hip", "sam_plan.cpp", "sam_api.cpp"]
+SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_plan.cpp", "sam_api.cpp"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -73,6 +73,21 @@ def _compile(src: str, stamp: str, verbose: bool) -> Path:
     return obj
 
 
+CEILINGS_SRC = PKG / "microbench" / "sam_ceilings.hip"
+CEILINGS_BIN = PKG / "microbench" / "sam_ceilings"
+
+
+def _build_ceilings(verbose: bool) -> Path:
+    """The MFMA-loop / HBM-copy ceiling probe (a standalone executable)."""
+    if CEILINGS_BIN.exists():
+        CEILINGS_BIN.unlink()
+    cmd = [HIPCC, *HIP_FLAGS, str(CEILINGS_SRC), "-o", str(CEILINGS_BIN)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {CEILINGS_SRC.name}:\n{r.stdout}{r.stderr}")
+    return CEILINGS_BIN
+
+
 def build(verbose: bool = False) -> Path:
     if LIB.exists():
         LIB.unlink()
@@ -86,6 +101,7 @@ def build(verbose: bool = False) -> Path:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    _build_ceilings(verbose)
     if verbose:
         print(f"built {LIB} ({stamp})", flush=True)
     return LIB

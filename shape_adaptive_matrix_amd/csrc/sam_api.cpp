@@ -118,6 +118,12 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
 {
     const unsigned long long es = p.dtype == sam::DT_F32 ? 4 : 2;
     if (M == 0 || N == 0) return SAM_OK;
+    // Kernels address a workgroup's operand panels with 32-bit byte offsets:
+    // up to 257 rows of A (K elements each), 129 rows of B and 257 rows of C.
+    const long long lim = 0x7FFFFFF0ll;
+    if ((long long)K * (long long)es * 257 >= lim || (long long)N * (long long)es * 129 >= lim ||
+        N * 4ll * 257 >= lim)
+        return fail(SAM_ERR_INVALID_ARG, "K=%lld or N=%lld beyond the supported offset range", K, N);
     if (!C) return fail(SAM_ERR_INVALID_ARG, "C is null");
     if (K > 0 && (!A || !B)) return fail(SAM_ERR_INVALID_ARG, "A or B is null");
     if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))) || (ws && !aligned16(ws)))

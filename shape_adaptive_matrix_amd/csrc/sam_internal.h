@@ -23,17 +23,23 @@ struct DeviceModel {
 };
 
 // Static description of a tile/schedule variant.
+enum Kind : int { KIND_STAGED = 0, KIND_DMA = 1 };
+
 struct Variant {
     int id;
     const char* name;
+    int kind;            // Kind
     int dtype_mask;      // bit (1 << Dt)
     int bm, bn;          // macro tile
     int wm, wn;          // wave grid
     int blk;             // MFMA block edge (32 or 16)
+    int nbuf;            // LDS stages (2 for staged variants, the ring depth otherwise)
+    int bk;              // K per LDS stage for ring variants (0: by dtype, staged variants)
     int group_m;         // grouped raster height (tiles)
     int xcd_remap;       // 1: remap workgroup ids so each XCD gets a contiguous range
     int max_split;       // largest split-K the variant is planned with
-    double eff;          // calibrated fraction of MFMA peak it sustains in steady state
+    double eff_f32;      // calibrated fraction of MFMA peak it sustains in steady state
+    double eff_h16;
 };
 
 int variant_count();
@@ -56,6 +62,7 @@ struct GemmArgs {
 // Fully resolved plan (internal form of sam_plan).
 struct Plan {
     int variant_id;
+    int kind;
     int dtype;
     int bm, bn, bk;
     int wm, wn, blk;
@@ -75,10 +82,11 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
                       int split_req, Plan* out);
 bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out);
 void plan_name(const Plan& p, char* buf, int n);
-int k_stage(int dtype);   // K per LDS stage: 128 bytes of one row
+int k_stage(const Variant& v, int dtype);   // K per LDS stage
 
 // Kernel launchers (sam_kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const float* parts, int split, long long part_stride,
                          float* C, long long count, hipStream_t s);
 hipError_t launch_zero(float* C, long long count, hipStream_t s);

@@ -99,10 +99,12 @@ template <> struct Mfma<DT_F16, 16> {
 };
 
 // Byte offset of 16-byte chunk `ch` of LDS row `row` (rows are 128 bytes).
-// XOR swizzle: eight consecutive rows read at one logical chunk land in
-// eight different 16-byte bank groups.
+// gfx950 serves a 128-bit LDS read 16 lanes at a time across 64 four-byte
+// banks, i.e. two 128-byte rows per bank sweep. XOR-ing the chunk with
+// (row >> 1) gives the 16 rows that one such group reads at one logical chunk
+// 16 distinct 16-byte bank groups (measured: no bank-conflict cycles).
 __device__ __forceinline__ int lds_off(int row, int ch) {
-    return (row << 7) + (((ch ^ row) & 7) << 4);
+    return (row << 7) + (((ch ^ (row >> 1)) & 7) << 4);
 }
 
 // Output row of accumulator element r held by `lane` (MFMA result layout).
@@ -139,12 +141,57 @@ __device__ __forceinline__ unsigned pack_halves(unsigned x, unsigned y) {
     return __builtin_amdgcn_perm(y, x, H ? 0x07060302u : 0x05040100u);
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int BLK, bool AV, bool BV>
+// Buffer-resource loads. A load whose byte offset is at or past the
+// resource's record count returns zero without touching memory, so every
+// tail (rows past M, columns past N, K past the end of the split) is a
+// zero-returning load instead of a branch, and every load instruction is
+// issued unconditionally (which keeps the outstanding-load counts exact).
+constexpr int kOOB = 0x7FFFFFF0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes >= kOOB ? kOOB : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ u4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// One 16-byte chunk of VE elements from an element-granular row: element i
+// is read only when bit i of `ok` is set (else zero).
+template <int DT>
+__device__ __forceinline__ u4 ld_elems(__amdgpu_buffer_rsrc_t r, int off, unsigned ok) {
+    u4 v;
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (ok >> i) & 1 ? off + 4 * i : kOOB, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned lo = __builtin_amdgcn_raw_buffer_load_b16(r, (ok >> (2 * i)) & 1 ? off + 4 * i : kOOB, 0, 0);
+            const unsigned hi = __builtin_amdgcn_raw_buffer_load_b16(r, (ok >> (2 * i + 1)) & 1 ? off + 4 * i + 2 : kOOB, 0, 0);
+            v[i] = (lo & 0xFFFFu) | (hi << 16);
+        }
+    }
+    return v;
+}
+
+template <int BM, int BN, int NT>
+struct Occupancy {
+    static constexpr int lds = 2 * (BM + BN) * 128;
+    static constexpr int wgs = (160 * 1024) / lds;
+    static constexpr int w = (wgs * (NT / 64)) / 4;
+    static constexpr int waves = w < 1 ? 1 : (w > 8 ? 8 : w);   // waves per SIMD the LDS allows
+};
+
+template <int DT, int BM, int BN, int WM, int WN, int BLK, bool AV, bool BV, int PF>
 __global__ void __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(1, Occupancy<BM, BN, WM * WN * 64>::waves)))
 gemm_kernel(GemmArgs args)
 {
-    typedef typename Elem<DT>::T T;
     constexpr int VE = Elem<DT>::VE;          // elements per 16-byte chunk
+    constexpr int ES = 16 / VE;               // bytes per element
     constexpr int BK = 8 * VE;                // K per stage: one 128-byte row
     constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -158,6 +205,7 @@ gemm_kernel(GemmArgs args)
     typedef typename Acc<BLK>::T acc_t;
     static_assert(WTM % BLK == 0 && WTN % BLK == 0, "wave tile must be whole MFMA blocks");
     static_assert(2 * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(PF == 1 || PF == 2, "prefetch depth");
 
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
 
@@ -171,79 +219,76 @@ gemm_kernel(GemmArgs args)
     const int kbeg = s * args.k_chunk;
     const int kend = min(K, kbeg + args.k_chunk);
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-    const T* __restrict__ A = static_cast<const T*>(args.A);
-    const T* __restrict__ B = static_cast<const T*>(args.B);
 
     const int wm0 = (wave / WN) * WTM;
     const int wn0 = (wave % WN) * WTN;
 
-    u4 ra[NA];
-    u4 rb[NB][VE];
+    // A: one resource for the workgroup's row panel; offsets (row * K + k) * ES.
+    // Thread tid owns chunk (tid & 7) of rows (tid >> 3) + q * NT / 8.
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(static_cast<const char*>(args.A) + (long long)m0 * K * ES,
+                                                (long long)(M - m0) * K * ES);
+    const int a_row0 = tid >> 3;
+    const int a_kk = (tid & 7) * VE;
+    // B: one resource per stage starting at row k0, column n0; offsets
+    // (row_in_stage * N + column_in_tile) * ES. Thread tid owns the VExVE
+    // block at stage rows (tid & 7) * VE.. and columns ((tid >> 3) + q * NT / 8) * VE..
+    const int b_kr = (tid & 7) * VE;
+    const long long b_bytes = (long long)K * N * ES;
 
-    auto load_stage = [&](int k0) {
+    auto issue = [&](u4 (&RA)[NA], u4 (&RB)[NB][VE], int k0) {
+        const int gk = k0 + a_kk;
 #pragma unroll
         for (int q = 0; q < NA; ++q) {
-            const int id = tid + q * NT;
-            u4 v = {0u, 0u, 0u, 0u};
-            if (id < BM * 8) {
-                const int gm = m0 + (id >> 3);
-                const int gk = k0 + (id & 7) * VE;
-                if (gm < M) {
-                    const T* p = A + (long long)gm * K + gk;
-                    if constexpr (AV) {
-                        if (gk < kend) v = *reinterpret_cast<const u4*>(p);
-                    } else {
-                        T e[VE];
-#pragma unroll
-                        for (int i = 0; i < VE; ++i) e[i] = (gk + i < kend) ? p[i] : T(0);
-                        v = __builtin_bit_cast(u4, e);
-                    }
-                }
+            const int r = a_row0 + q * (NT / 8);
+            const bool rok = (NA * NT == BM * 8 || r < BM) && m0 + r < M;
+            const int off = (r * K + gk) * ES;
+            if constexpr (AV) {
+                RA[q] = ld16(rA, rok && gk < kend ? off : kOOB);
+            } else {
+                const int left = kend - gk;
+                const unsigned ok = !rok || left <= 0 ? 0u : (left >= VE ? (1u << VE) - 1u : (1u << left) - 1u);
+                RA[q] = ld_elems<DT>(rA, off, ok);
             }
-            ra[q] = v;
         }
+        const long long bbase = ((long long)k0 * N + n0) * ES;
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(static_cast<const char*>(args.B) + bbase, b_bytes - bbase);
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-            const int id = tid + q * NT;
-            const int gk = k0 + (id & 7) * VE;
-            const int gn = n0 + (id >> 3) * VE;
+            const int nb = ((tid >> 3) + q * (NT / 8)) * VE;
+            const bool cok = (NB * NT == NBT || (tid >> 3) + q * (NT / 8) < BN / VE) && n0 + nb < N;
+            const int left = N - n0 - nb;
+            const unsigned cols = left >= VE ? (1u << VE) - 1u : (left > 0 ? (1u << left) - 1u : 0u);
 #pragma unroll
             for (int r = 0; r < VE; ++r) {
-                u4 v = {0u, 0u, 0u, 0u};
-                if (id < NBT && gk + r < kend) {
-                    const T* p = B + (long long)(gk + r) * N + gn;
-                    if constexpr (BV) {
-                        if (gn < N) v = *reinterpret_cast<const u4*>(p);
-                    } else {
-                        T e[VE];
-#pragma unroll
-                        for (int i = 0; i < VE; ++i) e[i] = (gn + i < N) ? p[i] : T(0);
-                        v = __builtin_bit_cast(u4, e);
-                    }
+                const bool ok = cok && k0 + b_kr + r < kend;
+                const int off = ((b_kr + r) * N + nb) * ES;
+                if constexpr (BV) {
+                    RB[q][r] = ld16(rB, ok ? off : kOOB);
+                } else {
+                    RB[q][r] = ld_elems<DT>(rB, off, ok ? cols : 0u);
                 }
-                rb[q][r] = v;
             }
         }
     };
 
-    auto store_stage = [&](unsigned char* buf) {
+    auto commit = [&](unsigned char* buf, const u4 (&RA)[NA], const u4 (&RB)[NB][VE]) {
 #pragma unroll
         for (int q = 0; q < NA; ++q) {
             const int id = tid + q * NT;
-            if (id < BM * 8)
-                *reinterpret_cast<u4*>(buf + lds_off(id >> 3, id & 7)) = ra[q];
+            if (NA * NT == BM * 8 || id < BM * 8)
+                *reinterpret_cast<u4*>(buf + lds_off(id >> 3, id & 7)) = RA[q];
         }
         unsigned char* bbuf = buf + BM * 128;
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
             const int id = tid + q * NT;
-            if (id >= NBT) continue;
+            if (NB * NT != NBT && id >= NBT) continue;
             const int kc = id & 7;
             const int nb = (id >> 3) * VE;
             if constexpr (VE == 4) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    u4 t = {rb[q][0][c], rb[q][1][c], rb[q][2][c], rb[q][3][c]};
+                    u4 t = {RB[q][0][c], RB[q][1][c], RB[q][2][c], RB[q][3][c]};
                     *reinterpret_cast<u4*>(bbuf + lds_off(nb + c, kc)) = t;
                 }
             } else {
@@ -252,15 +297,15 @@ gemm_kernel(GemmArgs args)
                     u4 t;
                     const int d = c >> 1;
                     if (c & 1) {
-                        t[0] = pack_halves<1>(rb[q][0][d], rb[q][1][d]);
-                        t[1] = pack_halves<1>(rb[q][2][d], rb[q][3][d]);
-                        t[2] = pack_halves<1>(rb[q][4][d], rb[q][5][d]);
-                        t[3] = pack_halves<1>(rb[q][6][d], rb[q][7][d]);
+                        t[0] = pack_halves<1>(RB[q][0][d], RB[q][1][d]);
+                        t[1] = pack_halves<1>(RB[q][2][d], RB[q][3][d]);
+                        t[2] = pack_halves<1>(RB[q][4][d], RB[q][5][d]);
+                        t[3] = pack_halves<1>(RB[q][6][d], RB[q][7][d]);
                     } else {
-                        t[0] = pack_halves<0>(rb[q][0][d], rb[q][1][d]);
-                        t[1] = pack_halves<0>(rb[q][2][d], rb[q][3][d]);
-                        t[2] = pack_halves<0>(rb[q][4][d], rb[q][5][d]);
-                        t[3] = pack_halves<0>(rb[q][6][d], rb[q][7][d]);
+                        t[0] = pack_halves<0>(RB[q][0][d], RB[q][1][d]);
+                        t[1] = pack_halves<0>(RB[q][2][d], RB[q][3][d]);
+                        t[2] = pack_halves<0>(RB[q][4][d], RB[q][5][d]);
+                        t[3] = pack_halves<0>(RB[q][6][d], RB[q][7][d]);
                     }
                     *reinterpret_cast<u4*>(bbuf + lds_off(nb + c, kc)) = t;
                 }
@@ -279,68 +324,127 @@ gemm_kernel(GemmArgs args)
     const int lrow = lane % BLK;       // row (or column) inside an MFMA block
     const int lgrp = lane / BLK;       // K-slot group
 
-    if (nk > 0) {
-        load_stage(kbeg);
-        store_stage(lds);
-    }
-    __syncthreads();
-
-    for (int kb = 0; kb < nk; ++kb) {
-        const bool more = kb + 1 < nk;
-        if (more) load_stage(kbeg + (kb + 1) * BK);
-
-        const unsigned char* abuf = lds + (kb & 1) * STAGE;
+    auto read_frags = [&](const unsigned char* abuf, u4 (&fa)[TM], u4 (&fb)[TN], int c) {
         const unsigned char* bbuf = abuf + BM * 128;
+        const int ch = c * G + lgrp;
 #pragma unroll
-        for (int c = 0; c < CS; ++c) {
-            const int ch = c * G + lgrp;
-            u4 fa[TM], fb[TN];
+        for (int i = 0; i < TM; ++i)
+            fa[i] = *reinterpret_cast<const u4*>(abuf + lds_off(wm0 + i * BLK + lrow, ch));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb[j] = *reinterpret_cast<const u4*>(bbuf + lds_off(wn0 + j * BLK + lrow, ch));
+    };
+
+    auto mfmas = [&](const u4 (&fa)[TM], const u4 (&fb)[TN]) {
+        constexpr int PC = Mfma<DT, BLK>::PER_CHUNK;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) Mfma<DT, BLK>::template run<0>(acc[i][j], fa[i], fb[j]);
+        if constexpr (PC == 4) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                fa[i] = *reinterpret_cast<const u4*>(abuf + lds_off(wm0 + i * BLK + lrow, ch));
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                fb[j] = *reinterpret_cast<const u4*>(bbuf + lds_off(wn0 + j * BLK + lrow, ch));
-            constexpr int PC = Mfma<DT, BLK>::PER_CHUNK;
-            if constexpr (PC == 4) {
+                for (int j = 0; j < TN; ++j) Mfma<DT, BLK>::template run<1>(acc[i][j], fa[i], fb[j]);
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) Mfma<DT, BLK>::template run<0>(acc[i][j], fa[i], fb[j]);
+                for (int j = 0; j < TN; ++j) Mfma<DT, BLK>::template run<2>(acc[i][j], fa[i], fb[j]);
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) Mfma<DT, BLK>::template run<1>(acc[i][j], fa[i], fb[j]);
+                for (int j = 0; j < TN; ++j) Mfma<DT, BLK>::template run<3>(acc[i][j], fa[i], fb[j]);
+        }
+    };
+
+    // Scheduling hint for one chunk step: spread the TM+TN fragment reads of
+    // the next step across this step's MFMAs, so LDS latency hides behind
+    // matrix work instead of stalling it.
+    constexpr int NMF = TM * TN * Mfma<DT, BLK>::PER_CHUNK;   // MFMAs per chunk step
+    constexpr int NRD = TM + TN;                              // LDS reads per chunk step
+    auto interleave = [&]() {
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < NRD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF / NRD > 0 ? NMF / NRD : 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+        __builtin_amdgcn_sched_barrier(0);   // nothing crosses a chunk-step boundary
+    };
+
+    // All CS chunk steps of one stage; the fragments of step c+1 are read
+    // while the MFMAs of step c are issued.
+    auto compute = [&](const unsigned char* abuf) {
+        u4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+        read_frags(abuf, fa0, fb0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) Mfma<DT, BLK>::template run<2>(acc[i][j], fa[i], fb[j]);
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) Mfma<DT, BLK>::template run<3>(acc[i][j], fa[i], fb[j]);
+        for (int c = 0; c < CS; c += 2) {
+            if (c + 1 < CS) {
+                read_frags(abuf, fa1, fb1, c + 1);
+                mfmas(fa0, fb0);
+                interleave();
+                if (c + 2 < CS) {
+                    read_frags(abuf, fa0, fb0, c + 2);
+                    mfmas(fa1, fb1);
+                    interleave();
+                } else {
+                    mfmas(fa1, fb1);
+                }
             } else {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) Mfma<DT, BLK>::template run<0>(acc[i][j], fa[i], fb[j]);
+                mfmas(fa0, fb0);
             }
         }
+    };
 
-        if (more) store_stage(lds + ((kb + 1) & 1) * STAGE);
+    unsigned char* buf0 = lds;
+    unsigned char* buf1 = lds + STAGE;
+    u4 RA0[NA], RB0[NB][VE];
+    if constexpr (PF == 1) {
+        issue(RA0, RB0, kbeg);
+        commit(buf0, RA0, RB0);
         __syncthreads();
+        for (int kb = 0; kb < nk; ++kb) {
+            issue(RA0, RB0, kbeg + (kb + 1) * BK);
+            compute((kb & 1) ? buf1 : buf0);
+            commit((kb & 1) ? buf0 : buf1, RA0, RB0);
+            __syncthreads();
+        }
+    } else {
+        u4 RA1[NA], RB1[NB][VE];
+        issue(RA0, RB0, kbeg);
+        issue(RA1, RB1, kbeg + BK);
+        commit(buf0, RA0, RB0);
+        __syncthreads();
+        issue(RA0, RB0, kbeg + 2 * BK);
+        for (int kb = 0; kb < nk; kb += 2) {
+            compute(buf0);
+            commit(buf1, RA1, RB1);
+            __syncthreads();
+            issue(RA1, RB1, kbeg + (kb + 3) * BK);
+            if (kb + 1 >= nk) break;
+            compute(buf1);
+            commit(buf0, RA0, RB0);
+            __syncthreads();
+            issue(RA0, RB0, kbeg + (kb + 4) * BK);
+        }
     }
 
-    float* __restrict__ out = args.out + (long long)s * args.part_stride;
+    // Epilogue: stores through a buffer resource over this tile's rows of the
+    // output; positions past M or N get an out-of-range offset and are dropped.
+    float* outp = args.out + (long long)s * args.part_stride + (long long)m0 * N + n0;
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(outp, ((long long)(M - m0) * N - n0) * 4);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn0 + j * BLK + lrow;
+            const int col = wn0 + j * BLK + lrow;
 #pragma unroll
             for (int r = 0; r < Acc<BLK>::N; ++r) {
-                const int row = m0 + wm0 + i * BLK + acc_row<BLK>(lane, r);
-                if (row < M && col < N) out[(long long)row * N + col] = acc[i][j][r];
+                const int row = wm0 + i * BLK + acc_row<BLK>(lane, r);
+                const bool ok = m0 + row < M && n0 + col < N;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rC,
+                                                      ok ? (row * N + col) * 4 : kOOB, 0, 0);
             }
         }
     }
@@ -389,13 +493,13 @@ zero_kernel(float* __restrict__ C, long long count)
 // Launch table: [variant][dtype][a_vec][b_vec] -> kernel.
 typedef void (*KernelFn)(GemmArgs);
 
-template <int DT, int BM, int BN, int WM, int WN, int BLK>
+template <int DT, int BM, int BN, int WM, int WN, int BLK, int PF>
 struct KernelSet {
     static constexpr KernelFn fn[2][2] = {
-        {gemm_kernel<DT, BM, BN, WM, WN, BLK, false, false>,
-         gemm_kernel<DT, BM, BN, WM, WN, BLK, false, true>},
-        {gemm_kernel<DT, BM, BN, WM, WN, BLK, true, false>,
-         gemm_kernel<DT, BM, BN, WM, WN, BLK, true, true>}};
+        {gemm_kernel<DT, BM, BN, WM, WN, BLK, false, false, PF>,
+         gemm_kernel<DT, BM, BN, WM, WN, BLK, false, true, PF>},
+        {gemm_kernel<DT, BM, BN, WM, WN, BLK, true, false, PF>,
+         gemm_kernel<DT, BM, BN, WM, WN, BLK, true, true, PF>}};
 };
 
 struct VariantKernels {
@@ -403,19 +507,33 @@ struct VariantKernels {
     int threads;
 };
 
-#define SAM_KERNELS_ENTRY(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16)              \
-    {{{{KernelSet<DT_F32, BM, BN, WM, WN, BLK>::fn[0][0], KernelSet<DT_F32, BM, BN, WM, WN, BLK>::fn[0][1]}, \
-       {KernelSet<DT_F32, BM, BN, WM, WN, BLK>::fn[1][0], KernelSet<DT_F32, BM, BN, WM, WN, BLK>::fn[1][1]}}, \
-      {{KernelSet<DT_BF16, BM, BN, WM, WN, BLK>::fn[0][0], KernelSet<DT_BF16, BM, BN, WM, WN, BLK>::fn[0][1]}, \
-       {KernelSet<DT_BF16, BM, BN, WM, WN, BLK>::fn[1][0], KernelSet<DT_BF16, BM, BN, WM, WN, BLK>::fn[1][1]}}, \
-      {{KernelSet<DT_F16, BM, BN, WM, WN, BLK>::fn[0][0], KernelSet<DT_F16, BM, BN, WM, WN, BLK>::fn[0][1]}, \
-       {KernelSet<DT_F16, BM, BN, WM, WN, BLK>::fn[1][0], KernelSet<DT_F16, BM, BN, WM, WN, BLK>::fn[1][1]}}}, \
-     WM * WN * 64},
+template <int DT, int BM, int BN, int WM, int WN, int BLK, int PF>
+constexpr void fill_kernels(KernelFn (&f)[2][2]) {
+    typedef KernelSet<DT, BM, BN, WM, WN, BLK, PF> S;
+    f[0][0] = S::fn[0][0];
+    f[0][1] = S::fn[0][1];
+    f[1][0] = S::fn[1][0];
+    f[1][1] = S::fn[1][1];
+}
 
-static const VariantKernels kTable[] = {SAM_VARIANT_LIST(SAM_KERNELS_ENTRY)};
+template <int BM, int BN, int WM, int WN, int BLK, int PF32, int PF16>
+VariantKernels make_variant_kernels() {
+    VariantKernels v{};
+    fill_kernels<DT_F32, BM, BN, WM, WN, BLK, PF32>(v.fn[DT_F32]);
+    fill_kernels<DT_BF16, BM, BN, WM, WN, BLK, PF16>(v.fn[DT_BF16]);
+    fill_kernels<DT_F16, BM, BN, WM, WN, BLK, PF16>(v.fn[DT_F16]);
+    v.threads = WM * WN * 64;
+    return v;
+}
+
+#define SAM_KERNELS_ENTRY(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16, pf32, pf16) \
+    make_variant_kernels<BM, BN, WM, WN, BLK, pf32, pf16>(),
+
+static const VariantKernels kTable[] = {SAM_STAGED_VARIANTS(SAM_KERNELS_ENTRY)};
 
 hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s)
 {
+    if (p.kind == KIND_DMA) return launch_gemm_dma(p, a, s);
     const VariantKernels& vk = kTable[p.variant_id];
     KernelFn fn = vk.fn[p.dtype][p.a_vec][p.b_vec];
     hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(vk.threads), 0, s, a);

@@ -1,0 +1,342 @@
+// 16-bit GEMM kernel for gfx950 built on the CDNA4 LDS data path.
+//
+// C = A*B with bfloat16 / binary16 operands, FP32 accumulation and output
+// (page "Measured data point on fixed-tile vs shape-adaptive GEMM", section
+// "One more result that surprised us": the 16-bit port that a fixed,
+// occupancy-bound design could not speed up). Shape: row-major A[M][K],
+// B[K][N], both K % 8 == 0 and N % 8 == 0 (16-byte rows pieces).
+//
+//  * Global -> LDS goes through buffer loads that write LDS directly (no
+//    VGPR staging, no VALU on the way): each wave instruction moves 1 KB,
+//    lane l landing at base + 16 l. Out-of-range offsets write zeros, so M,
+//    N and K tails cost nothing extra. A stage is BK = 32 values of K; the
+//    LDS holds a ring of NBUF stages, NBUF - 1 of them in flight while one is
+//    consumed, which covers HBM latency without registers.
+//  * A sits in LDS K-contiguous (64-byte rows, 16-byte chunks XOR-swizzled
+//    by row >> 2) and is read as one 128-bit fragment per MFMA block.
+//  * B sits in LDS in its natural N-contiguous layout (16-byte chunks
+//    XOR-swizzled by 4 (k & 3)) and is read with the transposing LDS load:
+//    within each 16-lane group, lane d receives, for k = kbase..kbase+3,
+//    the value at column (4 (source lane % 4) + d % 4) of the row that source
+//    lane 4 i + d / 4 points at. Two such loads give the eight consecutive K
+//    values of one column that the 32x32x16 MFMA takes per lane.
+//  * One barrier per stage, placed between the stage's two MFMA k-steps:
+//    before it every wave has finished reading the stage (so its buffer can
+//    be refilled) and has seen its own loads of the next stage land; after
+//    it, the next stage's first fragments are read while the second k-step's
+//    MFMAs run.
+// No atomics and a fixed K order per output: repeated runs give the same
+// bits.
+#include "sam_internal.h"
+#include "sam_variants.h"
+
+namespace sam {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+
+#define SAM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define SAM_LDS4S(p) ((__attribute__((address_space(3))) v4s*)(p))
+
+namespace dma {
+
+constexpr int kOOB = 0x7FFFFFF0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes >= kOOB ? kOOB : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+typedef int i4 __attribute__((ext_vector_type(4)));
+
+// The same raw buffer resource as four dwords (base, stride 0, record count
+// in bytes, default format word) for the LDS load below.
+__device__ __forceinline__ i4 rsrc_words(const void* base, long long bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes >= kOOB ? kOOB : (int)bytes);
+    const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+    return i4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xFFFFu), n, 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset `voff` into LDS at (wave-uniform)
+// `lds_base` + 16 * lane; offsets past the record count store zeros. Written
+// as inline assembly so that the compiler does not treat every later LDS
+// read as dependent on it (it would otherwise wait for all outstanding loads
+// before them); the kernel counts these loads itself with wait_cnt.
+__device__ __forceinline__ void lds_load16(const i4& rsrc, unsigned lds_base, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// s_waitcnt with vmcnt <= VM and lgkmcnt <= LG (expcnt untouched).
+template <int VM, int LG>
+__device__ __forceinline__ void wait_cnt() {
+    static_assert(VM >= 0 && VM < 64 && LG >= 0 && LG < 16, "counter range");
+    __builtin_amdgcn_s_waitcnt((VM & 0xF) | (0x7 << 4) | (LG << 8) | ((VM >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence __syncthreads adds (that fence
+// would drain every outstanding LDS load); the asm statements keep the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void tile_coords(int wg, const GemmArgs& a, int& tm, int& tn, int& s) {
+    const int total = a.tiles_m * a.tiles_n * a.split;
+    int L = wg;
+    if (a.xcd_remap) {
+        const int q = total >> 3, rem = total & 7, x = wg & 7, y = wg >> 3;
+        L = (x < rem) ? x * (q + 1) + y : rem * (q + 1) + (x - rem) * q + y;
+    }
+    const int tiles = a.tiles_m * a.tiles_n;
+    s = L / tiles;
+    const int t = L - s * tiles;
+    const int per_group = a.group_m * a.tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * a.group_m;
+    const int gsz = min(a.tiles_m - first_m, a.group_m);
+    const int r = t - g * per_group;
+    tm = first_m + r % gsz;
+    tn = r / gsz;
+}
+
+template <int DT>
+__device__ __forceinline__ void mfma(v16f& c, const u4& a, const u4& b) {
+    if constexpr (DT == DT_BF16)
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+    else
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+
+}  // namespace dma
+
+template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF>
+__global__ void __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(1, (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 > 0
+                                           ? (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 : 1)))
+gemm16_dma_kernel(GemmArgs args)
+{
+    using namespace dma;
+    static_assert(DT == DT_BF16 || DT == DT_F16, "16-bit operands only");
+    static_assert(BK == 32 || BK == 64, "K per stage: 64- or 128-byte A rows");
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int A_ROW = BK * 2;              // bytes per A row in LDS
+    constexpr int CPA = A_ROW / 16;            // 16-byte chunks per A row
+    constexpr int RPA = 64 / CPA;              // A rows per wave load
+    constexpr int RSW = 16 / CPA;              // A rows sharing one 256-byte bank sweep
+    constexpr int KSTEPS = BK / 16;            // MFMA k-steps per stage
+    constexpr int A_BYTES = BM * A_ROW;
+    constexpr int B_ROW = BN * 2;              // bytes per B row
+    constexpr int B_BYTES = BK * B_ROW;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_INS = A_BYTES / 1024, B_INS = B_BYTES / 1024;   // 1 KB wave loads per stage
+    constexpr int A_PW = A_INS / NW, B_PW = B_INS / NW;
+    constexpr int LPS = A_PW + B_PW;           // loads per stage per lane
+    constexpr int CPR = BN / 8;                // 16-byte chunks per B row
+    constexpr int RPI = 64 / CPR;              // B rows per wave load
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(A_INS % NW == 0 && B_INS % NW == 0, "loads must split evenly over waves");
+    static_assert(CPR >= 16 && 64 % CPR == 0, "BN must be 128 or 256");
+    static_assert(NBUF >= 2 && NBUF * STAGE <= 160 * 1024, "LDS ring");
+    static_assert((NBUF - 1) * LPS < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    int tm, tn, s;
+    tile_coords(blockIdx.x, args, tm, tn, s);
+    const int M = args.M, N = args.N, K = args.K;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kbeg = s * args.k_chunk;
+    const int kend = min(K, kbeg + args.k_chunk);
+    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+    const int wm0 = (wave / WN) * WTM;
+    const int wn0 = (wave % WN) * WTN;
+
+    const i4 rA = rsrc_words(static_cast<const char*>(args.A) + (long long)m0 * K * 2,
+                             (long long)(M - m0) * K * 2);
+    const long long b_bytes = (long long)K * N * 2;
+
+    // One 1 KB wave load of stage `st` (relative to this split): loads
+    // 0 .. A_PW-1 fetch A rows, the rest B rows.
+    auto issue_one = [&](int st, int q) {
+        const int k0 = kbeg + st * BK;
+        unsigned char* buf = lds + (st % NBUF) * STAGE;
+        if (q < A_PW) {
+            const int I = wave + q * NW;                   // RPA rows per load
+            const int row = I * RPA + lane / CPA;
+            const int c = (lane % CPA) ^ ((row / RSW) % CPA);   // logical chunk stored at this slot
+            const int gk = k0 + c * 8;
+            const bool ok = m0 + row < M && gk < kend;
+            lds_load16(rA, lds_addr(buf + I * 1024), ok ? (row * K + gk) * 2 : kOOB);
+        } else {
+            const int I = wave + (q - A_PW) * NW;
+            const int row = I * RPI + lane / CPR;
+            const int c = (lane % CPR) ^ (4 * (row & 3));
+            const bool ok = k0 + row < kend && n0 + c * 8 < N;
+            const long long bbase = ((long long)k0 * N + n0) * 2;
+            const i4 rB = rsrc_words(static_cast<const char*>(args.B) + bbase, b_bytes - bbase);
+            lds_load16(rB, lds_addr(buf + A_BYTES + I * 1024), ok ? (row * N + c * 8) * 2 : kOOB);
+        }
+    };
+
+    const int lrow = lane & 31;
+    const int lgrp = lane >> 5;
+    const int g16 = lane >> 4, s16 = lane & 15;
+    // Fragment reads, one LDS instruction each. Read r < TM: A block r;
+    // read TM + 2 j + h: half h (K rows 4h..4h+3 of the lane's eight) of B block j.
+    //  A: row wm0 + 32 i + lrow, K 16 t + 8 lgrp .. +7, one 128-bit read.
+    //  B: column wn0 + 32 j + lrow, the same K, two transposing 64-bit reads.
+    auto read_one = [&](const unsigned char* buf, int t, int r, u4 (&fa)[TM], u2 (&fb)[TN][2]) {
+        if (r < TM) {
+            const int row = wm0 + 32 * r + lrow;
+            const int c = (2 * t + lgrp) ^ ((row / RSW) % CPA);
+            fa[r] = *reinterpret_cast<const u4*>(buf + row * A_ROW + c * 16);
+        } else {
+            const int j = (r - TM) >> 1, half = (r - TM) & 1;
+            const int col = wn0 + 32 * j + 16 * (g16 & 1) + 4 * (s16 & 3);
+            const int row = 16 * t + 8 * (g16 >> 1) + 4 * half + (s16 >> 2);
+            const int c = (col >> 3) ^ (4 * (row & 3));
+            const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                SAM_LDS4S(buf + A_BYTES + row * B_ROW + c * 16 + (col & 7) * 2));
+            fb[j][half] = __builtin_bit_cast(u2, v);
+        }
+    };
+
+    v16f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto mfma_one = [&](int m, const u4 (&fa)[TM], const u2 (&fb)[TN][2]) {
+        const int i = m / TN, j = m % TN;
+        const u4 b = u4{fb[j][0][0], fb[j][0][1], fb[j][1][0], fb[j][1][1]};
+        mfma<DT>(acc[i][j], fa[i], b);
+    };
+
+    constexpr int NMF = TM * TN;          // MFMAs per k-step
+    constexpr int NRD = TM + 2 * TN;      // LDS reads per k-step
+    constexpr int RPS = (NRD + NMF - 1) / NMF;   // reads per MFMA slot
+
+    // One k-step: MFMA slot m issues MFMA m, then (while m < NRD) the next
+    // step's read m into the other fragment set, then (in the second k-step)
+    // one of this wave's LDS loads every NMF / LPS slots. The order is pinned
+    // so that no burst of loads ever blocks MFMA issue behind it.
+    auto kstep = [&](const u4 (&fa)[TM], const u2 (&fb)[TN][2], const unsigned char* rbuf, int rt,
+                     u4 (&na)[TM], u2 (&nb)[TN][2], int load_stage) {
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) {
+            mfma_one(m, fa, fb);
+#pragma unroll
+            for (int r = m * RPS; r < (m + 1) * RPS; ++r)
+                if (r < NRD) read_one(rbuf, rt, r, na, nb);
+            if (load_stage >= 0) {
+                // loads q with ceil(q * NMF / LPS) == m, i.e. spread evenly over the slots
+#pragma unroll
+                for (int q = (m * LPS + NMF - 1) / NMF; q < ((m + 1) * LPS + NMF - 1) / NMF; ++q)
+                    if (q < LPS) issue_one(load_stage, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Fill the whole ring, then wait for stage 0.
+#pragma unroll
+    for (int st = 0; st < NBUF; ++st)
+#pragma unroll
+        for (int q = 0; q < LPS; ++q) issue_one(st, q);
+    wait_cnt<(NBUF - 1) * LPS, 15>();
+    barrier();
+    u4 fa[2][TM];
+    u2 fb[2][TN][2];
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) read_one(lds, 0, r, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int k = 0; k < nk; ++k) {
+        const unsigned char* cur = lds + (k % NBUF) * STAGE;
+        const unsigned char* nxt = lds + ((k + 1) % NBUF) * STAGE;
+        // k-steps 0 .. KSTEPS-2 of stage k, each reading the next k-step.
+#pragma unroll
+        for (int t = 0; t + 1 < KSTEPS; ++t)
+            kstep(fa[t & 1], fb[t & 1], cur, t + 1, fa[(t + 1) & 1], fb[(t + 1) & 1], -1);
+        // Stage k fully read by this wave; this wave's part of stage k+1 landed.
+        wait_cnt<(NBUF - 2) * LPS, 0>();
+        barrier();
+        // Last k-step of stage k: read k-step 0 of stage k+1 and refill the
+        // slot stage k leaves with stage k + NBUF meanwhile.
+        constexpr int L = (KSTEPS - 1) & 1;
+        kstep(fa[L], fb[L], nxt, 0, fa[L ^ 1], fb[L ^ 1], k + NBUF);
+        if constexpr (L == 0) {   // odd number of k-steps: next stage starts in set 1
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[0][i] = fa[1][i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) { fb[0][j][0] = fb[1][j][0]; fb[0][j][1] = fb[1][j][1]; }
+        }
+    }
+    wait_cnt<0, 0>();   // no LDS load may still be in flight when the workgroup ends
+
+    float* outp = args.out + (long long)s * args.part_stride + (long long)m0 * N + n0;
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(outp, ((long long)(M - m0) * N - n0) * 4);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = wn0 + 32 * j + lrow;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm0 + 32 * i + ((r >> 2) << 3) + (lgrp << 2) + (r & 3);
+                const bool ok = m0 + row < M && n0 + col < N;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rC,
+                                                      ok ? (row * N + col) * 4 : kOOB, 0, 0);
+            }
+        }
+    }
+}
+
+typedef void (*KernelFn)(GemmArgs);
+
+struct DmaKernels {
+    int id;
+    KernelFn fn[3];
+    int threads;
+};
+
+#define SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, gm, xr, ms, e16)                      \
+    {id, {nullptr, gemm16_dma_kernel<DT_BF16, BM, BN, WM, WN, BK, NBUF>,                         \
+          gemm16_dma_kernel<DT_F16, BM, BN, WM, WN, BK, NBUF>}, WM * WN * 64},
+
+static const DmaKernels kDmaTable[] = {SAM_DMA_VARIANTS(SAM_DMA_ENTRY)};
+
+hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s)
+{
+    for (const DmaKernels& d : kDmaTable) {
+        if (d.id != p.variant_id) continue;
+        KernelFn fn = d.fn[p.dtype];
+        if (!fn) return hipErrorInvalidDeviceFunction;
+        hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(d.threads), 0, s, a);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidDeviceFunction;
+}
+
+}  // namespace sam

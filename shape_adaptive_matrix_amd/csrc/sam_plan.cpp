@@ -33,13 +33,12 @@
 
 namespace sam {
 
-#define SAM_VARIANT_ROW(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16) \
-    {id, name, 7, BM, BN, WM, WN, BLK, gm, xr, ms, 0.0},
+#define SAM_STAGED_ROW(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16, pf32, pf16) \
+    {id, name, KIND_STAGED, 7, BM, BN, WM, WN, BLK, 2, 0, gm, xr, ms, e32, e16},
+#define SAM_DMA_ROW(id, name, BM, BN, WM, WN, BK, NBUF, gm, xr, ms, e16) \
+    {id, name, KIND_DMA, (1 << DT_BF16) | (1 << DT_F16), BM, BN, WM, WN, 32, NBUF, BK, gm, xr, ms, 0.0, e16},
 
-static const Variant kVariants[] = {SAM_VARIANT_LIST(SAM_VARIANT_ROW)};
-
-#define SAM_VARIANT_EFF(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16) {e32, e16},
-static const double kEff[][2] = {SAM_VARIANT_LIST(SAM_VARIANT_EFF)};
+static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -50,7 +49,11 @@ const Variant* variant_get(int id)
     return (id >= 0 && id < kVariantCount) ? &kVariants[id] : nullptr;
 }
 
-int k_stage(int dtype) { return dtype == DT_F32 ? 32 : 64; }
+int k_stage(const Variant& v, int dtype)
+{
+    if (v.kind == KIND_DMA) return v.bk;
+    return dtype == DT_F32 ? 32 : 64;   // one 128-byte LDS row
+}
 
 static int vec_elems(int dtype) { return dtype == DT_F32 ? 4 : 8; }
 
@@ -61,14 +64,14 @@ static const DeviceModel kDev;
 static double estimate_us(const Variant& v, long long M, long long N, long long K, int dtype,
                           int split, int a_vec, int b_vec)
 {
-    const int bk = k_stage(dtype);
+    const int bk = k_stage(v, dtype);
     const long long nkb = cdiv(K, bk);
     const long long kc = cdiv(nkb, split) * bk;               // K per split, padded
     const long long tiles_m = cdiv(M, v.bm), tiles_n = cdiv(N, v.bn);
     const long long wgs = tiles_m * tiles_n * split;
     const double in_b = dtype == DT_F32 ? 4.0 : 2.0;
 
-    double eff = kEff[v.id][dtype == DT_F32 ? 0 : 1];
+    double eff = dtype == DT_F32 ? v.eff_f32 : v.eff_h16;
     if (!a_vec) eff *= 0.85;
     if (!b_vec) eff *= 0.85;
     const double peak_cu = (dtype == DT_F32 ? kDev.f32_flop_per_clk_cu : kDev.h16_flop_per_clk_cu) *
@@ -89,11 +92,11 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
     return t;
 }
 
-static bool split_admissible(long long K, int dtype, int split)
+static bool split_admissible(const Variant& v, long long K, int dtype, int split)
 {
     if (split < 1) return false;
     if (split == 1) return true;
-    const long long nkb = cdiv(K, k_stage(dtype));
+    const long long nkb = cdiv(K, k_stage(v, dtype));
     if (split > nkb) return false;
     const long long per = cdiv(nkb, split);
     return cdiv(nkb, per) == split;                           // no empty split
@@ -102,9 +105,10 @@ static bool split_admissible(long long K, int dtype, int split)
 static void fill_plan(const Variant& v, long long M, long long N, long long K, int dtype, int split,
                       Plan* p)
 {
-    const int bk = k_stage(dtype);
+    const int bk = k_stage(v, dtype);
     const int ve = vec_elems(dtype);
     p->variant_id = v.id;
+    p->kind = v.kind;
     p->dtype = dtype;
     p->bm = v.bm;
     p->bn = v.bn;
@@ -143,10 +147,11 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
 {
     const Variant* v = variant_get(vid);
     if (!v || dtype < DT_F32 || dtype > DT_F16 || !(v->dtype_mask & (1 << dtype))) return false;
-    if (2 * (v->bm + v->bn) * 128 > kDev.lds_bytes) return false;
     if (M < 0 || N < 0 || K < 0) return false;
+    // The LDS-ring kernels take whole 16-byte pieces of A and B rows.
+    if (v->kind == KIND_DMA && (K % 8 != 0 || N % 8 != 0)) return false;
     if (split_req > 0) {
-        if (split_req > 1 && (K == 0 || !split_admissible(K, dtype, split_req))) return false;
+        if (split_req > 1 && (K == 0 || !split_admissible(*v, K, dtype, split_req))) return false;
         fill_plan(*v, M, N, K, dtype, split_req, out);
         return out->grid < (1ll << 31);
     }
@@ -154,7 +159,7 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     Plan best{};
     for (int s : kSplits) {
         if (s > v->max_split) break;
-        if (s > 1 && (K == 0 || !split_admissible(K, dtype, s))) continue;
+        if (s > 1 && (K == 0 || !split_admissible(*v, K, dtype, s))) continue;
         Plan p{};
         fill_plan(*v, M, N, K, dtype, s, &p);
         if (p.grid >= (1ll << 31) || !split_wanted(p)) continue;
