@@ -36,10 +36,16 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense MFM
 PEAK_HBM_GBS = 8000.0
 
 
+KERNEL_SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_internal.h"]
+
+
 def src_digest() -> str:
+    """Hash of the kernel sources: a stored counter reading is only reported
+    while the kernels it was taken on are unchanged."""
     h = hashlib.sha256()
-    for p in sorted((ROOT / "shape_adaptive_matrix_amd" / "csrc").iterdir()):
-        h.update(p.name.encode())
+    for name in KERNEL_SOURCES:
+        p = ROOT / "shape_adaptive_matrix_amd" / "csrc" / name
+        h.update(name.encode())
         h.update(p.read_bytes())
     return h.hexdigest()[:16]
 

@@ -67,6 +67,14 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not LIB_PATH.exists():
         raise ImportError(f"{LIB_PATH} is missing: run `python -m shape_adaptive_matrix_amd.build`")
+    # torch ships its own HIP runtime under the same soname as the system one
+    # libsam.so links. Whichever is loaded first serves the whole process, and
+    # torch cannot initialise the GPU on the other; so when torch is present
+    # it is loaded first and the library binds to its runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(str(LIB_PATH))
     i64, u64, vp, i32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32
     P = ctypes.POINTER(SamPlan)

@@ -17,7 +17,8 @@ struct DeviceModel {
     double clock_ghz = 2.4;
     double f32_flop_per_clk_cu = 256.0;    // 4 SIMDs x 64 (32x32x2 f32 in 64 clk)
     double h16_flop_per_clk_cu = 4096.0;   // 4 SIMDs x 1024
-    double hbm_gbs = 8000.0;
+    double hbm_gbs = 5900.0;       // measured streaming read rate
+    double hbm_write_gbs = 6000.0; // rate the epilogue write phase drains at (calibrated)
     double l2_gbs = 20000.0;       // aggregate L2/MALL delivery, rough
     double launch_us = 4.0;        // per kernel launch, rough
 };

@@ -78,9 +78,14 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
                            kDev.clock_ghz * 1e3;              // FLOP per microsecond
     const double t_wg = 2.0 * v.bm * v.bn * (double)kc / (peak_cu * eff);
     const double rounds = (double)cdiv(wgs, kDev.cus);
-    const double t_mfma = rounds * t_wg;
-
+    // Every workgroup ends by writing its BM x BN FP32 tile (to C or to its
+    // split's partials). Workgroups of one round finish together, so that
+    // write is an HBM-bound phase of its own rather than hidden under MFMA.
     const double mb = 1e-6;                                   // bytes -> MB; GB/s = MB/ms
+    const double concurrent = (double)(wgs < kDev.cus ? wgs : kDev.cus);
+    const double t_epi = concurrent * v.bm * v.bn * 4.0 * mb / kDev.hbm_write_gbs * 1e3;
+    const double t_mfma = rounds * (t_wg + t_epi);
+
     const double alg = in_b * (double)(M * K + K * N) + 4.0 * (double)(M * N);
     const double part = split > 1 ? 4.0 * (double)(M * N) * split : 0.0;
     const double t_hbm = (alg + part) * mb / kDev.hbm_gbs * 1e3;

@@ -13,20 +13,20 @@
 #pragma once
 
 #define SAM_STAGED_VARIANTS(X)                                                           \
-    X(0, "t64x64_w2x2_b32",    64,  64, 2, 2, 32, 8, 1, 16, 0.45, 0.25, 1, 2)            \
-    X(1, "t128x128_w2x2_b32", 128, 128, 2, 2, 32, 8, 1, 16, 0.72, 0.30, 1, 2)            \
-    X(2, "t128x256_w2x2_b32", 128, 256, 2, 2, 32, 8, 1,  8, 0.72, 0.30, 1, 2)            \
-    X(3, "t256x128_w2x2_b32", 256, 128, 2, 2, 32, 8, 1,  8, 0.72, 0.30, 1, 2)            \
-    X(4, "t256x256_w2x2_b32", 256, 256, 2, 2, 32, 8, 1,  8, 0.78, 0.38, 1, 1)            \
-    X(5, "t16x256_w1x4_b16",   16, 256, 1, 4, 16, 1, 1, 32, 0.40, 0.20, 1, 2)            \
-    X(6, "t256x16_w4x1_b16",  256,  16, 4, 1, 16, 8, 1, 32, 0.40, 0.20, 1, 2)            \
-    X(7, "t256x256_w2x4_b32", 256, 256, 2, 4, 32, 8, 1,  8, 0.82, 0.30, 1, 1)
+    X(0, "t64x64_w2x2_b32",    64,  64, 2, 2, 32, 8, 1, 16, 0.74, 0.12, 1, 2)            \
+    X(1, "t128x128_w2x2_b32", 128, 128, 2, 2, 32, 8, 1, 16, 0.84, 0.28, 1, 2)            \
+    X(2, "t128x256_w2x2_b32", 128, 256, 2, 2, 32, 8, 1,  8, 0.78, 0.31, 1, 2)            \
+    X(3, "t256x128_w2x2_b32", 256, 128, 2, 2, 32, 8, 1,  8, 0.78, 0.31, 1, 2)            \
+    X(4, "t256x256_w2x2_b32", 256, 256, 2, 2, 32, 8, 1,  8, 0.825, 0.40, 1, 1)           \
+    X(5, "t16x256_w1x4_b16",   16, 256, 1, 4, 16, 1, 1, 32, 0.45, 0.05, 1, 2)            \
+    X(6, "t256x16_w4x1_b16",  256,  16, 4, 1, 16, 8, 1, 32, 0.54, 0.05, 1, 2)            \
+    X(7, "t256x256_w2x4_b32", 256, 256, 2, 4, 32, 8, 1,  8, 0.88, 0.35, 1, 1)
 
 #define SAM_DMA_VARIANTS(D)                                                              \
-    D(8, "r256x256_w2x2_k32n4",  256, 256, 2, 2, 32, 4, 8, 1, 8, 0.60)                   \
-    D(9, "r128x256_w2x2_k32n4",  128, 256, 2, 2, 32, 4, 8, 1, 8, 0.50)                   \
-    D(10, "r256x128_w2x2_k32n4", 256, 128, 2, 2, 32, 4, 8, 1, 8, 0.50)                   \
-    D(11, "r128x128_w2x2_k32n4", 128, 128, 2, 2, 32, 4, 8, 1, 16, 0.45)                  \
-    D(12, "r256x256_w2x2_k64n2", 256, 256, 2, 2, 64, 2, 8, 1, 8, 0.62)                   \
-    D(13, "r256x128_w2x2_k64n3", 256, 128, 2, 2, 64, 3, 8, 1, 8, 0.55)                   \
-    D(14, "r128x256_w2x2_k64n3", 128, 256, 2, 2, 64, 3, 8, 1, 8, 0.55)
+    D(8, "r256x256_w2x2_k32n4",  256, 256, 2, 2, 32, 4, 8, 1, 8, 0.45)                   \
+    D(9, "r128x256_w2x2_k32n4",  128, 256, 2, 2, 32, 4, 8, 1, 8, 0.37)                   \
+    D(10, "r256x128_w2x2_k32n4", 256, 128, 2, 2, 32, 4, 8, 1, 8, 0.36)                   \
+    D(11, "r128x128_w2x2_k32n4", 128, 128, 2, 2, 32, 4, 8, 1, 16, 0.34)                  \
+    D(12, "r256x256_w2x2_k64n2", 256, 256, 2, 2, 64, 2, 8, 1, 8, 0.47)                   \
+    D(13, "r256x128_w2x2_k64n3", 256, 128, 2, 2, 64, 3, 8, 1, 8, 0.38)                   \
+    D(14, "r128x256_w2x2_k64n3", 128, 256, 2, 2, 64, 3, 8, 1, 8, 0.37)
