@@ -128,11 +128,14 @@ def sweep(torch, sam, si, rounds: int = 5):
             "alg_gbs": round(w.alg_bytes / t_ms / 1e6, 1),
         }
         if min(w.M, w.N) <= 16:
+            # Evict the operands by reading 1 GiB: a read leaves clean lines,
+            # whereas a fill would leave dirty ones whose write-back the timed
+            # launch would pay for.
             if flush is None:
-                flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+                flush = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
             cold = []
             for _ in range(20):
-                flush.fill_(1.0)
+                flush.sum()
                 cold.append(time_steps(torch, step, 1))
             c_ms = statistics.median(cold)
             rec["cold_ms"] = round(c_ms, 5)

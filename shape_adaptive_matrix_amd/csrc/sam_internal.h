@@ -18,13 +18,14 @@ struct DeviceModel {
     double f32_flop_per_clk_cu = 256.0;    // 4 SIMDs x 64 (32x32x2 f32 in 64 clk)
     double h16_flop_per_clk_cu = 4096.0;   // 4 SIMDs x 1024
     double hbm_gbs = 5900.0;       // measured streaming read rate
+    double tiled_hbm_frac = 0.75;  // share of it the LDS-tiled kernels reach when HBM-bound (calibrated)
     double hbm_write_gbs = 6000.0; // rate the epilogue write phase drains at (calibrated)
     double l2_gbs = 20000.0;       // aggregate L2/MALL delivery, rough
     double launch_us = 4.0;        // per kernel launch, rough
 };
 
 // Static description of a tile/schedule variant.
-enum Kind : int { KIND_STAGED = 0, KIND_DMA = 1 };
+enum Kind : int { KIND_STAGED = 0, KIND_DMA = 1, KIND_STREAM = 2 };
 
 struct Variant {
     int id;
@@ -35,11 +36,13 @@ struct Variant {
     int wm, wn;          // wave grid
     int blk;             // MFMA block edge (32 or 16)
     int nbuf;            // LDS stages (2 for staged variants, the ring depth otherwise)
-    int bk;              // K per LDS stage for ring variants (0: by dtype, staged variants)
+    int bk;              // K per LDS stage for ring variants (0: by dtype, staged variants),
+                         // K block of a workgroup for streaming variants
     int group_m;         // grouped raster height (tiles)
     int xcd_remap;       // 1: remap workgroup ids so each XCD gets a contiguous range
     int max_split;       // largest split-K the variant is planned with
     double eff_f32;      // calibrated fraction of MFMA peak it sustains in steady state
+                         // (streaming variants: fraction of the HBM read rate)
     double eff_h16;
 };
 
@@ -88,6 +91,7 @@ int k_stage(const Variant& v, int dtype);   // K per LDS stage
 // Kernel launchers (sam_kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_stream(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const float* parts, int split, long long part_stride,
                          float* C, long long count, hipStream_t s);
 hipError_t launch_zero(float* C, long long count, hipStream_t s);

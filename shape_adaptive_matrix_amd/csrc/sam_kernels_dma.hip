@@ -112,6 +112,12 @@ __device__ __forceinline__ void tile_coords(int wg, const GemmArgs& a, int& tm, 
     tn = r / gsz;
 }
 
+// 16-bit lane select: half H of x and y -> (x_H | y_H << 16).
+template <int H>
+__device__ __forceinline__ unsigned pack_halves(unsigned x, unsigned y) {
+    return __builtin_amdgcn_perm(y, x, H ? 0x07060302u : 0x05040100u);
+}
+
 template <int DT>
 __device__ __forceinline__ void mfma(v16f& c, const u4& a, const u4& b) {
     if constexpr (DT == DT_BF16)
@@ -122,7 +128,16 @@ __device__ __forceinline__ void mfma(v16f& c, const u4& a, const u4& b) {
 
 }  // namespace dma
 
-template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF>
+// MODE 0: loads write LDS directly (ring of NBUF stages).
+// MODE 1: loads go to registers and are written to LDS with ds_write_b128
+//         (NBUF = 2): the loads of stage k+1 are spread over the first k-step
+//         of stage k and their LDS writes over the next-to-last one, so the
+//         faster register load path overlaps the MFMAs completely.
+// MODE 2: A as in MODE 0 (straight into LDS, NBUF = 2); B through registers,
+//         transposed there (one v_perm per output dword) and stored
+//         K-contiguous, so its fragments are full-rate 128-bit LDS reads
+//         instead of half-rate transposing reads.
+template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE>
 __global__ void __launch_bounds__(WM * WN * 64)
 __attribute__((amdgpu_waves_per_eu(1, (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 > 0
                                            ? (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 : 1)))
@@ -140,18 +155,24 @@ gemm16_dma_kernel(GemmArgs args)
     constexpr int RSW = 16 / CPA;              // A rows sharing one 256-byte bank sweep
     constexpr int KSTEPS = BK / 16;            // MFMA k-steps per stage
     constexpr int A_BYTES = BM * A_ROW;
-    constexpr int B_ROW = BN * 2;              // bytes per B row
+    constexpr int B_ROW = BN * 2;              // bytes per B row (MODE 0/1: N-contiguous rows)
     constexpr int B_BYTES = BK * B_ROW;
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int A_INS = A_BYTES / 1024, B_INS = B_BYTES / 1024;   // 1 KB wave loads per stage
     constexpr int A_PW = A_INS / NW, B_PW = B_INS / NW;
-    constexpr int LPS = A_PW + B_PW;           // loads per stage per lane
+    // MODE 2: B stored K-contiguous like A (BN rows of BK values); each thread
+    // owns NBS blocks of 8 K x 8 N values.
+    constexpr int NT = NW * 64;
+    constexpr int NBS = MODE == 2 ? (BK / 8) * (BN / 8) / NT : 0;
+    constexpr int LPS = MODE == 2 ? A_PW + 8 * NBS : A_PW + B_PW;   // loads per stage per lane
     constexpr int CPR = BN / 8;                // 16-byte chunks per B row
     constexpr int RPI = 64 / CPR;              // B rows per wave load
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(A_INS % NW == 0 && B_INS % NW == 0, "loads must split evenly over waves");
     static_assert(CPR >= 16 && 64 % CPR == 0, "BN must be 128 or 256");
     static_assert(NBUF >= 2 && NBUF * STAGE <= 160 * 1024, "LDS ring");
+    static_assert(MODE == 0 || (NBUF == 2 && BK / 16 >= 3), "register-filled stages need NBUF 2, >= 3 k-steps");
+    static_assert(MODE != 2 || NBS * NT == (BK / 8) * (BN / 8), "B blocks must split evenly over threads");
     static_assert((NBUF - 1) * LPS < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * STAGE];
@@ -171,10 +192,14 @@ gemm16_dma_kernel(GemmArgs args)
 
     const i4 rA = rsrc_words(static_cast<const char*>(args.A) + (long long)m0 * K * 2,
                              (long long)(M - m0) * K * 2);
+    const __amdgpu_buffer_rsrc_t rAb = make_rsrc(static_cast<const char*>(args.A) + (long long)m0 * K * 2,
+                                                 (long long)(M - m0) * K * 2);
     const long long b_bytes = (long long)K * N * 2;
 
     // One 1 KB wave load of stage `st` (relative to this split): loads
-    // 0 .. A_PW-1 fetch A rows, the rest B rows.
+    // 0 .. A_PW-1 fetch A rows, the rest B rows. Slot layout in LDS is the
+    // same in both modes: lane l of load q lands at dst(q) + 16 l.
+    u4 R[LPS];
     auto issue_one = [&](int st, int q) {
         const int k0 = kbeg + st * BK;
         unsigned char* buf = lds + (st % NBUF) * STAGE;
@@ -184,16 +209,81 @@ gemm16_dma_kernel(GemmArgs args)
             const int c = (lane % CPA) ^ ((row / RSW) % CPA);   // logical chunk stored at this slot
             const int gk = k0 + c * 8;
             const bool ok = m0 + row < M && gk < kend;
-            lds_load16(rA, lds_addr(buf + I * 1024), ok ? (row * K + gk) * 2 : kOOB);
+            const int off = ok ? (row * K + gk) * 2 : kOOB;
+            if constexpr (MODE != 1)
+                lds_load16(rA, lds_addr(buf + I * 1024), off);
+            else
+                R[q] = __builtin_amdgcn_raw_buffer_load_b128(rAb, off, 0, 0);
         } else {
             const int I = wave + (q - A_PW) * NW;
             const int row = I * RPI + lane / CPR;
             const int c = (lane % CPR) ^ (4 * (row & 3));
             const bool ok = k0 + row < kend && n0 + c * 8 < N;
             const long long bbase = ((long long)k0 * N + n0) * 2;
-            const i4 rB = rsrc_words(static_cast<const char*>(args.B) + bbase, b_bytes - bbase);
-            lds_load16(rB, lds_addr(buf + A_BYTES + I * 1024), ok ? (row * N + c * 8) * 2 : kOOB);
+            const int off = ok ? (row * N + c * 8) * 2 : kOOB;
+            if constexpr (MODE == 0) {
+                const i4 rB = rsrc_words(static_cast<const char*>(args.B) + bbase, b_bytes - bbase);
+                lds_load16(rB, lds_addr(buf + A_BYTES + I * 1024), off);
+            } else {
+                const __amdgpu_buffer_rsrc_t rB = make_rsrc(static_cast<const char*>(args.B) + bbase, b_bytes - bbase);
+                R[q] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
+            }
         }
+    };
+    // MODE 2: B block q (8 K rows x 8 columns) into registers, one 16-byte
+    // load per K row; rows past the split's K and columns past N load zero.
+    u4 RB[NBS > 0 ? NBS : 1][8];
+    auto issue_b = [&](int st, int q) {
+        const int k0 = kbeg + st * BK;
+        const int sb = tid + q * NT;
+        const int kc = sb % (BK / 8);
+        const int nb = (sb / (BK / 8)) * 8;
+        const long long bbase = ((long long)k0 * N + n0) * 2;
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(static_cast<const char*>(args.B) + bbase, b_bytes - bbase);
+        // Only K rows past the split's end must read zero. Columns past N read
+        // the next row's values (or zero past the end of B): they only reach
+        // output columns that are never stored.
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const bool ok = k0 + kc * 8 + r < kend;
+            RB[q][r] = __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? ((kc * 8 + r) * N + nb) * 2 : kOOB, 0, 0);
+        }
+    };
+    // MODE 2: transpose block q and store column nb + c as chunk kc of LDS
+    // row nb + c. Blocks with odd nb / 8 store their columns in the order
+    // c ^ 1, so the 16 lanes of one store hit rows of both parities (all 16
+    // bank groups).
+    auto write_b = [&](int st, int q) {
+        unsigned char* bb = lds + (st % NBUF) * STAGE + A_BYTES;
+        const int sb = tid + q * NT;
+        const int kc = sb % (BK / 8);
+        const int nb = (sb / (BK / 8)) * 8;
+        const unsigned odd = (nb >> 3) & 1;
+        // Column c ^ odd of the block is stored by store c: the 16-bit half
+        // picked from each dword is selected per lane through the v_perm
+        // selector, so no register is ever indexed by a lane-dependent value.
+        const unsigned sel_lo = odd ? 0x07060302u : 0x05040100u;   // even c
+        const unsigned sel_hi = odd ? 0x05040100u : 0x07060302u;   // odd c
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int d = c >> 1;
+            const unsigned sel = (c & 1) ? sel_hi : sel_lo;
+            u4 v;
+            v[0] = __builtin_amdgcn_perm(RB[q][1][d], RB[q][0][d], sel);
+            v[1] = __builtin_amdgcn_perm(RB[q][3][d], RB[q][2][d], sel);
+            v[2] = __builtin_amdgcn_perm(RB[q][5][d], RB[q][4][d], sel);
+            v[3] = __builtin_amdgcn_perm(RB[q][7][d], RB[q][6][d], sel);
+            const int row = nb + (c ^ (int)odd);
+            const int ph = kc ^ ((row / RSW) % CPA);
+            *reinterpret_cast<u4*>(bb + row * A_ROW + ph * 16) = v;
+        }
+    };
+
+    // MODE 1: write register slot q of stage `st` to its LDS place.
+    auto write_one = [&](int st, int q) {
+        unsigned char* buf = lds + (st % NBUF) * STAGE;
+        const int dst = q < A_PW ? (wave + q * NW) * 1024 : A_BYTES + (wave + (q - A_PW) * NW) * 1024;
+        *reinterpret_cast<u4*>(buf + dst + lane * 16) = R[q];
     };
 
     const int lrow = lane & 31;
@@ -208,6 +298,13 @@ gemm16_dma_kernel(GemmArgs args)
             const int row = wm0 + 32 * r + lrow;
             const int c = (2 * t + lgrp) ^ ((row / RSW) % CPA);
             fa[r] = *reinterpret_cast<const u4*>(buf + row * A_ROW + c * 16);
+        } else if constexpr (MODE == 2) {
+            const int j = r - TM;
+            const int row = wn0 + 32 * j + lrow;
+            const int c = (2 * t + lgrp) ^ ((row / RSW) % CPA);
+            const u4 v = *reinterpret_cast<const u4*>(buf + A_BYTES + row * A_ROW + c * 16);
+            fb[j][0] = u2{v[0], v[1]};
+            fb[j][1] = u2{v[2], v[3]};
         } else {
             const int j = (r - TM) >> 1, half = (r - TM) & 1;
             const int col = wn0 + 32 * j + 16 * (g16 & 1) + 4 * (s16 & 3);
@@ -234,7 +331,7 @@ gemm16_dma_kernel(GemmArgs args)
     };
 
     constexpr int NMF = TM * TN;          // MFMAs per k-step
-    constexpr int NRD = TM + 2 * TN;      // LDS reads per k-step
+    constexpr int NRD = MODE == 2 ? TM + TN : TM + 2 * TN;   // LDS reads per k-step
     constexpr int RPS = (NRD + NMF - 1) / NMF;   // reads per MFMA slot
 
     // One k-step: MFMA slot m issues MFMA m, then (while m < NRD) the next
@@ -242,32 +339,76 @@ gemm16_dma_kernel(GemmArgs args)
     // one of this wave's LDS loads every NMF / LPS slots. The order is pinned
     // so that no burst of loads ever blocks MFMA issue behind it.
     auto kstep = [&](const u4 (&fa)[TM], const u2 (&fb)[TN][2], const unsigned char* rbuf, int rt,
-                     u4 (&na)[TM], u2 (&nb)[TN][2], int load_stage) {
+                     u4 (&na)[TM], u2 (&nb)[TN][2], int load_stage, int write_stage, int bload_stage = -1) {
 #pragma unroll
         for (int m = 0; m < NMF; ++m) {
             mfma_one(m, fa, fb);
 #pragma unroll
             for (int r = m * RPS; r < (m + 1) * RPS; ++r)
                 if (r < NRD) read_one(rbuf, rt, r, na, nb);
-            if (load_stage >= 0) {
-                // loads q with ceil(q * NMF / LPS) == m, i.e. spread evenly over the slots
+            if constexpr (MODE == 2) {
+                // A: the A_PW straight-to-LDS loads; B: NBS blocks loaded (k-step 0)
+                // and transposed into LDS (next-to-last k-step), spread over slots.
+                if (load_stage >= 0) {
 #pragma unroll
-                for (int q = (m * LPS + NMF - 1) / NMF; q < ((m + 1) * LPS + NMF - 1) / NMF; ++q)
-                    if (q < LPS) issue_one(load_stage, q);
+                    for (int q = (m * A_PW + NMF - 1) / NMF; q < ((m + 1) * A_PW + NMF - 1) / NMF; ++q)
+                        if (q < A_PW) issue_one(load_stage, q);
+                }
+                if (bload_stage >= 0) {
+#pragma unroll
+                    for (int q = (m * NBS + NMF - 1) / NMF; q < ((m + 1) * NBS + NMF - 1) / NMF; ++q)
+                        if (q < NBS) issue_b(bload_stage, q);
+                }
+                if (write_stage >= 0) {
+#pragma unroll
+                    for (int q = (m * NBS + NMF - 1) / NMF; q < ((m + 1) * NBS + NMF - 1) / NMF; ++q)
+                        if (q < NBS) write_b(write_stage, q);
+                }
+            } else {
+                if (load_stage >= 0) {
+                    // loads q with ceil(q * NMF / LPS) == m, i.e. spread evenly over the slots
+#pragma unroll
+                    for (int q = (m * LPS + NMF - 1) / NMF; q < ((m + 1) * LPS + NMF - 1) / NMF; ++q)
+                        if (q < LPS) issue_one(load_stage, q);
+                }
+                if (write_stage >= 0) {
+#pragma unroll
+                    for (int q = (m * LPS + NMF - 1) / NMF; q < ((m + 1) * LPS + NMF - 1) / NMF; ++q)
+                        if (q < LPS) write_one(write_stage, q);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Fill the whole ring, then wait for stage 0.
-#pragma unroll
-    for (int st = 0; st < NBUF; ++st)
-#pragma unroll
-        for (int q = 0; q < LPS; ++q) issue_one(st, q);
-    wait_cnt<(NBUF - 1) * LPS, 15>();
-    barrier();
     u4 fa[2][TM];
     u2 fb[2][TN][2];
+    if constexpr (MODE == 0) {
+        // Fill the whole ring, then wait for stage 0.
+#pragma unroll
+        for (int st = 0; st < NBUF; ++st)
+#pragma unroll
+            for (int q = 0; q < LPS; ++q) issue_one(st, q);
+        wait_cnt<(NBUF - 1) * LPS, 15>();
+    } else if constexpr (MODE == 1) {
+#pragma unroll
+        for (int q = 0; q < LPS; ++q) issue_one(0, q);
+#pragma unroll
+        for (int q = 0; q < LPS; ++q) write_one(0, q);
+        wait_cnt<63, 0>();
+    } else {
+        // A of stages 0 and 1 straight to LDS, B of stage 0 through registers.
+#pragma unroll
+        for (int q = 0; q < A_PW; ++q) issue_one(0, q);
+#pragma unroll
+        for (int q = 0; q < NBS; ++q) issue_b(0, q);
+#pragma unroll
+        for (int q = 0; q < NBS; ++q) write_b(0, q);
+#pragma unroll
+        for (int q = 0; q < A_PW; ++q) issue_one(1, q);
+        wait_cnt<A_PW, 0>();   // everything but stage 1's A
+    }
+    barrier();
 #pragma unroll
     for (int r = 0; r < NRD; ++r) read_one(lds, 0, r, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
@@ -276,16 +417,31 @@ gemm16_dma_kernel(GemmArgs args)
         const unsigned char* cur = lds + (k % NBUF) * STAGE;
         const unsigned char* nxt = lds + ((k + 1) % NBUF) * STAGE;
         // k-steps 0 .. KSTEPS-2 of stage k, each reading the next k-step.
+        // MODE 1 loads stage k+1 into registers during k-step 0 and writes it
+        // to the free LDS slot during k-step KSTEPS-2; MODE 2 does the same
+        // for B only.
 #pragma unroll
-        for (int t = 0; t + 1 < KSTEPS; ++t)
-            kstep(fa[t & 1], fb[t & 1], cur, t + 1, fa[(t + 1) & 1], fb[(t + 1) & 1], -1);
+        for (int t = 0; t + 1 < KSTEPS; ++t) {
+            if constexpr (MODE == 2)
+                kstep(fa[t & 1], fb[t & 1], cur, t + 1, fa[(t + 1) & 1], fb[(t + 1) & 1], -1,
+                      t == KSTEPS - 2 ? k + 1 : -1, t == 0 ? k + 1 : -1);
+            else
+                kstep(fa[t & 1], fb[t & 1], cur, t + 1, fa[(t + 1) & 1], fb[(t + 1) & 1],
+                      (MODE == 1 && t == 0) ? k + 1 : -1, (MODE == 1 && t == KSTEPS - 2) ? k + 1 : -1);
+        }
         // Stage k fully read by this wave; this wave's part of stage k+1 landed.
-        wait_cnt<(NBUF - 2) * LPS, 0>();
+        if constexpr (MODE == 0)
+            wait_cnt<(NBUF - 2) * LPS, 0>();
+        else if constexpr (MODE == 1)
+            wait_cnt<63, 0>();
+        else
+            wait_cnt<0, 0>();
         barrier();
         // Last k-step of stage k: read k-step 0 of stage k+1 and refill the
-        // slot stage k leaves with stage k + NBUF meanwhile.
+        // LDS slot stage k leaves (MODE 0: whole stage k + NBUF; MODE 2: A of
+        // stage k + 2).
         constexpr int L = (KSTEPS - 1) & 1;
-        kstep(fa[L], fb[L], nxt, 0, fa[L ^ 1], fb[L ^ 1], k + NBUF);
+        kstep(fa[L], fb[L], nxt, 0, fa[L ^ 1], fb[L ^ 1], MODE == 0 ? k + NBUF : (MODE == 2 ? k + 2 : -1), -1);
         if constexpr (L == 0) {   // odd number of k-steps: next stage starts in set 1
 #pragma unroll
             for (int i = 0; i < TM; ++i) fa[0][i] = fa[1][i];
@@ -321,9 +477,9 @@ struct DmaKernels {
     int threads;
 };
 
-#define SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, gm, xr, ms, e16)                      \
-    {id, {nullptr, gemm16_dma_kernel<DT_BF16, BM, BN, WM, WN, BK, NBUF>,                         \
-          gemm16_dma_kernel<DT_F16, BM, BN, WM, WN, BK, NBUF>}, WM * WN * 64},
+#define SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, MODE, gm, xr, ms, e16)                \
+    {id, {nullptr, gemm16_dma_kernel<DT_BF16, BM, BN, WM, WN, BK, NBUF, MODE>,                   \
+          gemm16_dma_kernel<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE>}, WM * WN * 64},
 
 static const DmaKernels kDmaTable[] = {SAM_DMA_VARIANTS(SAM_DMA_ENTRY)};
 

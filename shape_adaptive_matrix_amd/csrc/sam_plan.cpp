@@ -35,10 +35,14 @@ namespace sam {
 
 #define SAM_STAGED_ROW(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16, pf32, pf16) \
     {id, name, KIND_STAGED, 7, BM, BN, WM, WN, BLK, 2, 0, gm, xr, ms, e32, e16},
-#define SAM_DMA_ROW(id, name, BM, BN, WM, WN, BK, NBUF, gm, xr, ms, e16) \
+#define SAM_DMA_ROW(id, name, BM, BN, WM, WN, BK, NBUF, MODE, gm, xr, ms, e16) \
     {id, name, KIND_DMA, (1 << DT_BF16) | (1 << DT_F16), BM, BN, WM, WN, 32, NBUF, BK, gm, xr, ms, 0.0, e16},
 
-static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)};
+#define SAM_STREAM_ROW(id, name, BM, BN, KB, ms, eff) \
+    {id, name, KIND_STREAM, (1 << DT_F32), BM, BN, 1, 1, 16, 1, KB, 1, 0, ms, eff, 0.0},
+
+static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
+                                        SAM_STREAM_VARIANTS(SAM_STREAM_ROW)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -51,7 +55,7 @@ const Variant* variant_get(int id)
 
 int k_stage(const Variant& v, int dtype)
 {
-    if (v.kind == KIND_DMA) return v.bk;
+    if (v.kind == KIND_DMA || v.kind == KIND_STREAM) return v.bk;
     return dtype == DT_F32 ? 32 : 64;   // one 128-byte LDS row
 }
 
@@ -70,6 +74,19 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
     const long long tiles_m = cdiv(M, v.bm), tiles_n = cdiv(N, v.bn);
     const long long wgs = tiles_m * tiles_n * split;
     const double in_b = dtype == DT_F32 ? 4.0 : 2.0;
+    const double mb = 1e-6;                                   // bytes -> MB; GB/s = MB/ms
+
+    if (v.kind == KIND_STREAM) {
+        // HBM-bound: the operands cross HBM once at the variant's share of the
+        // read rate, scaled down while fewer than two 8-wave workgroups per CU
+        // are resident to keep loads in flight; then the split-K partials.
+        const double alg = in_b * (double)(M * K + K * N) + 4.0 * (double)(M * N);
+        const double part = split > 1 ? 4.0 * (double)(M * N) * split : 0.0;
+        const double occ = fmin(1.0, (double)wgs / (2.0 * kDev.cus));
+        double t = (alg + part) * mb / (kDev.hbm_gbs * v.eff_f32 * occ) * 1e3 + kDev.launch_us;
+        if (split > 1) t += (part + 4.0 * M * N) * mb / kDev.hbm_gbs * 1e3 + kDev.launch_us;
+        return t;
+    }
 
     double eff = dtype == DT_F32 ? v.eff_f32 : v.eff_h16;
     if (!a_vec) eff *= 0.85;
@@ -81,14 +98,13 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
     // Every workgroup ends by writing its BM x BN FP32 tile (to C or to its
     // split's partials). Workgroups of one round finish together, so that
     // write is an HBM-bound phase of its own rather than hidden under MFMA.
-    const double mb = 1e-6;                                   // bytes -> MB; GB/s = MB/ms
     const double concurrent = (double)(wgs < kDev.cus ? wgs : kDev.cus);
     const double t_epi = concurrent * v.bm * v.bn * 4.0 * mb / kDev.hbm_write_gbs * 1e3;
     const double t_mfma = rounds * (t_wg + t_epi);
 
     const double alg = in_b * (double)(M * K + K * N) + 4.0 * (double)(M * N);
     const double part = split > 1 ? 4.0 * (double)(M * N) * split : 0.0;
-    const double t_hbm = (alg + part) * mb / kDev.hbm_gbs * 1e3;
+    const double t_hbm = (alg + part) * mb / (kDev.hbm_gbs * kDev.tiled_hbm_frac) * 1e3;
     const double tile_traffic = in_b * ((double)M * K * tiles_n + (double)K * N * tiles_m);
     const double t_l2 = tile_traffic * mb / kDev.l2_gbs * 1e3;
 
@@ -155,6 +171,9 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     if (M < 0 || N < 0 || K < 0) return false;
     // The LDS-ring kernels take whole 16-byte pieces of A and B rows.
     if (v->kind == KIND_DMA && (K % 8 != 0 || N % 8 != 0)) return false;
+    // The streaming kernels cover at most 16 rows (16 x 64 tile) or 16
+    // columns (64 x 16 tile) of C.
+    if (v->kind == KIND_STREAM && (v->bm == 16 ? M > 16 : N > 16)) return false;
     if (split_req > 0) {
         if (split_req > 1 && (K == 0 || !split_admissible(*v, K, dtype, split_req))) return false;
         fill_plan(*v, M, N, K, dtype, split_req, out);

@@ -7,7 +7,14 @@
 //   X(id, name, BM, BN, WM, WN, BLK, group_m, xcd_remap, max_split, eff_f32, eff_h16, pf_f32, pf_h16)
 // LDS-ring variants (sam_kernels_dma.hip): 16-bit operands with K % 8 == 0
 // and N % 8 == 0 only; loads write LDS directly into a ring of NBUF stages.
-//   D(id, name, BM, BN, WM, WN, BK, NBUF, group_m, xcd_remap, max_split, eff_h16)
+//   D(id, name, BM, BN, WM, WN, BK, NBUF, MODE, group_m, xcd_remap, max_split, eff_h16)
+// MODE 0 loads straight into LDS; MODE 1 loads into registers and writes LDS
+// (names start with "q"); MODE 2 loads A straight into LDS and B through
+// registers, transposed to K-contiguous rows (names start with "h").
+// Streaming variants (sam_kernels_stream.hip): FP32 only, M <= 16 (tile
+// 16 x 64) or N <= 16 (tile 64 x 16); the large operand streams from HBM into
+// registers, KB values of K per workgroup block.
+//   S(id, name, BM, BN, KB, max_split, eff_hbm)
 // eff_* is the fraction of the MFMA peak the variant sustains in steady
 // state, the calibration the cost model uses.
 #pragma once
@@ -23,10 +30,21 @@
     X(7, "t256x256_w2x4_b32", 256, 256, 2, 4, 32, 8, 1,  8, 0.88, 0.35, 1, 1)
 
 #define SAM_DMA_VARIANTS(D)                                                              \
-    D(8, "r256x256_w2x2_k32n4",  256, 256, 2, 2, 32, 4, 8, 1, 8, 0.45)                   \
-    D(9, "r128x256_w2x2_k32n4",  128, 256, 2, 2, 32, 4, 8, 1, 8, 0.37)                   \
-    D(10, "r256x128_w2x2_k32n4", 256, 128, 2, 2, 32, 4, 8, 1, 8, 0.36)                   \
-    D(11, "r128x128_w2x2_k32n4", 128, 128, 2, 2, 32, 4, 8, 1, 16, 0.34)                  \
-    D(12, "r256x256_w2x2_k64n2", 256, 256, 2, 2, 64, 2, 8, 1, 8, 0.47)                   \
-    D(13, "r256x128_w2x2_k64n3", 256, 128, 2, 2, 64, 3, 8, 1, 8, 0.38)                   \
-    D(14, "r128x256_w2x2_k64n3", 128, 256, 2, 2, 64, 3, 8, 1, 8, 0.37)
+    D(8, "r256x256_w2x2_k32n4",  256, 256, 2, 2, 32, 4, 0, 8, 1, 8, 0.45)                   \
+    D(9, "r128x256_w2x2_k32n4",  128, 256, 2, 2, 32, 4, 0, 8, 1, 8, 0.37)                   \
+    D(10, "r256x128_w2x2_k32n4", 256, 128, 2, 2, 32, 4, 0, 8, 1, 8, 0.36)                   \
+    D(11, "r128x128_w2x2_k32n4", 128, 128, 2, 2, 32, 4, 0, 8, 1, 16, 0.34)                  \
+    D(12, "r256x256_w2x2_k64n2", 256, 256, 2, 2, 64, 2, 0, 8, 1, 8, 0.47)                   \
+    D(13, "r256x128_w2x2_k64n3", 256, 128, 2, 2, 64, 3, 0, 8, 1, 8, 0.38)                   \
+    D(14, "r128x256_w2x2_k64n3", 128, 256, 2, 2, 64, 3, 0, 8, 1, 8, 0.37)                \
+    D(15, "q256x256_w2x2_k64",   256, 256, 2, 2, 64, 2, 1, 8, 1, 8, 0.44)                \
+    D(16, "h256x256_w2x2_k64",   256, 256, 2, 2, 64, 2, 2, 8, 1, 8, 0.36)                \
+    D(17, "r256x256_w2x4_k64n2", 256, 256, 2, 4, 64, 2, 0, 8, 1, 8, 0.50)                \
+    D(18, "r256x256_w4x2_k64n2", 256, 256, 4, 2, 64, 2, 0, 8, 1, 8, 0.495)                \
+    D(19, "r256x256_w2x4_k32n4", 256, 256, 2, 4, 32, 4, 0, 8, 1, 8, 0.47)
+
+#define SAM_STREAM_VARIANTS(S)                                                           \
+    S(20, "sm16x64_k2048", 16, 64, 2048, 32, 0.92)                                       \
+    S(21, "sn64x16_k2048", 64, 16, 2048, 32, 0.75)                                       \
+    S(22, "sm16x64_k1024", 16, 64, 1024, 32, 0.97)                                       \
+    S(23, "sn64x16_k1024", 64, 16, 1024, 32, 0.81)

@@ -88,6 +88,37 @@ def test_every_variant_random(vid, dtype):
     assert rel_rms(C, ref) <= tol
 
 
+# Skinny shapes (M <= 16 or N <= 16, the streaming variants' domain, also run
+# by every other variant that takes them): several K blocks per split, a K
+# tail inside a wave, K % 4 != 0 and N % 4 != 0 element paths, rows and
+# columns past one tile.
+SKINNY = [(16, 1000, 5000), (5, 77, 4100), (13, 4096, 2049), (1, 3, 9001), (16, 64, 2048),
+          (1000, 16, 5000), (777, 3, 4099), (2000, 12, 3002), (64, 16, 1024), (3, 5, 70)]
+_SKINNY_REF = {}
+
+
+@pytest.mark.parametrize("vid", range(sam.variant_count()))
+def test_every_variant_dyadic_skinny(vid):
+    ran = 0
+    for (M, N, K) in SKINNY:
+        if not _supported(vid, M, N, K, "f32", 1):
+            continue
+        A, B = ints_operands(M, N, K, "f32", seed=M * 5 + N * 11 + K)
+        if (M, N, K) not in _SKINNY_REF:
+            _SKINNY_REF[(M, N, K)] = orc().gemm("f32", A, B)
+        ref = _SKINNY_REF[(M, N, K)]
+        for s in (0, 1, 2, 3, 4, 8):
+            if not _supported(vid, M, N, K, "f32", s):
+                continue
+            print(f"[skinny] variant {vid} {(M, N, K)} split {s}", flush=True)
+            C = run(A, B, "f32", variant=vid, split=s)
+            bad = bitexact_mismatches(C, ref)
+            assert bad == 0, f"variant {vid} {(M, N, K)} split {s}: {bad} mismatches"
+            ran += 1
+    if ran == 0:
+        pytest.skip(f"variant {vid} takes no skinny FP32 shape")
+
+
 def test_c_is_write_only_and_fully_written():
     """NaN-prefilled C: every element written; guard band after C untouched."""
     M, N, K = 99, 77, 55
@@ -117,23 +148,26 @@ def test_k_zero_writes_positive_zero():
     assert np.all(C.cpu().numpy().view(np.uint32) == 0)
 
 
-def test_inf_beyond_k_tail_is_not_read():
-    """An Inf just past row i's K range in memory must not leak into C: the K
-    tail is zero-filled on both operands."""
-    M, N, K = 64, 64, 37
-    store = np.zeros((M * K + 64,), np.float32)
-    A = store[:M * K].reshape(M, K)
-    A[:] = 1.0
-    store[M * K:] = np.inf
-    B = np.ones((K, N), np.float32)
-    dstore = torch.from_numpy(store).cuda()
-    dA = dstore[:M * K].view(M, K)
+@pytest.mark.parametrize("shape", [(64, 64, 37), (5, 70, 1037), (70, 5, 1037)])
+def test_inf_beyond_k_tail_is_not_read(shape):
+    """An Inf just past A and just past B in memory must not leak into C: the
+    K tail is zero-filled on both operands."""
+    M, N, K = shape
+    sA = np.full((M * K + 64,), np.inf, np.float32)
+    sA[:M * K] = 1.0
+    sB = np.full((K * N + 64,), np.inf, np.float32)
+    sB[:K * N] = 1.0
+    dA = torch.from_numpy(sA).cuda()[:M * K].view(M, K)
+    dB = torch.from_numpy(sB).cuda()[:K * N].view(K, N)
+    ran = 0
     for vid in range(sam.variant_count()):
         if not _supported(vid, M, N, K, "f32"):
             continue
-        C = sam.gemm_variant(vid, dA, to_dev(B, "f32"))
+        C = sam.gemm_variant(vid, dA, dB)
         torch.cuda.synchronize()
         assert np.all(C.cpu().numpy() == K), vid
+        ran += 1
+    assert ran > 0
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
