@@ -36,7 +36,18 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense MFM
 PEAK_HBM_GBS = 8000.0
 
 
-KERNEL_SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_internal.h"]
+KERNEL_SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_kernels_stream.hip", "sam_kernels_f32ring.hip",
+                  "sam_dma.h", "sam_internal.h", "sam_variants.h"]
+
+# Kernel function of a plan, by the first letter of its variant name.
+KERNEL_OF = {"t": "sam::gemm_kernel", "r": "sam::gemm16_dma_kernel", "q": "sam::gemm16_dma_kernel",
+             "h": "sam::gemm16_dma_kernel", "s": "sam::stream_m_kernel / sam::stream_n_kernel",
+             "f": "sam::gemm_f32_ring_kernel"}
+
+
+def kernel_name(plan) -> str:
+    variant = plan["name"].split("_", 1)[1]
+    return KERNEL_OF.get(variant[0], "?")
 
 
 def src_digest() -> str:
@@ -187,8 +198,8 @@ def load_traffic(workload: str, digest: str):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="f32_2048")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -261,7 +272,7 @@ def main():
             "bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_TFLOPS[w.dtype],
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS[w.dtype], 4),
             "traffic": None if split else load_traffic(w.name, digest),
-            "kernel": "sam::gemm_kernel" + (" + splitk_reduce_kernel" if split else ""),
+            "kernel": kernel_name(g["plan"]) + (" + sam::splitk_reduce_kernel" if split else ""),
             "per_launch_flops": w.flops, "src_digest": digest,
         },
         "build": sam.build_info(),

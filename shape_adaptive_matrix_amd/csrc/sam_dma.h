@@ -1,0 +1,81 @@
+// Device helpers shared by the kernels that load LDS straight from memory.
+#pragma once
+
+#include "sam_internal.h"
+
+namespace sam {
+namespace dma {
+
+typedef int i4 __attribute__((ext_vector_type(4)));
+
+constexpr int kOOB = 0x7FFFFFF0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes >= kOOB ? kOOB : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// The same raw buffer resource as four dwords (base, stride 0, record count
+// in bytes, default format word) for the LDS load below.
+__device__ __forceinline__ i4 rsrc_words(const void* base, long long bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes >= kOOB ? kOOB : (int)bytes);
+    const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+    return i4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xFFFFu), n, 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset `voff` into LDS at (wave-uniform)
+// `lds_base` + 16 * lane; offsets past the record count store zeros. Written
+// as inline assembly so that the compiler does not treat every later LDS
+// read as dependent on it (it would otherwise wait for all outstanding loads
+// before them); the kernels count these loads themselves with wait_cnt.
+__device__ __forceinline__ void lds_load16(const i4& rsrc, unsigned lds_base, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// s_waitcnt with vmcnt <= VM and lgkmcnt <= LG (expcnt untouched).
+template <int VM, int LG>
+__device__ __forceinline__ void wait_cnt() {
+    static_assert(VM >= 0 && VM < 64 && LG >= 0 && LG < 16, "counter range");
+    __builtin_amdgcn_s_waitcnt((VM & 0xF) | (0x7 << 4) | (LG << 8) | ((VM >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence __syncthreads adds (that fence
+// would drain every outstanding LDS load); the asm statements keep the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup id -> (tile row, tile column, split): each XCD (workgroups go to
+// the 8 XCDs round-robin) owns one contiguous range of logical ids, walked in
+// grouped-raster order so neighbouring tiles share panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int wg, const GemmArgs& a, int& tm, int& tn, int& s) {
+    const int total = a.tiles_m * a.tiles_n * a.split;
+    int L = wg;
+    if (a.xcd_remap) {
+        const int q = total >> 3, rem = total & 7, x = wg & 7, y = wg >> 3;
+        L = (x < rem) ? x * (q + 1) + y : rem * (q + 1) + (x - rem) * q + y;
+    }
+    const int tiles = a.tiles_m * a.tiles_n;
+    s = L / tiles;
+    const int t = L - s * tiles;
+    const int per_group = a.group_m * a.tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * a.group_m;
+    const int gsz = min(a.tiles_m - first_m, a.group_m);
+    const int r = t - g * per_group;
+    tm = first_m + r % gsz;
+    tn = r / gsz;
+}
+
+}  // namespace dma
+}  // namespace sam

@@ -25,7 +25,7 @@ struct DeviceModel {
 };
 
 // Static description of a tile/schedule variant.
-enum Kind : int { KIND_STAGED = 0, KIND_DMA = 1, KIND_STREAM = 2 };
+enum Kind : int { KIND_STAGED = 0, KIND_DMA = 1, KIND_STREAM = 2, KIND_F32RING = 3 };
 
 struct Variant {
     int id;
@@ -92,6 +92,7 @@ int k_stage(const Variant& v, int dtype);   // K per LDS stage
 hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_stream(const Plan& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const float* parts, int split, long long part_stride,
                          float* C, long long count, hipStream_t s);
 hipError_t launch_zero(float* C, long long count, hipStream_t s);

@@ -1,0 +1,340 @@
+// FP32 GEMM kernel for gfx950 on the CDNA4 LDS data path.
+//
+// C = A*B in FP32 (page "Measured data point on fixed-tile vs shape-adaptive
+// GEMM", the FP32 square sizes of its results table), row-major A[M][K],
+// B[K][N], K % 4 == 0 and N % 4 == 0 (16-byte pieces of rows).
+//
+//  * Global -> LDS goes through buffer loads that write LDS directly, 1 KB
+//    per wave instruction (lane l lands at base + 16 l), so neither operand
+//    passes through registers and no VALU work is spent on the way. The LDS
+//    holds a ring of NBUF stages of BK values of K; the loads of a stage are
+//    issued NBUF - 1 stages ahead, spread one per MFMA slot. Out-of-range
+//    offsets write zeros, so M, N and K tails cost nothing extra.
+//  * A sits in LDS K-contiguous (BK * 4-byte rows, 16-byte chunks
+//    XOR-swizzled by the row) and is read as one 128-bit fragment per lane:
+//    four consecutive K values of one row.
+//  * B sits in LDS in its natural N-contiguous layout and is read V = 4 (or
+//    2) consecutive columns of one K row at a time (128- or 64-bit reads).
+//    The 32x32x2 MFMA takes one B value per lane (column lane % 32), so the V
+//    columns feed V MFMAs that each cover every V-th column of a 32 V-column
+//    group: MFMA v produces columns n + V j + v, j < 32. Only the output
+//    column order is permuted, and it is undone at the store, where each
+//    lane writes its V adjacent columns as one 4 V-byte store.
+//  * K slots: lanes 32..63 of an MFMA take the second K value of its pair.
+//    Within a chunk step a lane with K-slot group g reads A chunk 2 c + g
+//    (values 8 c + 4 g .. + 3) and B rows 8 c + 4 g + e; MFMA e of the step
+//    multiplies element e of both, so every product pairs matching K.
+//  * KS = 2 splits each stage's chunk steps between two halves of the
+//    workgroup's waves, so 8 waves can each own a 64x64 piece of a 128x128
+//    tile (more MFMAs per LDS read than 8 disjoint 32x64 pieces). The two
+//    partial sums of each piece meet once at the end through LDS; a + b is
+//    the same in either order, so the result does not depend on which wave
+//    adds, and the K order stays fixed.
+//  * One barrier per stage, between its last two chunk steps: before it
+//    every wave has read the whole stage and seen its own loads of the next
+//    stage land; after it the next stage's first fragments are read while
+//    the last chunk step's MFMAs run, and the freed slot is refilled.
+// No atomics and a fixed K order per output: repeated runs give the same
+// bits.
+#include "sam_dma.h"
+#include "sam_internal.h"
+#include "sam_variants.h"
+
+namespace sam {
+
+namespace f32ring {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void mfma(v16f& c, unsigned a, unsigned b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a), __uint_as_float(b), c, 0, 0, 0);
+}
+
+}  // namespace f32ring
+
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS>
+__global__ void __launch_bounds__(WM * WN * KS * 64)
+__attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / (NBUF * (BM + BN) * BK * 4)) * WM * WN * KS + 3) / 4)))
+gemm_f32_ring_kernel(GemmArgs args)
+{
+    using namespace dma;
+    using namespace f32ring;
+    static_assert(BK == 32 || BK == 64, "K per stage: 128- or 256-byte A rows");
+    constexpr int NP = WM * WN;                // wave positions in the tile
+    constexpr int NW = NP * KS;                // waves
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int CG = 32 * V;                 // columns per column group
+    constexpr int TM = WTM / 32, TN = WTN / CG;
+    constexpr int A_ROW = BK * 4;              // bytes per A row in LDS
+    constexpr int CPA = A_ROW / 16;            // 16-byte chunks per A row
+    constexpr int RPA = 1024 / A_ROW;          // A rows per wave load
+    constexpr int RSW = 256 / A_ROW;           // A rows sharing one 256-byte bank sweep
+    constexpr int KSTEPS = BK / 8;             // chunk steps per stage
+    constexpr int KH = KSTEPS / KS;            // chunk steps per stage per wave
+    constexpr int A_BYTES = BM * A_ROW;
+    constexpr int B_ROW = BN * 4;
+    constexpr int B_BYTES = BK * B_ROW;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_INS = A_BYTES / 1024, B_INS = B_BYTES / 1024;
+    constexpr int A_PW = A_INS / NW, B_PW = B_INS / NW;
+    constexpr int LPS = A_PW + B_PW;           // 1 KB loads per stage per wave
+    static_assert(V == 2 || V == 4, "B read width");
+    static_assert(WTM % 32 == 0 && WTN % CG == 0, "wave tile: 32-row blocks, 32 V-column groups");
+    static_assert(A_INS % NW == 0 && B_INS % NW == 0, "loads must split evenly over waves");
+    static_assert(NBUF >= 2 && NBUF * STAGE <= 160 * 1024, "LDS ring");
+    static_assert((NBUF - 1) * LPS < 64, "vmcnt range");
+    static_assert(KS == 1 || KS == 2, "intra-workgroup K split");
+    static_assert(KH >= 2, "the barrier sits before each wave's last chunk step");
+    static_assert(KS == 1 || TM % 2 == 0, "K-split halves exchange half of the row blocks");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    int tm, tn, s;
+    tile_coords(blockIdx.x, args, tm, tn, s);
+    const int M = args.M, N = args.N, K = args.K;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kbeg = s * args.k_chunk;
+    const int kend = min(K, kbeg + args.k_chunk);
+    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+    const int pos = wave % NP, half = wave / NP;
+    const int wm0 = (pos / WN) * WTM;
+    const int wn0 = (pos % WN) * WTN;
+    const int tbase = half * KH;               // this wave's first chunk step of a stage
+
+    const i4 rA = rsrc_words(reinterpret_cast<const char*>(args.A) + (long long)m0 * K * 4,
+                             (long long)(M - m0) * K * 4);
+    const long long b_bytes = (long long)K * N * 4;
+
+    // Wave load q of stage `st`: q < A_PW fetch A rows (RPA per load, chunks
+    // placed swizzled: the lane at physical chunk p loads logical chunk
+    // p ^ ((row / RSW) % CPA)), the rest B rows in natural order.
+    auto issue_one = [&](int st, int q) {
+        const int k0 = kbeg + st * BK;
+        unsigned char* buf = lds + (st % NBUF) * STAGE;
+        if (q < A_PW) {
+            const int I = wave + q * NW;
+            const int row = I * RPA + lane / CPA;
+            const int c = (lane % CPA) ^ ((row / RSW) % CPA);
+            const int gk = k0 + 4 * c;
+            const bool ok = m0 + row < M && gk < kend;
+            lds_load16(rA, lds_addr(buf + I * 1024), ok ? (row * K + gk) * 4 : kOOB);
+        } else {
+            const int I = wave + (q - A_PW) * NW;
+            const int byte = I * 1024 + 16 * lane;
+            const int row = byte / B_ROW, col = (byte % B_ROW) / 4;
+            const bool ok = k0 + row < kend && n0 + col < N;
+            const long long bbase = ((long long)k0 * N + n0) * 4;
+            const i4 rB = rsrc_words(reinterpret_cast<const char*>(args.B) + bbase, b_bytes - bbase);
+            lds_load16(rB, lds_addr(buf + A_BYTES + I * 1024), ok ? (row * N + col) * 4 : kOOB);
+        }
+    };
+
+    const int lrow = lane & 31;
+    const int g = lane >> 5;
+    // Fragment read r of chunk step t: r < TM is A block r (row wm0 + 32 r +
+    // lrow, chunk 2 t + g); then B reads (j, e) = ((r - TM) / 4, (r - TM) % 4):
+    // row 8 t + 4 g + e, columns wn0 + CG j + V lrow .. + V - 1.
+    constexpr int NRD = TM + 4 * TN;
+    auto read_one = [&](const unsigned char* buf, int t, int r, u4 (&fa)[TM], u4 (&fb)[TN][4]) {
+        if (r < TM) {
+            const int row = wm0 + 32 * r + lrow;
+            const int c = (2 * t + g) ^ ((row / RSW) % CPA);
+            fa[r] = *reinterpret_cast<const u4*>(buf + row * A_ROW + c * 16);
+        } else {
+            const int j = (r - TM) >> 2, e = (r - TM) & 3;
+            const int row = 8 * t + 4 * g + e;
+            const unsigned char* p = buf + A_BYTES + row * B_ROW + (wn0 + CG * j + V * lrow) * 4;
+            if constexpr (V == 4) {
+                fb[j][e] = *reinterpret_cast<const u4*>(p);
+            } else {
+                typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+                const u2 x = *reinterpret_cast<const u2*>(p);
+                fb[j][e] = u4{x[0], x[1], 0u, 0u};
+            }
+        }
+    };
+
+    v16f acc[TM][TN][V];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][v][r] = 0.0f;
+
+    // MFMA m of a chunk step: e = K element, then A block i, column group j,
+    // column phase v (so the same accumulator recurs every V TM TN MFMAs).
+    constexpr int NMF = 4 * V * TM * TN;
+    auto mfma_one = [&](int m, const u4 (&fa)[TM], const u4 (&fb)[TN][4]) {
+        const int e = m / (V * TM * TN);
+        const int rest = m % (V * TM * TN);
+        const int i = rest / (V * TN), j = (rest / V) % TN, v = rest % V;
+        mfma(acc[i][j][v], fa[i][e], fb[j][e][v]);
+    };
+
+    constexpr int RPS = (NRD + NMF - 1) / NMF;   // reads per MFMA slot
+    // One chunk step: MFMA slot m issues MFMA m, then (while reads remain) the
+    // next step's read(s) into the other fragment set, then the wave loads q
+    // with ceil(q NMF / LPS) == m when a stage is being loaded. The order is
+    // pinned so no burst of loads ever blocks MFMA issue behind it.
+    auto kstep = [&](const u4 (&fa)[TM], const u4 (&fb)[TN][4], const unsigned char* rbuf, int rt,
+                     u4 (&na)[TM], u4 (&nb)[TN][4], int load_stage) {
+#pragma unroll
+        for (int m = 0; m < NMF; ++m) {
+            mfma_one(m, fa, fb);
+#pragma unroll
+            for (int r = m * RPS; r < (m + 1) * RPS; ++r)
+                if (r < NRD) read_one(rbuf, rt, r, na, nb);
+            if (load_stage >= 0) {
+#pragma unroll
+                for (int q = (m * LPS + NMF - 1) / NMF; q < ((m + 1) * LPS + NMF - 1) / NMF; ++q)
+                    if (q < LPS) issue_one(load_stage, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    u4 fa[2][TM];
+    u4 fb[2][TN][4];
+    // Fill the whole ring, then wait for stage 0.
+#pragma unroll
+    for (int st = 0; st < NBUF; ++st)
+#pragma unroll
+        for (int q = 0; q < LPS; ++q) issue_one(st, q);
+    wait_cnt<(NBUF - 1) * LPS, 15>();
+    barrier();
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) read_one(lds, tbase, r, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int k = 0; k < nk; ++k) {
+        const unsigned char* cur = lds + (k % NBUF) * STAGE;
+        const unsigned char* nxt = lds + ((k + 1) % NBUF) * STAGE;
+#pragma unroll
+        for (int t = 0; t + 1 < KH; ++t)
+            kstep(fa[t & 1], fb[t & 1], cur, tbase + t + 1, fa[(t + 1) & 1], fb[(t + 1) & 1], -1);
+        // Stage k fully read by this wave; this wave's part of stage k+1 landed.
+        wait_cnt<(NBUF - 2) * LPS, 0>();
+        barrier();
+        // Last chunk step of stage k: read this wave's first step of stage k+1
+        // and refill the slot stage k leaves with stage k + NBUF.
+        constexpr int L = (KH - 1) & 1;
+        kstep(fa[L], fb[L], nxt, tbase, fa[L ^ 1], fb[L ^ 1], k + NBUF);
+        if constexpr (L == 0) {   // odd number of chunk steps: next stage starts in set 1
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[0][i] = fa[1][i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fb[0][j][e] = fb[1][j][e];
+        }
+    }
+    wait_cnt<0, 0>();   // no LDS load may still be in flight when the workgroup ends
+
+    // K split: the half-0 wave of a position keeps row blocks [0, TM/2) and
+    // the half-1 wave [TM/2, TM); each hands the other half's partial sums
+    // over through LDS (the ring is idle now) and adds the partner's. The
+    // tail is instantiated per half so every accumulator index is static.
+    constexpr int I0 = KS == 2 ? TM / 2 : TM;  // row blocks each wave stores
+    float* outp = args.out + (long long)s * args.part_stride + (long long)m0 * N + n0;
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(outp, ((long long)(M - m0) * N - n0) * 4);
+    auto finish = [&](auto hc) {
+        constexpr int H = decltype(hc)::value;
+        constexpr int IB = KS == 2 ? H * I0 : 0;
+        if constexpr (KS == 2) {
+            constexpr int GF = I0 * TN * V * 16;   // floats handed over per lane
+            static_assert(NP * 2 * 64 * GF * 4 <= NBUF * STAGE, "exchange fits the ring");
+            typedef float v4f __attribute__((ext_vector_type(4)));
+            v4f* xs = reinterpret_cast<v4f*>(lds);
+            const int mine = (pos * 2 + H) * 64 * (GF / 4), theirs = (pos * 2 + (1 - H)) * 64 * (GF / 4);
+            barrier();   // every wave is past its last read of the ring
+#pragma unroll
+            for (int ii = 0; ii < I0; ++ii)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < V; ++v)
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int f4 = ((ii * TN + j) * V + v) * 4 + r4;
+                            const v16f& x = acc[(1 - H) * I0 + ii][j][v];
+                            xs[mine + f4 * 64 + lane] = v4f{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]};
+                        }
+            __syncthreads();
+#pragma unroll
+            for (int ii = 0; ii < I0; ++ii)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < V; ++v)
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int f4 = ((ii * TN + j) * V + v) * 4 + r4;
+                            const v4f x = xs[theirs + f4 * 64 + lane];
+                            v16f& y = acc[IB + ii][j][v];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) y[4 * r4 + q] = y[4 * r4 + q] + x[q];
+                        }
+        }
+        // Accumulator element r of acc[i][j][v], lane (lrow, g): row wm0 +
+        // 32 i + 8 (r / 4) + 4 g + r % 4, column wn0 + CG j + V lrow + v.
+#pragma unroll
+        for (int ii = 0; ii < I0; ++ii)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int i = IB + ii;
+                const int col = wn0 + CG * j + V * lrow;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm0 + 32 * i + ((r >> 2) << 3) + (g << 2) + (r & 3);
+                    const bool ok = m0 + row < M && n0 + col < N;
+                    const int off = ok ? (row * N + col) * 4 : kOOB;
+                    if constexpr (V == 4) {
+                        const u4 v = {__float_as_uint(acc[IB + ii][j][0][r]), __float_as_uint(acc[IB + ii][j][1][r]),
+                                      __float_as_uint(acc[IB + ii][j][2][r]), __float_as_uint(acc[IB + ii][j][3][r])};
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, 0);
+                    } else {
+                        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+                        const u2 v = {__float_as_uint(acc[IB + ii][j][0][r]), __float_as_uint(acc[IB + ii][j][1][r])};
+                        __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
+                    }
+                }
+            }
+    };
+    if (KS == 1 || half == 0)
+        finish(std::integral_constant<int, 0>{});
+    else
+        finish(std::integral_constant<int, 1>{});
+}
+
+typedef void (*F32RingFn)(GemmArgs);
+
+struct F32RingKernel {
+    int id;
+    F32RingFn fn;
+    int threads;
+};
+
+#define SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, gm, xr, ms, e32) \
+    {id, gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS>, WM * WN * KS * 64},
+
+static const F32RingKernel kF32RingTable[] = {SAM_F32RING_VARIANTS(SAM_F32RING_ENTRY)};
+
+hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s)
+{
+    for (const F32RingKernel& k : kF32RingTable) {
+        if (k.id != p.variant_id) continue;
+        if (p.dtype != DT_F32) return hipErrorInvalidDeviceFunction;
+        hipLaunchKernelGGL(k.fn, dim3((unsigned)p.grid), dim3(k.threads), 0, s, a);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidDeviceFunction;
+}
+
+}  // namespace sam

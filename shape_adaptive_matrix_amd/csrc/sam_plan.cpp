@@ -41,8 +41,11 @@ namespace sam {
 #define SAM_STREAM_ROW(id, name, BM, BN, KB, ms, eff) \
     {id, name, KIND_STREAM, (1 << DT_F32), BM, BN, 1, 1, 16, 1, KB, 1, 0, ms, eff, 0.0},
 
+#define SAM_F32RING_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, gm, xr, ms, e32) \
+    {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, 32, NBUF, BK, gm, xr, ms, e32, 0.0},
+
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
-                                        SAM_STREAM_VARIANTS(SAM_STREAM_ROW)};
+                                        SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -55,7 +58,7 @@ const Variant* variant_get(int id)
 
 int k_stage(const Variant& v, int dtype)
 {
-    if (v.kind == KIND_DMA || v.kind == KIND_STREAM) return v.bk;
+    if (v.kind != KIND_STAGED) return v.bk;
     return dtype == DT_F32 ? 32 : 64;   // one 128-byte LDS row
 }
 
@@ -171,6 +174,8 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     if (M < 0 || N < 0 || K < 0) return false;
     // The LDS-ring kernels take whole 16-byte pieces of A and B rows.
     if (v->kind == KIND_DMA && (K % 8 != 0 || N % 8 != 0)) return false;
+    // The FP32 ring kernels take whole 16-byte pieces of A and B rows.
+    if (v->kind == KIND_F32RING && (K % 4 != 0 || N % 4 != 0)) return false;
     // The streaming kernels cover at most 16 rows (16 x 64 tile) or 16
     // columns (64 x 16 tile) of C.
     if (v->kind == KIND_STREAM && (v->bm == 16 ? M > 16 : N > 16)) return false;

@@ -15,6 +15,12 @@
 // 16 x 64) or N <= 16 (tile 64 x 16); the large operand streams from HBM into
 // registers, KB values of K per workgroup block.
 //   S(id, name, BM, BN, KB, max_split, eff_hbm)
+// FP32 LDS-ring variants (sam_kernels_f32ring.hip): K % 4 == 0 and
+// N % 4 == 0 only; both operands load straight into a ring of NBUF LDS
+// stages of BK values of K; wave tiles of 32-row blocks x 32 V-column groups
+// (B read V columns at a time); KS = 2 runs two waves per tile position, each
+// on half of every stage's K steps (names "...s2").
+//   F(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, group_m, xcd_remap, max_split, eff_f32)
 // eff_* is the fraction of the MFMA peak the variant sustains in steady
 // state, the calibration the cost model uses.
 #pragma once
@@ -48,3 +54,16 @@
     S(21, "sn64x16_k2048", 64, 16, 2048, 32, 0.75)                                       \
     S(22, "sm16x64_k1024", 16, 64, 1024, 32, 0.97)                                       \
     S(23, "sn64x16_k1024", 64, 16, 1024, 32, 0.81)
+
+#define SAM_F32RING_VARIANTS(F)                                                          \
+    F(24, "f128x128_w4x1_k64n2", 128, 128, 4, 1, 64, 2, 4, 1, 8, 1, 16, 0.84)               \
+    F(25, "f128x128_w4x1_k32n4", 128, 128, 4, 1, 32, 4, 4, 1, 8, 1, 16, 0.82)               \
+    F(26, "f256x128_w8x1_k32n3", 256, 128, 8, 1, 32, 3, 4, 1, 8, 1,  8, 0.89)               \
+    F(27, "f128x256_w4x2_k32n3", 128, 256, 4, 2, 32, 3, 4, 1, 8, 1,  8, 0.89)               \
+    F(28, "f64x128_w2x1_k32n2",   64, 128, 2, 1, 32, 2, 4, 1, 8, 1, 16, 0.5)               \
+    F(29, "f256x256_w4x2_k32n2", 256, 256, 4, 2, 32, 2, 4, 1, 8, 1,  8, 0.94)               \
+    F(30, "f128x128_w4x2_k64n2", 128, 128, 4, 2, 64, 2, 2, 1, 8, 1, 16, 0.885)               \
+    F(31, "f128x128_w4x2_k32n4", 128, 128, 4, 2, 32, 4, 2, 1, 8, 1, 16, 0.875)               \
+    F(32, "f256x128_w8x2_k32n3", 256, 128, 8, 2, 32, 3, 2, 1, 8, 1,  8, 0.89)                \
+    F(33, "f128x128_w2x2s2_k64n2", 128, 128, 2, 2, 64, 2, 2, 2, 8, 1, 16, 0.895)            \
+    F(34, "f128x128_w2x2s2_k32n4", 128, 128, 2, 2, 32, 4, 2, 2, 8, 1, 16, 0.885)
