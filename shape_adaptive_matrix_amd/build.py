@@ -33,6 +33,10 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # Packed FP32 instructions stay off in all device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The MFMA chunk steps are fully unrolled by pragma; the largest (128
+    # MFMAs each) exceed the default size limit and would otherwise stay
+    # rolled with their accumulators in scratch.
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     "-Wall", "-Wno-unused-function",
 ]
 
@@ -81,7 +85,9 @@ def _build_ceilings(verbose: bool) -> Path:
     """The MFMA-loop / HBM-copy ceiling probe (a standalone executable)."""
     if CEILINGS_BIN.exists():
         CEILINGS_BIN.unlink()
-    cmd = [HIPCC, *HIP_FLAGS, str(CEILINGS_SRC), "-o", str(CEILINGS_BIN)]
+    # Accumulators in ordinary VGPRs: with AGPRs the compiler shuffles the
+    # 16x16x32 accumulators between iterations and serialises the loop.
+    cmd = [HIPCC, *HIP_FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form", str(CEILINGS_SRC), "-o", str(CEILINGS_BIN)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {CEILINGS_SRC.name}:\n{r.stdout}{r.stderr}")

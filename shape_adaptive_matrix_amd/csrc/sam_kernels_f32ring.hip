@@ -44,16 +44,33 @@ namespace sam {
 
 namespace f32ring {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void mfma(v16f& c, unsigned a, unsigned b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a), __uint_as_float(b), c, 0, 0, 0);
-}
+// The two FP32 MFMA shapes: G K-slot groups of BLK lanes, N accumulator
+// values per lane, and the output row of accumulator value r of a lane.
+template <int BLK> struct Blk;
+template <> struct Blk<32> {
+    typedef v16f T;
+    static constexpr int G = 2, N = 16;
+    static __device__ __forceinline__ void mfma(T& c, unsigned a, unsigned b) {
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a), __uint_as_float(b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int lane, int r) { return ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3); }
+};
+template <> struct Blk<16> {
+    typedef v4f T;
+    static constexpr int G = 4, N = 4;
+    static __device__ __forceinline__ void mfma(T& c, unsigned a, unsigned b) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a), __uint_as_float(b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int lane, int r) { return ((lane >> 4) << 2) + r; }
+};
 
 }  // namespace f32ring
 
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS>
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK>
 __global__ void __launch_bounds__(WM * WN * KS * 64)
 __attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / (NBUF * (BM + BN) * BK * 4)) * WM * WN * KS + 3) / 4)))
 gemm_f32_ring_kernel(GemmArgs args)
@@ -64,13 +81,16 @@ gemm_f32_ring_kernel(GemmArgs args)
     constexpr int NP = WM * WN;                // wave positions in the tile
     constexpr int NW = NP * KS;                // waves
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int CG = 32 * V;                 // columns per column group
-    constexpr int TM = WTM / 32, TN = WTN / CG;
+    typedef Blk<BLK> MF;
+    typedef typename MF::T acc_t;
+    constexpr int G = MF::G;                   // K-slot groups per MFMA
+    constexpr int CG = BLK * V;                // columns per column group
+    constexpr int TM = WTM / BLK, TN = WTN / CG;
     constexpr int A_ROW = BK * 4;              // bytes per A row in LDS
     constexpr int CPA = A_ROW / 16;            // 16-byte chunks per A row
     constexpr int RPA = 1024 / A_ROW;          // A rows per wave load
     constexpr int RSW = 256 / A_ROW;           // A rows sharing one 256-byte bank sweep
-    constexpr int KSTEPS = BK / 8;             // chunk steps per stage
+    constexpr int KSTEPS = BK / (4 * G);       // chunk steps per stage
     constexpr int KH = KSTEPS / KS;            // chunk steps per stage per wave
     constexpr int A_BYTES = BM * A_ROW;
     constexpr int B_ROW = BN * 4;
@@ -80,7 +100,7 @@ gemm_f32_ring_kernel(GemmArgs args)
     constexpr int A_PW = A_INS / NW, B_PW = B_INS / NW;
     constexpr int LPS = A_PW + B_PW;           // 1 KB loads per stage per wave
     static_assert(V == 2 || V == 4, "B read width");
-    static_assert(WTM % 32 == 0 && WTN % CG == 0, "wave tile: 32-row blocks, 32 V-column groups");
+    static_assert(WTM % BLK == 0 && WTN % CG == 0, "wave tile: BLK-row blocks, BLK V-column groups");
     static_assert(A_INS % NW == 0 && B_INS % NW == 0, "loads must split evenly over waves");
     static_assert(NBUF >= 2 && NBUF * STAGE <= 160 * 1024, "LDS ring");
     static_assert((NBUF - 1) * LPS < 64, "vmcnt range");
@@ -133,20 +153,20 @@ gemm_f32_ring_kernel(GemmArgs args)
         }
     };
 
-    const int lrow = lane & 31;
-    const int g = lane >> 5;
-    // Fragment read r of chunk step t: r < TM is A block r (row wm0 + 32 r +
-    // lrow, chunk 2 t + g); then B reads (j, e) = ((r - TM) / 4, (r - TM) % 4):
-    // row 8 t + 4 g + e, columns wn0 + CG j + V lrow .. + V - 1.
+    const int lrow = lane % BLK;
+    const int g = lane / BLK;
+    // Fragment read r of chunk step t: r < TM is A block r (row wm0 + BLK r +
+    // lrow, chunk G t + g); then B reads (j, e) = ((r - TM) / 4, (r - TM) % 4):
+    // row 4 (G t + g) + e, columns wn0 + CG j + V lrow .. + V - 1.
     constexpr int NRD = TM + 4 * TN;
     auto read_one = [&](const unsigned char* buf, int t, int r, u4 (&fa)[TM], u4 (&fb)[TN][4]) {
         if (r < TM) {
-            const int row = wm0 + 32 * r + lrow;
-            const int c = (2 * t + g) ^ ((row / RSW) % CPA);
+            const int row = wm0 + BLK * r + lrow;
+            const int c = (G * t + g) ^ ((row / RSW) % CPA);
             fa[r] = *reinterpret_cast<const u4*>(buf + row * A_ROW + c * 16);
         } else {
             const int j = (r - TM) >> 2, e = (r - TM) & 3;
-            const int row = 8 * t + 4 * g + e;
+            const int row = 4 * (G * t + g) + e;
             const unsigned char* p = buf + A_BYTES + row * B_ROW + (wn0 + CG * j + V * lrow) * 4;
             if constexpr (V == 4) {
                 fb[j][e] = *reinterpret_cast<const u4*>(p);
@@ -158,7 +178,7 @@ gemm_f32_ring_kernel(GemmArgs args)
         }
     };
 
-    v16f acc[TM][TN][V];
+    acc_t acc[TM][TN][V];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -166,7 +186,7 @@ gemm_f32_ring_kernel(GemmArgs args)
 #pragma unroll
             for (int v = 0; v < V; ++v)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][v][r] = 0.0f;
+                for (int r = 0; r < MF::N; ++r) acc[i][j][v][r] = 0.0f;
 
     // MFMA m of a chunk step: e = K element, then A block i, column group j,
     // column phase v (so the same accumulator recurs every V TM TN MFMAs).
@@ -175,7 +195,7 @@ gemm_f32_ring_kernel(GemmArgs args)
         const int e = m / (V * TM * TN);
         const int rest = m % (V * TM * TN);
         const int i = rest / (V * TN), j = (rest / V) % TN, v = rest % V;
-        mfma(acc[i][j][v], fa[i][e], fb[j][e][v]);
+        MF::mfma(acc[i][j][v], fa[i][e], fb[j][e][v]);
     };
 
     constexpr int RPS = (NRD + NMF - 1) / NMF;   // reads per MFMA slot
@@ -248,9 +268,8 @@ gemm_f32_ring_kernel(GemmArgs args)
         constexpr int H = decltype(hc)::value;
         constexpr int IB = KS == 2 ? H * I0 : 0;
         if constexpr (KS == 2) {
-            constexpr int GF = I0 * TN * V * 16;   // floats handed over per lane
+            constexpr int GF = I0 * TN * V * MF::N;   // floats handed over per lane
             static_assert(NP * 2 * 64 * GF * 4 <= NBUF * STAGE, "exchange fits the ring");
-            typedef float v4f __attribute__((ext_vector_type(4)));
             v4f* xs = reinterpret_cast<v4f*>(lds);
             const int mine = (pos * 2 + H) * 64 * (GF / 4), theirs = (pos * 2 + (1 - H)) * 64 * (GF / 4);
             barrier();   // every wave is past its last read of the ring
@@ -261,9 +280,9 @@ gemm_f32_ring_kernel(GemmArgs args)
 #pragma unroll
                     for (int v = 0; v < V; ++v)
 #pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            const int f4 = ((ii * TN + j) * V + v) * 4 + r4;
-                            const v16f& x = acc[(1 - H) * I0 + ii][j][v];
+                        for (int r4 = 0; r4 < MF::N / 4; ++r4) {
+                            const int f4 = ((ii * TN + j) * V + v) * (MF::N / 4) + r4;
+                            const acc_t& x = acc[(1 - H) * I0 + ii][j][v];
                             xs[mine + f4 * 64 + lane] = v4f{x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]};
                         }
             __syncthreads();
@@ -274,16 +293,16 @@ gemm_f32_ring_kernel(GemmArgs args)
 #pragma unroll
                     for (int v = 0; v < V; ++v)
 #pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            const int f4 = ((ii * TN + j) * V + v) * 4 + r4;
+                        for (int r4 = 0; r4 < MF::N / 4; ++r4) {
+                            const int f4 = ((ii * TN + j) * V + v) * (MF::N / 4) + r4;
                             const v4f x = xs[theirs + f4 * 64 + lane];
-                            v16f& y = acc[IB + ii][j][v];
+                            acc_t& y = acc[IB + ii][j][v];
 #pragma unroll
                             for (int q = 0; q < 4; ++q) y[4 * r4 + q] = y[4 * r4 + q] + x[q];
                         }
         }
         // Accumulator element r of acc[i][j][v], lane (lrow, g): row wm0 +
-        // 32 i + 8 (r / 4) + 4 g + r % 4, column wn0 + CG j + V lrow + v.
+        // BLK i + MF::row(lane, r), column wn0 + CG j + V lrow + v.
 #pragma unroll
         for (int ii = 0; ii < I0; ++ii)
 #pragma unroll
@@ -291,8 +310,8 @@ gemm_f32_ring_kernel(GemmArgs args)
                 const int i = IB + ii;
                 const int col = wn0 + CG * j + V * lrow;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wm0 + 32 * i + ((r >> 2) << 3) + (g << 2) + (r & 3);
+                for (int r = 0; r < MF::N; ++r) {
+                    const int row = wm0 + BLK * i + MF::row(lane, r);
                     const bool ok = m0 + row < M && n0 + col < N;
                     const int off = ok ? (row * N + col) * 4 : kOOB;
                     if constexpr (V == 4) {
@@ -321,8 +340,8 @@ struct F32RingKernel {
     int threads;
 };
 
-#define SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, gm, xr, ms, e32) \
-    {id, gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS>, WM * WN * KS * 64},
+#define SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, gm, xr, ms, e32) \
+    {id, gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK>, WM * WN * KS * 64},
 
 static const F32RingKernel kF32RingTable[] = {SAM_F32RING_VARIANTS(SAM_F32RING_ENTRY)};
 

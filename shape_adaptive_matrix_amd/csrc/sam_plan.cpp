@@ -41,8 +41,8 @@ namespace sam {
 #define SAM_STREAM_ROW(id, name, BM, BN, KB, ms, eff) \
     {id, name, KIND_STREAM, (1 << DT_F32), BM, BN, 1, 1, 16, 1, KB, 1, 0, ms, eff, 0.0},
 
-#define SAM_F32RING_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, gm, xr, ms, e32) \
-    {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, 32, NBUF, BK, gm, xr, ms, e32, 0.0},
+#define SAM_F32RING_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, gm, xr, ms, e32) \
+    {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, BLK, NBUF, BK, gm, xr, ms, e32, 0.0},
 
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
                                         SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)};

@@ -26,40 +26,49 @@ typedef unsigned int u4 __attribute__((ext_vector_type(4)));
         }                                                                             \
     } while (0)
 
+// Eight independent accumulators per wave, each with its own start value and
+// its own A operand, so the compiler keeps them in fixed registers (with
+// identical ones it rotated registers between iterations and chained every
+// MFMA on the previous one). The empty asm per iteration keeps the loop from
+// being collapsed.
 template <int KIND>
 __global__ void __launch_bounds__(256) mfma_loop(float* out, int iters, float seed)
 {
     const float x = seed + threadIdx.x;
+    u4 av[8];
+    for (int i = 0; i < 8; ++i)
+        av[i] = u4{__float_as_uint(x + i), __float_as_uint(x + 2 * i), __float_as_uint(x - i), __float_as_uint(x * i)};
+    const u4 bv = {__float_as_uint(x), __float_as_uint(x + 1), __float_as_uint(x + 2), __float_as_uint(x + 3)};
     if constexpr (KIND == 0 || KIND == 2 || KIND == 3) {   // 32x32 blocks: 16 acc regs
         v16f acc[8];
-        for (int i = 0; i < 8; ++i) for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
-        u4 av = {__float_as_uint(x), __float_as_uint(x + 1), __float_as_uint(x + 2), __float_as_uint(x + 3)};
+        for (int i = 0; i < 8; ++i) for (int r = 0; r < 16; ++r) acc[i][r] = (float)(i * 16 + r);
         for (int it = 0; it < iters; ++it) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 if constexpr (KIND == 0)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(x, x, acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(av[i][0]), x, acc[i], 0, 0, 0);
                 else if constexpr (KIND == 2)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av), __builtin_bit_cast(v8bf, av), acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av[i]), __builtin_bit_cast(v8bf, bv), acc[i], 0, 0, 0);
                 else
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, av), __builtin_bit_cast(v8h, av), acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, av[i]), __builtin_bit_cast(v8h, bv), acc[i], 0, 0, 0);
             }
+            asm volatile("" ::: "memory");
         }
         float s = 0.0f;
         for (int i = 0; i < 8; ++i) for (int r = 0; r < 16; ++r) s += acc[i][r];
         out[blockIdx.x * blockDim.x + threadIdx.x] = s;
     } else {                                                // 16x16 blocks: 4 acc regs
         v4f acc[8];
-        for (int i = 0; i < 8; ++i) for (int r = 0; r < 4; ++r) acc[i][r] = 0.0f;
-        u4 av = {__float_as_uint(x), __float_as_uint(x + 1), __float_as_uint(x + 2), __float_as_uint(x + 3)};
+        for (int i = 0; i < 8; ++i) for (int r = 0; r < 4; ++r) acc[i][r] = (float)(i * 4 + r);
         for (int it = 0; it < iters; ++it) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 if constexpr (KIND == 1)
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, x, acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av[i][0]), x, acc[i], 0, 0, 0);
                 else
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av), __builtin_bit_cast(v8bf, av), acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[i]), __builtin_bit_cast(v8bf, bv), acc[i], 0, 0, 0);
             }
+            asm volatile("" ::: "memory");
         }
         float s = 0.0f;
         for (int i = 0; i < 8; ++i) for (int r = 0; r < 4; ++r) s += acc[i][r];
