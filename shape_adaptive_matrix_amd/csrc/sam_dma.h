@@ -35,6 +35,14 @@ __device__ __forceinline__ void lds_load16(const i4& rsrc, unsigned lds_base, in
                  : "memory", "m0");
 }
 
+// The same with 4 bytes per lane: LDS at `lds_base` + 4 * lane.
+__device__ __forceinline__ void lds_load4(const i4& rsrc, unsigned lds_base, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return (unsigned)(size_t)(__attribute__((address_space(3))) const void*)p;
 }

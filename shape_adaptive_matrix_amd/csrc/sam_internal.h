@@ -41,6 +41,7 @@ struct Variant {
     int group_m;         // grouped raster height (tiles)
     int xcd_remap;       // 1: remap workgroup ids so each XCD gets a contiguous range
     int max_split;       // largest split-K the variant is planned with
+    int elem_loads;      // takes rows that are not whole 16-byte pieces (K or N odd for FP32)
     double eff_f32;      // calibrated fraction of MFMA peak it sustains in steady state
                          // (streaming variants: fraction of the HBM read rate)
     double eff_h16;

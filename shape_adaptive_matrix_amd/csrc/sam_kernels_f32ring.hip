@@ -2,10 +2,14 @@
 //
 // C = A*B in FP32 (page "Measured data point on fixed-tile vs shape-adaptive
 // GEMM", the FP32 square sizes of its results table), row-major A[M][K],
-// B[K][N], K % 4 == 0 and N % 4 == 0 (16-byte pieces of rows).
+// B[K][N]; K % 4 == 0 and N % 4 == 0 take 16-byte loads, other shapes the
+// element-load form.
 //
 //  * Global -> LDS goes through buffer loads that write LDS directly, 1 KB
-//    per wave instruction (lane l lands at base + 16 l), so neither operand
+//    per wave instruction (lane l lands at base + 16 l); an operand whose rows
+//    are not 16-byte pieces (A with K % 4 != 0, B with N % 4 != 0) takes 256
+//    bytes per instruction, one element per lane, into the same layout
+//    (its element form, ELA / ELB). Neither operand
 //    passes through registers and no VALU work is spent on the way. The LDS
 //    holds a ring of NBUF stages of BK values of K; the loads of a stage are
 //    issued NBUF - 1 stages ahead, spread one per MFMA slot. Out-of-range
@@ -70,7 +74,7 @@ template <> struct Blk<16> {
 
 }  // namespace f32ring
 
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK>
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB>
 __global__ void __launch_bounds__(WM * WN * KS * 64)
 __attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / (NBUF * (BM + BN) * BK * 4)) * WM * WN * KS + 3) / 4)))
 gemm_f32_ring_kernel(GemmArgs args)
@@ -98,7 +102,8 @@ gemm_f32_ring_kernel(GemmArgs args)
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int A_INS = A_BYTES / 1024, B_INS = B_BYTES / 1024;
     constexpr int A_PW = A_INS / NW, B_PW = B_INS / NW;
-    constexpr int LPS = A_PW + B_PW;           // 1 KB loads per stage per wave
+    constexpr int LA = ELA ? 4 : 1, LB = ELB ? 4 : 1;   // load instructions per 1 KB block
+    constexpr int LPS = A_PW * LA + B_PW * LB;          // load instructions per stage per wave
     static_assert(V == 2 || V == 4, "B read width");
     static_assert(WTM % BLK == 0 && WTN % CG == 0, "wave tile: BLK-row blocks, BLK V-column groups");
     static_assert(A_INS % NW == 0 && B_INS % NW == 0, "loads must split evenly over waves");
@@ -129,10 +134,41 @@ gemm_f32_ring_kernel(GemmArgs args)
                              (long long)(M - m0) * K * 4);
     const long long b_bytes = (long long)K * N * 4;
 
-    // Wave load q of stage `st`: q < A_PW fetch A rows (RPA per load, chunks
-    // placed swizzled: the lane at physical chunk p loads logical chunk
-    // p ^ ((row / RSW) % CPA)), the rest B rows in natural order.
+    // Wave load q of stage `st`: the first A_PW LA loads fetch A rows into
+    // 1 KB blocks (RPA rows per block, chunks placed swizzled: physical chunk
+    // p holds logical chunk p ^ ((row / RSW) % CPA)), the rest B rows in
+    // natural order. An operand in element form (ELA / ELB: its rows are not
+    // 16-byte pieces) fills each block with four loads, load u covering bytes
+    // 256 u .. + 255 of the block, one float per lane.
+    auto issue_el = [&](int st, int q) {
+        const int k0 = kbeg + st * BK;
+        unsigned char* buf = lds + (st % NBUF) * STAGE;
+        if (q < A_PW * LA) {
+            const int qb = q / 4, d = 64 * (q % 4) + lane;      // dword of the block
+            const int I = wave + qb * NW;
+            const int row = I * RPA + (4 * d) / A_ROW;
+            const int p = ((4 * d) % A_ROW) / 16;
+            const int gk = k0 + 4 * (p ^ ((row / RSW) % CPA)) + (d & 3);
+            const bool ok = m0 + row < M && gk < kend;
+            lds_load4(rA, lds_addr(buf + I * 1024 + 256 * (q % 4)), ok ? (row * K + gk) * 4 : kOOB);
+        } else {
+            const int qq = q - A_PW * LA;
+            const int qb = qq / 4, d = 64 * (qq % 4) + lane;
+            const int I = wave + qb * NW;
+            const int byte = I * 1024 + 4 * d;
+            const int row = byte / B_ROW, col = (byte % B_ROW) / 4;
+            const bool ok = k0 + row < kend && n0 + col < N;
+            const long long bbase = ((long long)k0 * N + n0) * 4;
+            const i4 rB = rsrc_words(reinterpret_cast<const char*>(args.B) + bbase, b_bytes - bbase);
+            lds_load4(rB, lds_addr(buf + A_BYTES + I * 1024 + 256 * (qq % 4)), ok ? (row * N + col) * 4 : kOOB);
+        }
+    };
     auto issue_one = [&](int st, int q) {
+        if ((ELA && q < A_PW * LA) || (ELB && q >= A_PW * LA)) {
+            issue_el(st, q);
+            return;
+        }
+        if (q >= A_PW * LA) q = A_PW + (q - A_PW * LA);   // 16-byte B loads follow A's
         const int k0 = kbeg + st * BK;
         unsigned char* buf = lds + (st % NBUF) * STAGE;
         if (q < A_PW) {
@@ -312,6 +348,17 @@ gemm_f32_ring_kernel(GemmArgs args)
 #pragma unroll
                 for (int r = 0; r < MF::N; ++r) {
                     const int row = wm0 + BLK * i + MF::row(lane, r);
+                    if constexpr (ELB) {
+                        // Rows need not be 16-byte pieces: one float per store,
+                        // each column checked against N.
+#pragma unroll
+                        for (int v = 0; v < V; ++v) {
+                            const bool okv = m0 + row < M && n0 + col + v < N;
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[IB + ii][j][v][r]), rC,
+                                                                  okv ? (row * N + col + v) * 4 : kOOB, 0, 0);
+                        }
+                        continue;
+                    }
                     const bool ok = m0 + row < M && n0 + col < N;
                     const int off = ok ? (row * N + col) * 4 : kOOB;
                     if constexpr (V == 4) {
@@ -334,14 +381,33 @@ gemm_f32_ring_kernel(GemmArgs args)
 
 typedef void (*F32RingFn)(GemmArgs);
 
+// The element-load form, for variants that have one (EL = 1 in the table):
+// it needs four times the loads in flight, and its address arithmetic costs
+// registers that the largest tiles do not have to spare.
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, int EL, bool ELA, bool ELB>
+constexpr F32RingFn el_kernel() {
+    if constexpr (EL != 0) {
+        static_assert((NBUF - 1) * (((BM + BN) * BK * 4 / 1024) / (WM * WN * KS) * 4) < 64,
+                      "element loads in flight must stay countable");
+        return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB>;
+    } else {
+        return nullptr;
+    }
+}
+
 struct F32RingKernel {
     int id;
-    F32RingFn fn;
+    F32RingFn fn[2][2];   // [a_vec][b_vec]: 16-byte loads for an operand whose rows are 16-byte pieces
     int threads;
 };
 
-#define SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, gm, xr, ms, e32) \
-    {id, gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK>, WM * WN * KS * 64},
+#define SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32) \
+    {id,                                                                                \
+     {{el_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, true>(),                 \
+       el_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, false>()},               \
+      {el_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false, true>(),                \
+       gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false>}},        \
+     WM * WN * KS * 64},
 
 static const F32RingKernel kF32RingTable[] = {SAM_F32RING_VARIANTS(SAM_F32RING_ENTRY)};
 
@@ -350,7 +416,9 @@ hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s)
     for (const F32RingKernel& k : kF32RingTable) {
         if (k.id != p.variant_id) continue;
         if (p.dtype != DT_F32) return hipErrorInvalidDeviceFunction;
-        hipLaunchKernelGGL(k.fn, dim3((unsigned)p.grid), dim3(k.threads), 0, s, a);
+        const F32RingFn fn = k.fn[p.a_vec ? 1 : 0][p.b_vec ? 1 : 0];
+        if (!fn) return hipErrorInvalidDeviceFunction;
+        hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(k.threads), 0, s, a);
         return hipGetLastError();
     }
     return hipErrorInvalidDeviceFunction;

@@ -34,15 +34,15 @@
 namespace sam {
 
 #define SAM_STAGED_ROW(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16, pf32, pf16) \
-    {id, name, KIND_STAGED, 7, BM, BN, WM, WN, BLK, 2, 0, gm, xr, ms, e32, e16},
+    {id, name, KIND_STAGED, 7, BM, BN, WM, WN, BLK, 2, 0, gm, xr, ms, 1, e32, e16},
 #define SAM_DMA_ROW(id, name, BM, BN, WM, WN, BK, NBUF, MODE, gm, xr, ms, e16) \
-    {id, name, KIND_DMA, (1 << DT_BF16) | (1 << DT_F16), BM, BN, WM, WN, 32, NBUF, BK, gm, xr, ms, 0.0, e16},
+    {id, name, KIND_DMA, (1 << DT_BF16) | (1 << DT_F16), BM, BN, WM, WN, 32, NBUF, BK, gm, xr, ms, 0, 0.0, e16},
 
 #define SAM_STREAM_ROW(id, name, BM, BN, KB, ms, eff) \
-    {id, name, KIND_STREAM, (1 << DT_F32), BM, BN, 1, 1, 16, 1, KB, 1, 0, ms, eff, 0.0},
+    {id, name, KIND_STREAM, (1 << DT_F32), BM, BN, 1, 1, 16, 1, KB, 1, 0, ms, 1, eff, 0.0},
 
-#define SAM_F32RING_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, gm, xr, ms, e32) \
-    {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, BLK, NBUF, BK, gm, xr, ms, e32, 0.0},
+#define SAM_F32RING_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32) \
+    {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, BLK, NBUF, BK, gm, xr, ms, EL, e32, 0.0},
 
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
                                         SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)};
@@ -174,8 +174,9 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     if (M < 0 || N < 0 || K < 0) return false;
     // The LDS-ring kernels take whole 16-byte pieces of A and B rows.
     if (v->kind == KIND_DMA && (K % 8 != 0 || N % 8 != 0)) return false;
-    // The FP32 ring kernels take whole 16-byte pieces of A and B rows.
-    if (v->kind == KIND_F32RING && (K % 4 != 0 || N % 4 != 0)) return false;
+    // FP32 ring kernels take rows that are not 16-byte pieces only in their
+    // element-load form, which not every variant has.
+    if (v->kind == KIND_F32RING && (K % 4 != 0 || N % 4 != 0) && !v->elem_loads) return false;
     // The streaming kernels cover at most 16 rows (16 x 64 tile) or 16
     // columns (64 x 16 tile) of C.
     if (v->kind == KIND_STREAM && (v->bm == 16 ? M > 16 : N > 16)) return false;

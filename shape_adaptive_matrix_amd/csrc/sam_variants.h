@@ -20,8 +20,9 @@
 // stages of BK values of K; wave tiles of 32-row blocks x 32 V-column groups
 // (B read V columns at a time); KS = 2 runs two waves per tile position, each
 // on half of every stage's K steps (names "...s2"); BLK is the MFMA block
-// edge, 32 (32x32x2) or 16 (16x16x4, names "...b16").
-//   F(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, group_m, xcd_remap, max_split, eff_f32)
+// edge, 32 (32x32x2) or 16 (16x16x4, names "...b16"); EL = 1: the variant
+// also has an element-load form for K or N not a multiple of 4.
+//   F(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, group_m, xcd_remap, max_split, eff_f32)
 // eff_* is the fraction of the MFMA peak the variant sustains in steady
 // state, the calibration the cost model uses.
 #pragma once
@@ -57,17 +58,17 @@
     S(23, "sn64x16_k1024", 64, 16, 1024, 32, 0.81)
 
 #define SAM_F32RING_VARIANTS(F)                                                          \
-    F(24, "f128x128_w4x1_k64n2", 128, 128, 4, 1, 64, 2, 4, 1, 32, 8, 1, 16, 0.84)               \
-    F(25, "f128x128_w4x1_k32n4", 128, 128, 4, 1, 32, 4, 4, 1, 32, 8, 1, 16, 0.82)               \
-    F(26, "f256x128_w8x1_k32n3", 256, 128, 8, 1, 32, 3, 4, 1, 32, 8, 1,  8, 0.89)               \
-    F(27, "f128x256_w4x2_k32n3", 128, 256, 4, 2, 32, 3, 4, 1, 32, 8, 1,  8, 0.89)               \
-    F(28, "f64x128_w2x1_k32n2",   64, 128, 2, 1, 32, 2, 4, 1, 32, 8, 1, 16, 0.5)               \
-    F(29, "f256x256_w4x2_k32n2", 256, 256, 4, 2, 32, 2, 4, 1, 32, 8, 1,  8, 0.94)               \
-    F(30, "f128x128_w4x2_k64n2", 128, 128, 4, 2, 64, 2, 2, 1, 32, 8, 1, 16, 0.885)               \
-    F(31, "f128x128_w4x2_k32n4", 128, 128, 4, 2, 32, 4, 2, 1, 32, 8, 1, 16, 0.875)               \
-    F(32, "f256x128_w8x2_k32n3", 256, 128, 8, 2, 32, 3, 2, 1, 32, 8, 1,  8, 0.89)                \
-    F(33, "f128x128_w2x2s2_k64n2", 128, 128, 2, 2, 64, 2, 2, 2, 32, 8, 1, 16, 0.895)            \
-    F(34, "f128x128_w2x2s2_k32n4", 128, 128, 2, 2, 32, 4, 2, 2, 32, 8, 1, 16, 0.885)            \
-    F(35, "f128x128_w2x2s2_k64n2_b16", 128, 128, 2, 2, 64, 2, 4, 2, 16, 8, 1, 16, 0.91)   \
-    F(36, "f256x256_w4x2_k32n2_b16",   256, 256, 4, 2, 32, 2, 4, 1, 16, 8, 1,  8, 0.95)   \
-    F(37, "f128x128_w4x2_k64n2_b16",   128, 128, 4, 2, 64, 2, 4, 1, 16, 8, 1, 16, 0.895)
+    F(24, "f128x128_w4x1_k64n2", 128, 128, 4, 1, 64, 2, 4, 1, 32, 0, 8, 1, 16, 0.84)               \
+    F(25, "f128x128_w4x1_k32n4", 128, 128, 4, 1, 32, 4, 4, 1, 32, 0, 8, 1, 16, 0.82)               \
+    F(26, "f256x128_w8x1_k32n3", 256, 128, 8, 1, 32, 3, 4, 1, 32, 1, 8, 1,  8, 0.89)               \
+    F(27, "f128x256_w4x2_k32n3", 128, 256, 4, 2, 32, 3, 4, 1, 32, 1, 8, 1,  8, 0.89)               \
+    F(28, "f64x128_w2x1_k32n2",   64, 128, 2, 1, 32, 2, 4, 1, 32, 1, 8, 1, 16, 0.5)               \
+    F(29, "f256x256_w4x2_k32n2", 256, 256, 4, 2, 32, 2, 4, 1, 32, 1, 8, 1,  8, 0.94)               \
+    F(30, "f128x128_w4x2_k64n2", 128, 128, 4, 2, 64, 2, 2, 1, 32, 1, 8, 1, 16, 0.885)               \
+    F(31, "f128x128_w4x2_k32n4", 128, 128, 4, 2, 32, 4, 2, 1, 32, 1, 8, 1, 16, 0.875)               \
+    F(32, "f256x128_w8x2_k32n3", 256, 128, 8, 2, 32, 3, 2, 1, 32, 1, 8, 1,  8, 0.89)                \
+    F(33, "f128x128_w2x2s2_k64n2", 128, 128, 2, 2, 64, 2, 2, 2, 32, 1, 8, 1, 16, 0.895)            \
+    F(34, "f128x128_w2x2s2_k32n4", 128, 128, 2, 2, 32, 4, 2, 2, 32, 1, 8, 1, 16, 0.885)            \
+    F(35, "f128x128_w2x2s2_k64n2_b16", 128, 128, 2, 2, 64, 2, 4, 2, 16, 1, 8, 1, 16, 0.91)   \
+    F(36, "f256x256_w4x2_k32n2_b16",   256, 256, 4, 2, 32, 2, 4, 1, 16, 0, 8, 1,  8, 0.95)   \
+    F(37, "f128x128_w4x2_k64n2_b16",   128, 128, 4, 2, 64, 2, 4, 1, 16, 1, 8, 1, 16, 0.895)
