@@ -80,6 +80,7 @@ struct Plan {
     long long grid;
     unsigned long long ws_bytes;
     double est_us;
+    int tuned;           // 1: taken from the frozen table of measured shapes
 };
 
 // Dispatcher (sam_plan.cpp). Host only, pure.

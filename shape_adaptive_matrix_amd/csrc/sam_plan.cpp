@@ -23,12 +23,16 @@
 //  * Ties go to the lowest variant id, so list order can never leak into the
 //    choice through an unstable sort (the tie-break problem raised in the
 //    review of that same page).
+//  * Shapes that were measured offline (tune.py) take the fastest measured
+//    (variant, split) from the frozen table in sam_tuned.h before the cost
+//    model is consulted.
 // No timing at run time: the same shape always gets the same plan.
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
 
 #include "sam_internal.h"
+#include "sam_tuned.h"
 #include "sam_variants.h"
 
 namespace sam {
@@ -202,8 +206,26 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     return found;
 }
 
+struct TunedPlan {
+    int dtype;
+    long long M, N, K;
+    int variant, split;
+};
+
+#define SAM_TUNED_ROW(dt, M, N, K, v, s) {dt, M, N, K, v, s},
+static const TunedPlan kTuned[] = {SAM_TUNED_PLANS(SAM_TUNED_ROW){-1, 0, 0, 0, 0, 0}};
+
 bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out)
 {
+    for (const TunedPlan& t : kTuned) {
+        if (t.dtype != dtype || t.M != M || t.N != N || t.K != K) continue;
+        Plan p{};
+        if (plan_for_variant(t.variant, M, N, K, dtype, t.split, &p)) {
+            p.tuned = 1;
+            *out = p;
+            return true;
+        }
+    }
     bool found = false;
     Plan best{};
     for (int id = 0; id < kVariantCount; ++id) {
@@ -222,8 +244,8 @@ void plan_name(const Plan& p, char* buf, int n)
 {
     static const char* dt[] = {"f32", "bf16", "f16"};
     const Variant* v = variant_get(p.variant_id);
-    snprintf(buf, n, "%s_%s_s%d%s%s", dt[p.dtype], v ? v->name : "?", p.split,
-             p.a_vec ? "" : "_ua", p.b_vec ? "" : "_ub");
+    snprintf(buf, n, "%s_%s_s%d%s%s%s", dt[p.dtype], v ? v->name : "?", p.split,
+             p.a_vec ? "" : "_ua", p.b_vec ? "" : "_ub", p.tuned ? "_tuned" : "");
 }
 
 }  // namespace sam

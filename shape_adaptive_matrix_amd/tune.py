@@ -1,0 +1,211 @@
+"""Offline tuning: measure every admissible (variant, split-K) pair on a fixed
+set of shapes and freeze the fastest into the dispatcher's table.
+
+Two steps, so that selection at run time never times anything (the
+measured-tactic shortlist idea of page "fix(fp4_gemm autotune) SM107 kernel
+family excluded from autotune candidates and heuristics update - #4856",
+section "Reviewer Notes", with the result frozen in source; the same shape
+always gets the same plan):
+
+  1. on a gfx950 machine, measure and append JSON lines to a record:
+        python -m shape_adaptive_matrix_amd.tune measure shape_adaptive_matrix_amd/tuning/tuning_sweep.jsonl
+  2. anywhere, turn the record into the frozen table:
+        python -m shape_adaptive_matrix_amd.tune emit shape_adaptive_matrix_amd/tuning/tuning_sweep.jsonl
+     which rewrites csrc/sam_tuned.h, and a readable summary with
+        python -m shape_adaptive_matrix_amd.tune report shape_adaptive_matrix_amd/tuning/tuning_sweep.jsonl
+
+Timing protocol per candidate: 3 warm-up calls, then the median of 5
+batches of back-to-back calls lasting at least 15 ms each, HIP events on the
+launch stream. Inputs are the seeded generators of ``sam_inputs``.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import statistics
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+TUNED_H = PKG / "csrc" / "sam_tuned.h"
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
+
+# Shapes beyond the named workloads: square sizes between and around them,
+# K-heavy and K-light rectangles, skinny-ish panels, and the LLM-like shapes
+# of page "Measured data point on fixed-tile vs shape-adaptive GEMM".
+EXTRA = {
+    "f32": [(512, 512, 512), (1024, 1024, 1024), (1536, 1536, 1536), (3072, 3072, 3072),
+            (6144, 6144, 6144), (1000, 1000, 1000), (3000, 3000, 3000), (2048, 2048, 512),
+            (2048, 2048, 8192), (4096, 4096, 1024), (64, 4096, 4096), (4096, 64, 4096),
+            (32, 8192, 8192), (256, 11008, 4096), (4096, 4096, 11008), (2049, 4097, 1025)],
+    "bf16": [(1024, 1024, 1024), (2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144),
+             (4096, 4096, 1024), (2048, 8192, 2048), (256, 11008, 4096), (4096, 4096, 11008)],
+    "f16": [(2048, 2048, 2048), (6144, 6144, 6144), (4096, 4096, 11008)],
+}
+
+SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
+
+
+def shapes():
+    import sam_inputs as si
+    out = [(w.dtype, w.M, w.N, w.K, w.name) for w in si.WORKLOADS]
+    seen = {(d, m, n, k) for d, m, n, k, _ in out}
+    for dt, lst in EXTRA.items():
+        for (m, n, k) in lst:
+            if (dt, m, n, k) not in seen:
+                out.append((dt, m, n, k, f"{dt}_{m}x{n}x{k}"))
+                seen.add((dt, m, n, k))
+    return out
+
+
+def candidates(sam, dt, M, N, K):
+    """(variant, split) pairs: every admissible variant with its own split
+    choice, plus the other admissible splits of the four variants the cost
+    model ranks best, when their tile count leaves CUs idle."""
+    own = []
+    for vid in range(sam.variant_count()):
+        try:
+            own.append(sam.variant_plan(vid, M, N, K, dt, 0))
+        except sam.SamError:
+            continue
+    out = {(p["variant_id"], p["split_k"]) for p in own}
+    for p in sorted(own, key=lambda p: (p["est_us"], p["variant_id"]))[:4]:
+        if p["grid_wgs"] // p["split_k"] >= 256:
+            continue
+        for s in SPLITS:
+            try:
+                sam.variant_plan(p["variant_id"], M, N, K, dt, s)
+                out.add((p["variant_id"], s))
+            except sam.SamError:
+                pass
+    return sorted(out)
+
+
+def measure(record: Path, only=None):
+    import torch
+
+    import sam_inputs as si
+    import shape_adaptive_matrix_amd as sam
+
+    sam.device_check()
+    done = set()
+    if record.exists():
+        for line in record.read_text().splitlines():
+            r = json.loads(line)
+            done.add((r["dtype"], r["M"], r["N"], r["K"], r["variant"], r["split"]))
+    fn = sam.lib().sam_gemm_variant
+    with record.open("a") as f:
+        for (dt, M, N, K, name) in shapes():
+            if only and name not in only:
+                continue
+            w = si.Workload(name, dt, M, N, K, "uniform" if dt == "f32" else "normal16", 77)
+            A, B = si.make_operands(w)
+            if dt == "f32":
+                dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+            else:
+                t = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+                dA = torch.from_numpy(A.view("int16")).cuda().view(t)
+                dB = torch.from_numpy(B.view("int16")).cuda().view(t)
+            del A, B
+            C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            stream = torch.cuda.current_stream()
+            auto = sam.plan(M, N, K, dt)
+            print(f"[tune] {name}: {len(candidates(sam, dt, M, N, K))} candidates", flush=True)
+            for (vid, split) in candidates(sam, dt, M, N, K):
+                if (dt, M, N, K, vid, split) in done:
+                    continue
+                p = sam.variant_plan(vid, M, N, K, dt, split)
+                ws = sam.workspace_for(p, dA.device)
+                args = (vid, sam.DTYPES[dt], split, ctypes.c_void_p(dA.data_ptr()),
+                        ctypes.c_void_p(dB.data_ptr()), ctypes.c_void_p(C.data_ptr()), M, N, K,
+                        ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
+                        ws.numel() * 4 if ws is not None else 0, ctypes.c_void_p(stream.cuda_stream))
+                for _ in range(3):
+                    rc = fn(*args)
+                    if rc != 0:
+                        raise RuntimeError(f"{name} variant {vid} split {split}: {sam.last_error()}")
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn(*args)
+                e1.record()
+                e1.synchronize()
+                n = max(3, int(15.0 / max(e0.elapsed_time(e1), 1e-3)))
+                samples = []
+                for _ in range(5):
+                    e0.record()
+                    for _ in range(n):
+                        fn(*args)
+                    e1.record()
+                    e1.synchronize()
+                    samples.append(e0.elapsed_time(e1) / n)
+                ms = statistics.median(samples)
+                f.write(json.dumps({"shape": name, "dtype": dt, "M": M, "N": N, "K": K, "variant": vid,
+                                    "split": split, "plan": p["name"], "ms": round(ms, 5),
+                                    "tflops": round(2.0 * M * N * K / ms / 1e9, 2),
+                                    "est_us": round(p["est_us"], 1),
+                                    "model_pick": vid == auto["variant_id"] and split == auto["split_k"]}) + "\n")
+                f.flush()
+                del ws
+            del dA, dB, C
+            torch.cuda.empty_cache()
+
+
+def load(record: Path):
+    """Per shape: the measured candidates, fastest first (ties: lower id, then
+    lower split)."""
+    by = {}
+    for line in record.read_text().splitlines():
+        r = json.loads(line)
+        by.setdefault((r["dtype"], r["M"], r["N"], r["K"]), {})[(r["variant"], r["split"])] = r
+    return {k: sorted(v.values(), key=lambda r: (r["ms"], r["variant"], r["split"])) for k, v in by.items()}
+
+
+def emit(record: Path, out: Path = TUNED_H) -> str:
+    table = load(record)
+    lines = [
+        "// Frozen dispatch table: the fastest measured (variant, split-K) per shape.",
+        "// Generated by shape_adaptive_matrix_amd/tune.py from tuning/" + record.name + ";",
+        "// regenerate with `python -m shape_adaptive_matrix_amd.tune emit <record>`, do not edit.",
+        "//   T(dtype, M, N, K, variant, split)   dtype: 0 f32, 1 bf16, 2 f16",
+        "#pragma once",
+        "",
+        "#define SAM_TUNED_PLANS(T) \\",
+    ]
+    rows = []
+    for (dt, M, N, K), rs in sorted(table.items(), key=lambda kv: (DTYPE_CODE[kv[0][0]], kv[0][1:])):
+        best = rs[0]
+        rows.append(f"    T({DTYPE_CODE[dt]}, {M}, {N}, {K}, {best['variant']}, {best['split']})")
+    lines += [r + " \\" for r in rows[:-1]] + rows[-1:]
+    text = "\n".join(lines) + "\n"
+    out.write_text(text)
+    return text
+
+
+def report(record: Path) -> str:
+    table = load(record)
+    out = ["| shape | dtype | best plan | TFLOP/s | cost-model pick | its TFLOP/s | candidates |",
+           "|---|---|---|---:|---|---:|---:|"]
+    for (dt, M, N, K), rs in sorted(table.items(), key=lambda kv: (DTYPE_CODE[kv[0][0]], kv[0][1:])):
+        best = rs[0]
+        model = next((r for r in rs if r["model_pick"]), None)
+        out.append(f"| {M}x{N}x{K} | {dt} | {best['plan']} | {best['tflops']} | "
+                   f"{model['plan'] if model else '-'} | {model['tflops'] if model else '-'} | {len(rs)} |")
+    return "\n".join(out) + "\n"
+
+
+def main(argv):
+    if len(argv) < 2 or argv[0] not in ("measure", "emit", "report"):
+        print(__doc__)
+        return 2
+    rec = Path(argv[1])
+    if argv[0] == "measure":
+        measure(rec, set(argv[2:]) or None)
+    elif argv[0] == "emit":
+        print(emit(rec), end="")
+    else:
+        print(report(rec), end="")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

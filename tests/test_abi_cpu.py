@@ -49,21 +49,24 @@ SHAPES = [(256, 256, 256), (2048, 2048, 2048), (4096, 4096, 4096), (8192, 8192, 
 @pytest.mark.parametrize("shape", SHAPES, ids=str)
 def test_plan_is_audited_argmin(shape, dtype):
     """The automatic plan is the minimum estimate over every admissible
-    variant, ties to the lowest id, and asking twice gives the same plan."""
+    variant, ties to the lowest id, and asking twice gives the same plan.
+    Shapes in the frozen table of measured plans take the table's entry
+    instead (checked against the measurement record in test_tuning)."""
     M, N, K = shape
     p = sam.plan(M, N, K, dtype)
     assert p == sam.plan(M, N, K, dtype)
-    best = None
-    for vid in range(sam.variant_count()):
-        try:
-            q = sam.variant_plan(vid, M, N, K, dtype, 0)
-        except sam.SamError:
-            continue
-        if best is None or q["est_us"] < best["est_us"]:
-            best = q
-    assert best is not None
-    assert p["variant_id"] == best["variant_id"]
-    assert p["split_k"] == best["split_k"]
+    if not p["name"].endswith("_tuned"):
+        best = None
+        for vid in range(sam.variant_count()):
+            try:
+                q = sam.variant_plan(vid, M, N, K, dtype, 0)
+            except sam.SamError:
+                continue
+            if best is None or q["est_us"] < best["est_us"]:
+                best = q
+        assert best is not None
+        assert p["variant_id"] == best["variant_id"]
+        assert p["split_k"] == best["split_k"]
     assert p["grid_wgs"] == -(-M // p["tile_m"]) * -(-N // p["tile_n"]) * p["split_k"]
     if p["split_k"] > 1:
         assert p["workspace_bytes"] == p["split_k"] * M * N * 4
