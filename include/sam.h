@@ -76,7 +76,10 @@ typedef struct {
     int32_t tile_m, tile_n, tile_k; /* macro tile; tile_k = K per LDS stage  */
     int32_t waves_m, waves_n;  /* wave grid inside a workgroup               */
     int32_t mfma_m;            /* MFMA block edge: 32 or 16                   */
-    int32_t split_k;           /* 1 = single pass; >1 = partials + ordered sum */
+    int32_t split_k;           /* 1 = single pass; >1 = partials + ordered sum;
+                                  -1 = stream-K: grid_wgs persistent workgroups
+                                  share the tiles' K iterations evenly, shared
+                                  tiles are summed in a fixed order after */
     int32_t group_m;           /* grouped-raster height in tiles             */
     int32_t xcd_remap;         /* 1 = workgroup ids remapped per XCD          */
     int32_t a_vector, b_vector;/* 1 = 16-byte loads of A / B rows            */
@@ -115,8 +118,11 @@ int32_t sam_variant_count(void);
 sam_status sam_variant_info(int32_t id, sam_plan* out);
 
 /* The plan for a forced variant and split. split_k = 0 lets the dispatcher
- * pick the split for that variant. SAM_ERR_UNSUPPORTED if the variant does
- * not take `dtype` or the split is not admissible for K. */
+ * pick the split for that variant, -1 asks for its stream-K form (FP32 ring
+ * variants with tiles up to 128 x 256, when the shape has at least as many K
+ * iterations as resident workgroups). SAM_ERR_UNSUPPORTED if the variant does
+ * not take `dtype` or the split is not admissible for the shape;
+ * SAM_ERR_INVALID_ARG for split_k < -1. */
 sam_status sam_variant_plan(int32_t id, int64_t M, int64_t N, int64_t K,
                             sam_dtype dtype, int32_t split_k, sam_plan* out);
 

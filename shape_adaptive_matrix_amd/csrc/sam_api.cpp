@@ -102,7 +102,7 @@ void to_public(const sam::Plan& p, sam_plan* out)
     out->waves_m = p.wm;
     out->waves_n = p.wn;
     out->mfma_m = p.blk;
-    out->split_k = p.split;
+    out->split_k = p.sk ? -1 : p.split;
     out->group_m = p.group_m;
     out->xcd_remap = p.xcd_remap;
     out->a_vector = p.a_vec;
@@ -162,9 +162,15 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         a.group_m = p.group_m;
         a.xcd_remap = p.xcd_remap;
         a.part_stride = M * N;
+        if (p.sk) {
+            a.ws = static_cast<float*>(ws);
+            a.sk_iters = (int)((K + p.bk - 1) / p.bk);
+            a.sk_grid = (int)p.grid;
+        }
         e = sam::launch_gemm(p, a, s);
         if (e == hipSuccess && p.split > 1)
             e = sam::launch_reduce(static_cast<const float*>(ws), p.split, M * N, C, M * N, s);
+        if (e == hipSuccess && p.sk) e = sam::launch_sk_fixup(p, a, s);
     }
     if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
     g_err[0] = '\0';
@@ -244,7 +250,7 @@ sam_status sam_variant_plan(int32_t id, int64_t M, int64_t N, int64_t K, sam_dty
 {
     if (!out) return fail(SAM_ERR_INVALID_ARG, "out is null");
     if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
-    if (split_k < 0) return fail(SAM_ERR_INVALID_ARG, "negative split");
+    if (split_k < -1) return fail(SAM_ERR_INVALID_ARG, "split %d (-1 is stream-K, 0 the variant's choice)", split_k);
     sam_status st = check_shape(M, N, K);
     if (st != SAM_OK) return st;
     if (!sam::variant_get(id)) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);
@@ -261,7 +267,7 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k, const 
                             uint64_t workspace_bytes, void* stream)
 {
     if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
-    if (split_k < 0) return fail(SAM_ERR_INVALID_ARG, "negative split");
+    if (split_k < -1) return fail(SAM_ERR_INVALID_ARG, "split %d (-1 is stream-K, 0 the variant's choice)", split_k);
     sam_status st = check_shape(M, N, K);
     if (st != SAM_OK) return st;
     if (!sam::variant_get(id)) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);

@@ -63,26 +63,35 @@ __device__ __forceinline__ void barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Workgroup id -> (tile row, tile column, split): each XCD (workgroups go to
-// the 8 XCDs round-robin) owns one contiguous range of logical ids, walked in
-// grouped-raster order so neighbouring tiles share panels in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int wg, const GemmArgs& a, int& tm, int& tn, int& s) {
-    const int total = a.tiles_m * a.tiles_n * a.split;
-    int L = wg;
-    if (a.xcd_remap) {
-        const int q = total >> 3, rem = total & 7, x = wg & 7, y = wg >> 3;
-        L = (x < rem) ? x * (q + 1) + y : rem * (q + 1) + (x - rem) * q + y;
-    }
-    const int tiles = a.tiles_m * a.tiles_n;
-    s = L / tiles;
-    const int t = L - s * tiles;
+// Logical index of workgroup `wg` of `total`: workgroups go to the 8 XCDs
+// round-robin, and with `remap` each XCD owns one contiguous range of
+// logical indices, so work with neighbouring indices shares an XCD's L2.
+__device__ __forceinline__ int logical_wg(int wg, int total, int remap) {
+    if (!remap) return wg;
+    const int q = total >> 3, rem = total & 7, x = wg & 7, y = wg >> 3;
+    return (x < rem) ? x * (q + 1) + y : rem * (q + 1) + (x - rem) * q + y;
+}
+
+// Tile index -> (tile row, tile column) in grouped-raster order: group_m tile
+// rows sweep the tile columns together.
+__device__ __forceinline__ void tile_of(int t, const GemmArgs& a, int& tm, int& tn) {
     const int per_group = a.group_m * a.tiles_n;
-    const int g = t / per_group;
-    const int first_m = g * a.group_m;
+    const int grp = t / per_group;
+    const int first_m = grp * a.group_m;
     const int gsz = min(a.tiles_m - first_m, a.group_m);
-    const int r = t - g * per_group;
+    const int r = t - grp * per_group;
     tm = first_m + r % gsz;
     tn = r / gsz;
+}
+
+// Workgroup id -> (tile row, tile column, split); the split index is the
+// outermost part of the logical id.
+__device__ __forceinline__ void tile_coords(int wg, const GemmArgs& a, int& tm, int& tn, int& s) {
+    const int total = a.tiles_m * a.tiles_n * a.split;
+    const int L = logical_wg(wg, total, a.xcd_remap);
+    const int tiles = a.tiles_m * a.tiles_n;
+    s = L / tiles;
+    tile_of(L - s * tiles, a, tm, tn);
 }
 
 }  // namespace dma

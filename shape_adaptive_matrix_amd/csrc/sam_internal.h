@@ -62,6 +62,9 @@ struct GemmArgs {
     int group_m;
     int xcd_remap;
     long long part_stride;  // M*N (elements between consecutive partials)
+    float* ws;           // stream-K: partial-tile slots (2 per workgroup, BM*BN floats each)
+    int sk_iters;        // stream-K: K iterations per tile (0: data-parallel launch)
+    int sk_grid;         // stream-K: workgroups of the main kernel
 };
 
 // Fully resolved plan (internal form of sam_plan).
@@ -81,6 +84,7 @@ struct Plan {
     unsigned long long ws_bytes;
     double est_us;
     int tuned;           // 1: taken from the frozen table of measured shapes
+    int sk;              // 1: stream-K (grid = persistent workgroups, split == 1)
 };
 
 // Dispatcher (sam_plan.cpp). Host only, pure.
@@ -95,6 +99,7 @@ hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_stream(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const float* parts, int split, long long part_stride,
                          float* C, long long count, hipStream_t s);
 hipError_t launch_zero(float* C, long long count, hipStream_t s);

@@ -74,10 +74,18 @@ template <> struct Blk<16> {
 
 }  // namespace f32ring
 
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB>
-__global__ void __launch_bounds__(WM * WN * KS * 64)
-__attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / (NBUF * (BM + BN) * BK * 4)) * WM * WN * KS + 3) / 4)))
-gemm_f32_ring_kernel(GemmArgs args)
+template <int BM, int BN, int BK, int NBUF>
+constexpr int ring_lds_bytes() { return NBUF * (BM + BN) * BK * 4; }
+
+// One output tile over K values [kbeg, kend): the whole ring pipeline from
+// the first loads to the stores. The ring is this function's own LDS array
+// (one per instantiation; each kernel instantiates it once), so the
+// direct-to-LDS loads address it without a generic-to-LDS conversion. SEG: the tile's result goes to `outp` (row
+// stride `ostride` floats), of which `orows` x `ocols` are stored; otherwise
+// to C or to the partial slice of split `ostride`.
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool SEG>
+__device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int tn, int kbeg, int kend, float* outp,
+                                             int ostride, int orows, int ocols)
 {
     using namespace dma;
     using namespace f32ring;
@@ -115,15 +123,15 @@ gemm_f32_ring_kernel(GemmArgs args)
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * STAGE];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    // SEG (one of several segments of a stream-K workgroup): the thread id is
+    // made opaque so values derived from it are recomputed per segment
+    // instead of being kept live across all of them.
+    int tid = threadIdx.x;
+    if constexpr (SEG) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, lane_id = lane;
     const int wave = tid >> 6;
-    int tm, tn, s;
-    tile_coords(blockIdx.x, args, tm, tn, s);
     const int M = args.M, N = args.N, K = args.K;
     const int m0 = tm * BM, n0 = tn * BN;
-    const int kbeg = s * args.k_chunk;
-    const int kend = min(K, kbeg + args.k_chunk);
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
     const int pos = wave % NP, half = wave / NP;
     const int wm0 = (pos / WN) * WTM;
@@ -141,6 +149,8 @@ gemm_f32_ring_kernel(GemmArgs args)
     // 16-byte pieces) fills each block with four loads, load u covering bytes
     // 256 u .. + 255 of the block, one float per lane.
     auto issue_el = [&](int st, int q) {
+        int lane = lane_id;
+        if constexpr (SEG) asm volatile("" : "+v"(lane));   // see issue_one
         const int k0 = kbeg + st * BK;
         unsigned char* buf = lds + (st % NBUF) * STAGE;
         if (q < A_PW * LA) {
@@ -169,6 +179,13 @@ gemm_f32_ring_kernel(GemmArgs args)
             return;
         }
         if (q >= A_PW * LA) q = A_PW + (q - A_PW * LA);   // 16-byte B loads follow A's
+        // Stream-K segments form load offsets at issue rather than keeping
+        // them live across segments; the data-parallel form keeps them (the
+        // compiler hoists them out of the K loop, which leaves only an add
+        // per load inside it: forming them per load costs enough VALU issue
+        // to leave the matrix pipe idle).
+        int lane = lane_id;
+        if constexpr (SEG) asm volatile("" : "+v"(lane));
         const int k0 = kbeg + st * BK;
         unsigned char* buf = lds + (st % NBUF) * STAGE;
         if (q < A_PW) {
@@ -298,8 +315,18 @@ gemm_f32_ring_kernel(GemmArgs args)
     // over through LDS (the ring is idle now) and adds the partner's. The
     // tail is instantiated per half so every accumulator index is static.
     constexpr int I0 = KS == 2 ? TM / 2 : TM;  // row blocks each wave stores
-    float* outp = args.out + (long long)s * args.part_stride + (long long)m0 * N + n0;
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(outp, ((long long)(M - m0) * N - n0) * 4);
+    // Data-parallel form (outp carries nothing): the tile goes to C, or to
+    // split `ostride`'s partial slice, at (m0, n0) with row stride N. Formed
+    // here rather than by the caller, so it is not live through the K loop.
+    if constexpr (!SEG) {
+        outp = args.out + (long long)ostride * args.part_stride + (long long)m0 * N + n0;
+        orows = M - m0;
+        ocols = N - n0;
+        ostride = N;
+    }
+    const __amdgpu_buffer_rsrc_t rC =
+        SEG ? make_rsrc(outp, orows > 0 && ocols > 0 ? ((long long)(orows - 1) * ostride + ocols) * 4 : 0)
+            : make_rsrc(outp, ((long long)(M - m0) * N - n0) * 4);
     auto finish = [&](auto hc) {
         constexpr int H = decltype(hc)::value;
         constexpr int IB = KS == 2 ? H * I0 : 0;
@@ -353,14 +380,14 @@ gemm_f32_ring_kernel(GemmArgs args)
                         // each column checked against N.
 #pragma unroll
                         for (int v = 0; v < V; ++v) {
-                            const bool okv = m0 + row < M && n0 + col + v < N;
+                            const bool okv = row < orows && col + v < ocols;
                             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[IB + ii][j][v][r]), rC,
-                                                                  okv ? (row * N + col + v) * 4 : kOOB, 0, 0);
+                                                                  okv ? (row * ostride + col + v) * 4 : kOOB, 0, 0);
                         }
                         continue;
                     }
-                    const bool ok = m0 + row < M && n0 + col < N;
-                    const int off = ok ? (row * N + col) * 4 : kOOB;
+                    const bool ok = row < orows && col < ocols;
+                    const int off = ok ? (row * ostride + col) * 4 : kOOB;
                     if constexpr (V == 4) {
                         const u4 v = {__float_as_uint(acc[IB + ii][j][0][r]), __float_as_uint(acc[IB + ii][j][1][r]),
                                       __float_as_uint(acc[IB + ii][j][2][r]), __float_as_uint(acc[IB + ii][j][3][r])};
@@ -379,17 +406,136 @@ gemm_f32_ring_kernel(GemmArgs args)
         finish(std::integral_constant<int, 1>{});
 }
 
+// Data-parallel form: one workgroup per (tile, split); split s covers K
+// values [s k_chunk, (s + 1) k_chunk) and writes C or its partial slice.
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB>
+__global__ void __launch_bounds__(WM * WN * KS * 64)
+__attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / ring_lds_bytes<BM, BN, BK, NBUF>()) * WM * WN * KS + 3) / 4)))
+gemm_f32_ring_kernel(GemmArgs args)
+{
+    int tm, tn, s;
+    dma::tile_coords(blockIdx.x, args, tm, tn, s);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kbeg = s * args.k_chunk;
+    const int kend = min(args.K, kbeg + args.k_chunk);
+    ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, false>(args, tm, tn, kbeg, kend, nullptr, s, 0, 0);
+}
+
+// Stream-K form (page "fix(fp4_gemm autotune) SM107 kernel family excluded
+// from autotune candidates and heuristics update - #4856", section "Swap
+// microbenchmarks across M, N, and K": tile counts that do not fill the
+// machine). The T tiles x I K-iterations (BK values each) form one range of
+// W = T I iterations, and workgroup g of the G launched owns iterations
+// [floor(W g / G), floor(W (g + 1) / G)). A tile wholly inside one range is
+// written to C; a tile shared by several ranges leaves each share in a
+// workspace slot (the range's first segment in slot 2 g, its last in slot
+// 2 g + 1, BM x BN floats each) and the fix-up kernel adds the shares in
+// range order. Ranges are numbered by logical workgroup (each XCD holds
+// consecutive ranges). The split points depend only on the plan, so the
+// result does not depend on timing.
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB>
+__global__ void __launch_bounds__(WM * WN * KS * 64)
+__attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / ring_lds_bytes<BM, BN, BK, NBUF>()) * WM * WN * KS + 3) / 4)))
+gemm_f32_ring_sk_kernel(GemmArgs args)
+{
+    const long long I = args.sk_iters, T = (long long)args.tiles_m * args.tiles_n;
+    const long long W = T * I, G = gridDim.x;
+    const long long g = dma::logical_wg(blockIdx.x, (int)G, args.xcd_remap);
+    long long it = W * g / G;
+    const long long end = W * (g + 1) / G;
+    // A range spans at most three tiles: the planner keeps W / G <= 2 I.
+#pragma unroll
+    for (int seg = 0; seg < 3; ++seg) {
+        if (it >= end) break;
+        const bool first = seg == 0;
+        const long long t = it / I;
+        const int k0 = (int)(it - t * I);
+        const int k1 = (int)min(I, (long long)k0 + (end - it));
+        int tm, tn;
+        dma::tile_of((int)t, args, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        if (!first) dma::barrier();   // the previous segment's last LDS reads are done
+        const int kbeg = k0 * BK, kend = min(args.K, k1 * BK);
+        const bool whole = k0 == 0 && k1 == I;
+        float* outp = whole ? args.out + (long long)m0 * args.N + n0
+                            : args.ws + (2 * g + (first ? 0 : 1)) * (long long)(BM * BN);
+        ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, true>(
+            args, tm, tn, kbeg, kend, outp, whole ? args.N : BN, whole ? args.M - m0 : BM,
+            whole ? args.N - n0 : BN);
+        it += k1 - k0;
+    }
+}
+
+// Stream-K fix-up: sk_fixup_wgs workgroups per tile. A tile that lies in one
+// range was written by the main kernel; otherwise its shares are added in
+// range order, (((share of range g0) + share of g0 + 1) + ...), and the sum
+// is stored.
+__device__ __forceinline__ long long sk_start(long long W, long long G, long long g) { return W * g / G; }
+
+__device__ __forceinline__ long long sk_range_of(long long W, long long G, long long x) {
+    long long g = x * G / W;
+    while (g + 1 < G && sk_start(W, G, g + 1) <= x) ++g;
+    while (g > 0 && sk_start(W, G, g) > x) --g;
+    return g;
+}
+
+// Workgroups per tile in the fix-up: one float4 of the tile per thread.
+template <int BM, int BN>
+constexpr int sk_fixup_wgs() { return BM * BN / (256 * 4); }
+
+template <int BM, int BN>
+__global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs args)
+{
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    constexpr int CH = sk_fixup_wgs<BM, BN>();
+    const long long I = args.sk_iters, T = (long long)args.tiles_m * args.tiles_n;
+    const long long W = T * I, G = args.sk_grid, t = blockIdx.x / CH;
+    const long long lo = t * I, hi = (t + 1) * I - 1;
+    const long long g0 = sk_range_of(W, G, lo), g1 = sk_range_of(W, G, hi);
+    if (g0 == g1) return;
+    int tm, tn;
+    dma::tile_of((int)t, args, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int e4 = (blockIdx.x % CH) * 256 + threadIdx.x;
+    const int r = e4 / (BN / 4), c = (e4 % (BN / 4)) * 4;
+    if (m0 + r >= args.M || n0 + c >= args.N) return;
+    const long long first_slot = sk_start(W, G, g0) == lo ? 2 * g0 : 2 * g0 + 1;
+    v4f sum = reinterpret_cast<const v4f*>(args.ws + first_slot * (BM * BN))[e4];
+#pragma unroll 4
+    for (long long g = g0 + 1; g <= g1; ++g) {
+        if (sk_start(W, G, g) == sk_start(W, G, g + 1)) continue;   // empty range
+        const v4f x = reinterpret_cast<const v4f*>(args.ws + 2 * g * (BM * BN))[e4];
+        sum[0] = sum[0] + x[0];
+        sum[1] = sum[1] + x[1];
+        sum[2] = sum[2] + x[2];
+        sum[3] = sum[3] + x[3];
+    }
+    float* crow = args.out + (long long)(m0 + r) * args.N + n0 + c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (n0 + c + q < args.N) crow[q] = sum[q];
+}
+
 typedef void (*F32RingFn)(GemmArgs);
 
-// The element-load form, for variants that have one (EL = 1 in the table):
-// it needs four times the loads in flight, and its address arithmetic costs
-// registers that the largest tiles do not have to spare.
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, int EL, bool ELA, bool ELB>
-constexpr F32RingFn el_kernel() {
-    if constexpr (EL != 0) {
-        static_assert((NBUF - 1) * (((BM + BN) * BK * 4 / 1024) / (WM * WN * KS) * 4) < 64,
-                      "element loads in flight must stay countable");
-        return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB>;
+// Stream-K forms exist for tiles up to 128 x 256: larger tiles run out of
+// registers across segments, and their tile counts fill the machine anyway.
+constexpr int kSkMaxTile = 128 * 256;
+
+// A kernel of the table: data-parallel or stream-K (SK), each operand in
+// 16-byte or element form. The element forms exist only for variants that
+// have them (EL = 1 in the table): they need four times the loads in flight,
+// and their address arithmetic costs registers that the largest tiles do not
+// have to spare.
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, int EL, bool ELA, bool ELB, bool SK>
+constexpr F32RingFn ring_kernel() {
+    if constexpr ((EL != 0 || (!ELA && !ELB)) && (!SK || BM * BN <= kSkMaxTile)) {
+        static_assert((NBUF - 1) * (((BM + BN) * BK * 4 / 1024) / (WM * WN * KS) * (ELA || ELB ? 4 : 1)) < 64,
+                      "loads in flight must stay countable");
+        if constexpr (SK)
+            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB>;
+        else
+            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB>;
     } else {
         return nullptr;
     }
@@ -397,17 +543,23 @@ constexpr F32RingFn el_kernel() {
 
 struct F32RingKernel {
     int id;
-    F32RingFn fn[2][2];   // [a_vec][b_vec]: 16-byte loads for an operand whose rows are 16-byte pieces
+    F32RingFn fn[2][2][2];   // [stream-K][a_vec][b_vec]: 16-byte loads for an operand whose rows are 16-byte pieces
+    F32RingFn fixup;
+    int fixup_wgs;   // fix-up workgroups per tile
     int threads;
 };
 
-#define SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32) \
-    {id,                                                                                \
-     {{el_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, true>(),                 \
-       el_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, false>()},               \
-      {el_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false, true>(),                \
-       gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false>}},        \
-     WM * WN * KS * 64},
+#define SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, SK)                              \
+    {{ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, true, SK>(),                     \
+      ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, false, SK>()},                   \
+     {ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false, true, SK>(),                    \
+      ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false, false, SK>()}}
+
+#define SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32)      \
+    {id,                                                                                         \
+     {SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false),                          \
+      SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true)},                          \
+     sk_fixup_kernel<BM, BN>, sk_fixup_wgs<BM, BN>(), WM * WN * KS * 64},
 
 static const F32RingKernel kF32RingTable[] = {SAM_F32RING_VARIANTS(SAM_F32RING_ENTRY)};
 
@@ -416,9 +568,20 @@ hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s)
     for (const F32RingKernel& k : kF32RingTable) {
         if (k.id != p.variant_id) continue;
         if (p.dtype != DT_F32) return hipErrorInvalidDeviceFunction;
-        const F32RingFn fn = k.fn[p.a_vec ? 1 : 0][p.b_vec ? 1 : 0];
+        const F32RingFn fn = k.fn[p.sk ? 1 : 0][p.a_vec ? 1 : 0][p.b_vec ? 1 : 0];
         if (!fn) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(k.threads), 0, s, a);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidDeviceFunction;
+}
+
+hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s)
+{
+    for (const F32RingKernel& k : kF32RingTable) {
+        if (k.id != p.variant_id) continue;
+        hipLaunchKernelGGL(k.fixup, dim3((unsigned)((long long)p.tiles_m * p.tiles_n * k.fixup_wgs)), dim3(256), 0, s,
+                           a);
         return hipGetLastError();
     }
     return hipErrorInvalidDeviceFunction;

@@ -157,6 +157,56 @@ static void fill_plan(const Variant& v, long long M, long long N, long long K, i
     p->est_us = estimate_us(v, M, N, K, dtype, split, p->a_vec, p->b_vec);
 }
 
+// Stream-K (split_k = -1 in the ABI): FP32 ring variants with tiles of at
+// most 128 x 256, G = resident workgroups (256 CUs x those that fit one CU's
+// LDS), W = tiles x I K-iterations with W >= G (no empty range) and at most
+// 2 I iterations per range (a range then touches at most three tiles).
+static int sk_wgs_per_cu(const Variant& v)
+{
+    const int lds = v.nbuf * (v.bm + v.bn) * v.bk * 4;
+    const int w = kDev.lds_bytes / lds;
+    return w < 1 ? 1 : w;
+}
+
+static bool sk_geometry(const Variant& v, long long M, long long N, long long K, long long* G, long long* I)
+{
+    if (v.kind != KIND_F32RING || (long long)v.bm * v.bn > 128 * 256 || K == 0 || M == 0 || N == 0) return false;
+    const long long tiles = cdiv(M, v.bm) * cdiv(N, v.bn);
+    *I = cdiv(K, v.bk);
+    *G = (long long)kDev.cus * sk_wgs_per_cu(v);
+    const long long W = tiles * *I;
+    return W >= *G && cdiv(W, *G) <= 2 * *I && tiles < (1ll << 31);
+}
+
+static double estimate_sk_us(const Variant& v, long long M, long long N, long long K, int dtype, long long G,
+                             long long I, int a_vec, int b_vec)
+{
+    double eff = dtype == DT_F32 ? v.eff_f32 : v.eff_h16;
+    if (!a_vec) eff *= 0.85;
+    if (!b_vec) eff *= 0.85;
+    const double peak_cu = kDev.f32_flop_per_clk_cu * kDev.clock_ghz * 1e3;   // FLOP per microsecond
+    const double t_iter = 2.0 * v.bm * v.bn * v.bk / (peak_cu * eff);
+    const long long W = cdiv(M, v.bm) * cdiv(N, v.bn) * I;
+    const double mb = 1e-6;
+    // Every range runs ceil(W / G) iterations with the CU shared by the
+    // workgroups resident on it, and ends up to three segments with a tile
+    // store; the fix-up reads at most two slots per range and writes C.
+    const double t_main = (double)cdiv(W, G) * t_iter * sk_wgs_per_cu(v);
+    const double t_epi = 3.0 * kDev.cus * v.bm * v.bn * 4.0 * mb / kDev.hbm_write_gbs * 1e3;
+    const double fix = (2.0 * G * v.bm * v.bn * 4.0 + 4.0 * M * N) * mb / kDev.hbm_gbs * 1e3;
+    return t_main + t_epi + fix + 2 * kDev.launch_us;
+}
+
+static void fill_plan_sk(const Variant& v, long long M, long long N, long long K, int dtype, long long G, long long I,
+                         Plan* p)
+{
+    fill_plan(v, M, N, K, dtype, 1, p);
+    p->sk = 1;
+    p->grid = G;
+    p->ws_bytes = 2ull * (unsigned long long)G * (unsigned long long)(v.bm * v.bn) * 4ull;
+    p->est_us = estimate_sk_us(v, M, N, K, dtype, G, I, p->a_vec, p->b_vec);
+}
+
 static const int kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
 
 // Split-K is for filling the machine when there are fewer output tiles than
@@ -184,6 +234,13 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     // The streaming kernels cover at most 16 rows (16 x 64 tile) or 16
     // columns (64 x 16 tile) of C.
     if (v->kind == KIND_STREAM && (v->bm == 16 ? M > 16 : N > 16)) return false;
+    long long G = 0, I = 0;
+    const bool sk_ok = sk_geometry(*v, M, N, K, &G, &I);
+    if (split_req == -1) {
+        if (!sk_ok) return false;
+        fill_plan_sk(*v, M, N, K, dtype, G, I, out);
+        return true;
+    }
     if (split_req > 0) {
         if (split_req > 1 && (K == 0 || !split_admissible(*v, K, dtype, split_req))) return false;
         fill_plan(*v, M, N, K, dtype, split_req, out);
@@ -197,6 +254,14 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
         Plan p{};
         fill_plan(*v, M, N, K, dtype, s, &p);
         if (p.grid >= (1ll << 31) || !split_wanted(p)) continue;
+        if (!found || p.est_us < best.est_us) {
+            best = p;
+            found = true;
+        }
+    }
+    if (sk_ok) {
+        Plan p{};
+        fill_plan_sk(*v, M, N, K, dtype, G, I, &p);
         if (!found || p.est_us < best.est_us) {
             best = p;
             found = true;
@@ -244,8 +309,13 @@ void plan_name(const Plan& p, char* buf, int n)
 {
     static const char* dt[] = {"f32", "bf16", "f16"};
     const Variant* v = variant_get(p.variant_id);
-    snprintf(buf, n, "%s_%s_s%d%s%s%s", dt[p.dtype], v ? v->name : "?", p.split,
-             p.a_vec ? "" : "_ua", p.b_vec ? "" : "_ub", p.tuned ? "_tuned" : "");
+    char sp[16];
+    if (p.sk)
+        snprintf(sp, sizeof(sp), "sk");
+    else
+        snprintf(sp, sizeof(sp), "s%d", p.split);
+    snprintf(buf, n, "%s_%s_%s%s%s%s", dt[p.dtype], v ? v->name : "?", sp, p.a_vec ? "" : "_ua",
+             p.b_vec ? "" : "_ub", p.tuned ? "_tuned" : "");
 }
 
 }  // namespace sam

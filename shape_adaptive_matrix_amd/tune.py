@@ -60,8 +60,9 @@ def shapes():
 
 def candidates(sam, dt, M, N, K):
     """(variant, split) pairs: every admissible variant with its own split
-    choice, plus the other admissible splits of the four variants the cost
-    model ranks best, when their tile count leaves CUs idle."""
+    choice and its stream-K form (split -1) where it has one, plus the other
+    admissible splits of the four variants the cost model ranks best, when
+    their tile count leaves CUs idle."""
     own = []
     for vid in range(sam.variant_count()):
         try:
@@ -69,6 +70,12 @@ def candidates(sam, dt, M, N, K):
         except sam.SamError:
             continue
     out = {(p["variant_id"], p["split_k"]) for p in own}
+    for p in own:   # stream-K forms (split -1) where the variant has one
+        try:
+            sam.variant_plan(p["variant_id"], M, N, K, dt, -1)
+            out.add((p["variant_id"], -1))
+        except sam.SamError:
+            pass
     for p in sorted(own, key=lambda p: (p["est_us"], p["variant_id"]))[:4]:
         if p["grid_wgs"] // p["split_k"] >= 256:
             continue

@@ -159,3 +159,24 @@ def test_no_gpu_is_reported_not_hidden():
         pytest.skip("a gfx950 device is present")
     assert _call(A_, B_, C_, 64, 64, 64) == -5
     assert sam.last_error()
+
+
+def test_stream_k_plans():
+    """split_k = -1 asks for a variant's stream-K form: 256 CUs x resident
+    workgroups, two BM x BN float slots per workgroup; only the FP32 ring
+    variants with tiles up to 128 x 256 have one, and only when there are at
+    least as many K iterations as workgroups and at most 2 tiles' worth each."""
+    p = sam.variant_plan(35, 300, 300, 4096, "f32", -1)
+    assert p["split_k"] == -1 and p["grid_wgs"] == 256
+    assert p["workspace_bytes"] == 2 * 256 * 128 * 128 * 4
+    assert p["name"].endswith("_sk")
+    with pytest.raises(sam.SamError) as e:
+        sam.variant_plan(0, 300, 300, 4096, "f32", -1)      # staged variant: no stream-K form
+    assert e.value.status == -4
+    with pytest.raises(sam.SamError):
+        sam.variant_plan(36, 300, 300, 4096, "f32", -1)     # 256 x 256 tiles: none either
+    with pytest.raises(sam.SamError):
+        sam.variant_plan(35, 64, 64, 64, "f32", -1)         # 1 tile x 1 iteration < 256 workgroups
+    with pytest.raises(sam.SamError) as e:
+        sam.variant_plan(35, 300, 300, 4096, "f32", -2)
+    assert e.value.status == -1

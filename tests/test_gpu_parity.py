@@ -119,6 +119,48 @@ def test_every_variant_dyadic_skinny(vid):
         pytest.skip(f"variant {vid} takes no skinny FP32 shape")
 
 
+# Stream-K (split -1): shapes where ranges cut tiles into several shares
+# (300x300x4096: ~28 shares per tile), ragged and odd-K/N ones, and a range
+# that touches three tiles.
+SK_SHAPES = [(300, 300, 4096), (768, 768, 768), (129, 257, 2000), (1000, 1000, 1000), (17, 2000, 3000),
+             (1536, 1536, 1536), (260, 1030, 2052)]
+_SK_REF = {}
+
+
+@pytest.mark.parametrize("vid", range(sam.variant_count()))
+def test_every_variant_stream_k_dyadic(vid):
+    ran = 0
+    for (M, N, K) in SK_SHAPES:
+        if not _supported(vid, M, N, K, "f32", -1):
+            continue
+        A, B = ints_operands(M, N, K, "f32", seed=M + 3 * N + 7 * K)
+        if (M, N, K) not in _SK_REF:
+            _SK_REF[(M, N, K)] = orc().gemm("f32", A, B)
+        print(f"[sk] variant {vid} {(M, N, K)}", flush=True)
+        C = run(A, B, "f32", variant=vid, split=-1)
+        bad = bitexact_mismatches(C, _SK_REF[(M, N, K)])
+        assert bad == 0, f"variant {vid} {(M, N, K)} stream-K: {bad} mismatches"
+        ran += 1
+    if ran == 0:
+        pytest.skip(f"variant {vid} has no stream-K form for these shapes")
+
+
+def test_stream_k_random_and_repeatable():
+    """Random inputs: within the FP32 bound, and bitwise identical on repeats
+    (the shares of a tile are always added in the same order)."""
+    M, N, K = 300, 300, 4096
+    rng = np.random.default_rng(5)
+    A, B = si.uniform_pm1(rng, (M, K)), si.uniform_pm1(rng, (K, N))
+    ref = orc().gemm("f32", A, B)
+    vids = [v for v in range(sam.variant_count()) if _supported(v, M, N, K, "f32", -1)]
+    assert vids
+    for vid in vids:
+        outs = [run(A, B, "f32", variant=vid, split=-1) for _ in range(3)]
+        assert rel_rms(outs[0], ref) <= 1e-5
+        for o in outs[1:]:
+            assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), vid
+
+
 def test_c_is_write_only_and_fully_written():
     """NaN-prefilled C: every element written; guard band after C untouched."""
     M, N, K = 99, 77, 55
