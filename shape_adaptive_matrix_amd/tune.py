@@ -88,6 +88,20 @@ def candidates(sam, dt, M, N, K):
     return sorted(out)
 
 
+def model_plan(sam, dt, M, N, K):
+    """The cost model's own pick, ignoring the frozen table: the lowest
+    estimate over every variant's own plan, ties to the lower id."""
+    best = None
+    for vid in range(sam.variant_count()):
+        try:
+            p = sam.variant_plan(vid, M, N, K, dt, 0)
+        except sam.SamError:
+            continue
+        if best is None or p["est_us"] < best["est_us"]:
+            best = p
+    return best
+
+
 def measure(record: Path, only=None):
     import torch
 
@@ -116,7 +130,7 @@ def measure(record: Path, only=None):
             del A, B
             C = torch.empty((M, N), dtype=torch.float32, device="cuda")
             stream = torch.cuda.current_stream()
-            auto = sam.plan(M, N, K, dt)
+            auto = model_plan(sam, dt, M, N, K)
             print(f"[tune] {name}: {len(candidates(sam, dt, M, N, K))} candidates", flush=True)
             for (vid, split) in candidates(sam, dt, M, N, K):
                 if (dt, M, N, K, vid, split) in done:
@@ -189,12 +203,14 @@ def emit(record: Path, out: Path = TUNED_H) -> str:
 
 
 def report(record: Path) -> str:
+    import shape_adaptive_matrix_amd as sam
     table = load(record)
     out = ["| shape | dtype | best plan | TFLOP/s | cost-model pick | its TFLOP/s | candidates |",
            "|---|---|---|---:|---|---:|---:|"]
     for (dt, M, N, K), rs in sorted(table.items(), key=lambda kv: (DTYPE_CODE[kv[0][0]], kv[0][1:])):
         best = rs[0]
-        model = next((r for r in rs if r["model_pick"]), None)
+        mp = model_plan(sam, dt, M, N, K)
+        model = next((r for r in rs if (r["variant"], r["split"]) == (mp["variant_id"], mp["split_k"])), None)
         out.append(f"| {M}x{N}x{K} | {dt} | {best['plan']} | {best['tflops']} | "
                    f"{model['plan'] if model else '-'} | {model['tflops'] if model else '-'} | {len(rs)} |")
     return "\n".join(out) + "\n"
