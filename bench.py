@@ -99,6 +99,43 @@ def prepare(w, torch, sam, si, variant=None, split=0):
     return {"step": step, "plan": plan, "keep": (dA, dB, C, ws), "stream": stream}
 
 
+def prepare_ex(w, torch, sam, si, ta: bool, tb: bool, alpha: float, beta: float, pad: int):
+    """One call of the general entry point sam_gemm_ex on the workload's
+    operands, stored transposed where asked and with `pad` extra elements per
+    row (the leading dimensions); C is read when beta != 0."""
+    import numpy as np
+    A, B = si.make_operands(w)
+    if ta:
+        A = np.ascontiguousarray(A.T)
+    if tb:
+        B = np.ascontiguousarray(B.T)
+
+    def dev(x):
+        x = np.pad(x, ((0, 0), (0, pad)))
+        t = torch.from_numpy(x if w.dtype == "f32" else x.view("int16")).cuda()
+        return t if w.dtype == "f32" else t.view({"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype])
+
+    dA, dB = dev(A), dev(B)
+    del A, B
+    lda, ldb, ldc = dA.shape[1], dB.shape[1], w.N + pad
+    C = torch.zeros((w.M, ldc), dtype=torch.float32, device="cuda")
+    n = sam.ex_workspace_bytes(w.M, w.N, w.K, ta, tb, lda, ldb, ldc, alpha, beta, w.dtype)
+    ws = torch.empty((n + 3) // 4, dtype=torch.float32, device="cuda") if n else None
+    L = sam.lib()
+    stream = torch.cuda.current_stream()
+    args = (sam.DTYPES[w.dtype], int(ta), int(tb), w.M, w.N, w.K, ctypes.c_float(alpha),
+            ctypes.c_void_p(dA.data_ptr()), lda, ctypes.c_void_p(dB.data_ptr()), ldb, ctypes.c_float(beta),
+            ctypes.c_void_p(C.data_ptr()), ldc, ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
+            n, ctypes.c_void_p(stream.cuda_stream))
+
+    def step():
+        rc = L.sam_gemm_ex(*args)
+        if rc != 0:
+            raise RuntimeError(f"{sam.STATUS.get(rc, rc)}: {sam.last_error()}")
+
+    return {"step": step, "plan": sam.plan(w.M, w.N, w.K, w.dtype), "keep": (dA, dB, C, ws), "stream": stream}
+
+
 def time_steps(torch, step, steps: int) -> float:
     """Milliseconds for `steps` back-to-back calls, HIP events on the stream the
     kernels run on (torch's current stream, which the calls are given)."""
@@ -209,6 +246,9 @@ def main():
     ap.add_argument("--variant", type=int, default=None,
                     help="force this variant id (calibration); default: the dispatcher's plan")
     ap.add_argument("--split", type=int, default=0, help="split-K for --variant (0: the variant's pick)")
+    ap.add_argument("--ex", default=None, metavar="TA,TB,ALPHA,BETA,PAD",
+                    help="time the general entry point instead (e.g. T,N,2,1,8: A stored transposed, "
+                         "alpha 2, beta 1, rows padded by 8 elements)")
     ap.add_argument("--ceilings", action="store_true",
                     help="also run the MFMA-loop / HBM-copy ceiling probe and report its figures")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -244,7 +284,11 @@ def main():
         w = si.Workload(f"{dt}_{M}x{N}x{K}", dt, M, N, K, "uniform" if dt == "f32" else "normal16", 99)
     else:
         w = si.by_name(args.workload)
-    g = prepare(w, torch, sam, si, args.variant, args.split)
+    if args.ex:
+        ta, tb, alpha, beta, pad = args.ex.split(",")
+        g = prepare_ex(w, torch, sam, si, ta == "T", tb == "T", float(alpha), float(beta), int(pad))
+    else:
+        g = prepare(w, torch, sam, si, args.variant, args.split)
     step = g["step"]
     for _ in range(args.warmup):
         step()
@@ -265,7 +309,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: C=A*B, M={w.M} N={w.N} K={w.K}, {w.dtype} operands, "
                                f"FP32 accumulate/output, {w.dist} inputs seed {w.seed}",
-                   "M": w.M, "N": w.N, "K": w.K, "plan": g["plan"]["name"]},
+                   "M": w.M, "N": w.N, "K": w.K, "plan": g["plan"]["name"],
+                   **({"general_entry_point": args.ex} if args.ex else {})},
         "pct_mfma_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2),
         "wall_s": round(wall, 4),
         "roofline": {

@@ -111,6 +111,44 @@ sam_status sam_gemm_f16(const uint16_t* A, const uint16_t* B, float* C,
                         int64_t M, int64_t N, int64_t K, void* workspace,
                         uint64_t workspace_bytes, void* stream);
 
+/* Operand forms of the general entry point. */
+typedef enum { SAM_OP_N = 0, SAM_OP_T = 1 } sam_op;
+
+/* General form C = alpha * op(A) * op(B) + beta * C, the usual BLAS
+ * definition (the pages' GEMM is its alpha = 1, beta = 0, no-transpose
+ * case: page "Scale coverage exposes a remaining GEMM gap", section
+ * "Measurement contract and evidence"). Row-major storage with row strides:
+ *   op(A) is M x K: SAM_OP_N reads A as M rows of K values (lda >= K),
+ *                   SAM_OP_T reads A as K rows of M values (lda >= M);
+ *   op(B) is K x N: SAM_OP_N reads K rows of N (ldb >= N), SAM_OP_T N rows of
+ *                   K (ldb >= K);
+ *   C is M rows of N values, ldc >= N.
+ * Element types as for sam_gemm_<dtype>; alpha and beta are FP32. C is read
+ * only when beta != 0 (with beta == 0 whatever C held never reaches the
+ * result); A and B are not read when alpha == 0 or K == 0. The result is
+ * fmaf(alpha, P, beta * C) with P the FP32 product of the GEMM path (alpha * P
+ * when beta == 0).
+ * How: a call with SAM_OP_N, SAM_OP_N, compact strides, alpha 1 and beta 0 is
+ * exactly sam_gemm_<dtype>. Otherwise op(A) and op(B) are first copied into
+ * compact rows in the workspace (transposing where asked), the GEMM path runs
+ * on them (into a workspace temporary unless ldc == N and beta == 0), and a
+ * last pass applies alpha and beta; the copies cost extra HBM traffic.
+ * Base pointers must be 16-byte aligned; the workspace must hold
+ * sam_gemm_ex_workspace() bytes (SAM_ERR_WORKSPACE otherwise).
+ * Asynchronous on `stream`, like the other entry points. */
+sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b,
+                       int64_t M, int64_t N, int64_t K, float alpha,
+                       const void* A, int64_t lda, const void* B, int64_t ldb,
+                       float beta, float* C, int64_t ldc, void* workspace,
+                       uint64_t workspace_bytes, void* stream);
+
+/* Workspace bytes sam_gemm_ex needs for these arguments (host only). */
+sam_status sam_gemm_ex_workspace(sam_dtype dtype, sam_op trans_a,
+                                 sam_op trans_b, int64_t M, int64_t N,
+                                 int64_t K, int64_t lda, int64_t ldb,
+                                 int64_t ldc, float alpha, float beta,
+                                 uint64_t* bytes);
+
 /* Number of entries in the variant table (ids 0 .. count-1). */
 int32_t sam_variant_count(void);
 

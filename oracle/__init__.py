@@ -75,6 +75,9 @@ class Oracle:
         lib.oracle_decode_bf16.restype = ctypes.c_double
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_f16.restype = ctypes.c_double
+        lib.oracle_gemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_double,
+                                       vp, i64, vp, i64, ctypes.c_double, vp, dp, ctypes.c_int]
+        lib.oracle_gemm_ex.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -139,6 +142,30 @@ class Oracle:
                                          self._ptr(out), nthreads)
         if rc != 0:
             raise ValueError("oracle_gemm_points rejected its arguments")
+        return out
+
+    def gemm_ex(self, dtype: str, M: int, N: int, K: int, A, lda: int, B, ldb: int, trans_a: bool,
+                       trans_b: bool, alpha: float, beta: float, C0=None, nthreads: int = 0) -> np.ndarray:
+        """alpha·op(A)·op(B) + beta·C0 as float64[M, N] (oracle_gemm_ex), with
+        A and B given as flat buffers and explicit row strides."""
+        code = _DTYPES[dtype]
+        want = np.float32 if code == F32 else np.uint16
+        A = np.ascontiguousarray(A).ravel()
+        B = np.ascontiguousarray(B).ravel()
+        if A.dtype != want or B.dtype != want:
+            raise TypeError(f"{dtype} operands must be {np.dtype(want).name}")
+        C0p = None
+        if C0 is not None:   # handed over as given: the C side must not read it when beta is 0
+            C0 = np.ascontiguousarray(C0, dtype=np.float32)
+            if C0.shape != (M, N):
+                raise ValueError("C0 must be [M, N]")
+            C0p = self._ptr(C0)
+        out = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_gemm_ex(code, int(bool(trans_a)), int(bool(trans_b)), M, N, K, float(alpha),
+                                     self._ptr(A), lda, self._ptr(B), ldb, float(beta), C0p, self._ptr(out),
+                                     nthreads)
+        if rc != 0:
+            raise ValueError("oracle_gemm_ex rejected its arguments")
         return out
 
     def decode(self, dtype: str, bits: int) -> float:

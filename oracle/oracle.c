@@ -177,3 +177,46 @@ int oracle_gemm_points(int dtype, const void* A, const void* B, int64_t M,
     }
     return 0;
 }
+
+/* The general form out = alpha * op(A) * op(B) + beta * C0, the usual BLAS
+ * definition (the pages fix alpha = 1, beta = 0 and no transposes; this
+ * wider form is the reading used for the general entry point). Storage is
+ * row-major with explicit row strides:
+ *   op(A) = A (M rows of K, stride lda) or A^T (A holds K rows of M, stride lda);
+ *   op(B) = B (K rows of N, stride ldb) or B^T (B holds N rows of K, stride ldb).
+ * C0 is compact [M][N] and is read only when beta != 0; the product is not
+ * evaluated when alpha == 0 or K == 0 (so nothing in A or B can reach out).
+ * Per element: P = sum over ascending k of exact products, in double from
+ * +0.0; out = alpha * P + beta * C0 in double, returned unrounded. */
+int oracle_gemm_ex(int dtype, int trans_a, int trans_b, int64_t M, int64_t N,
+                   int64_t K, double alpha, const void* A, int64_t lda,
+                   const void* B, int64_t ldb, double beta, const float* C0,
+                   double* out, int nthreads)
+{
+    if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
+    if (M < 0 || N < 0 || K < 0 || (trans_a != 0 && trans_a != 1) ||
+        (trans_b != 0 && trans_b != 1)) return -1;
+    if (lda < (trans_a ? M : K) || ldb < (trans_b ? K : N)) return -1;
+    const int product = alpha != 0.0 && K > 0;
+    if (product && M > 0 && N > 0 && (!A || !B)) return -1;
+    if (beta != 0.0 && M > 0 && N > 0 && !C0) return -1;
+    if (M > 0 && N > 0 && !out) return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double p = 0.0;
+            if (product) {
+                for (int64_t k = 0; k < K; ++k) {
+                    const double a = load_val(dtype, A, trans_a ? k * lda + i : i * lda + k);
+                    const double b = load_val(dtype, B, trans_b ? j * ldb + k : k * ldb + j);
+                    p = p + a * b;
+                }
+            }
+            double v = product ? alpha * p : 0.0;
+            if (beta != 0.0) v = v + beta * (double)C0[i * N + j];
+            out[i * N + j] = v;
+        }
+    }
+    return 0;
+}

@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
         "sam_variant_info": ([i32, P], ctypes.c_int),
         "sam_variant_plan": ([i32, i64, i64, i64, ctypes.c_int, i32, P], ctypes.c_int),
         "sam_gemm_variant": ([i32, ctypes.c_int, i32, vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
+        "sam_gemm_ex": ([ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_float, vp, i64, vp, i64,
+                         ctypes.c_float, vp, i64, vp, u64, vp], ctypes.c_int),
+        "sam_gemm_ex_workspace": ([ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                   ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
         "sam_device_check": ([], ctypes.c_int),
         "sam_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "sam_last_error": ([], ctypes.c_char_p),
@@ -226,3 +230,50 @@ def gemm_variant(vid: int, A, B, C=None, split_k: int = 0, dtype=None, workspace
     _check(lib().sam_gemm_variant(vid, code, p["split_k"], _ptr(A), _ptr(B), _ptr(C), M, N, K,
                                   _ptr(workspace), ws_bytes, _stream_ptr(stream)))
     return C
+
+
+def _rows(t, name):
+    """Row stride of a 2-D tensor whose rows are contiguous (a compact matrix
+    or a view of one with padded rows)."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return max(int(t.stride(0)), int(t.shape[1]), 1)
+
+
+def ex_workspace_bytes(M, N, K, trans_a, trans_b, lda, ldb, ldc, alpha, beta, dtype="f32") -> int:
+    n = ctypes.c_uint64()
+    _check(lib().sam_gemm_ex_workspace(_dt(dtype), int(trans_a), int(trans_b), M, N, K, lda, ldb, ldc,
+                                       float(alpha), float(beta), ctypes.byref(n)))
+    return int(n.value)
+
+
+def gemm_ex(A, B, C=None, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, dtype=None, workspace=None,
+            stream=None):
+    """C = alpha·op(A)·op(B) + beta·C (sam_gemm_ex); returns C. op(A) is A or
+    A.T as stored (A is K x M when trans_a), likewise B; A, B and C may be
+    views with padded rows (their row stride is the leading dimension)."""
+    import torch
+    code = _torch_dtype_code(A, dtype)
+    want = 4 if code == F32 else 2
+    if A.element_size() != want or B.element_size() != want:
+        raise TypeError("operand element size does not match the dtype")
+    lda, ldb = _rows(A, "A"), _rows(B, "B")
+    M, K = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
+    Kb, N = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
+    if Kb != K:
+        raise ValueError(f"op(A) is {M}x{K} but op(B) is {Kb}x{N}")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (M, N) or C.dtype != torch.float32:
+        raise ValueError(f"C must be float32 [{M}, {N}]")
+    ldc = _rows(C, "C")
+    if workspace is None:
+        n = ex_workspace_bytes(M, N, K, trans_a, trans_b, lda, ldb, ldc, alpha, beta, code)
+        workspace = torch.empty((n + 3) // 4, dtype=torch.float32, device=A.device) if n else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sam_gemm_ex(code, int(trans_a), int(trans_b), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+                             float(beta), _ptr(C), ldc, _ptr(workspace), ws_bytes, _stream_ptr(stream)))
+    return C
+

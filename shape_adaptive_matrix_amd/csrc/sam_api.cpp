@@ -187,9 +187,129 @@ sam_status gemm_auto(int dtype, const void* A, const void* B, float* C, int64_t 
     return run(p, A, B, C, M, N, K, ws, ws_bytes, stream);
 }
 
+// The general entry point: which passes a call needs and where each one's
+// buffer sits in the caller's workspace (256-byte aligned regions).
+struct ExLayout {
+    bool fast;            // plain C = A*B: straight to the GEMM path
+    bool product;         // alpha != 0 and K > 0
+    bool pack_a, pack_b;  // op(A) / op(B) copied into compact rows first
+    bool use_t;           // product into a temporary, then C = alpha T + beta C
+    unsigned long long off_a, off_b, off_t, off_w, total;
+    sam::Plan plan;
+};
+
+unsigned long long align256(unsigned long long x) { return (x + 255ull) & ~255ull; }
+
+sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long long K, long long lda, long long ldb,
+                     long long ldc, float alpha, float beta, ExLayout* L)
+{
+    if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", dtype);
+    if ((ta != SAM_OP_N && ta != SAM_OP_T) || (tb != SAM_OP_N && tb != SAM_OP_T))
+        return fail(SAM_ERR_INVALID_ARG, "trans flags must be SAM_OP_N or SAM_OP_T");
+    sam_status st = check_shape(M, N, K);
+    if (st != SAM_OK) return st;
+    const long long min_lda = ta ? M : K, min_ldb = tb ? K : N;
+    if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) || ldc < (N > 1 ? N : 1))
+        return fail(SAM_ERR_INVALID_ARG, "leading dimension too small (lda=%lld ldb=%lld ldc=%lld)", lda, ldb, ldc);
+    const long long lim = (1ll << 61);
+    if ((M && lda > lim / (M > K ? M : (K ? K : 1))) || (N && ldb > lim / (N > K ? N : (K ? K : 1))) ||
+        (M && ldc > lim / M))
+        return fail(SAM_ERR_INVALID_ARG, "strided operand size overflows int64");
+    const unsigned long long es = dtype == SAM_F32 ? 4 : 2;
+    *L = ExLayout{};
+    L->product = alpha != 0.0f && K > 0 && M > 0 && N > 0;
+    L->fast = !ta && !tb && lda == K && ldb == N && ldc == N && alpha == 1.0f && beta == 0.0f;
+    if (L->product || L->fast) {
+        if (!sam::plan_auto(M, N, K, dtype, &L->plan)) return fail(SAM_ERR_INTERNAL, "no admissible plan");
+    }
+    if (L->fast) {
+        L->total = L->plan.ws_bytes;
+        return SAM_OK;
+    }
+    L->pack_a = L->product && (ta || lda != K);
+    L->pack_b = L->product && (tb || ldb != N);
+    L->use_t = L->product && !(ldc == N && beta == 0.0f);
+    L->off_a = 0;
+    L->off_b = align256(L->off_a + (L->pack_a ? (unsigned long long)(M * K) * es : 0));
+    L->off_t = align256(L->off_b + (L->pack_b ? (unsigned long long)(K * N) * es : 0));
+    L->off_w = align256(L->off_t + (L->use_t ? (unsigned long long)(M * N) * 4 : 0));
+    L->total = L->off_w + (L->product ? L->plan.ws_bytes : 0);
+    return SAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+sam_status sam_gemm_ex_workspace(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t M, int64_t N, int64_t K,
+                                 int64_t lda, int64_t ldb, int64_t ldc, float alpha, float beta, uint64_t* bytes)
+{
+    if (!bytes) return fail(SAM_ERR_INVALID_ARG, "bytes is null");
+    ExLayout L;
+    sam_status st = ex_layout(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc, alpha, beta, &L);
+    if (st != SAM_OK) return st;
+    *bytes = L.total;
+    return SAM_OK;
+}
+
+sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t M, int64_t N, int64_t K, float alpha,
+                       const void* A, int64_t lda, const void* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                       void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    ExLayout L;
+    sam_status st = ex_layout(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc, alpha, beta, &L);
+    if (st != SAM_OK) return st;
+    if (L.fast) return run(L.plan, A, B, C, M, N, K, workspace, workspace_bytes, stream);
+    if (M == 0 || N == 0) return SAM_OK;
+    if (!C) return fail(SAM_ERR_INVALID_ARG, "C is null");
+    if (L.product && (!A || !B)) return fail(SAM_ERR_INVALID_ARG, "A or B is null");
+    if (!aligned16(C) || (L.product && (!aligned16(A) || !aligned16(B))) || (workspace && !aligned16(workspace)))
+        return fail(SAM_ERR_MISALIGNED, "A, B, C and workspace must be 16-byte aligned");
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total))
+        return fail(SAM_ERR_WORKSPACE, "sam_gemm_ex needs %llu workspace bytes, got %llu", L.total,
+                    (unsigned long long)(workspace ? workspace_bytes : 0));
+    const unsigned long long es = dtype == SAM_F32 ? 4 : 2;
+    const unsigned long long cbytes = ((unsigned long long)(M - 1) * ldc + N) * 4;
+    const unsigned long long abytes = L.product ? ((unsigned long long)((trans_a ? K : M) - 1) * lda + (trans_a ? M : K)) * es : 0;
+    const unsigned long long bbytes = L.product ? ((unsigned long long)((trans_b ? N : K) - 1) * ldb + (trans_b ? K : N)) * es : 0;
+    if (ranges_overlap(C, cbytes, A, abytes) || ranges_overlap(C, cbytes, B, bbytes))
+        return fail(SAM_ERR_INVALID_ARG, "C overlaps A or B");
+    if (ranges_overlap(workspace, L.total, C, cbytes) || ranges_overlap(workspace, L.total, A, abytes) ||
+        ranges_overlap(workspace, L.total, B, bbytes))
+        return fail(SAM_ERR_INVALID_ARG, "workspace overlaps A, B or C");
+    sam_status d = device_check_impl();
+    if (d != SAM_OK) return d;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e = hipSuccess;
+    if (!L.product) {
+        e = sam::launch_axpby(nullptr, 0, C, ldc, M, N, alpha, beta, s);   // alpha * 0 + beta * C
+    } else {
+        const void* a = A;
+        const void* b = B;
+        if (L.pack_a) {
+            e = sam::launch_pack(A, lda, ws + L.off_a, M, K, (int)es, trans_a, s);
+            a = ws + L.off_a;
+        }
+        if (e == hipSuccess && L.pack_b) {
+            e = sam::launch_pack(B, ldb, ws + L.off_b, K, N, (int)es, trans_b, s);
+            b = ws + L.off_b;
+        }
+        if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+        float* out = L.use_t ? reinterpret_cast<float*>(ws + L.off_t) : C;
+        st = run(L.plan, a, b, out, M, N, K, L.plan.ws_bytes ? ws + L.off_w : nullptr, L.plan.ws_bytes, stream);
+        if (st != SAM_OK) return st;
+        if (L.use_t)
+            e = sam::launch_axpby(out, N, C, ldc, M, N, alpha, beta, s);
+        else if (alpha != 1.0f)
+            e = sam::launch_axpby(C, ldc, C, ldc, M, N, alpha, 0.0f, s);   // in place: C = alpha C
+    }
+    if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+    g_err[0] = '\0';
+    return SAM_OK;
+}
+
 
 sam_status sam_gemm_plan(int64_t M, int64_t N, int64_t K, sam_dtype dtype, sam_plan* out)
 {

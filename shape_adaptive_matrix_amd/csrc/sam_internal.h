@@ -103,6 +103,12 @@ hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const float* parts, int split, long long part_stride,
                          float* C, long long count, hipStream_t s);
 hipError_t launch_zero(float* C, long long count, hipStream_t s);
+// General entry point (sam_kernels_ex.hip): pack an operand (transposing
+// when `trans`) into compact rows, and C = alpha T + beta C.
+hipError_t launch_pack(const void* in, long long ld, void* out, long long rows, long long cols, int elem_bytes,
+                       int trans, hipStream_t s);
+hipError_t launch_axpby(const float* T, long long ldt, float* C, long long ldc, long long M, long long N, float alpha,
+                        float beta, hipStream_t s);
 // A representative kernel symbol for loadability checks.
 const void* probe_kernel();
 

@@ -259,8 +259,79 @@ def pin_degenerate(o):
     assert o.gemm("f32", np.ones((2, 5), np.float32), np.ones((5, 0), np.float32)).shape == (2, 0)
 
 
+def _encode_small(fmt, vals):
+    """Small integers (exact in every format) as operand arrays of `fmt`."""
+    v = np.asarray(vals, dtype=np.float32)
+    if fmt == "f32":
+        return v
+    if fmt == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def pin_ex_bruteforce(o):
+    """General form alpha·op(A)·op(B) + beta·C0 with transposes and padded row
+    strides equals exact rational arithmetic from the definition (small
+    integer operands, dyadic alpha and beta: every intermediate is exact).
+    C0 holds NaN wherever beta is 0, and A and B hold NaN in the padding and
+    everywhere when alpha is 0: neither may reach the result."""
+    rng = np.random.default_rng(111)
+    alphas = [1.0, 2.0, -0.5, 0.25, 0.0]
+    betas = [0.0, 1.0, -2.0, 0.5]
+    for case in range(120):
+        fmt = ("f32", "bf16", "f16")[case % 3]
+        M, N, K = (int(x) for x in rng.integers(1, 6, size=3))
+        ta, tb = bool(case & 4), bool(case & 8)
+        alpha, beta = alphas[case % 5], betas[(case // 5) % 4]
+        ra, ca = (K, M) if ta else (M, K)          # stored A: ra rows of ca values
+        rb, cb = (N, K) if tb else (K, N)
+        lda, ldb = ca + int(rng.integers(0, 3)), cb + int(rng.integers(0, 3))
+        Aval = rng.integers(-4, 5, size=(ra, ca))
+        Bval = rng.integers(-4, 5, size=(rb, cb))
+        A = np.full((ra, lda), np.nan, np.float32)
+        B = np.full((rb, ldb), np.nan, np.float32)
+        if alpha != 0.0:
+            A[:, :ca] = Aval
+            B[:, :cb] = Bval
+        C0 = rng.integers(-4, 5, size=(M, N)).astype(np.float32)
+        if beta == 0.0:
+            C0[:] = np.nan
+        Ae, Be = _encode_small(fmt, A), _encode_small(fmt, B)
+        got = o.gemm_ex(fmt, M, N, K, Ae, lda, Be, ldb, ta, tb, alpha, beta, C0)
+        for i in range(M):
+            for j in range(N):
+                want = Fraction(0)
+                if alpha != 0.0:
+                    p = sum(Fraction(int(Aval[k, i] if ta else Aval[i, k])) *
+                            Fraction(int(Bval[j, k] if tb else Bval[k, j])) for k in range(K))
+                    want += Fraction(alpha) * p
+                if beta != 0.0:
+                    want += Fraction(beta) * Fraction(float(C0[i, j]))
+                assert Fraction(got[i, j]) == want, (case, fmt, ta, tb, alpha, beta, i, j)
+
+
+def pin_ex_inexact_scales(o):
+    """Non-dyadic alpha and beta on random operands: within a few double
+    roundings of the exact rational value of the definition."""
+    rng = np.random.default_rng(112)
+    for (ta, tb) in [(False, False), (True, False), (False, True), (True, True)]:
+        M, N, K = 4, 5, 9
+        A = rng.uniform(-1, 1, size=(K, M) if ta else (M, K)).astype(np.float32)
+        B = rng.uniform(-1, 1, size=(N, K) if tb else (K, N)).astype(np.float32)
+        C0 = rng.uniform(-1, 1, size=(M, N)).astype(np.float32)
+        alpha, beta = 0.1, -0.3
+        got = o.gemm_ex("f32", M, N, K, A, A.shape[1], B, B.shape[1], ta, tb, alpha, beta, C0)
+        for i in range(M):
+            for j in range(N):
+                terms = [Fraction(float(A[k, i] if ta else A[i, k])) * Fraction(float(B[j, k] if tb else B[k, j]))
+                         for k in range(K)]
+                want = Fraction(alpha) * sum(terms) + Fraction(beta) * Fraction(float(C0[i, j]))
+                scale = Fraction(abs(alpha)) * sum(abs(t) for t in terms) + abs(Fraction(beta) * Fraction(float(C0[i, j])))
+                assert abs(Fraction(got[i, j]) - want) <= (K + 3) * Fraction(2) ** -52 * scale, (ta, tb, i, j)
+
+
 ALL_PINS = [pin_golden_small, pin_decode_table, pin_decode_library,
             pin_bruteforce_ints, pin_bruteforce_16bit, pin_fsum_bound,
             pin_closed_forms, pin_identity_permutation,
             pin_associativity_linearity, pin_numpy_matmul,
-            pin_rows_points_consistent, pin_degenerate]
+            pin_rows_points_consistent, pin_degenerate, pin_ex_bruteforce, pin_ex_inexact_scales]

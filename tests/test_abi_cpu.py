@@ -180,3 +180,19 @@ def test_stream_k_plans():
     with pytest.raises(sam.SamError) as e:
         sam.variant_plan(35, 300, 300, 4096, "f32", -2)
     assert e.value.status == -1
+
+
+def test_gemm_ex_rejections_before_any_device_call():
+    """Bad flags, short leading dimensions and a short workspace are refused on
+    the host (no GPU here: the calls must fail before touching one)."""
+    f = L.sam_gemm_ex
+    A_, B_, C_, W_ = 1 << 20, 2 << 20, 3 << 20, 4 << 20      # aligned, never dereferenced
+    vp = ctypes.c_void_p
+    assert f(0, 2, 0, 4, 4, 4, 1.0, vp(A_), 4, vp(B_), 4, 0.0, vp(C_), 4, None, 0, None) == -1   # bad trans
+    assert f(0, 0, 0, 4, 4, 4, 1.0, vp(A_), 3, vp(B_), 4, 0.0, vp(C_), 4, None, 0, None) == -1   # lda < K
+    assert f(0, 1, 0, 8, 4, 4, 1.0, vp(A_), 4, vp(B_), 4, 0.0, vp(C_), 4, None, 0, None) == -1   # lda < M for A^T
+    assert f(0, 0, 0, 4, 4, 4, 1.0, vp(A_), 4, vp(B_), 4, 0.0, vp(C_), 3, None, 0, None) == -1   # ldc < N
+    need = sam.ex_workspace_bytes(64, 64, 64, True, False, 64, 64, 64, 1.0, 0.0, "f32")
+    assert need >= 64 * 64 * 4
+    assert f(0, 1, 0, 64, 64, 64, 1.0, vp(A_), 64, vp(B_), 64, 0.0, vp(C_), 64, vp(W_), need - 1, None) == -3
+    assert sam.ex_workspace_bytes(64, 64, 64, False, False, 64, 64, 64, 1.0, 0.0, "f32") == 0

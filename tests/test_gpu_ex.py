@@ -1,0 +1,111 @@
+"""The general entry point C = alpha·op(A)·op(B) + beta·C (sam_gemm_ex) on an
+MI355X, against the oracle's gemm_ex. Small-integer operands and dyadic
+alpha/beta make every step exact, so the bits must match; random operands
+use the FP32 rel_rms bound."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import shape_adaptive_matrix_amd as sam
+from tests.compare import bitexact_mismatches, rel_rms
+from tests.gpu_util import TORCH16
+
+pytestmark = pytest.mark.gpu
+
+_ORC = None
+
+
+def orc():
+    global _ORC
+    if _ORC is None:
+        _ORC = oracle.get()
+    return _ORC
+
+
+def _enc(dtype, x):
+    x = np.asarray(x, np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _dev(dtype, bits):
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(bits)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(TORCH16[dtype])
+
+
+CASES = [((70, 130, 100), 0), ((129, 64, 72), 1), ((33, 257, 40), 2), ((256, 256, 256), 3)]
+SCALES = [(1.0, 0.0), (2.0, -1.0), (0.5, 0.25), (0.0, 2.0), (-1.0, 0.0)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True), (True, True)])
+def test_ex_dyadic(dtype, ta, tb):
+    for (M, N, K), pad in CASES:
+        rng = np.random.default_rng(M + 3 * N + 5 * K + pad + 17 * ta + 31 * tb)
+        ra, ca = (K, M) if ta else (M, K)
+        rb, cb = (N, K) if tb else (K, N)
+        lda, ldb, ldc = ca + pad, cb + 2 * pad, N + pad
+        Av = rng.integers(-3, 4, size=(ra, lda)).astype(np.float32)
+        Bv = rng.integers(-3, 4, size=(rb, ldb)).astype(np.float32)
+        for alpha, beta in SCALES:
+            C0 = rng.integers(-3, 4, size=(M, ldc)).astype(np.float32)
+            if beta == 0.0:
+                C0[:, :N] = np.nan                       # must never reach the result
+            C0[:, N:] = 12345.0                          # padding columns: untouched
+            Cd = torch.from_numpy(C0.copy()).cuda()
+            sam.gemm_ex(_dev(dtype, _enc(dtype, Av))[:, :ca], _dev(dtype, _enc(dtype, Bv))[:, :cb],
+                        Cd[:, :N], trans_a=ta, trans_b=tb, alpha=alpha, beta=beta)
+            torch.cuda.synchronize()
+            got = Cd.cpu().numpy()
+            ref = orc().gemm_ex(dtype, M, N, K, _enc(dtype, Av), lda, _enc(dtype, Bv), ldb, ta, tb, alpha, beta,
+                                np.ascontiguousarray(C0[:, :N]))
+            bad = bitexact_mismatches(got[:, :N], ref)
+            assert bad == 0, (dtype, ta, tb, (M, N, K), pad, alpha, beta, bad)
+            assert np.all(got[:, N:] == 12345.0), (dtype, ta, tb, (M, N, K), alpha, beta)
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True), (True, True)])
+def test_ex_random_f32(ta, tb):
+    M, N, K = 300, 250, 520
+    rng = np.random.default_rng(7 + ta + 2 * tb)
+    A = rng.uniform(-1, 1, size=(K, M) if ta else (M, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, size=(N, K) if tb else (K, N)).astype(np.float32)
+    C0 = rng.uniform(-1, 1, size=(M, N)).astype(np.float32)
+    Cd = torch.from_numpy(C0.copy()).cuda()
+    sam.gemm_ex(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), Cd, trans_a=ta, trans_b=tb, alpha=0.7,
+                beta=-0.3)
+    torch.cuda.synchronize()
+    ref = orc().gemm_ex("f32", M, N, K, A, A.shape[1], B, B.shape[1], ta, tb, 0.7, -0.3, C0)
+    assert rel_rms(Cd.cpu().numpy(), ref) <= 1e-5
+
+
+def test_ex_plain_case_is_the_gemm_path():
+    rng = np.random.default_rng(3)
+    A = torch.from_numpy(rng.uniform(-1, 1, size=(2048, 2048)).astype(np.float32)).cuda()
+    B = torch.from_numpy(rng.uniform(-1, 1, size=(2048, 2048)).astype(np.float32)).cuda()
+    C1 = sam.gemm(A, B)
+    C2 = sam.gemm_ex(A, B)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
+
+
+def test_ex_k_zero_and_alpha_zero():
+    M, N = 40, 70
+    C0 = np.arange(M * N, dtype=np.float32).reshape(M, N)
+    A = torch.full((M, 0), float("nan"), device="cuda")
+    B = torch.full((0, N), float("nan"), device="cuda")
+    Cd = torch.from_numpy(C0.copy()).cuda()
+    sam.gemm_ex(A, B, Cd, alpha=3.0, beta=-2.0)                      # K = 0: C = beta C
+    torch.cuda.synchronize()
+    assert np.array_equal(Cd.cpu().numpy(), -2.0 * C0)
+    A = torch.full((M, 33), float("nan"), device="cuda")              # alpha = 0: A, B never read
+    B = torch.full((33, N), float("nan"), device="cuda")
+    Cd = torch.from_numpy(C0.copy()).cuda()
+    sam.gemm_ex(A, B, Cd, alpha=0.0, beta=0.5)
+    torch.cuda.synchronize()
+    assert np.array_equal(Cd.cpu().numpy(), 0.5 * C0)

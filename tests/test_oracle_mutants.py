@@ -27,6 +27,11 @@ MUTANTS = {
     "float_point_accumulator": ("double s = 0.0;", "float s = 0.0f;"),
     "points_column_reversed": ("load_val(dtype, B, k * N + j);\n        out[p]",
                                "load_val(dtype, B, k * N + (N - 1 - j));\n        out[p]"),
+    "ex_ignores_trans_a": ("trans_a ? k * lda + i : i * lda + k", "i * lda + k"),
+    "ex_ldb_taken_as_n": ("trans_b ? j * ldb + k : k * ldb + j", "trans_b ? j * ldb + k : k * N + j"),
+    "ex_beta_sign": ("v = v + beta * (double)C0[i * N + j];", "v = v - beta * (double)C0[i * N + j];"),
+    "ex_product_when_alpha_zero": ("const int product = alpha != 0.0 && K > 0;", "const int product = K > 0;"),
+    "ex_reads_c_when_beta_zero": ("if (beta != 0.0) v = v + beta", "if (C0) v = v + beta"),
 }
 
 
