@@ -71,4 +71,6 @@
     F(34, "f128x128_w2x2s2_k32n4", 128, 128, 2, 2, 32, 4, 2, 2, 32, 1, 8, 1, 16, 0.885)            \
     F(35, "f128x128_w2x2s2_k64n2_b16", 128, 128, 2, 2, 64, 2, 4, 2, 16, 1, 8, 1, 16, 0.91)   \
     F(36, "f256x256_w4x2_k32n2_b16",   256, 256, 4, 2, 32, 2, 4, 1, 16, 0, 8, 1,  8, 0.95)   \
-    F(37, "f128x128_w4x2_k64n2_b16",   128, 128, 4, 2, 64, 2, 4, 1, 16, 1, 8, 1, 16, 0.895)
+    F(37, "f128x128_w4x2_k64n2_b16",   128, 128, 4, 2, 64, 2, 4, 1, 16, 1, 8, 1, 16, 0.895)            \
+    F(38, "f128x128_w4x2_k32n2_b16",   128, 128, 4, 2, 32, 2, 4, 1, 16, 1, 8, 1, 16, 0.88)   \
+    F(39, "f128x128_w4x2_k32n2",       128, 128, 4, 2, 32, 2, 2, 1, 32, 1, 8, 1, 16, 0.87)

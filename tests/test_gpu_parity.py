@@ -288,3 +288,23 @@ def test_run_to_run_bitwise(name):
     C2 = sam.gemm(to_dev(A2, w.dtype), to_dev(B2, w.dtype))
     torch.cuda.synchronize()
     assert not np.array_equal(C2.cpu().numpy().view(np.uint32), outs[0])
+
+
+# -- the dispatcher's own plans on arbitrary shapes ---------------------------------
+def test_auto_plans_random_shapes_dyadic():
+    """Seeded random shapes through the automatic path (whatever plan the
+    dispatcher picks: tuned or cost model, split-K, stream-K, element forms),
+    every dtype, bit-exact on small integers."""
+    rng = np.random.default_rng(2024)
+    shapes = set()
+    while len(shapes) < 24:
+        M, N, K = (int(x) for x in rng.integers(1, 700, size=3))
+        shapes.add((M, N, K))
+    for i, (M, N, K) in enumerate(sorted(shapes)):
+        dtype = ("f32", "bf16", "f16")[i % 3]
+        A, B = ints_operands(M, N, K, dtype, seed=i)
+        p = sam.plan(M, N, K, dtype)
+        print(f"[auto] {dtype} {(M, N, K)} {p['name']}", flush=True)
+        C = run(A, B, dtype)
+        bad = bitexact_mismatches(C, orc().gemm(dtype, A, B))
+        assert bad == 0, (dtype, (M, N, K), p["name"], bad)
