@@ -10,7 +10,11 @@ zero (page "Scale coverage exposes a remaining GEMM gap", section "Measurement
 contract and evidence"), with FP32 or 16-bit (bfloat16 / binary16) operands as
 in page "Measured data point on fixed-tile vs shape-adaptive GEMM", section
 "One more result that surprised us". Values are decoded exactly to double and
-summed in double in ascending k. The arithmetic lives in ``oracle.c``; this
+summed in double in ascending k. Block-scaled 8-bit operands (the OCP MX
+formats E4M3 / E5M2 with E8M0 scales per 32 values of K, the reading taken
+for the block-scaled FP4 GEMM of page "fix(fp4_gemm autotune) SM107 kernel
+family excluded from autotune candidates and heuristics update - #4856")
+follow the same rule with each value multiplied by its block's scale. The arithmetic lives in ``oracle.c``; this
 module only builds and calls it.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` (brute force,
@@ -31,6 +35,7 @@ LIB = HERE / "liboracle.so"
 
 F32, BF16, F16 = 0, 1, 2
 _DTYPES = {"f32": F32, "bf16": BF16, "f16": F16}
+FP8 = {"e4m3": 0, "e5m2": 1}
 
 CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
           "-shared", "-fPIC", "-std=c11"]
@@ -78,6 +83,16 @@ class Oracle:
         lib.oracle_gemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_double,
                                        vp, i64, vp, i64, ctypes.c_double, vp, dp, ctypes.c_int]
         lib.oracle_gemm_ex.restype = ctypes.c_int
+        lib.oracle_decode_fp8.argtypes = [ctypes.c_int, ctypes.c_uint8]
+        lib.oracle_decode_fp8.restype = ctypes.c_double
+        lib.oracle_decode_e8m0.argtypes = [ctypes.c_uint8]
+        lib.oracle_decode_e8m0.restype = ctypes.c_double
+        lib.oracle_gemm_mxfp8.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, dp,
+                                          ctypes.c_int]
+        lib.oracle_gemm_mxfp8.restype = ctypes.c_int
+        lib.oracle_gemm_mxfp8_points.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64,
+                                                 vp, vp, i64, dp, ctypes.c_int]
+        lib.oracle_gemm_mxfp8_points.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -175,6 +190,55 @@ class Oracle:
         if dtype == "f16":
             return self.lib.oracle_decode_f16(bits)
         raise ValueError(dtype)
+
+    # -- block-scaled 8-bit operands (OCP MX formats) ------------------------
+    @staticmethod
+    def _mx_operands(A, SA, Bt, SB):
+        A, SA, Bt, SB = (np.ascontiguousarray(x) for x in (A, SA, Bt, SB))
+        for x in (A, SA, Bt, SB):
+            if x.dtype != np.uint8 or x.ndim != 2:
+                raise TypeError("MX operands and scales are 2-D uint8 arrays")
+        M, K = A.shape
+        N = Bt.shape[0]
+        if Bt.shape[1] != K or SA.shape != (M, K // 32) or SB.shape != (N, K // 32):
+            raise ValueError(f"bad MX shapes A{A.shape} SA{SA.shape} Bt{Bt.shape} SB{SB.shape}")
+        return A, SA, Bt, SB, M, N, K
+
+    def gemm_mxfp8(self, fmt_a: str, fmt_b: str, A, SA, Bt, SB, nthreads: int = 0) -> np.ndarray:
+        """C = (SA-scaled A)·(SB-scaled B) as float64[M, N] (oracle_gemm_mxfp8):
+        A [M][K] and Bt [N][K] element codes, SA [M][K/32] and SB [N][K/32]
+        scale codes; formats "e4m3" or "e5m2"."""
+        A, SA, Bt, SB, M, N, K = self._mx_operands(A, SA, Bt, SB)
+        C = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_gemm_mxfp8(FP8[fmt_a], FP8[fmt_b], self._ptr(A), self._ptr(SA), self._ptr(Bt),
+                                        self._ptr(SB), M, N, K, self._ptr(C), nthreads)
+        if rc != 0:
+            raise ValueError("oracle_gemm_mxfp8 rejected its arguments")
+        return C
+
+    def gemm_mxfp8_points(self, fmt_a: str, fmt_b: str, A, SA, Bt, SB, rows, cols,
+                          nthreads: int = 0) -> np.ndarray:
+        """C[rows[p], cols[p]] of gemm_mxfp8, as float64[npts]."""
+        A, SA, Bt, SB, M, N, K = self._mx_operands(A, SA, Bt, SB)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        cols = np.ascontiguousarray(cols, dtype=np.int64)
+        if rows.shape != cols.shape or rows.ndim != 1:
+            raise ValueError("rows and cols must be equal-length vectors")
+        out = np.empty(rows.shape[0], dtype=np.float64)
+        rc = self.lib.oracle_gemm_mxfp8_points(FP8[fmt_a], FP8[fmt_b], self._ptr(A), self._ptr(SA),
+                                               self._ptr(Bt), self._ptr(SB), M, N, K, self._ptr(rows),
+                                               self._ptr(cols), rows.shape[0], self._ptr(out), nthreads)
+        if rc != 0:
+            raise ValueError("oracle_gemm_mxfp8_points rejected its arguments")
+        return out
+
+    def decode_fp8(self, fmt: str, code: int) -> float:
+        """Exact value of one 8-bit element code ("e4m3" or "e5m2")."""
+        return self.lib.oracle_decode_fp8(FP8[fmt], code)
+
+    def decode_e8m0(self, code: int) -> float:
+        """Exact value of one 8-bit scale code."""
+        return self.lib.oracle_decode_e8m0(code)
 
     def max_threads(self) -> int:
         return self.lib.oracle_max_threads()

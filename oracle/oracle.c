@@ -25,6 +25,11 @@
  *
  * The double result is handed back as is; rounding it (for a bit-exact
  * comparison) is the caller's business.
+ *
+ * A second family, at the end of the file, does the same for block-scaled
+ * 8-bit operands (OCP MX formats): each value is its element times its
+ * block's power-of-two scale, then the same exact products and ascending-k
+ * double sum.
  */
 #include <math.h>
 #include <stdint.h>
@@ -217,6 +222,116 @@ int oracle_gemm_ex(int dtype, int trans_a, int trans_b, int64_t M, int64_t N,
             if (beta != 0.0) v = v + beta * (double)C0[i * N + j];
             out[i * N + j] = v;
         }
+    }
+    return 0;
+}
+
+/* ---- Block-scaled 8-bit operands (OCP Microscaling, MXFP8) ---------------
+ *
+ * The FP4 GEMM of page "fix(fp4_gemm autotune) SM107 kernel family excluded
+ * from autotune candidates and heuristics update - #4856" runs on
+ * block-scaled operands but the page does not define a format. This oracle
+ * takes the formats of the OCP Microscaling (MX) specification v1.0 that
+ * gfx950's matrix cores implement, with 8-bit elements:
+ *
+ *   E4M3: 1 sign, 4 exponent bits (bias 7), 3 fraction bits. Exponent field
+ *         0 is zero/subnormal (0.f * 2^-6); S.1111.111 is NaN; there is no
+ *         infinity, so S.1111.110 is the largest finite value, 448.
+ *   E5M2: 1 sign, 5 exponent bits (bias 15), 2 fraction bits, IEEE rules:
+ *         field 0 is zero/subnormal (0.f * 2^-14), field 31 is Inf (f = 0)
+ *         or NaN.
+ *   E8M0 scale: 2^(code - 127); code 255 is NaN.
+ *
+ * A block is 32 consecutive values of K. Every row i of A carries one scale
+ * per block, SA[i][b], and every column j of B carries one, SB[j][b], and the
+ * operand value at k is the element times the scale of its block:
+ *   a(i,k) = 2^(SA[i][k/32]-127) * A[i][k],  b(k,j) = 2^(SB[j][k/32]-127) * B[k][j]
+ *   C[i][j] = sum over ascending k of a(i,k) * b(k,j).
+ * Storage (both operands K-contiguous, the form block scaling along K is
+ * given in): A is M rows of K codes; B is given as Bt, N rows of K codes
+ * (Bt[j][k] = B[k][j]); SA is M rows and SB N rows of K/32 scale codes.
+ * K must be a multiple of 32.
+ *
+ * How: the scaled values are exact in double (an element has at most 4
+ * significant bits and the scale is a power of two within double's range),
+ * so each product is exact; products are added in double in ascending k
+ * from +0.0, as in the plain GEMM above. */
+enum { ORACLE_E4M3 = 0, ORACLE_E5M2 = 1 };
+
+double oracle_decode_fp8(int fmt, uint8_t code)
+{
+    const int sign = code >> 7;
+    double v;
+    if (fmt == ORACLE_E4M3) {
+        const int e = (code >> 3) & 0xF, f = code & 0x7;
+        if (e == 0xF && f == 0x7)
+            v = NAN;
+        else if (e == 0)
+            v = ldexp((double)f, -6 - 3);
+        else
+            v = ldexp((double)(0x8 | f), e - 7 - 3);
+    } else {
+        const int e = (code >> 2) & 0x1F, f = code & 0x3;
+        if (e == 0x1F)
+            v = f ? NAN : INFINITY;
+        else if (e == 0)
+            v = ldexp((double)f, -14 - 2);
+        else
+            v = ldexp((double)(0x4 | f), e - 15 - 2);
+    }
+    return sign ? -v : v;
+}
+
+double oracle_decode_e8m0(uint8_t code)
+{
+    return code == 0xFF ? NAN : ldexp(1.0, (int)code - 127);
+}
+
+static double mx_val(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t row, int64_t K, int64_t k)
+{
+    return oracle_decode_fp8(fmt, codes[row * K + k]) * oracle_decode_e8m0(scales[row * (K / 32) + k / 32]);
+}
+
+/* out[i][j] (M x N doubles) for every i, j. Returns 0 or -1. */
+int oracle_gemm_mxfp8(int fmt_a, int fmt_b, const uint8_t* A, const uint8_t* SA, const uint8_t* Bt,
+                      const uint8_t* SB, int64_t M, int64_t N, int64_t K, double* out, int nthreads)
+{
+    if ((fmt_a != ORACLE_E4M3 && fmt_a != ORACLE_E5M2) || (fmt_b != ORACLE_E4M3 && fmt_b != ORACLE_E5M2))
+        return -1;
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return -1;
+    if (M == 0 || N == 0) return 0;
+    if (!out || (K > 0 && (!A || !SA || !Bt || !SB))) return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s = s + mx_val(fmt_a, A, SA, i, K, k) * mx_val(fmt_b, Bt, SB, j, K, k);
+            out[i * N + j] = s;
+        }
+    }
+    return 0;
+}
+
+/* Single elements out[p] = C[rows[p]][cols[p]] of the product above. */
+int oracle_gemm_mxfp8_points(int fmt_a, int fmt_b, const uint8_t* A, const uint8_t* SA, const uint8_t* Bt,
+                             const uint8_t* SB, int64_t M, int64_t N, int64_t K, const int64_t* rows,
+                             const int64_t* cols, int64_t npts, double* out, int nthreads)
+{
+    if ((fmt_a != ORACLE_E4M3 && fmt_a != ORACLE_E5M2) || (fmt_b != ORACLE_E4M3 && fmt_b != ORACLE_E5M2))
+        return -1;
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || npts < 0) return -1;
+    if (npts > 0 && (!rows || !cols || !out || (K > 0 && (!A || !SA || !Bt || !SB)))) return -1;
+    for (int64_t p = 0; p < npts; ++p)
+        if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npts; ++p) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s = s + mx_val(fmt_a, A, SA, rows[p], K, k) * mx_val(fmt_b, Bt, SB, cols[p], K, k);
+        out[p] = s;
     }
     return 0;
 }

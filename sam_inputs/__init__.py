@@ -1,9 +1,9 @@
 """Seeded synthetic operands for the GEMM workloads.
 
 Shared by the tests, the benchmark and the smoke check. It holds no GEMM
-arithmetic: only random draws, the rounding of a draw to a 16-bit storage
-format (part of the input's definition: normal(0,1) values stored as bfloat16
-or binary16), and the workload table.
+arithmetic: only random draws, the rounding of a draw to a 16- or 8-bit
+storage format (part of the input's definition: normal(0,1) values stored as
+bfloat16, binary16 or an 8-bit float), and the workload table.
 
 Recipes:
   * ``uniform``: FP32 uniform on [-1, 1). Drawn directly as float32 (24 random
@@ -14,6 +14,21 @@ Recipes:
   * ``normal16``: float32 standard normal, rounded to nearest-even to bfloat16
     or binary16; the 16-bit bit patterns are returned as uint16.
 A is always drawn before B from one ``numpy.random.default_rng(seed)``.
+
+Block-scaled 8-bit operands (``mxfp8`` workloads: element codes of the OCP
+MX formats E4M3 / E5M2 and E8M0 scale codes, one per 32 values of K; A is M
+rows and B is given as N rows of K codes):
+  * ``mx_normal``: float32 standard normal stored in the element format
+    (round to nearest-even by torch's float8 conversion; no draw comes near
+    the largest finite value), scale codes uniform on [123, 131] (block
+    scales a few octaves apart).
+  * ``mx_dyadic``: codes assembled from random fields: sign uniform, the
+    exponent field one of two adjacent values (values in [1, 4)), the
+    fraction field uniform, one code in 16 replaced by zero; scale codes
+    uniform on [126, 128]. Every value is a multiple of 2^-4 below 8, so for
+    K <= 1024 every partial sum is a multiple of 2^-8 below 2^16 and exact in
+    FP32, whatever the order.
+Draw order: A codes, B codes, A scales, B scales.
 """
 from __future__ import annotations
 
@@ -21,8 +36,11 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "by_name", "uniform_pm1", "small_ints",
-           "normal16", "make_operands", "sample_points", "bf16_rne_bits"]
+__all__ = ["Workload", "WORKLOADS", "MX_WORKLOADS", "by_name", "uniform_pm1", "small_ints",
+           "normal16", "make_operands", "sample_points", "bf16_rne_bits",
+           "mx_codes", "mx_scales", "make_mx_operands", "MX_BLOCK"]
+
+MX_BLOCK = 32   # values of K per scale
 
 
 def uniform_pm1(rng: np.random.Generator, shape) -> np.ndarray:
@@ -53,19 +71,47 @@ def normal16(rng: np.random.Generator, shape, kind: str) -> np.ndarray:
     raise ValueError(kind)
 
 
+def mx_codes(rng: np.random.Generator, shape, fmt: str, dist: str) -> np.ndarray:
+    """uint8 element codes of ``fmt`` ("e4m3" | "e5m2") drawn per ``dist``."""
+    if dist == "mx_normal":
+        import torch
+        x = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32))
+        t = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
+        return x.to(t).view(torch.uint8).numpy().copy()
+    if dist == "mx_dyadic":
+        sign = rng.integers(0, 2, size=shape, dtype=np.uint8)
+        if fmt == "e4m3":   # exponent field 7 or 8 (bias 7), 3 fraction bits
+            code = (sign << 7) | (rng.integers(7, 9, size=shape, dtype=np.uint8) << 3) | \
+                rng.integers(0, 8, size=shape, dtype=np.uint8)
+        else:               # exponent field 15 or 16 (bias 15), 2 fraction bits
+            code = (sign << 7) | (rng.integers(15, 17, size=shape, dtype=np.uint8) << 2) | \
+                rng.integers(0, 4, size=shape, dtype=np.uint8)
+        zero = rng.integers(0, 16, size=shape) == 0
+        return np.where(zero, np.uint8(0), code).astype(np.uint8)
+    raise ValueError(dist)
+
+
+def mx_scales(rng: np.random.Generator, rows: int, K: int, dist: str) -> np.ndarray:
+    """uint8 E8M0 scale codes, ``rows`` x K/32."""
+    lo, hi = (123, 131) if dist == "mx_normal" else (126, 128)
+    return rng.integers(lo, hi + 1, size=(rows, K // MX_BLOCK), dtype=np.uint8)
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str          # "f32" | "bf16" | "f16"
+    dtype: str          # "f32" | "bf16" | "f16" | "mxfp8"
     M: int
     N: int
     K: int
-    dist: str           # "uniform" | "ints" | "normal16"
+    dist: str           # "uniform" | "ints" | "normal16" | "mx_normal" | "mx_dyadic"
     seed: int
     lo: int = 0         # integer range for "ints"
     hi: int = 0
     check: str = "rel_rms"   # "bitexact" | "rel_rms"
     tol: float = 1e-5
+    fmt_a: str = "e4m3"      # mxfp8 element formats
+    fmt_b: str = "e4m3"
 
     @property
     def flops(self) -> int:
@@ -73,12 +119,16 @@ class Workload:
 
     @property
     def in_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        return {"f32": 4, "bf16": 2, "f16": 2, "mxfp8": 1}[self.dtype]
 
     @property
     def alg_bytes(self) -> int:
-        """Operands read once, C written once (beta = 0, C is never read)."""
-        return self.in_bytes * (self.M * self.K + self.K * self.N) + 4 * self.M * self.N
+        """Operands (and block scales) read once, C written once (beta = 0, C
+        is never read)."""
+        b = self.in_bytes * (self.M * self.K + self.K * self.N) + 4 * self.M * self.N
+        if self.dtype == "mxfp8":
+            b += (self.M + self.N) * (self.K // MX_BLOCK)
+        return b
 
 
 def _u(name, M, N, K, seed):
@@ -103,7 +153,16 @@ WORKLOADS = [
     _u("f32_8192x8192x64", 8192, 8192, 64, 15),
 ]
 
-_BY_NAME = {w.name: w for w in WORKLOADS}
+# Block-scaled 8-bit workloads (the block-scaled low-precision extension),
+# kept apart from the FP32 / 16-bit list above.
+MX_WORKLOADS = [
+    Workload("mxfp8_4096", "mxfp8", 4096, 4096, 4096, "mx_normal", 16, tol=1e-5),
+    Workload("mxfp8_8192", "mxfp8", 8192, 8192, 8192, "mx_normal", 17, tol=1e-5),
+    Workload("mxfp8_e5m2_4096", "mxfp8", 4096, 4096, 4096, "mx_normal", 18, tol=1e-5,
+             fmt_a="e5m2", fmt_b="e5m2"),
+]
+
+_BY_NAME = {w.name: w for w in WORKLOADS + MX_WORKLOADS}
 
 
 def by_name(name: str) -> Workload:
@@ -121,6 +180,15 @@ def make_operands(w: Workload, seed: int | None = None):
     if w.dist == "normal16":
         return normal16(rng, sa, w.dtype), normal16(rng, sb, w.dtype)
     raise ValueError(w.dist)
+
+
+def make_mx_operands(w: Workload, seed: int | None = None):
+    """(A, SA, Bt, SB) uint8 arrays for an ``mxfp8`` workload: A [M][K] and
+    Bt [N][K] element codes, SA [M][K/32] and SB [N][K/32] scale codes."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    A = mx_codes(rng, (w.M, w.K), w.fmt_a, w.dist)
+    Bt = mx_codes(rng, (w.N, w.K), w.fmt_b, w.dist)
+    return A, mx_scales(rng, w.M, w.K, w.dist), Bt, mx_scales(rng, w.N, w.K, w.dist)
 
 
 def sample_points(M: int, N: int, count: int, seed: int):

@@ -330,8 +330,156 @@ def pin_ex_inexact_scales(o):
                 assert abs(Fraction(got[i, j]) - want) <= (K + 3) * Fraction(2) ** -52 * scale, (ta, tb, i, j)
 
 
+# -- block-scaled 8-bit operands (OCP MX formats) ---------------------------
+def fp8_decode_table():
+    rows = []
+    for line in (GOLDEN / "decode_fp8.txt").read_text().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        fmt, code, val = line.split()[:3]
+        rows.append((fmt, int(code, 16), math.nan if val == "nan" else _parse_value(val)))
+    return rows
+
+
+def _same(got: float, want: float) -> bool:
+    if math.isnan(want):
+        return math.isnan(got)
+    return got == want and math.copysign(1, got) == math.copysign(1, want)
+
+
+def _mx_decode(o, fmt, code):
+    return o.decode_e8m0(code) if fmt == "e8m0" else o.decode_fp8(fmt, code)
+
+
+def _torch_values(fmt: str, codes: np.ndarray) -> np.ndarray:
+    """Values of uint8 codes by torch's own float8 / e8m0 types, as float64."""
+    import torch
+    t = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2, "e8m0": torch.float8_e8m0fnu}[fmt]
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(t).to(torch.float64).numpy()
+
+
+def pin_mx_decode_table(o):
+    """8-bit element and scale decoding matches the hand-worked table."""
+    for fmt, code, val in fp8_decode_table():
+        got = _mx_decode(o, fmt, code)
+        assert _same(got, val), (fmt, hex(code), got, val)
+
+
+def pin_mx_decode_library(o):
+    """All 256 codes of each 8-bit format decode to what torch's float8_e4m3fn,
+    float8_e5m2 and float8_e8m0fnu types give."""
+    codes = np.arange(256, dtype=np.uint8)
+    for fmt in ("e4m3", "e5m2", "e8m0"):
+        ref = _torch_values(fmt, codes)
+        for c in range(256):
+            got = _mx_decode(o, fmt, c)
+            assert _same(got, float(ref[c])), (fmt, hex(c), got, ref[c])
+
+
+def _mx_random(rng, M, N, K, fa, fb, slo, shi):
+    """Random finite codes of every magnitude and random scale codes."""
+    def finite(fmt, shape):
+        c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        bad = np.isnan(_torch_values(fmt, c)) | np.isinf(_torch_values(fmt, c))
+        return np.where(bad, np.uint8(0x38 if fmt == "e4m3" else 0x3C), c).astype(np.uint8)
+    A, Bt = finite(fa, (M, K)), finite(fb, (N, K))
+    SA = rng.integers(slo, shi + 1, size=(M, K // 32), dtype=np.uint8)
+    SB = rng.integers(slo, shi + 1, size=(N, K // 32), dtype=np.uint8)
+    return A, SA, Bt, SB
+
+
+def _mx_exact_terms(fa, fb, A, SA, Bt, SB, i, j):
+    """The K products of element (i, j) as exact rationals, from torch-decoded
+    codes and scales."""
+    K = A.shape[1]
+    a = _torch_values(fa, A[i]); b = _torch_values(fb, Bt[j])
+    sa = _torch_values("e8m0", SA[i]); sb = _torch_values("e8m0", SB[j])
+    return [Fraction(float(a[k])) * Fraction(float(sa[k // 32])) * Fraction(float(b[k])) *
+            Fraction(float(sb[k // 32])) for k in range(K)]
+
+
+def pin_mx_bruteforce(o):
+    """Random codes and scales of every magnitude: each element is within the
+    recursive-summation bound (K-1)*u*sum|terms| of the exact rational sum of
+    the definition (terms from torch-decoded values), and equal to it when
+    the terms are all multiples of one power of two that keeps the sums exact."""
+    rng = np.random.default_rng(120)
+    u = Fraction(1, 2 ** 53)
+    for (M, N, K, fa, fb) in [(3, 4, 32, "e4m3", "e4m3"), (2, 5, 64, "e5m2", "e4m3"),
+                              (4, 3, 96, "e4m3", "e5m2"), (1, 2, 128, "e5m2", "e5m2")]:
+        A, SA, Bt, SB = _mx_random(rng, M, N, K, fa, fb, 100, 154)
+        got = o.gemm_mxfp8(fa, fb, A, SA, Bt, SB)
+        for i in range(M):
+            for j in range(N):
+                terms = _mx_exact_terms(fa, fb, A, SA, Bt, SB, i, j)
+                want = sum(terms, Fraction(0))
+                bound = (K - 1) * u * sum((abs(t) for t in terms), Fraction(0))
+                assert abs(Fraction(got[i, j]) - want) <= bound, (fa, fb, M, N, K, i, j)
+    import sam_inputs as si
+    for fa, fb in [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")]:
+        w = si.Workload("pin", "mxfp8", 3, 5, 160, "mx_dyadic", 121, fmt_a=fa, fmt_b=fb)
+        A, SA, Bt, SB = si.make_mx_operands(w)
+        got = o.gemm_mxfp8(fa, fb, A, SA, Bt, SB)
+        for i in range(3):
+            for j in range(5):
+                want = sum(_mx_exact_terms(fa, fb, A, SA, Bt, SB, i, j), Fraction(0))
+                assert Fraction(got[i, j]) == want, (fa, fb, i, j)
+
+
+def pin_mx_unit_scales(o):
+    """With every scale code 127 (scale 1) the block-scaled product is the
+    plain product of the decoded values: bit for bit the FP32 oracle run on
+    torch-decoded A and on B = Bt transposed (same values, same ascending-k
+    double sums)."""
+    rng = np.random.default_rng(122)
+    for (M, N, K, fa, fb) in [(5, 7, 64, "e4m3", "e4m3"), (6, 3, 96, "e5m2", "e4m3"), (4, 4, 32, "e5m2", "e5m2")]:
+        A, SA, Bt, SB = _mx_random(rng, M, N, K, fa, fb, 127, 127)
+        got = o.gemm_mxfp8(fa, fb, A, SA, Bt, SB)
+        Ad = _torch_values(fa, A).astype(np.float32)
+        Bd = np.ascontiguousarray(_torch_values(fb, Bt).astype(np.float32).T)
+        ref = o.gemm("f32", Ad, Bd)
+        assert np.array_equal(_bits(got), _bits(ref)), (M, N, K, fa, fb)
+
+
+def pin_mx_scale_closed_form(o):
+    """All elements 1 (e4m3 0x38) with SA[i][b] = 127 + b and SB[j][b] = 127 + j
+    gives C[i][j] = 32 * 2^j * (2^(K/32) - 1): each block scale reaches its
+    own block of its own row / column only."""
+    M, N, K = 3, 5, 128
+    A = np.full((M, K), 0x38, np.uint8); Bt = np.full((N, K), 0x38, np.uint8)
+    SA = np.tile(np.arange(127, 127 + K // 32, dtype=np.uint8), (M, 1))
+    SB = np.repeat(np.arange(127, 127 + N, dtype=np.uint8)[:, None], K // 32, axis=1)
+    got = o.gemm_mxfp8("e4m3", "e4m3", A, SA, Bt, SB)
+    for i in range(M):
+        for j in range(N):
+            assert got[i, j] == 32.0 * 2.0 ** j * (2.0 ** (K // 32) - 1), (i, j, got[i, j])
+
+
+def pin_mx_points_and_degenerate(o):
+    """Single points are the full product's sums bit for bit; K = 0 gives +0;
+    K not a multiple of 32 is rejected."""
+    rng = np.random.default_rng(123)
+    A, SA, Bt, SB = _mx_random(rng, 6, 9, 64, "e4m3", "e5m2", 110, 140)
+    full = o.gemm_mxfp8("e4m3", "e5m2", A, SA, Bt, SB)
+    rows = np.array([0, 5, 3, 5, 0]); cols = np.array([0, 8, 4, 0, 8])
+    pts = o.gemm_mxfp8_points("e4m3", "e5m2", A, SA, Bt, SB, rows, cols)
+    assert np.array_equal(_bits(pts), _bits(full[rows, cols]))
+    z = o.gemm_mxfp8("e4m3", "e4m3", np.zeros((2, 0), np.uint8), np.zeros((2, 0), np.uint8),
+                     np.zeros((3, 0), np.uint8), np.zeros((3, 0), np.uint8))
+    assert z.shape == (2, 3) and (z == 0).all() and not np.signbit(z).any()
+    try:
+        o.gemm_mxfp8("e4m3", "e4m3", np.zeros((2, 48), np.uint8), np.zeros((2, 1), np.uint8),
+                     np.zeros((3, 48), np.uint8), np.zeros((3, 1), np.uint8))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("K = 48 accepted")
+
+
 ALL_PINS = [pin_golden_small, pin_decode_table, pin_decode_library,
             pin_bruteforce_ints, pin_bruteforce_16bit, pin_fsum_bound,
             pin_closed_forms, pin_identity_permutation,
             pin_associativity_linearity, pin_numpy_matmul,
-            pin_rows_points_consistent, pin_degenerate, pin_ex_bruteforce, pin_ex_inexact_scales]
+            pin_rows_points_consistent, pin_degenerate, pin_ex_bruteforce, pin_ex_inexact_scales,
+            pin_mx_decode_table, pin_mx_decode_library, pin_mx_bruteforce,
+            pin_mx_unit_scales, pin_mx_scale_closed_form, pin_mx_points_and_degenerate]

@@ -35,7 +35,30 @@ def test_workloads_match_the_stated_configs():
     for s in [(768, 768, 768), (4097, 3071, 8191), (8191, 8193, 4096), (16, 8192, 8192),
               (8192, 16, 8192), (8192, 8192, 64)]:
         assert s in shapes
-    assert len({w.seed for w in si.WORKLOADS}) == len(si.WORKLOADS)
+    every = si.WORKLOADS + si.MX_WORKLOADS
+    assert len({w.seed for w in every}) == len(every)
+
+
+def test_mx_recipes():
+    """Codes are finite in their format; dyadic codes stay in [1, 4) or are
+    zero; scale codes stay in their stated ranges; draws are reproducible."""
+    import torch
+    for fmt, t in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        for dist in ("mx_normal", "mx_dyadic"):
+            w = si.Workload("t", "mxfp8", 37, 29, 96, dist, 5, fmt_a=fmt, fmt_b=fmt)
+            A, SA, Bt, SB = si.make_mx_operands(w)
+            assert A.shape == (37, 96) and Bt.shape == (29, 96) and SA.shape == (37, 3) and SB.shape == (29, 3)
+            for x in (A, Bt):
+                v = torch.from_numpy(x).view(t).double().numpy()
+                assert np.isfinite(v).all()
+                if dist == "mx_dyadic":
+                    a = np.abs(v)
+                    assert ((a == 0) | ((a >= 1) & (a < 4))).all()
+            lo, hi = (123, 131) if dist == "mx_normal" else (126, 128)
+            for s in (SA, SB):
+                assert s.min() >= lo and s.max() <= hi
+            again = si.make_mx_operands(w)
+            assert all(np.array_equal(x, y) for x, y in zip((A, SA, Bt, SB), again))
 
 
 def test_sample_points_distinct_and_cover_tails():

@@ -24,7 +24,8 @@ MUTANTS = {
     "f16_hidden_bit": ("v = ldexp((double)(0x400 | f), e - 15 - 10);",
                        "v = ldexp((double)f, e - 15 - 10);"),
     "negative_zero_start": ("acc[j] = 0.0;", "acc[j] = -0.0;"),
-    "float_point_accumulator": ("double s = 0.0;", "float s = 0.0f;"),
+    "float_point_accumulator": ("double s = 0.0;\n        for (int64_t k = 0; k < K; ++k)\n            s = s + load_val",
+                                "float s = 0.0f;\n        for (int64_t k = 0; k < K; ++k)\n            s = s + load_val"),
     "points_column_reversed": ("load_val(dtype, B, k * N + j);\n        out[p]",
                                "load_val(dtype, B, k * N + (N - 1 - j));\n        out[p]"),
     "ex_ignores_trans_a": ("trans_a ? k * lda + i : i * lda + k", "i * lda + k"),
@@ -32,6 +33,23 @@ MUTANTS = {
     "ex_beta_sign": ("v = v + beta * (double)C0[i * N + j];", "v = v - beta * (double)C0[i * N + j];"),
     "ex_product_when_alpha_zero": ("const int product = alpha != 0.0 && K > 0;", "const int product = K > 0;"),
     "ex_reads_c_when_beta_zero": ("if (beta != 0.0) v = v + beta", "if (C0) v = v + beta"),
+    "mx_e4m3_bias": ("v = ldexp((double)(0x8 | f), e - 7 - 3);", "v = ldexp((double)(0x8 | f), e - 8 - 3);"),
+    "mx_e4m3_subnormal_scale": ("v = ldexp((double)f, -6 - 3);", "v = ldexp((double)f, -7 - 3);"),
+    "mx_e4m3_nan_taken_as_value": ("if (e == 0xF && f == 0x7)", "if (e == 0xF && f == 0x7 && sign)"),
+    "mx_e5m2_hidden_bit": ("v = ldexp((double)(0x4 | f), e - 15 - 2);", "v = ldexp((double)f, e - 15 - 2);"),
+    "mx_e5m2_no_inf": ("v = f ? NAN : INFINITY;\n        else if (e == 0)\n            v = ldexp((double)f, -14 - 2);",
+                       "v = NAN;\n        else if (e == 0)\n            v = ldexp((double)f, -14 - 2);"),
+    "mx_e8m0_bias": ("ldexp(1.0, (int)code - 127)", "ldexp(1.0, (int)code - 126)"),
+    "mx_scale_block_shifted": ("scales[row * (K / 32) + k / 32]", "scales[row * (K / 32) + (k / 32 + 1) % (K / 32)]"),
+    "mx_scale_row_ignored": ("scales[row * (K / 32) + k / 32]", "scales[k / 32]"),
+    "mx_block_of_16": ("scales[row * (K / 32) + k / 32]", "scales[row * (K / 32) + (k / 16) % (K / 32)]"),
+    "mx_format_b_ignored": ("s = s + mx_val(fmt_a, A, SA, i, K, k) * mx_val(fmt_b, Bt, SB, j, K, k);",
+                            "s = s + mx_val(fmt_a, A, SA, i, K, k) * mx_val(fmt_a, Bt, SB, j, K, k);"),
+    "mx_b_taken_row_major": ("s = s + mx_val(fmt_a, A, SA, i, K, k) * mx_val(fmt_b, Bt, SB, j, K, k);",
+                             "s = s + mx_val(fmt_a, A, SA, i, K, k) * oracle_decode_fp8(fmt_b, Bt[k * N + j]) * "
+                             "oracle_decode_e8m0(SB[j * (K / 32) + k / 32]);"),
+    "mx_last_block_dropped": ("for (int64_t k = 0; k < K; ++k)\n                s = s + mx_val(fmt_a, A, SA, i, K, k)",
+                              "for (int64_t k = 0; k < K - 32; ++k)\n                s = s + mx_val(fmt_a, A, SA, i, K, k)"),
 }
 
 
