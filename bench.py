@@ -32,7 +32,7 @@ from pathlib import Path
 ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}   # MI355X dense MFMA, 2.4 GHz
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "mxfp8": 5000.0}   # MI355X dense MFMA, 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
 
@@ -42,7 +42,7 @@ KERNEL_SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_kernels_stream.
 # Kernel function of a plan, by the first letter of its variant name.
 KERNEL_OF = {"t": "sam::gemm_kernel", "r": "sam::gemm16_dma_kernel", "q": "sam::gemm16_dma_kernel",
              "h": "sam::gemm16_dma_kernel", "s": "sam::stream_m_kernel / sam::stream_n_kernel",
-             "f": "sam::gemm_f32_ring_kernel"}
+             "f": "sam::gemm_f32_ring_kernel", "x": "sam::gemm_mx8_kernel"}
 
 
 def kernel_name(plan) -> str:
@@ -61,7 +61,38 @@ def src_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def prepare_mx(w, torch, sam, si, variant=None, split=0):
+    """Block-scaled 8-bit workload: sam_gemm_mxfp8 (or the forced variant)."""
+    ops = [torch.from_numpy(x).cuda() for x in si.make_mx_operands(w)]
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    if variant is None:
+        plan = sam.plan(w.M, w.N, w.K, "mxfp8")
+    else:
+        plan = sam.variant_plan(variant, w.M, w.N, w.K, "mxfp8", split)
+    ws = sam.workspace_for(plan, C.device)
+    L = sam.lib()
+    stream = torch.cuda.current_stream()
+    fa, fb = sam.FP8_FORMATS[w.fmt_a], sam.FP8_FORMATS[w.fmt_b]
+    args = (fa, fb, *(ctypes.c_void_p(t.data_ptr()) for t in ops), ctypes.c_void_p(C.data_ptr()),
+            w.M, w.N, w.K, ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
+            ws.numel() * 4 if ws is not None else 0, ctypes.c_void_p(stream.cuda_stream))
+    if variant is None:
+        fn = L.sam_gemm_mxfp8
+    else:
+        def fn(*a):
+            return L.sam_gemm_mxfp8_variant(variant, plan["split_k"], *a)
+
+    def step():
+        rc = fn(*args)
+        if rc != 0:
+            raise RuntimeError(f"{sam.STATUS.get(rc, rc)}: {sam.last_error()}")
+
+    return {"step": step, "plan": plan, "keep": (ops, C, ws), "stream": stream}
+
+
 def prepare(w, torch, sam, si, variant=None, split=0):
+    if w.dtype == "mxfp8":
+        return prepare_mx(w, torch, sam, si, variant, split)
     A, B = si.make_operands(w)
     if w.dtype == "f32":
         dA = torch.from_numpy(A).cuda()
@@ -154,7 +185,7 @@ def sweep(torch, sam, si, rounds: int = 5):
     lasting >= 20 ms; cold-cache single launches for the skinny shapes."""
     out = []
     flush = None
-    for w in si.WORKLOADS:
+    for w in si.WORKLOADS + si.MX_WORKLOADS:
         g = prepare(w, torch, sam, si)
         step = g["step"]
         for _ in range(3):
@@ -201,17 +232,26 @@ def cpu_baseline(w, si, seconds: float):
     repeated until that long when the whole product is quicker."""
     import oracle
     o = oracle.get()
-    A, B = si.make_operands(w)
     threads = o.max_threads()
+    if w.dtype == "mxfp8":
+        A, SA, Bt, SB = si.make_mx_operands(w)
+
+        def slab(n):
+            o.gemm_mxfp8(w.fmt_a, w.fmt_b, A[:n], SA[:n], Bt, SB)
+    else:
+        A, B = si.make_operands(w)
+
+        def slab(n):
+            o.gemm_rows(w.dtype, A, B, 0, n)
     rows = max(1, min(w.M, 16))
     t0 = time.perf_counter()
-    o.gemm_rows(w.dtype, A, B, 0, rows)
+    slab(rows)
     t = time.perf_counter() - t0
     target = max(1, min(w.M, int(rows * seconds / max(t, 1e-6))))
     reps, elapsed = 0, 0.0
     while elapsed < 0.8 * seconds or reps == 0:
         t0 = time.perf_counter()
-        o.gemm_rows(w.dtype, A, B, 0, target)
+        slab(target)
         elapsed += time.perf_counter() - t0
         reps += 1
     flops = 2.0 * target * w.N * w.K * reps
@@ -281,7 +321,8 @@ def main():
         parts = args.shape.split(",")
         M, N, K = (int(x) for x in parts[:3])
         dt = parts[3] if len(parts) > 3 else "f32"
-        w = si.Workload(f"{dt}_{M}x{N}x{K}", dt, M, N, K, "uniform" if dt == "f32" else "normal16", 99)
+        dist = {"f32": "uniform", "mxfp8": "mx_normal"}.get(dt, "normal16")
+        w = si.Workload(f"{dt}_{M}x{N}x{K}", dt, M, N, K, dist, 99)
     else:
         w = si.by_name(args.workload)
     if args.ex:

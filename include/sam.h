@@ -53,7 +53,9 @@
 extern "C" {
 #endif
 
-typedef enum { SAM_F32 = 0, SAM_BF16 = 1, SAM_F16 = 2 } sam_dtype;
+/* SAM_MXFP8 names block-scaled 8-bit operands (sam_gemm_mxfp8) in plan
+ * queries; the other entry points take the first three. */
+typedef enum { SAM_F32 = 0, SAM_BF16 = 1, SAM_F16 = 2, SAM_MXFP8 = 3 } sam_dtype;
 
 typedef enum {
     SAM_OK = 0,
@@ -111,6 +113,48 @@ sam_status sam_gemm_f16(const uint16_t* A, const uint16_t* B, float* C,
                         int64_t M, int64_t N, int64_t K, void* workspace,
                         uint64_t workspace_bytes, void* stream);
 
+/* Element formats of block-scaled 8-bit operands (OCP Microscaling
+ * specification v1.0): E4M3 (bias 7, 3 fraction bits, no infinity, largest
+ * finite 448) and E5M2 (bias 15, 2 fraction bits, IEEE-style Inf/NaN). */
+typedef enum { SAM_E4M3 = 0, SAM_E5M2 = 1 } sam_fp8_format;
+
+/* Block-scaled 8-bit GEMM (the block-scaled low-precision operands whose
+ * tile variants page "fix(fp4_gemm autotune) SM107 kernel family excluded
+ * from autotune candidates and heuristics update - #4856" tunes; the page
+ * fixes no format, this takes the OCP MX formats gfx950's matrix cores
+ * implement):
+ *   C[i][j] = sum over k of (2^(scale_a[i][k/32] - 127) * A[i][k])
+ *                         * (2^(scale_b[j][k/32] - 127) * Bt[j][k])
+ * with products accumulated in FP32 and C written in FP32.
+ *   A       device, M rows of K element codes (format fmt_a), row stride K.
+ *   Bt      device, N rows of K element codes (format fmt_b): B given
+ *           K-contiguous, Bt[j][k] = B[k][j], row stride K.
+ *   scale_a device, M rows of K/32 E8M0 codes (2^(code-127)), row stride K/32.
+ *   scale_b device, N rows of K/32 E8M0 codes, row stride K/32.
+ *   C       device, M rows of N floats, row stride N; write-only.
+ * K must be a multiple of 32 (SAM_ERR_INVALID_ARG otherwise). A, Bt, C and
+ * the workspace must be 16-byte aligned; the scale arrays may have any
+ * alignment. Codes that encode NaN or Inf, and the scale code 255, are not
+ * valid inputs: the elements of C they reach are then unspecified (no
+ * fault). Workspace as for sam_gemm_f32 (sam_gemm_plan with SAM_MXFP8 gives
+ * the plan and its workspace_bytes). Asynchronous on `stream`. */
+sam_status sam_gemm_mxfp8(sam_fp8_format fmt_a, sam_fp8_format fmt_b,
+                          const uint8_t* A, const uint8_t* scale_a,
+                          const uint8_t* Bt, const uint8_t* scale_b, float* C,
+                          int64_t M, int64_t N, int64_t K, void* workspace,
+                          uint64_t workspace_bytes, void* stream);
+
+/* The same with a forced block-scaled variant `id` and split (0 = the
+ * variant's own choice; stream-K is not offered). SAM_ERR_UNSUPPORTED when
+ * the variant is not a block-scaled one or the split is not admissible. */
+sam_status sam_gemm_mxfp8_variant(int32_t id, int32_t split_k,
+                                  sam_fp8_format fmt_a, sam_fp8_format fmt_b,
+                                  const uint8_t* A, const uint8_t* scale_a,
+                                  const uint8_t* Bt, const uint8_t* scale_b,
+                                  float* C, int64_t M, int64_t N, int64_t K,
+                                  void* workspace, uint64_t workspace_bytes,
+                                  void* stream);
+
 /* Operand forms of the general entry point. */
 typedef enum { SAM_OP_N = 0, SAM_OP_T = 1 } sam_op;
 
@@ -165,7 +209,9 @@ sam_status sam_variant_plan(int32_t id, int64_t M, int64_t N, int64_t K,
                             sam_dtype dtype, int32_t split_k, sam_plan* out);
 
 /* Run a forced variant (tests, profiling and calibration). Operands as for
- * sam_gemm_<dtype> (16-bit ones as uint16_t patterns). */
+ * sam_gemm_<dtype> (16-bit ones as uint16_t patterns). SAM_MXFP8 is refused
+ * with SAM_ERR_INVALID_ARG: block-scaled operands go through
+ * sam_gemm_mxfp8_variant. */
 sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k,
                             const void* A, const void* B, float* C, int64_t M,
                             int64_t N, int64_t K, void* workspace,

@@ -112,11 +112,20 @@ void to_public(const sam::Plan& p, sam_plan* out)
     out->est_us = p.est_us;
 }
 
+// Block-scaled operands: scale codes and element formats (B is then given
+// as N rows of K codes).
+struct MxExtra {
+    const uint8_t* sa;
+    const uint8_t* sb;
+    int fmt_a, fmt_b;
+};
+
 // Shared body of every GEMM entry point once a plan is known.
 sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long long M, long long N,
-               long long K, void* ws, unsigned long long ws_bytes, void* stream)
+               long long K, void* ws, unsigned long long ws_bytes, void* stream, const MxExtra* mx = nullptr)
 {
-    const unsigned long long es = p.dtype == sam::DT_F32 ? 4 : 2;
+    const unsigned long long es = p.dtype == sam::DT_F32 ? 4 : (p.dtype == sam::DT_MX8 ? 1 : 2);
+    if ((p.dtype == sam::DT_MX8) != (mx != nullptr)) return fail(SAM_ERR_INTERNAL, "scale arguments mismatch");
     if (M == 0 || N == 0) return SAM_OK;
     // Kernels address a workgroup's operand panels with 32-bit byte offsets:
     // up to 257 rows of A (K elements each), 129 rows of B and 257 rows of C.
@@ -126,12 +135,16 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         return fail(SAM_ERR_INVALID_ARG, "K=%lld or N=%lld beyond the supported offset range", K, N);
     if (!C) return fail(SAM_ERR_INVALID_ARG, "C is null");
     if (K > 0 && (!A || !B)) return fail(SAM_ERR_INVALID_ARG, "A or B is null");
+    if (mx && K > 0 && (!mx->sa || !mx->sb)) return fail(SAM_ERR_INVALID_ARG, "a scale array is null");
     if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))) || (ws && !aligned16(ws)))
         return fail(SAM_ERR_MISALIGNED, "A, B, C and workspace must be 16-byte aligned");
     const unsigned long long cbytes = (unsigned long long)(M * N) * 4ull;
     if (ranges_overlap(C, cbytes, A, (unsigned long long)(M * K) * es) ||
         ranges_overlap(C, cbytes, B, (unsigned long long)(K * N) * es))
         return fail(SAM_ERR_INVALID_ARG, "C overlaps A or B");
+    if (mx && (ranges_overlap(C, cbytes, mx->sa, (unsigned long long)(M * (K / 32))) ||
+               ranges_overlap(C, cbytes, mx->sb, (unsigned long long)(N * (K / 32)))))
+        return fail(SAM_ERR_INVALID_ARG, "C overlaps a scale array");
     if (p.ws_bytes > 0) {
         if (!ws || ws_bytes < p.ws_bytes)
             return fail(SAM_ERR_WORKSPACE, "plan %d needs %llu workspace bytes, got %llu", p.variant_id,
@@ -162,6 +175,12 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         a.group_m = p.group_m;
         a.xcd_remap = p.xcd_remap;
         a.part_stride = M * N;
+        if (mx) {
+            a.sa = mx->sa;
+            a.sb = mx->sb;
+            a.fmt_a = mx->fmt_a;
+            a.fmt_b = mx->fmt_b;
+        }
         if (p.sk) {
             a.ws = static_cast<float*>(ws);
             a.sk_iters = (int)((K + p.bk - 1) / p.bk);
@@ -314,9 +333,11 @@ sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t 
 sam_status sam_gemm_plan(int64_t M, int64_t N, int64_t K, sam_dtype dtype, sam_plan* out)
 {
     if (!out) return fail(SAM_ERR_INVALID_ARG, "out is null");
-    if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+    if (dtype < SAM_F32 || dtype > SAM_MXFP8) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
     sam_status st = check_shape(M, N, K);
     if (st != SAM_OK) return st;
+    if (dtype == SAM_MXFP8 && K % 32 != 0)
+        return fail(SAM_ERR_INVALID_ARG, "block-scaled operands need K %% 32 == 0 (K=%lld)", (long long)K);
     sam::Plan p{};
     if (!sam::plan_auto(M, N, K, dtype, &p)) return fail(SAM_ERR_INTERNAL, "no admissible plan");
     to_public(p, out);
@@ -369,7 +390,7 @@ sam_status sam_variant_plan(int32_t id, int64_t M, int64_t N, int64_t K, sam_dty
                             int32_t split_k, sam_plan* out)
 {
     if (!out) return fail(SAM_ERR_INVALID_ARG, "out is null");
-    if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+    if (dtype < SAM_F32 || dtype > SAM_MXFP8) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
     if (split_k < -1) return fail(SAM_ERR_INVALID_ARG, "split %d (-1 is stream-K, 0 the variant's choice)", split_k);
     sam_status st = check_shape(M, N, K);
     if (st != SAM_OK) return st;
@@ -386,6 +407,8 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k, const 
                             float* C, int64_t M, int64_t N, int64_t K, void* workspace,
                             uint64_t workspace_bytes, void* stream)
 {
+    if (dtype == SAM_MXFP8)
+        return fail(SAM_ERR_INVALID_ARG, "block-scaled operands go through sam_gemm_mxfp8_variant");
     if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
     if (split_k < -1) return fail(SAM_ERR_INVALID_ARG, "split %d (-1 is stream-K, 0 the variant's choice)", split_k);
     sam_status st = check_shape(M, N, K);
@@ -396,6 +419,49 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k, const 
         return fail(SAM_ERR_UNSUPPORTED, "variant %d cannot run dtype %d with split %d for K=%lld", id,
                     (int)dtype, split_k, (long long)K);
     return run(p, A, B, C, M, N, K, workspace, workspace_bytes, stream);
+}
+
+static sam_status gemm_mxfp8_impl(int32_t id, int32_t split_k, sam_fp8_format fmt_a, sam_fp8_format fmt_b,
+                                  const uint8_t* A, const uint8_t* scale_a, const uint8_t* Bt,
+                                  const uint8_t* scale_b, float* C, int64_t M, int64_t N, int64_t K,
+                                  void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    if ((fmt_a != SAM_E4M3 && fmt_a != SAM_E5M2) || (fmt_b != SAM_E4M3 && fmt_b != SAM_E5M2))
+        return fail(SAM_ERR_INVALID_ARG, "element formats must be SAM_E4M3 or SAM_E5M2 (got %d, %d)", (int)fmt_a,
+                    (int)fmt_b);
+    if (split_k < 0) return fail(SAM_ERR_INVALID_ARG, "split %d (0 is the variant's choice)", split_k);
+    sam_status st = check_shape(M, N, K);
+    if (st != SAM_OK) return st;
+    if (K % 32 != 0)
+        return fail(SAM_ERR_INVALID_ARG, "block-scaled operands need K %% 32 == 0 (K=%lld)", (long long)K);
+    sam::Plan p{};
+    if (id < 0) {
+        if (!sam::plan_auto(M, N, K, sam::DT_MX8, &p)) return fail(SAM_ERR_INTERNAL, "no admissible plan");
+    } else {
+        if (!sam::variant_get(id)) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);
+        if (!sam::plan_for_variant(id, M, N, K, sam::DT_MX8, split_k, &p))
+            return fail(SAM_ERR_UNSUPPORTED, "variant %d cannot run block-scaled operands with split %d", id, split_k);
+    }
+    const MxExtra mx{scale_a, scale_b, (int)fmt_a, (int)fmt_b};
+    return run(p, A, Bt, C, M, N, K, workspace, workspace_bytes, stream, &mx);
+}
+
+sam_status sam_gemm_mxfp8(sam_fp8_format fmt_a, sam_fp8_format fmt_b, const uint8_t* A, const uint8_t* scale_a,
+                          const uint8_t* Bt, const uint8_t* scale_b, float* C, int64_t M, int64_t N, int64_t K,
+                          void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    return gemm_mxfp8_impl(-1, 0, fmt_a, fmt_b, A, scale_a, Bt, scale_b, C, M, N, K, workspace, workspace_bytes,
+                           stream);
+}
+
+sam_status sam_gemm_mxfp8_variant(int32_t id, int32_t split_k, sam_fp8_format fmt_a, sam_fp8_format fmt_b,
+                                  const uint8_t* A, const uint8_t* scale_a, const uint8_t* Bt,
+                                  const uint8_t* scale_b, float* C, int64_t M, int64_t N, int64_t K,
+                                  void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    if (id < 0) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);
+    return gemm_mxfp8_impl(id, split_k, fmt_a, fmt_b, A, scale_a, Bt, scale_b, C, M, N, K, workspace,
+                           workspace_bytes, stream);
 }
 
 sam_status sam_device_check(void) { return device_check_impl(); }

@@ -6,7 +6,8 @@
 
 namespace sam {
 
-enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+// DT_MX8: block-scaled 8-bit elements (E4M3 / E5M2 with E8M0 scales per 32 of K).
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_MX8 = 3 };
 
 // Fixed facts of one MI355X (gfx950) used by the cost model. They are frozen
 // here rather than queried so that a plan is a pure function of the shape.
@@ -17,6 +18,7 @@ struct DeviceModel {
     double clock_ghz = 2.4;
     double f32_flop_per_clk_cu = 256.0;    // 4 SIMDs x 64 (32x32x2 f32 in 64 clk)
     double h16_flop_per_clk_cu = 4096.0;   // 4 SIMDs x 1024
+    double mx8_flop_per_clk_cu = 8192.0;   // 4 SIMDs x 2048 (32x32x64 8-bit in 64 clk)
     double hbm_gbs = 5900.0;       // measured streaming read rate
     double tiled_hbm_frac = 0.75;  // share of it the LDS-tiled kernels reach when HBM-bound (calibrated)
     double hbm_write_gbs = 6000.0; // rate the epilogue write phase drains at (calibrated)
@@ -25,7 +27,7 @@ struct DeviceModel {
 };
 
 // Static description of a tile/schedule variant.
-enum Kind : int { KIND_STAGED = 0, KIND_DMA = 1, KIND_STREAM = 2, KIND_F32RING = 3 };
+enum Kind : int { KIND_STAGED = 0, KIND_DMA = 1, KIND_STREAM = 2, KIND_F32RING = 3, KIND_MX8 = 4 };
 
 struct Variant {
     int id;
@@ -45,6 +47,7 @@ struct Variant {
     double eff_f32;      // calibrated fraction of MFMA peak it sustains in steady state
                          // (streaming variants: fraction of the HBM read rate)
     double eff_h16;
+    double eff_mx8;      // block-scaled 8-bit variants
 };
 
 int variant_count();
@@ -65,6 +68,9 @@ struct GemmArgs {
     float* ws;           // stream-K: partial-tile slots (2 per workgroup, BM*BN floats each)
     int sk_iters;        // stream-K: K iterations per tile (0: data-parallel launch)
     int sk_grid;         // stream-K: workgroups of the main kernel
+    const unsigned char* sa;   // block-scaled operands: scale codes of A (M x K/32)
+    const unsigned char* sb;   // ... and of B (N x K/32); B is then N rows of K codes
+    int fmt_a, fmt_b;    // element formats: 0 E4M3, 1 E5M2
 };
 
 // Fully resolved plan (internal form of sam_plan).
@@ -100,6 +106,7 @@ hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_stream(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mx8(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const float* parts, int split, long long part_stride,
                          float* C, long long count, hipStream_t s);
 hipError_t launch_zero(float* C, long long count, hipStream_t s);

@@ -48,8 +48,12 @@ namespace sam {
 #define SAM_F32RING_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32) \
     {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, BLK, NBUF, BK, gm, xr, ms, EL, e32, 0.0},
 
+#define SAM_MX8_ROW(id, name, BM, BN, WM, WN, BK, SD, gm, xr, ms, e8) \
+    {id, name, KIND_MX8, (1 << DT_MX8), BM, BN, WM, WN, 32, 2, BK, gm, xr, ms, 0, 0.0, 0.0, e8},
+
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
-                                        SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)};
+                                        SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)
+                                            SAM_MX8_VARIANTS(SAM_MX8_ROW)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -66,7 +70,9 @@ int k_stage(const Variant& v, int dtype)
     return dtype == DT_F32 ? 32 : 64;   // one 128-byte LDS row
 }
 
-static int vec_elems(int dtype) { return dtype == DT_F32 ? 4 : 8; }
+static int vec_elems(int dtype) { return dtype == DT_F32 ? 4 : (dtype == DT_MX8 ? 16 : 8); }
+
+static double in_bytes(int dtype) { return dtype == DT_F32 ? 4.0 : (dtype == DT_MX8 ? 1.0 : 2.0); }
 
 static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
@@ -80,7 +86,7 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
     const long long kc = cdiv(nkb, split) * bk;               // K per split, padded
     const long long tiles_m = cdiv(M, v.bm), tiles_n = cdiv(N, v.bn);
     const long long wgs = tiles_m * tiles_n * split;
-    const double in_b = dtype == DT_F32 ? 4.0 : 2.0;
+    const double in_b = in_bytes(dtype);
     const double mb = 1e-6;                                   // bytes -> MB; GB/s = MB/ms
 
     if (v.kind == KIND_STREAM) {
@@ -95,10 +101,11 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
         return t;
     }
 
-    double eff = dtype == DT_F32 ? v.eff_f32 : v.eff_h16;
+    double eff = dtype == DT_F32 ? v.eff_f32 : (dtype == DT_MX8 ? v.eff_mx8 : v.eff_h16);
     if (!a_vec) eff *= 0.85;
     if (!b_vec) eff *= 0.85;
-    const double peak_cu = (dtype == DT_F32 ? kDev.f32_flop_per_clk_cu : kDev.h16_flop_per_clk_cu) *
+    const double peak_cu = (dtype == DT_F32 ? kDev.f32_flop_per_clk_cu
+                                            : (dtype == DT_MX8 ? kDev.mx8_flop_per_clk_cu : kDev.h16_flop_per_clk_cu)) *
                            kDev.clock_ghz * 1e3;              // FLOP per microsecond
     const double t_wg = 2.0 * v.bm * v.bn * (double)kc / (peak_cu * eff);
     const double rounds = (double)cdiv(wgs, kDev.cus);
@@ -149,7 +156,7 @@ static void fill_plan(const Variant& v, long long M, long long N, long long K, i
     p->group_m = v.group_m;
     p->xcd_remap = v.xcd_remap;
     p->a_vec = (K % ve) == 0;
-    p->b_vec = (N % ve) == 0;
+    p->b_vec = v.kind == KIND_MX8 ? p->a_vec : (N % ve) == 0;   // block-scaled B rows run along K
     p->tiles_m = (int)cdiv(M, v.bm);
     p->tiles_n = (int)cdiv(N, v.bn);
     p->grid = (long long)p->tiles_m * p->tiles_n * split;
@@ -224,8 +231,10 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
                       Plan* out)
 {
     const Variant* v = variant_get(vid);
-    if (!v || dtype < DT_F32 || dtype > DT_F16 || !(v->dtype_mask & (1 << dtype))) return false;
+    if (!v || dtype < DT_F32 || dtype > DT_MX8 || !(v->dtype_mask & (1 << dtype))) return false;
     if (M < 0 || N < 0 || K < 0) return false;
+    // Block-scaled operands come in whole blocks of 32 values of K.
+    if (v->kind == KIND_MX8 && K % 32 != 0) return false;
     // The LDS-ring kernels take whole 16-byte pieces of A and B rows.
     if (v->kind == KIND_DMA && (K % 8 != 0 || N % 8 != 0)) return false;
     // FP32 ring kernels take rows that are not 16-byte pieces only in their
@@ -307,7 +316,7 @@ bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out)
 
 void plan_name(const Plan& p, char* buf, int n)
 {
-    static const char* dt[] = {"f32", "bf16", "f16"};
+    static const char* dt[] = {"f32", "bf16", "f16", "mxfp8"};
     const Variant* v = variant_get(p.variant_id);
     char sp[16];
     if (p.sk)

@@ -16,6 +16,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 #define CHECK(x)                                                                      \
     do {                                                                              \
@@ -39,7 +40,10 @@ __global__ void __launch_bounds__(256) mfma_loop(float* out, int iters, float se
     for (int i = 0; i < 8; ++i)
         av[i] = u4{__float_as_uint(x + i), __float_as_uint(x + 2 * i), __float_as_uint(x - i), __float_as_uint(x * i)};
     const u4 bv = {__float_as_uint(x), __float_as_uint(x + 1), __float_as_uint(x + 2), __float_as_uint(x + 3)};
-    if constexpr (KIND == 0 || KIND == 2 || KIND == 3) {   // 32x32 blocks: 16 acc regs
+    // KIND 5: the block-scaled 8-bit 32x32x64 MFMA (E4M3 operands) with
+    // per-lane scales in registers.
+    const int sc = 120 + (threadIdx.x & 7);
+    if constexpr (KIND == 0 || KIND == 2 || KIND == 3 || KIND == 5) {   // 32x32 blocks: 16 acc regs
         v16f acc[8];
         for (int i = 0; i < 8; ++i) for (int r = 0; r < 16; ++r) acc[i][r] = (float)(i * 16 + r);
         for (int it = 0; it < iters; ++it) {
@@ -49,8 +53,13 @@ __global__ void __launch_bounds__(256) mfma_loop(float* out, int iters, float se
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(av[i][0]), x, acc[i], 0, 0, 0);
                 else if constexpr (KIND == 2)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av[i]), __builtin_bit_cast(v8bf, bv), acc[i], 0, 0, 0);
-                else
+                else if constexpr (KIND == 3)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, av[i]), __builtin_bit_cast(v8h, bv), acc[i], 0, 0, 0);
+                else
+                    acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        __builtin_bit_cast(v8i, __builtin_shufflevector(av[i], bv, 0, 1, 2, 3, 4, 5, 6, 7)),
+                        __builtin_bit_cast(v8i, __builtin_shufflevector(bv, av[i], 0, 1, 2, 3, 4, 5, 6, 7)), acc[i],
+                        0, 0, 0, sc, 0, sc + 1);
             }
             asm volatile("" ::: "memory");
         }
@@ -115,9 +124,9 @@ int main(int argc, char** argv)
     struct { int kind; const char* name; double flops; } kinds[] = {
         {0, "f32_32x32x2", 32.0 * 32 * 2 * 2}, {1, "f32_16x16x4", 16.0 * 16 * 4 * 2},
         {2, "bf16_32x32x16", 32.0 * 32 * 16 * 2}, {3, "f16_32x32x16", 32.0 * 32 * 16 * 2},
-        {4, "bf16_16x16x32", 16.0 * 16 * 32 * 2}};
+        {4, "bf16_16x16x32", 16.0 * 16 * 32 * 2}, {5, "mxfp8_32x32x64", 32.0 * 32 * 64 * 2}};
     printf("{\"device\": \"%s\", \"cus\": %d, \"clock_khz\": %d, \"mfma\": {", prop.gcnArchName, cus, prop.clockRate);
-    for (int k = 0; k < 5; ++k) {
+    for (int k = 0; k < 6; ++k) {
         const int iters = kinds[k].kind <= 1 ? 2000 : 8000;
         for (int rep = 0; rep < 2; ++rep) {   // first pass warms the clocks
             CHECK(hipEventRecord(e0, 0));
@@ -126,7 +135,8 @@ int main(int argc, char** argv)
             case 1: hipLaunchKernelGGL(mfma_loop<1>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
             case 2: hipLaunchKernelGGL(mfma_loop<2>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
             case 3: hipLaunchKernelGGL(mfma_loop<3>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
-            default: hipLaunchKernelGGL(mfma_loop<4>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
+            case 4: hipLaunchKernelGGL(mfma_loop<4>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
+            default: hipLaunchKernelGGL(mfma_loop<5>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
             }
             CHECK(hipGetLastError());
             CHECK(hipEventRecord(e1, 0));

@@ -28,7 +28,7 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 TUNED_H = PKG / "csrc" / "sam_tuned.h"
-DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "mxfp8": 3}
 
 # Shapes beyond the named workloads: square sizes between and around them,
 # K-heavy and K-light rectangles, skinny-ish panels, and the LLM-like shapes
@@ -41,6 +41,8 @@ EXTRA = {
     "bf16": [(1024, 1024, 1024), (2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144),
              (4096, 4096, 1024), (2048, 8192, 2048), (256, 11008, 4096), (4096, 4096, 11008)],
     "f16": [(2048, 2048, 2048), (6144, 6144, 6144), (4096, 4096, 11008)],
+    "mxfp8": [(2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144), (4096, 4096, 1024),
+              (256, 11008, 4096), (4096, 4096, 11008), (2048, 8192, 2048)],
 }
 
 SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
@@ -48,7 +50,8 @@ SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
 
 def shapes():
     import sam_inputs as si
-    out = [(w.dtype, w.M, w.N, w.K, w.name) for w in si.WORKLOADS]
+    out = [(w.dtype, w.M, w.N, w.K, w.name) for w in si.WORKLOADS + si.MX_WORKLOADS
+           if (w.fmt_a, w.fmt_b) == ("e4m3", "e4m3")]
     seen = {(d, m, n, k) for d, m, n, k, _ in out}
     for dt, lst in EXTRA.items():
         for (m, n, k) in lst:
@@ -114,20 +117,23 @@ def measure(record: Path, only=None):
         for line in record.read_text().splitlines():
             r = json.loads(line)
             done.add((r["dtype"], r["M"], r["N"], r["K"], r["variant"], r["split"]))
-    fn = sam.lib().sam_gemm_variant
     with record.open("a") as f:
         for (dt, M, N, K, name) in shapes():
             if only and name not in only:
                 continue
-            w = si.Workload(name, dt, M, N, K, "uniform" if dt == "f32" else "normal16", 77)
-            A, B = si.make_operands(w)
-            if dt == "f32":
+            dist = {"f32": "uniform", "mxfp8": "mx_normal"}.get(dt, "normal16")
+            w = si.Workload(name, dt, M, N, K, dist, 77)
+            if dt == "mxfp8":
+                mx = [torch.from_numpy(x).cuda() for x in si.make_mx_operands(w)]
+                dA = mx[0]
+            elif dt == "f32":
+                A, B = si.make_operands(w)
                 dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
             else:
+                A, B = si.make_operands(w)
                 t = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
                 dA = torch.from_numpy(A.view("int16")).cuda().view(t)
                 dB = torch.from_numpy(B.view("int16")).cuda().view(t)
-            del A, B
             C = torch.empty((M, N), dtype=torch.float32, device="cuda")
             stream = torch.cuda.current_stream()
             auto = model_plan(sam, dt, M, N, K)
@@ -137,10 +143,15 @@ def measure(record: Path, only=None):
                     continue
                 p = sam.variant_plan(vid, M, N, K, dt, split)
                 ws = sam.workspace_for(p, dA.device)
-                args = (vid, sam.DTYPES[dt], split, ctypes.c_void_p(dA.data_ptr()),
-                        ctypes.c_void_p(dB.data_ptr()), ctypes.c_void_p(C.data_ptr()), M, N, K,
-                        ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
+                tail = (ctypes.c_void_p(C.data_ptr()), M, N, K, ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
                         ws.numel() * 4 if ws is not None else 0, ctypes.c_void_p(stream.cuda_stream))
+                if dt == "mxfp8":   # E4M3 operands, scales as drawn
+                    fn = sam.lib().sam_gemm_mxfp8_variant
+                    args = (vid, split, 0, 0, *(ctypes.c_void_p(x.data_ptr()) for x in mx), *tail)
+                else:
+                    fn = sam.lib().sam_gemm_variant
+                    args = (vid, sam.DTYPES[dt], split, ctypes.c_void_p(dA.data_ptr()), ctypes.c_void_p(dB.data_ptr()),
+                            *tail)
                 for _ in range(3):
                     rc = fn(*args)
                     if rc != 0:
@@ -167,7 +178,11 @@ def measure(record: Path, only=None):
                                     "model_pick": vid == auto["variant_id"] and split == auto["split_k"]}) + "\n")
                 f.flush()
                 del ws
-            del dA, dB, C
+            del dA, C
+            if dt == "mxfp8":
+                del mx
+            else:
+                del dB
             torch.cuda.empty_cache()
 
 

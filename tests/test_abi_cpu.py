@@ -196,3 +196,36 @@ def test_gemm_ex_rejections_before_any_device_call():
     assert need >= 64 * 64 * 4
     assert f(0, 1, 0, 64, 64, 64, 1.0, vp(A_), 64, vp(B_), 64, 0.0, vp(C_), 64, vp(W_), need - 1, None) == -3
     assert sam.ex_workspace_bytes(64, 64, 64, False, False, 64, 64, 64, 1.0, 0.0, "f32") == 0
+
+
+def test_mxfp8_plans_and_rejections_before_any_device_call():
+    """Block-scaled plans come from the block-scaled variants only; K not a
+    multiple of 32, bad formats, a negative split, null scales and the plain
+    forced-variant entry point are refused on the host."""
+    p = sam.plan(4096, 4096, 4096, "mxfp8")
+    assert p["name"].startswith("mxfp8_x") and p["dtype"] == sam.MXFP8
+    for shape in [(1, 1, 32), (4096, 4096, 4096), (37, 45, 96), (16, 8192, 8192)]:
+        assert sam.plan(*shape, "mxfp8")["name"].startswith("mxfp8_x")
+    for vid in range(sam.variant_count()):
+        name = sam.variant_info(vid)["name"]
+        for dt in ("f32", "bf16", "f16"):
+            if name.startswith("x"):
+                with pytest.raises(sam.SamError):
+                    sam.variant_plan(vid, 256, 256, 256, dt)
+        if not name.startswith("x"):
+            with pytest.raises(sam.SamError):
+                sam.variant_plan(vid, 256, 256, 256, "mxfp8")
+    with pytest.raises(sam.SamError):
+        sam.plan(64, 64, 48, "mxfp8")
+    f = L.sam_gemm_mxfp8
+    vp = ctypes.c_void_p
+    A_, SA_, B_, SB_, C_ = 1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20   # aligned, never dereferenced
+    assert f(0, 0, vp(A_), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 48, None, 0, None) == -1   # K % 32
+    assert f(2, 0, vp(A_), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -1   # format
+    assert f(0, 0, vp(A_), None, vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -1      # null scale
+    assert f(0, 0, vp(A_ + 8), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -2  # misaligned
+    g = L.sam_gemm_mxfp8_variant
+    vid = next(v for v in range(sam.variant_count()) if sam.variant_info(v)["name"].startswith("x"))
+    assert g(vid, -1, 0, 0, vp(A_), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -1
+    assert g(0, 0, 0, 0, vp(A_), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -4   # not MX
+    assert L.sam_gemm_variant(vid, sam.MXFP8, 0, vp(A_), vp(B_), vp(C_), 64, 64, 64, None, 0, None) == -1

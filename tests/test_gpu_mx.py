@@ -1,0 +1,197 @@
+"""Parity of the block-scaled 8-bit path (sam_gemm_mxfp8) with the oracle on
+an MI355X (gfx950), through the C ABI.
+
+Dyadic inputs (``mx_dyadic``: every partial sum is exact in FP32) must match
+the oracle bit for bit. Random inputs (``mx_normal``) are held to the
+precision of the scaled matrix instruction, which sums each group of 64
+products with fewer bits than FP32 (measured with one-hot and two-term
+operands: sums across instructions are exact to 2^-23, and random operands
+give rel_rms about 1.3e-5 for E4M3 and 9e-6 for E5M2 already at K = 64, with
+|error| at most about 640 u sum_k |a_k b_k|, u = 2^-24). The gates: every
+element within 2^-12 sum_k |a_k b_k| of the oracle's exact sum (a wrong
+scale or a dropped block moves an element by far more), and rel_rms <= 5e-5.
+Repeated runs must give the same bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sam_inputs as si
+import shape_adaptive_matrix_amd as sam
+from tests.compare import bitexact_mismatches, rel_rms
+
+pytestmark = pytest.mark.gpu
+
+MX_VARIANTS = [v for v in range(sam.variant_count()) if sam.variant_info(v)["name"].startswith("x")]
+FORMATS = [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")]
+RAGGED = [(1, 1, 32), (37, 45, 96), (64, 64, 64), (130, 257, 160), (256, 256, 256), (300, 200, 1024),
+          (513, 129, 224), (16, 300, 128)]
+
+ORC = None
+
+
+def orc():
+    global ORC
+    if ORC is None:
+        ORC = oracle.get()
+    return ORC
+
+
+def _dev(*xs):
+    return [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in xs]
+
+
+def _operands(M, N, K, fa, fb, dist, seed):
+    w = si.Workload("t", "mxfp8", M, N, K, dist, seed, fmt_a=fa, fmt_b=fb)
+    return si.make_mx_operands(w)
+
+
+def _run(ops, fa, fb, variant=None, split=0):
+    A, SA, Bt, SB = _dev(*ops)
+    C = torch.full((A.shape[0], Bt.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
+    if variant is None:
+        sam.gemm_mxfp8(A, SA, Bt, SB, fa, fb, C)
+    else:
+        sam.gemm_mxfp8_variant(variant, A, SA, Bt, SB, fa, fb, C, split_k=split)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def _abs_sum(ops, fa, fb):
+    """sum_k |a_k b_k| per element: the oracle on codes with the sign bit
+    cleared (every term then positive)."""
+    A, SA, Bt, SB = ops
+    return orc().gemm_mxfp8(fa, fb, A & 0x7F, SA, Bt & 0x7F, SB)
+
+
+def _check_bound(C, ref, absum, K):
+    assert np.isfinite(C).all()
+    err = np.abs(C.astype(np.float64) - ref)
+    bound = 2.0 ** -12 * absum
+    worst = np.max(err - bound)
+    assert worst <= 0, f"error exceeds the FP32 accumulation bound by {worst}"
+
+
+def _supported(vid, M, N, K, split=0):
+    try:
+        sam.variant_plan(vid, M, N, K, "mxfp8", split)
+        return True
+    except sam.SamError:
+        return False
+
+
+def test_variants_present():
+    assert len(MX_VARIANTS) >= 3
+    for v in MX_VARIANTS:
+        assert _supported(v, 256, 256, 256)
+
+
+@pytest.mark.parametrize("fa,fb", FORMATS)
+@pytest.mark.parametrize("vid", MX_VARIANTS)
+def test_every_mx_variant_dyadic_ragged(vid, fa, fb):
+    """Each block-scaled variant, forced, on ragged shapes with exact sums:
+    bit-exact, for splits 1, 2 and 3 where admissible."""
+    for (M, N, K) in RAGGED:
+        ops = _operands(M, N, K, fa, fb, "mx_dyadic", seed=M * 7 + N * 3 + K)
+        ref = orc().gemm_mxfp8(fa, fb, *ops)
+        tk = sam.variant_plan(vid, M, N, K, "mxfp8", 1)["tile_k"]
+        for s in [0, 1] + [s for s in (2, 3) if s * tk <= K]:
+            if not _supported(vid, M, N, K, s):
+                continue
+            print(f"[mx] variant {vid} {fa}x{fb} {(M, N, K)} split {s}", flush=True)
+            C = _run(ops, fa, fb, variant=vid, split=s)
+            bad = bitexact_mismatches(C, ref)
+            assert bad == 0, f"variant {vid} {fa}x{fb} {(M, N, K)} split {s}: {bad} mismatches"
+
+
+@pytest.mark.parametrize("vid", MX_VARIANTS)
+def test_every_mx_variant_random(vid):
+    """Normal data stored in 8-bit formats with scales a few octaves apart:
+    within the FP32 accumulation bound of the oracle, element by element."""
+    M, N, K = 200, 328, 576
+    for fa, fb in FORMATS:
+        ops = _operands(M, N, K, fa, fb, "mx_normal", seed=vid + 300)
+        ref = orc().gemm_mxfp8(fa, fb, *ops)
+        C = _run(ops, fa, fb, variant=vid)
+        _check_bound(C, ref, _abs_sum(ops, fa, fb), K)
+        assert rel_rms(C, ref) <= 5e-5
+
+
+def test_mx_auto_plans_random_shapes():
+    """The dispatcher's own plans on seeded random shapes (K a multiple of 32)."""
+    rng = np.random.default_rng(77)
+    for n in range(10):
+        M, N = (int(x) for x in rng.integers(1, 700, size=2))
+        K = 32 * int(rng.integers(1, 40))
+        fa, fb = FORMATS[n % 4]
+        ops = _operands(M, N, K, fa, fb, "mx_dyadic", seed=1000 + n)
+        ref = orc().gemm_mxfp8(fa, fb, *ops)
+        print(f"[mx] auto {fa}x{fb} {(M, N, K)} plan={sam.plan(M, N, K, 'mxfp8')['name']}", flush=True)
+        C = _run(ops, fa, fb)
+        assert bitexact_mismatches(C, ref) == 0, (M, N, K, fa, fb)
+
+
+@pytest.mark.parametrize("name", [w.name for w in si.MX_WORKLOADS])
+def test_mx_workload_sampled(name):
+    """Full-size workloads in the launch configuration the benchmark times:
+    sampled outputs (random points plus the corners and tail rows/columns)
+    against the oracle's single-point sums."""
+    w = si.by_name(name)
+    ops = si.make_mx_operands(w)
+    print(f"[mx] {name} plan={sam.plan(w.M, w.N, w.K, 'mxfp8')['name']}", flush=True)
+    C = _run(ops, w.fmt_a, w.fmt_b)
+    rows, cols = si.sample_points(w.M, w.N, 1500, seed=w.seed)
+    ref = orc().gemm_mxfp8_points(w.fmt_a, w.fmt_b, *ops, rows, cols)
+    A, SA, Bt, SB = ops
+    absum = orc().gemm_mxfp8_points(w.fmt_a, w.fmt_b, A & 0x7F, SA, Bt & 0x7F, SB, rows, cols)
+    got = C[rows, cols]
+    _check_bound(got, ref, absum, w.K)
+    assert rel_rms(got, ref) <= w.tol
+    assert np.isfinite(C).all()
+
+
+def test_mx_run_to_run_bitwise():
+    """Five runs give identical bytes; another seed gives different bytes."""
+    M, N, K = 1024, 1536, 2048
+    ops = _operands(M, N, K, "e4m3", "e4m3", "mx_normal", seed=5)
+    first = _run(ops, "e4m3", "e4m3")
+    for _ in range(4):
+        assert np.array_equal(first.view(np.uint32), _run(ops, "e4m3", "e4m3").view(np.uint32))
+    other = _run(_operands(M, N, K, "e4m3", "e4m3", "mx_normal", seed=6), "e4m3", "e4m3")
+    assert not np.array_equal(first.view(np.uint32), other.view(np.uint32))
+
+
+def test_mx_nan_beyond_operands_never_reaches_c():
+    """NaN codes stored right after A's and Bt's last rows, and NaN scale
+    codes after the scale arrays, must never reach C (tails are masked)."""
+    M, N, K = 70, 45, 96
+    for fa, fb in FORMATS:
+        A, SA, Bt, SB = _operands(M, N, K, fa, fb, "mx_dyadic", seed=11)
+        ref = orc().gemm_mxfp8(fa, fb, A, SA, Bt, SB)
+        nan_a = 0x7F if fa == "e4m3" else 0x7F   # S.1111.111 (E4M3) / S.11111.11 (E5M2): NaN
+        nan_b = 0x7F
+        pA = np.full((M + 8, K), nan_a, np.uint8); pA[:M] = A
+        pB = np.full((N + 8, K), nan_b, np.uint8); pB[:N] = Bt
+        pSA = np.full((M + 8, K // 32), 0xFF, np.uint8); pSA[:M] = SA
+        pSB = np.full((N + 8, K // 32), 0xFF, np.uint8); pSB[:N] = SB
+        dA, dB, dSA, dSB = _dev(pA, pB, pSA, pSB)
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        sam.gemm_mxfp8(dA[:M], dSA[:M], dB[:N], dSB[:N], fa, fb, C)
+        torch.cuda.synchronize()
+        assert bitexact_mismatches(C.cpu().numpy(), ref) == 0, (fa, fb)
+
+
+def test_mx_degenerate_sizes():
+    """K = 0 writes +0; M = 0 or N = 0 leaves C untouched."""
+    z = torch.zeros((0,), dtype=torch.uint8, device="cuda")
+    C = torch.full((3, 5), float("nan"), dtype=torch.float32, device="cuda")
+    sam.gemm_mxfp8(z.view(3, 0), z.view(3, 0), z.view(5, 0), z.view(5, 0), "e4m3", "e4m3", C)
+    torch.cuda.synchronize()
+    c = C.cpu().numpy()
+    assert (c == 0).all() and not np.signbit(c).any()
+    C = torch.full((4, 4), 7.0, dtype=torch.float32, device="cuda")
+    sam.gemm_mxfp8(z.view(0, 64), z.view(0, 2), torch.zeros((4, 64), dtype=torch.uint8, device="cuda"),
+                   torch.zeros((4, 2), dtype=torch.uint8, device="cuda"), "e4m3", "e4m3", C[:0])
+    torch.cuda.synchronize()
+    assert (C.cpu().numpy() == 7.0).all()
