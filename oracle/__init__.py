@@ -93,6 +93,12 @@ class Oracle:
         lib.oracle_gemm_mxfp8_points.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, i64, i64,
                                                  vp, vp, i64, dp, ctypes.c_int]
         lib.oracle_gemm_mxfp8_points.restype = ctypes.c_int
+        lib.oracle_decode_fp4.argtypes = [ctypes.c_uint8]
+        lib.oracle_decode_fp4.restype = ctypes.c_double
+        lib.oracle_gemm_mxfp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, dp, ctypes.c_int]
+        lib.oracle_gemm_mxfp4.restype = ctypes.c_int
+        lib.oracle_gemm_mxfp4_points.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, i64, dp, ctypes.c_int]
+        lib.oracle_gemm_mxfp4_points.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -231,6 +237,45 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_gemm_mxfp8_points rejected its arguments")
         return out
+
+    @staticmethod
+    def _mx4_operands(A, SA, Bt, SB):
+        A, SA, Bt, SB = (np.ascontiguousarray(x) for x in (A, SA, Bt, SB))
+        for x in (A, SA, Bt, SB):
+            if x.dtype != np.uint8 or x.ndim != 2:
+                raise TypeError("MXFP4 operands and scales are 2-D uint8 arrays")
+        M, K = A.shape[0], 2 * A.shape[1]
+        N = Bt.shape[0]
+        if Bt.shape[1] != K // 2 or SA.shape != (M, K // 32) or SB.shape != (N, K // 32):
+            raise ValueError(f"bad MXFP4 shapes A{A.shape} SA{SA.shape} Bt{Bt.shape} SB{SB.shape}")
+        return A, SA, Bt, SB, M, N, K
+
+    def gemm_mxfp4(self, A, SA, Bt, SB, nthreads: int = 0) -> np.ndarray:
+        """C for E2M1 operands packed two per byte (low nibble first): A [M][K/2],
+        Bt [N][K/2] bytes, SA [M][K/32], SB [N][K/32] scale codes."""
+        A, SA, Bt, SB, M, N, K = self._mx4_operands(A, SA, Bt, SB)
+        C = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_gemm_mxfp4(self._ptr(A), self._ptr(SA), self._ptr(Bt), self._ptr(SB), M, N, K,
+                                        self._ptr(C), nthreads)
+        if rc != 0:
+            raise ValueError("oracle_gemm_mxfp4 rejected its arguments")
+        return C
+
+    def gemm_mxfp4_points(self, A, SA, Bt, SB, rows, cols, nthreads: int = 0) -> np.ndarray:
+        A, SA, Bt, SB, M, N, K = self._mx4_operands(A, SA, Bt, SB)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        cols = np.ascontiguousarray(cols, dtype=np.int64)
+        out = np.empty(rows.shape[0], dtype=np.float64)
+        rc = self.lib.oracle_gemm_mxfp4_points(self._ptr(A), self._ptr(SA), self._ptr(Bt), self._ptr(SB), M, N, K,
+                                               self._ptr(rows), self._ptr(cols), rows.shape[0], self._ptr(out),
+                                               nthreads)
+        if rc != 0:
+            raise ValueError("oracle_gemm_mxfp4_points rejected its arguments")
+        return out
+
+    def decode_fp4(self, code: int) -> float:
+        """Exact value of one 4-bit E2M1 code."""
+        return self.lib.oracle_decode_fp4(code)
 
     def decode_fp8(self, fmt: str, code: int) -> float:
         """Exact value of one 8-bit element code ("e4m3" or "e5m2")."""

@@ -335,3 +335,66 @@ int oracle_gemm_mxfp8_points(int fmt_a, int fmt_b, const uint8_t* A, const uint8
     }
     return 0;
 }
+
+/* ---- Block-scaled 4-bit operands (OCP MX, MXFP4) ---------------------------
+ *
+ * E2M1 elements: 1 sign, 2 exponent bits (bias 1), 1 fraction bit; exponent
+ * field 0 is zero/subnormal (0.f * 2^0); no infinity or NaN, so the largest
+ * magnitude is 6. Two elements per byte: element k of a row is the low
+ * nibble of byte k/2 when k is even and the high nibble when k is odd (the
+ * reading taken for the packing, which the pages do not give). Scales and
+ * blocks as for MXFP8: E8M0 per 32 values of K, per row of A and per column
+ * of B. Storage: A is M rows of K/2 bytes, B is given as Bt, N rows of K/2
+ * bytes; SA and SB as above. Every value is exact in double and the products
+ * are summed in ascending k from +0.0. */
+double oracle_decode_fp4(uint8_t code)
+{
+    const int sign = (code >> 3) & 1, e = (code >> 1) & 3, f = code & 1;
+    const double v = e == 0 ? ldexp((double)f, -1) : ldexp((double)(0x2 | f), e - 1 - 1);
+    return sign ? -v : v;
+}
+
+static double mx4_val(const uint8_t* codes, const uint8_t* scales, int64_t row, int64_t K, int64_t k)
+{
+    const uint8_t byte = codes[row * (K / 2) + k / 2];
+    const uint8_t code = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF);
+    return oracle_decode_fp4(code) * oracle_decode_e8m0(scales[row * (K / 32) + k / 32]);
+}
+
+int oracle_gemm_mxfp4(const uint8_t* A, const uint8_t* SA, const uint8_t* Bt, const uint8_t* SB, int64_t M,
+                      int64_t N, int64_t K, double* out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return -1;
+    if (M == 0 || N == 0) return 0;
+    if (!out || (K > 0 && (!A || !SA || !Bt || !SB))) return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s = s + mx4_val(A, SA, i, K, k) * mx4_val(Bt, SB, j, K, k);
+            out[i * N + j] = s;
+        }
+    }
+    return 0;
+}
+
+int oracle_gemm_mxfp4_points(const uint8_t* A, const uint8_t* SA, const uint8_t* Bt, const uint8_t* SB, int64_t M,
+                             int64_t N, int64_t K, const int64_t* rows, const int64_t* cols, int64_t npts,
+                             double* out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || npts < 0) return -1;
+    if (npts > 0 && (!rows || !cols || !out || (K > 0 && (!A || !SA || !Bt || !SB)))) return -1;
+    for (int64_t p = 0; p < npts; ++p)
+        if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npts; ++p) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s = s + mx4_val(A, SA, rows[p], K, k) * mx4_val(Bt, SB, cols[p], K, k);
+        out[p] = s;
+    }
+    return 0;
+}

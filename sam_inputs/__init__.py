@@ -28,6 +28,11 @@ rows and B is given as N rows of K codes):
     uniform on [126, 128]. Every value is a multiple of 2^-4 below 8, so for
     K <= 1024 every partial sum is a multiple of 2^-8 below 2^16 and exact in
     FP32, whatever the order.
+  * E2M1 (``mxfp4`` workloads): packed bytes uniform over all values, i.e.
+    both 4-bit codes uniform over the 16 codes (for either recipe; the
+    recipe only sets the scale range). With scales on [126, 128] every value
+    is a multiple of 2^-2 of magnitude at most 12, so for K <= 1024 every
+    partial sum is a multiple of 2^-4 below 2^18: exact in FP32.
 Draw order: A codes, B codes, A scales, B scales.
 """
 from __future__ import annotations
@@ -72,7 +77,10 @@ def normal16(rng: np.random.Generator, shape, kind: str) -> np.ndarray:
 
 
 def mx_codes(rng: np.random.Generator, shape, fmt: str, dist: str) -> np.ndarray:
-    """uint8 element codes of ``fmt`` ("e4m3" | "e5m2") drawn per ``dist``."""
+    """uint8 element codes of ``fmt`` ("e4m3" | "e5m2") drawn per ``dist``;
+    for "e2m1", rows of packed bytes (two codes each, shape[1] // 2 per row)."""
+    if fmt == "e2m1":
+        return rng.integers(0, 256, size=(shape[0], shape[1] // 2), dtype=np.uint8)
     if dist == "mx_normal":
         import torch
         x = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32))
@@ -100,7 +108,7 @@ def mx_scales(rng: np.random.Generator, rows: int, K: int, dist: str) -> np.ndar
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str          # "f32" | "bf16" | "f16" | "mxfp8"
+    dtype: str          # "f32" | "bf16" | "f16" | "mxfp8" | "mxfp4"
     M: int
     N: int
     K: int
@@ -119,14 +127,14 @@ class Workload:
 
     @property
     def in_bytes(self) -> int:
-        return {"f32": 4, "bf16": 2, "f16": 2, "mxfp8": 1}[self.dtype]
+        return {"f32": 4, "bf16": 2, "f16": 2, "mxfp8": 1, "mxfp4": 0.5}[self.dtype]
 
     @property
     def alg_bytes(self) -> int:
         """Operands (and block scales) read once, C written once (beta = 0, C
         is never read)."""
-        b = self.in_bytes * (self.M * self.K + self.K * self.N) + 4 * self.M * self.N
-        if self.dtype == "mxfp8":
+        b = int(self.in_bytes * (self.M * self.K + self.K * self.N)) + 4 * self.M * self.N
+        if self.dtype in ("mxfp8", "mxfp4"):
             b += (self.M + self.N) * (self.K // MX_BLOCK)
         return b
 
@@ -160,6 +168,8 @@ MX_WORKLOADS = [
     Workload("mxfp8_8192", "mxfp8", 8192, 8192, 8192, "mx_normal", 17, tol=5e-5),
     Workload("mxfp8_e5m2_4096", "mxfp8", 4096, 4096, 4096, "mx_normal", 18, tol=5e-5,
              fmt_a="e5m2", fmt_b="e5m2"),
+    Workload("mxfp4_4096", "mxfp4", 4096, 4096, 4096, "mx_normal", 19, tol=5e-5, fmt_a="e2m1", fmt_b="e2m1"),
+    Workload("mxfp4_8192", "mxfp4", 8192, 8192, 8192, "mx_normal", 20, tol=5e-5, fmt_a="e2m1", fmt_b="e2m1"),
 ]
 
 _BY_NAME = {w.name: w for w in WORKLOADS + MX_WORKLOADS}
@@ -183,8 +193,9 @@ def make_operands(w: Workload, seed: int | None = None):
 
 
 def make_mx_operands(w: Workload, seed: int | None = None):
-    """(A, SA, Bt, SB) uint8 arrays for an ``mxfp8`` workload: A [M][K] and
-    Bt [N][K] element codes, SA [M][K/32] and SB [N][K/32] scale codes."""
+    """(A, SA, Bt, SB) uint8 arrays for an ``mxfp8`` / ``mxfp4`` workload: A
+    [M][K] and Bt [N][K] element codes (E2M1: [M][K/2] and [N][K/2] packed
+    bytes), SA [M][K/32] and SB [N][K/32] scale codes."""
     rng = np.random.default_rng(w.seed if seed is None else seed)
     A = mx_codes(rng, (w.M, w.K), w.fmt_a, w.dist)
     Bt = mx_codes(rng, (w.N, w.K), w.fmt_b, w.dist)

@@ -348,7 +348,11 @@ def _same(got: float, want: float) -> bool:
 
 
 def _mx_decode(o, fmt, code):
-    return o.decode_e8m0(code) if fmt == "e8m0" else o.decode_fp8(fmt, code)
+    if fmt == "e8m0":
+        return o.decode_e8m0(code)
+    if fmt == "e2m1":
+        return o.decode_fp4(code)
+    return o.decode_fp8(fmt, code)
 
 
 def _torch_values(fmt: str, codes: np.ndarray) -> np.ndarray:
@@ -476,10 +480,95 @@ def pin_mx_points_and_degenerate(o):
         raise AssertionError("K = 48 accepted")
 
 
+# -- block-scaled 4-bit operands (MXFP4) ---------------------------------------
+def _e2m1_values(codes: np.ndarray) -> np.ndarray:
+    """E2M1 values through torch's E4M3 decoder: a normal E2M1 code (exponent
+    field e >= 1, bias 1, fraction f) is the E4M3 code with exponent field
+    e + 6 (bias 7) and fraction 4 f; the subnormal 0.5 is E4M3 0x30."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    sign, e, f = (codes >> 3) & 1, (codes >> 1) & 3, codes & 1
+    mag = np.where(e == 0, np.where(f == 1, 0x30, 0x00), ((e + 6) << 3) | (f << 2)).astype(np.uint8)
+    return _torch_values("e4m3", (sign.astype(np.uint8) << 7) | mag)
+
+
+def _unpack4(b: np.ndarray) -> np.ndarray:
+    """Rows of packed bytes -> rows of 4-bit codes, element 2i in the low nibble."""
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty((b.shape[0], 2 * b.shape[1]), dtype=np.uint8)
+    out[:, 0::2] = b & 0xF
+    out[:, 1::2] = b >> 4
+    return out
+
+
+def _mx4_random(rng, M, N, K, slo, shi):
+    A = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    Bt = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    SA = rng.integers(slo, shi + 1, size=(M, K // 32), dtype=np.uint8)
+    SB = rng.integers(slo, shi + 1, size=(N, K // 32), dtype=np.uint8)
+    return A, SA, Bt, SB
+
+
+def pin_mx4_decode_via_e4m3(o):
+    """Every E2M1 code decodes to the value torch's E4M3 type gives for the
+    same number written in E4M3."""
+    codes = np.arange(16, dtype=np.uint8)
+    ref = _e2m1_values(codes)
+    for c in range(16):
+        assert _same(o.decode_fp4(c), float(ref[c])), (hex(c), o.decode_fp4(c), ref[c])
+
+
+def pin_mx4_bruteforce(o):
+    """Random packed codes and scales: within (K-1)*u*sum|terms| of the exact
+    rational sum (values unpacked and decoded independently), and exactly
+    equal with scales near 1."""
+    rng = np.random.default_rng(130)
+    u = Fraction(1, 2 ** 53)
+    for (M, N, K, slo, shi) in [(3, 4, 32, 100, 154), (2, 5, 96, 100, 154), (4, 3, 64, 126, 128)]:
+        A, SA, Bt, SB = _mx4_random(rng, M, N, K, slo, shi)
+        got = o.gemm_mxfp4(A, SA, Bt, SB)
+        a, b = _e2m1_values(_unpack4(A)), _e2m1_values(_unpack4(Bt))
+        sa, sb = _torch_values("e8m0", SA), _torch_values("e8m0", SB)
+        for i in range(M):
+            for j in range(N):
+                terms = [Fraction(float(a[i, k])) * Fraction(float(sa[i, k // 32])) * Fraction(float(b[j, k])) *
+                         Fraction(float(sb[j, k // 32])) for k in range(K)]
+                want = sum(terms, Fraction(0))
+                if shi - slo <= 2:
+                    assert Fraction(got[i, j]) == want, (M, N, K, i, j)
+                else:
+                    bound = (K - 1) * u * sum((abs(t) for t in terms), Fraction(0))
+                    assert abs(Fraction(got[i, j]) - want) <= bound, (M, N, K, i, j)
+
+
+def pin_mx4_unit_scales(o):
+    """Scales of 1 reduce the MXFP4 product bit for bit to the FP32 oracle on
+    the unpacked, independently decoded values (B = Bt transposed)."""
+    rng = np.random.default_rng(131)
+    for (M, N, K) in [(5, 7, 64), (3, 2, 160)]:
+        A, SA, Bt, SB = _mx4_random(rng, M, N, K, 127, 127)
+        got = o.gemm_mxfp4(A, SA, Bt, SB)
+        Ad = _e2m1_values(_unpack4(A)).astype(np.float32)
+        Bd = np.ascontiguousarray(_e2m1_values(_unpack4(Bt)).astype(np.float32).T)
+        assert np.array_equal(_bits(got), _bits(o.gemm("f32", Ad, Bd))), (M, N, K)
+
+
+def pin_mx4_packing_closed_form(o):
+    """Byte 0 of A's row = 0x21 puts 0.5 at k = 0 and 1.0 at k = 1; a B column
+    that is one-hot at k = 0 (byte 0x02) or k = 1 (byte 0x20) picks each out;
+    a scale of 2 on block 1 reaches only k >= 32 (A value 3 at k = 33)."""
+    K = 64
+    A = np.zeros((1, K // 2), np.uint8); A[0, 0] = 0x21; A[0, 16] = 0x50   # k = 33: code 5 = 3
+    Bt = np.zeros((3, K // 2), np.uint8); Bt[0, 0] = 0x02; Bt[1, 0] = 0x20; Bt[2, 16] = 0x20
+    SA = np.array([[127, 128]], np.uint8); SB = np.full((3, 2), 127, np.uint8)
+    got = o.gemm_mxfp4(A, SA, Bt, SB)
+    assert got.tolist() == [[0.5, 1.0, 6.0]], got
+
+
 ALL_PINS = [pin_golden_small, pin_decode_table, pin_decode_library,
             pin_bruteforce_ints, pin_bruteforce_16bit, pin_fsum_bound,
             pin_closed_forms, pin_identity_permutation,
             pin_associativity_linearity, pin_numpy_matmul,
             pin_rows_points_consistent, pin_degenerate, pin_ex_bruteforce, pin_ex_inexact_scales,
             pin_mx_decode_table, pin_mx_decode_library, pin_mx_bruteforce,
-            pin_mx_unit_scales, pin_mx_scale_closed_form, pin_mx_points_and_degenerate]
+            pin_mx_unit_scales, pin_mx_scale_closed_form, pin_mx_points_and_degenerate,
+            pin_mx4_decode_via_e4m3, pin_mx4_bruteforce, pin_mx4_unit_scales, pin_mx4_packing_closed_form]

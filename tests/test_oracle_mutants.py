@@ -48,6 +48,15 @@ MUTANTS = {
     "mx_b_taken_row_major": ("s = s + mx_val(fmt_a, A, SA, i, K, k) * mx_val(fmt_b, Bt, SB, j, K, k);",
                              "s = s + mx_val(fmt_a, A, SA, i, K, k) * oracle_decode_fp8(fmt_b, Bt[k * N + j]) * "
                              "oracle_decode_e8m0(SB[j * (K / 32) + k / 32]);"),
+    "mx4_bias": ("ldexp((double)(0x2 | f), e - 1 - 1)", "ldexp((double)(0x2 | f), e - 2 - 1)"),
+    "mx4_subnormal_scale": ("e == 0 ? ldexp((double)f, -1)", "e == 0 ? ldexp((double)f, 0)"),
+    "mx4_hidden_bit": ("ldexp((double)(0x2 | f), e - 1 - 1)", "ldexp((double)f, e - 1 - 1)"),
+    "mx4_byte_index_shifted": ("const uint8_t byte = codes[row * (K / 2) + k / 2];",
+                               "const uint8_t byte = codes[row * (K / 2) + (k / 2 + 1) % (K / 2)];"),
+    "mx4_one_nibble_for_both": ("(k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF)",
+                                "(uint8_t)(byte & 0xF)"),
+    "mx4_scale_row_ignored": ("return oracle_decode_fp4(code) * oracle_decode_e8m0(scales[row * (K / 32) + k / 32]);",
+                              "return oracle_decode_fp4(code) * oracle_decode_e8m0(scales[k / 32]);"),
     "mx_last_block_dropped": ("for (int64_t k = 0; k < K; ++k)\n                s = s + mx_val(fmt_a, A, SA, i, K, k)",
                               "for (int64_t k = 0; k < K - 32; ++k)\n                s = s + mx_val(fmt_a, A, SA, i, K, k)"),
 }
