@@ -40,9 +40,12 @@ MUTANTS = {
     "mx_e5m2_no_inf": ("v = f ? NAN : INFINITY;\n        else if (e == 0)\n            v = ldexp((double)f, -14 - 2);",
                        "v = NAN;\n        else if (e == 0)\n            v = ldexp((double)f, -14 - 2);"),
     "mx_e8m0_bias": ("ldexp(1.0, (int)code - 127)", "ldexp(1.0, (int)code - 126)"),
-    "mx_scale_block_shifted": ("scales[row * (K / 32) + k / 32]", "scales[row * (K / 32) + (k / 32 + 1) % (K / 32)]"),
-    "mx_scale_row_ignored": ("scales[row * (K / 32) + k / 32]", "scales[k / 32]"),
-    "mx_block_of_16": ("scales[row * (K / 32) + k / 32]", "scales[row * (K / 32) + (k / 16) % (K / 32)]"),
+    "mx_scale_block_shifted": ("codes[row * K + k]) * oracle_decode_e8m0(scales[row * (K / 32) + k / 32]",
+                               "codes[row * K + k]) * oracle_decode_e8m0(scales[row * (K / 32) + (k / 32 + 1) % (K / 32)]"),
+    "mx_scale_row_ignored": ("codes[row * K + k]) * oracle_decode_e8m0(scales[row * (K / 32) + k / 32]",
+                             "codes[row * K + k]) * oracle_decode_e8m0(scales[k / 32]"),
+    "mx_block_of_16": ("codes[row * K + k]) * oracle_decode_e8m0(scales[row * (K / 32) + k / 32]",
+                       "codes[row * K + k]) * oracle_decode_e8m0(scales[row * (K / 32) + (k / 16) % (K / 32)]"),
     "mx_format_b_ignored": ("s = s + mx_val(fmt_a, A, SA, i, K, k) * mx_val(fmt_b, Bt, SB, j, K, k);",
                             "s = s + mx_val(fmt_a, A, SA, i, K, k) * mx_val(fmt_a, Bt, SB, j, K, k);"),
     "mx_b_taken_row_major": ("s = s + mx_val(fmt_a, A, SA, i, K, k) * mx_val(fmt_b, Bt, SB, j, K, k);",
