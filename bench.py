@@ -32,7 +32,7 @@ from pathlib import Path
 ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "mxfp8": 5000.0}   # MI355X dense MFMA, 2.4 GHz
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "mxfp8": 5000.0, "mxfp4": 10100.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -62,25 +62,29 @@ def src_digest() -> str:
 
 
 def prepare_mx(w, torch, sam, si, variant=None, split=0):
-    """Block-scaled 8-bit workload: sam_gemm_mxfp8 (or the forced variant)."""
+    """Block-scaled workload: sam_gemm_mxfp8 / sam_gemm_mxfp4 (or the forced
+    variant)."""
     ops = [torch.from_numpy(x).cuda() for x in si.make_mx_operands(w)]
     C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
     if variant is None:
-        plan = sam.plan(w.M, w.N, w.K, "mxfp8")
+        plan = sam.plan(w.M, w.N, w.K, w.dtype)
     else:
-        plan = sam.variant_plan(variant, w.M, w.N, w.K, "mxfp8", split)
+        plan = sam.variant_plan(variant, w.M, w.N, w.K, w.dtype, split)
     ws = sam.workspace_for(plan, C.device)
     L = sam.lib()
     stream = torch.cuda.current_stream()
-    fa, fb = sam.FP8_FORMATS[w.fmt_a], sam.FP8_FORMATS[w.fmt_b]
-    args = (fa, fb, *(ctypes.c_void_p(t.data_ptr()) for t in ops), ctypes.c_void_p(C.data_ptr()),
+    fp4 = w.dtype == "mxfp4"
+    fmts = () if fp4 else (sam.FP8_FORMATS[w.fmt_a], sam.FP8_FORMATS[w.fmt_b])
+    args = (*fmts, *(ctypes.c_void_p(t.data_ptr()) for t in ops), ctypes.c_void_p(C.data_ptr()),
             w.M, w.N, w.K, ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
             ws.numel() * 4 if ws is not None else 0, ctypes.c_void_p(stream.cuda_stream))
     if variant is None:
-        fn = L.sam_gemm_mxfp8
+        fn = L.sam_gemm_mxfp4 if fp4 else L.sam_gemm_mxfp8
     else:
+        forced = L.sam_gemm_mxfp4_variant if fp4 else L.sam_gemm_mxfp8_variant
+
         def fn(*a):
-            return L.sam_gemm_mxfp8_variant(variant, plan["split_k"], *a)
+            return forced(variant, plan["split_k"], *a)
 
     def step():
         rc = fn(*args)
@@ -91,7 +95,7 @@ def prepare_mx(w, torch, sam, si, variant=None, split=0):
 
 
 def prepare(w, torch, sam, si, variant=None, split=0):
-    if w.dtype == "mxfp8":
+    if w.dtype in ("mxfp8", "mxfp4"):
         return prepare_mx(w, torch, sam, si, variant, split)
     A, B = si.make_operands(w)
     if w.dtype == "f32":
@@ -238,6 +242,11 @@ def cpu_baseline(w, si, seconds: float):
 
         def slab(n):
             o.gemm_mxfp8(w.fmt_a, w.fmt_b, A[:n], SA[:n], Bt, SB)
+    elif w.dtype == "mxfp4":
+        A, SA, Bt, SB = si.make_mx_operands(w)
+
+        def slab(n):
+            o.gemm_mxfp4(A[:n], SA[:n], Bt, SB)
     else:
         A, B = si.make_operands(w)
 
@@ -321,8 +330,9 @@ def main():
         parts = args.shape.split(",")
         M, N, K = (int(x) for x in parts[:3])
         dt = parts[3] if len(parts) > 3 else "f32"
-        dist = {"f32": "uniform", "mxfp8": "mx_normal"}.get(dt, "normal16")
-        w = si.Workload(f"{dt}_{M}x{N}x{K}", dt, M, N, K, dist, 99)
+        dist = {"f32": "uniform", "mxfp8": "mx_normal", "mxfp4": "mx_normal"}.get(dt, "normal16")
+        fmt = "e2m1" if dt == "mxfp4" else "e4m3"
+        w = si.Workload(f"{dt}_{M}x{N}x{K}", dt, M, N, K, dist, 99, fmt_a=fmt, fmt_b=fmt)
     else:
         w = si.by_name(args.workload)
     if args.ex:

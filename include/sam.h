@@ -53,9 +53,10 @@
 extern "C" {
 #endif
 
-/* SAM_MXFP8 names block-scaled 8-bit operands (sam_gemm_mxfp8) in plan
- * queries; the other entry points take the first three. */
-typedef enum { SAM_F32 = 0, SAM_BF16 = 1, SAM_F16 = 2, SAM_MXFP8 = 3 } sam_dtype;
+/* SAM_MXFP8 / SAM_MXFP4 name block-scaled 8-bit / 4-bit operands
+ * (sam_gemm_mxfp8, sam_gemm_mxfp4) in plan queries; the other entry points
+ * take the first three. */
+typedef enum { SAM_F32 = 0, SAM_BF16 = 1, SAM_F16 = 2, SAM_MXFP8 = 3, SAM_MXFP4 = 4 } sam_dtype;
 
 typedef enum {
     SAM_OK = 0,
@@ -155,6 +156,29 @@ sam_status sam_gemm_mxfp8_variant(int32_t id, int32_t split_k,
                                   void* workspace, uint64_t workspace_bytes,
                                   void* stream);
 
+/* Block-scaled 4-bit GEMM (MXFP4, OCP Microscaling v1.0): the product of
+ * sam_gemm_mxfp8 with E2M1 elements (1 sign, 2 exponent bits with bias 1, 1
+ * fraction bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives) packed
+ * two per byte: element k of a row is the low nibble of byte k/2 for even k
+ * and the high nibble for odd k.
+ *   A       device, M rows of K/2 bytes, row stride K/2.
+ *   Bt      device, N rows of K/2 bytes (Bt[j] holds column j of B).
+ *   scale_a, scale_b, C, K, alignment, workspace and errors as for
+ *           sam_gemm_mxfp8 (sam_gemm_plan with SAM_MXFP4 gives the plan). */
+sam_status sam_gemm_mxfp4(const uint8_t* A, const uint8_t* scale_a,
+                          const uint8_t* Bt, const uint8_t* scale_b, float* C,
+                          int64_t M, int64_t N, int64_t K, void* workspace,
+                          uint64_t workspace_bytes, void* stream);
+
+/* The same with a forced block-scaled variant `id` and split (0 = the
+ * variant's own choice). */
+sam_status sam_gemm_mxfp4_variant(int32_t id, int32_t split_k,
+                                  const uint8_t* A, const uint8_t* scale_a,
+                                  const uint8_t* Bt, const uint8_t* scale_b,
+                                  float* C, int64_t M, int64_t N, int64_t K,
+                                  void* workspace, uint64_t workspace_bytes,
+                                  void* stream);
+
 /* Operand forms of the general entry point. */
 typedef enum { SAM_OP_N = 0, SAM_OP_T = 1 } sam_op;
 
@@ -209,9 +233,9 @@ sam_status sam_variant_plan(int32_t id, int64_t M, int64_t N, int64_t K,
                             sam_dtype dtype, int32_t split_k, sam_plan* out);
 
 /* Run a forced variant (tests, profiling and calibration). Operands as for
- * sam_gemm_<dtype> (16-bit ones as uint16_t patterns). SAM_MXFP8 is refused
- * with SAM_ERR_INVALID_ARG: block-scaled operands go through
- * sam_gemm_mxfp8_variant. */
+ * sam_gemm_<dtype> (16-bit ones as uint16_t patterns). SAM_MXFP8 and
+ * SAM_MXFP4 are refused with SAM_ERR_INVALID_ARG: block-scaled operands go
+ * through sam_gemm_mxfp8_variant / sam_gemm_mxfp4_variant. */
 sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k,
                             const void* A, const void* B, float* C, int64_t M,
                             int64_t N, int64_t K, void* workspace,

@@ -21,8 +21,8 @@ PKG = Path(__file__).resolve().parent
 LIB_PATH = Path(os.environ.get("SAM_LIBRARY", PKG / "libsam.so"))
 HEADER = PKG.parent / "include" / "sam.h"
 
-F32, BF16, F16, MXFP8 = 0, 1, 2, 3
-DTYPES = {"f32": F32, "bf16": BF16, "f16": F16, "mxfp8": MXFP8}
+F32, BF16, F16, MXFP8, MXFP4 = 0, 1, 2, 3, 4
+DTYPES = {"f32": F32, "bf16": BF16, "f16": F16, "mxfp8": MXFP8, "mxfp4": MXFP4}
 FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
 DTYPE_NAMES = {v: k for k, v in DTYPES.items()}
 
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
                            ctypes.c_int),
         "sam_gemm_mxfp8_variant": ([i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, vp,
                                     u64, vp], ctypes.c_int),
+        "sam_gemm_mxfp4": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
+        "sam_gemm_mxfp4_variant": ([i32, i32, vp, vp, vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
         "sam_device_check": ([], ctypes.c_int),
         "sam_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "sam_last_error": ([], ctypes.c_char_p),
@@ -326,4 +328,48 @@ def gemm_mxfp8_variant(vid: int, A, SA, Bt, SB, fmt_a="e4m3", fmt_b="e4m3", C=No
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().sam_gemm_mxfp8_variant(vid, p["split_k"], fa, fb, _ptr(A), _ptr(SA), _ptr(Bt), _ptr(SB), _ptr(C),
                                         M, N, K, _ptr(workspace), ws_bytes, _stream_ptr(stream)))
+    return C
+
+
+def _mx4_operands(A, SA, Bt, SB):
+    import torch
+    for t, name in ((A, "A"), (SA, "scale_a"), (Bt, "Bt"), (SB, "scale_b")):
+        if t.dtype != torch.uint8 or t.dim() != 2 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous 2-D uint8 tensor")
+    M, K = A.shape[0], 2 * A.shape[1]
+    N = Bt.shape[0]
+    if Bt.shape[1] != K // 2 or tuple(SA.shape) != (M, K // 32) or tuple(SB.shape) != (N, K // 32):
+        raise ValueError(f"bad shapes A{tuple(A.shape)} scale_a{tuple(SA.shape)} Bt{tuple(Bt.shape)} "
+                         f"scale_b{tuple(SB.shape)}")
+    return M, N, K
+
+
+def gemm_mxfp4(A, SA, Bt, SB, C=None, workspace=None, stream=None):
+    """Block-scaled 4-bit GEMM (sam_gemm_mxfp4): A [M][K/2] and Bt [N][K/2]
+    bytes of packed E2M1 codes (low nibble first), SA [M][K/32] and SB
+    [N][K/32] E8M0 scale codes, all uint8 on the device; returns C [M][N] FP32."""
+    import torch
+    M, N, K = _mx4_operands(A, SA, Bt, SB)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if workspace is None:
+        workspace = workspace_for(plan(M, N, K, MXFP4), A.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sam_gemm_mxfp4(_ptr(A), _ptr(SA), _ptr(Bt), _ptr(SB), _ptr(C), M, N, K, _ptr(workspace), ws_bytes,
+                                _stream_ptr(stream)))
+    return C
+
+
+def gemm_mxfp4_variant(vid: int, A, SA, Bt, SB, C=None, split_k: int = 0, workspace=None, stream=None):
+    """gemm_mxfp4 with a forced variant and split (0 = the variant's pick)."""
+    import torch
+    M, N, K = _mx4_operands(A, SA, Bt, SB)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    p = variant_plan(vid, M, N, K, MXFP4, split_k)
+    if workspace is None:
+        workspace = workspace_for(p, A.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().sam_gemm_mxfp4_variant(vid, p["split_k"], _ptr(A), _ptr(SA), _ptr(Bt), _ptr(SB), _ptr(C), M, N, K,
+                                        _ptr(workspace), ws_bytes, _stream_ptr(stream)))
     return C

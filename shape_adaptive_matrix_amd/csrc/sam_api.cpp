@@ -124,8 +124,11 @@ struct MxExtra {
 sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long long M, long long N,
                long long K, void* ws, unsigned long long ws_bytes, void* stream, const MxExtra* mx = nullptr)
 {
-    const unsigned long long es = p.dtype == sam::DT_F32 ? 4 : (p.dtype == sam::DT_MX8 ? 1 : 2);
-    if ((p.dtype == sam::DT_MX8) != (mx != nullptr)) return fail(SAM_ERR_INTERNAL, "scale arguments mismatch");
+    const bool blockscaled = p.dtype == sam::DT_MX8 || p.dtype == sam::DT_MX4;
+    // Bytes per element (E2M1: counted as one here; the operand sizes below halve it).
+    const unsigned long long es = p.dtype == sam::DT_F32 ? 4 : (blockscaled ? 1 : 2);
+    const unsigned long long half = p.dtype == sam::DT_MX4 ? 2 : 1;
+    if (blockscaled != (mx != nullptr)) return fail(SAM_ERR_INTERNAL, "scale arguments mismatch");
     if (M == 0 || N == 0) return SAM_OK;
     // Kernels address a workgroup's operand panels with 32-bit byte offsets:
     // up to 257 rows of A (K elements each), 129 rows of B and 257 rows of C.
@@ -139,8 +142,8 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
     if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))) || (ws && !aligned16(ws)))
         return fail(SAM_ERR_MISALIGNED, "A, B, C and workspace must be 16-byte aligned");
     const unsigned long long cbytes = (unsigned long long)(M * N) * 4ull;
-    if (ranges_overlap(C, cbytes, A, (unsigned long long)(M * K) * es) ||
-        ranges_overlap(C, cbytes, B, (unsigned long long)(K * N) * es))
+    if (ranges_overlap(C, cbytes, A, (unsigned long long)(M * K) * es / half) ||
+        ranges_overlap(C, cbytes, B, (unsigned long long)(K * N) * es / half))
         return fail(SAM_ERR_INVALID_ARG, "C overlaps A or B");
     if (mx && (ranges_overlap(C, cbytes, mx->sa, (unsigned long long)(M * (K / 32))) ||
                ranges_overlap(C, cbytes, mx->sb, (unsigned long long)(N * (K / 32)))))
@@ -149,8 +152,8 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         if (!ws || ws_bytes < p.ws_bytes)
             return fail(SAM_ERR_WORKSPACE, "plan %d needs %llu workspace bytes, got %llu", p.variant_id,
                         (unsigned long long)p.ws_bytes, (unsigned long long)(ws ? ws_bytes : 0));
-        if (ranges_overlap(C, cbytes, ws, p.ws_bytes) || ranges_overlap(A, (unsigned long long)(M * K) * es, ws, p.ws_bytes) ||
-            ranges_overlap(B, (unsigned long long)(K * N) * es, ws, p.ws_bytes))
+        if (ranges_overlap(C, cbytes, ws, p.ws_bytes) || ranges_overlap(A, (unsigned long long)(M * K) * es / half, ws, p.ws_bytes) ||
+            ranges_overlap(B, (unsigned long long)(K * N) * es / half, ws, p.ws_bytes))
             return fail(SAM_ERR_INVALID_ARG, "workspace overlaps A, B or C");
     }
     sam_status d = device_check_impl();
@@ -333,10 +336,10 @@ sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t 
 sam_status sam_gemm_plan(int64_t M, int64_t N, int64_t K, sam_dtype dtype, sam_plan* out)
 {
     if (!out) return fail(SAM_ERR_INVALID_ARG, "out is null");
-    if (dtype < SAM_F32 || dtype > SAM_MXFP8) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+    if (dtype < SAM_F32 || dtype > SAM_MXFP4) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
     sam_status st = check_shape(M, N, K);
     if (st != SAM_OK) return st;
-    if (dtype == SAM_MXFP8 && K % 32 != 0)
+    if ((dtype == SAM_MXFP8 || dtype == SAM_MXFP4) && K % 32 != 0)
         return fail(SAM_ERR_INVALID_ARG, "block-scaled operands need K %% 32 == 0 (K=%lld)", (long long)K);
     sam::Plan p{};
     if (!sam::plan_auto(M, N, K, dtype, &p)) return fail(SAM_ERR_INTERNAL, "no admissible plan");
@@ -390,7 +393,7 @@ sam_status sam_variant_plan(int32_t id, int64_t M, int64_t N, int64_t K, sam_dty
                             int32_t split_k, sam_plan* out)
 {
     if (!out) return fail(SAM_ERR_INVALID_ARG, "out is null");
-    if (dtype < SAM_F32 || dtype > SAM_MXFP8) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+    if (dtype < SAM_F32 || dtype > SAM_MXFP4) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
     if (split_k < -1) return fail(SAM_ERR_INVALID_ARG, "split %d (-1 is stream-K, 0 the variant's choice)", split_k);
     sam_status st = check_shape(M, N, K);
     if (st != SAM_OK) return st;
@@ -407,8 +410,8 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k, const 
                             float* C, int64_t M, int64_t N, int64_t K, void* workspace,
                             uint64_t workspace_bytes, void* stream)
 {
-    if (dtype == SAM_MXFP8)
-        return fail(SAM_ERR_INVALID_ARG, "block-scaled operands go through sam_gemm_mxfp8_variant");
+    if (dtype == SAM_MXFP8 || dtype == SAM_MXFP4)
+        return fail(SAM_ERR_INVALID_ARG, "block-scaled operands go through sam_gemm_mxfp8_variant / sam_gemm_mxfp4_variant");
     if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
     if (split_k < -1) return fail(SAM_ERR_INVALID_ARG, "split %d (-1 is stream-K, 0 the variant's choice)", split_k);
     sam_status st = check_shape(M, N, K);
@@ -421,12 +424,14 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k, const 
     return run(p, A, B, C, M, N, K, workspace, workspace_bytes, stream);
 }
 
-static sam_status gemm_mxfp8_impl(int32_t id, int32_t split_k, sam_fp8_format fmt_a, sam_fp8_format fmt_b,
-                                  const uint8_t* A, const uint8_t* scale_a, const uint8_t* Bt,
-                                  const uint8_t* scale_b, float* C, int64_t M, int64_t N, int64_t K,
-                                  void* workspace, uint64_t workspace_bytes, void* stream)
+// dtype DT_MX8 (formats fmt_a / fmt_b) or DT_MX4 (E2M1; formats ignored).
+static sam_status gemm_mx_impl(int dtype, int32_t id, int32_t split_k, int fmt_a, int fmt_b, const uint8_t* A,
+                               const uint8_t* scale_a, const uint8_t* Bt, const uint8_t* scale_b, float* C,
+                               int64_t M, int64_t N, int64_t K, void* workspace, uint64_t workspace_bytes,
+                               void* stream)
 {
-    if ((fmt_a != SAM_E4M3 && fmt_a != SAM_E5M2) || (fmt_b != SAM_E4M3 && fmt_b != SAM_E5M2))
+    if (dtype == sam::DT_MX8 &&
+        ((fmt_a != SAM_E4M3 && fmt_a != SAM_E5M2) || (fmt_b != SAM_E4M3 && fmt_b != SAM_E5M2)))
         return fail(SAM_ERR_INVALID_ARG, "element formats must be SAM_E4M3 or SAM_E5M2 (got %d, %d)", (int)fmt_a,
                     (int)fmt_b);
     if (split_k < 0) return fail(SAM_ERR_INVALID_ARG, "split %d (0 is the variant's choice)", split_k);
@@ -436,13 +441,13 @@ static sam_status gemm_mxfp8_impl(int32_t id, int32_t split_k, sam_fp8_format fm
         return fail(SAM_ERR_INVALID_ARG, "block-scaled operands need K %% 32 == 0 (K=%lld)", (long long)K);
     sam::Plan p{};
     if (id < 0) {
-        if (!sam::plan_auto(M, N, K, sam::DT_MX8, &p)) return fail(SAM_ERR_INTERNAL, "no admissible plan");
+        if (!sam::plan_auto(M, N, K, dtype, &p)) return fail(SAM_ERR_INTERNAL, "no admissible plan");
     } else {
         if (!sam::variant_get(id)) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);
-        if (!sam::plan_for_variant(id, M, N, K, sam::DT_MX8, split_k, &p))
+        if (!sam::plan_for_variant(id, M, N, K, dtype, split_k, &p))
             return fail(SAM_ERR_UNSUPPORTED, "variant %d cannot run block-scaled operands with split %d", id, split_k);
     }
-    const MxExtra mx{scale_a, scale_b, (int)fmt_a, (int)fmt_b};
+    const MxExtra mx{scale_a, scale_b, dtype == sam::DT_MX8 ? fmt_a : 4, dtype == sam::DT_MX8 ? fmt_b : 4};
     return run(p, A, Bt, C, M, N, K, workspace, workspace_bytes, stream, &mx);
 }
 
@@ -450,8 +455,8 @@ sam_status sam_gemm_mxfp8(sam_fp8_format fmt_a, sam_fp8_format fmt_b, const uint
                           const uint8_t* Bt, const uint8_t* scale_b, float* C, int64_t M, int64_t N, int64_t K,
                           void* workspace, uint64_t workspace_bytes, void* stream)
 {
-    return gemm_mxfp8_impl(-1, 0, fmt_a, fmt_b, A, scale_a, Bt, scale_b, C, M, N, K, workspace, workspace_bytes,
-                           stream);
+    return gemm_mx_impl(sam::DT_MX8, -1, 0, fmt_a, fmt_b, A, scale_a, Bt, scale_b, C, M, N, K, workspace,
+                        workspace_bytes, stream);
 }
 
 sam_status sam_gemm_mxfp8_variant(int32_t id, int32_t split_k, sam_fp8_format fmt_a, sam_fp8_format fmt_b,
@@ -460,8 +465,25 @@ sam_status sam_gemm_mxfp8_variant(int32_t id, int32_t split_k, sam_fp8_format fm
                                   void* workspace, uint64_t workspace_bytes, void* stream)
 {
     if (id < 0) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);
-    return gemm_mxfp8_impl(id, split_k, fmt_a, fmt_b, A, scale_a, Bt, scale_b, C, M, N, K, workspace,
-                           workspace_bytes, stream);
+    return gemm_mx_impl(sam::DT_MX8, id, split_k, fmt_a, fmt_b, A, scale_a, Bt, scale_b, C, M, N, K, workspace,
+                        workspace_bytes, stream);
+}
+
+sam_status sam_gemm_mxfp4(const uint8_t* A, const uint8_t* scale_a, const uint8_t* Bt, const uint8_t* scale_b,
+                          float* C, int64_t M, int64_t N, int64_t K, void* workspace, uint64_t workspace_bytes,
+                          void* stream)
+{
+    return gemm_mx_impl(sam::DT_MX4, -1, 0, 0, 0, A, scale_a, Bt, scale_b, C, M, N, K, workspace, workspace_bytes,
+                        stream);
+}
+
+sam_status sam_gemm_mxfp4_variant(int32_t id, int32_t split_k, const uint8_t* A, const uint8_t* scale_a,
+                                  const uint8_t* Bt, const uint8_t* scale_b, float* C, int64_t M, int64_t N,
+                                  int64_t K, void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    if (id < 0) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);
+    return gemm_mx_impl(sam::DT_MX4, id, split_k, 0, 0, A, scale_a, Bt, scale_b, C, M, N, K, workspace,
+                        workspace_bytes, stream);
 }
 
 sam_status sam_device_check(void) { return device_check_impl(); }

@@ -6,8 +6,9 @@
 
 namespace sam {
 
-// DT_MX8: block-scaled 8-bit elements (E4M3 / E5M2 with E8M0 scales per 32 of K).
-enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_MX8 = 3 };
+// DT_MX8: block-scaled 8-bit elements (E4M3 / E5M2 with E8M0 scales per 32 of K);
+// DT_MX4: block-scaled E2M1 elements, two per byte.
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_MX8 = 3, DT_MX4 = 4 };
 
 // Fixed facts of one MI355X (gfx950) used by the cost model. They are frozen
 // here rather than queried so that a plan is a pure function of the shape.
@@ -19,6 +20,7 @@ struct DeviceModel {
     double f32_flop_per_clk_cu = 256.0;    // 4 SIMDs x 64 (32x32x2 f32 in 64 clk)
     double h16_flop_per_clk_cu = 4096.0;   // 4 SIMDs x 1024
     double mx8_flop_per_clk_cu = 8192.0;   // 4 SIMDs x 2048 (32x32x64 8-bit in 64 clk)
+    double mx4_flop_per_clk_cu = 16384.0;  // 4 SIMDs x 4096 (32x32x64 4-bit in 32 clk)
     double hbm_gbs = 5900.0;       // measured streaming read rate
     double tiled_hbm_frac = 0.75;  // share of it the LDS-tiled kernels reach when HBM-bound (calibrated)
     double hbm_write_gbs = 6000.0; // rate the epilogue write phase drains at (calibrated)
@@ -48,6 +50,7 @@ struct Variant {
                          // (streaming variants: fraction of the HBM read rate)
     double eff_h16;
     double eff_mx8;      // block-scaled 8-bit variants
+    double eff_mx4;      // ... running E2M1 elements
 };
 
 int variant_count();

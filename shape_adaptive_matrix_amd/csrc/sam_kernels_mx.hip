@@ -54,7 +54,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef unsigned u8v __attribute__((ext_vector_type(8)));
 
-template <int FA, int FB, int BM, int BN, int WM, int WN, int BK, bool SDMA>
+// EB: element bits, 8 (FA, FB: 0 E4M3, 1 E5M2) or 4 (FA = FB = 4, E2M1 packed
+// two per byte, element 2 i in the low nibble). BK counts values of K.
+template <int FA, int FB, int BM, int BN, int WM, int WN, int BK, bool SDMA, int EB>
 __global__ void __launch_bounds__(WM * WN * 64)
 __attribute__((amdgpu_waves_per_eu(1, (160 * 1024 / (2 * (BM + BN) * (BK + 8))) * WM * WN / 4 > 0
                                            ? (160 * 1024 / (2 * (BM + BN) * (BK + 8))) * WM * WN / 4 : 1)))
@@ -65,7 +67,9 @@ gemm_mx8_kernel(GemmArgs args)
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int ROW = BK;                            // bytes per LDS row (one code per K value)
+    constexpr int ROW = BK * EB / 8;                   // bytes per LDS row
+    constexpr int VPC = 128 / EB;                      // values of K per 16-byte chunk
+    constexpr int RPB = EB == 8 ? 2 : 1;               // 128-bit LDS reads per MFMA operand block
     constexpr int CPR = ROW / 16;                      // 16-byte chunks per row
     constexpr int RPL = 64 / CPR;                      // rows per 1 KB wave load
     constexpr int RSW = CPR >= 16 ? 1 : 16 / CPR;      // rows sharing one 256-byte bank sweep
@@ -80,7 +84,9 @@ gemm_mx8_kernel(GemmArgs args)
     constexpr int LPS = A_PW + B_PW + SPW;             // wave loads per stage (a wave may skip its last)
     constexpr int NSB = TM + TN;                       // MFMA blocks whose scales a lane uses
     constexpr int NSR = SDMA ? SDW : KSTEPS;           // raw scale registers per block
-    static_assert(BK == 128 || BK == 256, "K per stage: 128- or 256-byte rows");
+    static_assert(EB == 8 || (EB == 4 && FA == 4 && FB == 4), "8-bit formats or E2M1");
+    static_assert(ROW == 128 || ROW == 256, "K per stage: 128- or 256-byte rows");
+    static_assert(BK % 128 == 0, "whole scale dwords per stage");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "loads must split evenly over waves");
     static_assert(NBUF * STAGE <= 160 * 1024, "LDS");
@@ -97,6 +103,7 @@ gemm_mx8_kernel(GemmArgs args)
     tile_coords(blockIdx.x, args, tm, tn, s);
     const int M = args.M, N = args.N, K = args.K;
     const int KB = K / 32;                             // scale codes per row
+    const int RB = K * EB / 8;                         // bytes per operand row
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = s * args.k_chunk;
     const int kend = min(K, kbeg + args.k_chunk);
@@ -104,8 +111,8 @@ gemm_mx8_kernel(GemmArgs args)
     const int wm0 = (wave / WN) * WTM;
     const int wn0 = (wave % WN) * WTN;
 
-    const i4 rA = rsrc_words(static_cast<const char*>(args.A) + (long long)m0 * K, (long long)(M - m0) * K);
-    const i4 rB = rsrc_words(static_cast<const char*>(args.B) + (long long)n0 * K, (long long)(N - n0) * K);
+    const i4 rA = rsrc_words(static_cast<const char*>(args.A) + (long long)m0 * RB, (long long)(M - m0) * RB);
+    const i4 rB = rsrc_words(static_cast<const char*>(args.B) + (long long)n0 * RB, (long long)(N - n0) * RB);
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(args.sa + (long long)m0 * KB, (long long)(M - m0) * KB);
     const __amdgpu_buffer_rsrc_t rSB = make_rsrc(args.sb + (long long)n0 * KB, (long long)(N - n0) * KB);
     const i4 rSAw = rsrc_words(args.sa + (long long)m0 * KB, (long long)(M - m0) * KB);
@@ -141,8 +148,8 @@ gemm_mx8_kernel(GemmArgs args)
         const int I = wave + (is_a ? q : q - A_PW) * NW;
         const int row = I * RPL + lane / CPR;
         const int c = (lane % CPR) ^ ((row / RSW) % CPR);
-        const int gk = k0 + c * 16;
-        const int off = gk < kend ? row * K + gk : kOOB;
+        const int gk = k0 + c * VPC;                   // first value of K in the chunk
+        const int off = gk < kend ? row * RB + gk * EB / 8 : kOOB;
         if (is_a)
             lds_load16(rA, lds_addr(buf + I * 1024), off);
         else
@@ -183,22 +190,27 @@ gemm_mx8_kernel(GemmArgs args)
             sn[b][d] = *reinterpret_cast<const unsigned*>(buf + A_BYTES + B_BYTES + (d * (BM + BN) + r) * 4);
     };
 
-    // Fragment reads, one 128-bit LDS read each: read r < 2 TM is half r & 1
-    // of A block r >> 1, the rest halves of Bt blocks. Half h of A block i in
-    // k-step t: row wm0 + 32 i + (lane & 31), K 64 t + 32 h + 16 (lane >> 5)
-    // .. + 15 of the stage, i.e. logical chunk 4 t + 2 h + (lane >> 5).
+    // Fragment reads, one 128-bit LDS read each; RPB per MFMA block: read
+    // r < RPB TM is part r % RPB of A block r / RPB, the rest parts of Bt
+    // blocks. A block i of k-step t sits in row wm0 + 32 i + (lane & 31).
+    //  8-bit: half h holds K 64 t + 32 h + 16 (lane >> 5) .. + 15 of the
+    //  stage (logical chunk 4 t + 2 h + (lane >> 5)), registers 4 h .. 4 h + 3:
+    //  the instruction's scale block h is the h halves of both lane groups.
+    //  4-bit: the lane holds K 64 t + 32 (lane >> 5) .. + 31 (logical chunk
+    //  2 t + (lane >> 5)) in registers 0..3 (4..7 stay zero): for E2M1 the
+    //  instruction applies lane group g's scale to all of lane group g's
+    //  values, so each lane's share is exactly one MX block. (Both layouts
+    //  were established with one-hot operands and distinct block scales.)
     auto read_one = [&](const unsigned char* buf, int t, int r, u8v (&fa)[TM], u8v (&fb)[TN]) {
-        const bool is_a = r < 2 * TM;
-        const int blk = is_a ? (r >> 1) : ((r - 2 * TM) >> 1);
-        const int h = r & 1;
+        const bool is_a = r < RPB * TM;
+        const int blk = is_a ? r / RPB : (r - RPB * TM) / RPB;
+        const int h = r % RPB;
         const int row = (is_a ? wm0 : wn0) + 32 * blk + (lane & 31);
-        const int c = (4 * t + 2 * h + (lane >> 5)) ^ ((row / RSW) % CPR);
+        u8v& f = is_a ? fa[blk] : fb[blk];
+        const int lc = EB == 8 ? 4 * t + 2 * h + (lane >> 5) : 2 * t + (lane >> 5);
+        const int c = lc ^ ((row / RSW) % CPR);
         const u4 v = *reinterpret_cast<const u4*>(buf + (is_a ? 0 : A_BYTES) + row * ROW + c * 16);
-        if (is_a) {
-            if (h) fa[blk].hi = v; else fa[blk].lo = v;
-        } else {
-            if (h) fb[blk].hi = v; else fb[blk].lo = v;
-        }
+        if (h) f.hi = v; else f.lo = v;
     };
 
     v16f acc[TM][TN];
@@ -210,9 +222,9 @@ gemm_mx8_kernel(GemmArgs args)
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     constexpr int NMF = TM * TN;                  // MFMAs per k-step
-    constexpr int NRB = 2 * TN;                   // LDS reads of Bt fragments per k-step
+    constexpr int NRB = RPB * TN;                 // LDS reads of Bt fragments per k-step
     constexpr int RPS = (NRB + NMF - 1) / NMF;    // ... per MFMA slot
-    constexpr int NRD = 2 * (TM + TN);            // all fragment reads of a k-step
+    constexpr int NRD = RPB * (TM + TN);          // all fragment reads of a k-step
 
     // One k-step: slot m issues MFMA m (A block m / TN, Bt block m % TN),
     // then the next k-step's Bt reads m * RPS .. (into the other Bt set),
@@ -243,10 +255,10 @@ gemm_mx8_kernel(GemmArgs args)
             }
 #pragma unroll
             for (int r = m * RPS; r < (m + 1) * RPS; ++r)
-                if (r < NRB) read_one(rbuf, rt, 2 * TM + r, fa, nb);
+                if (r < NRB) read_one(rbuf, rt, RPB * TM + r, fa, nb);
             if (j == TN - 1) {
-                read_one(rbuf, rt, 2 * i, fa, nb);
-                read_one(rbuf, rt, 2 * i + 1, fa, nb);
+#pragma unroll
+                for (int h = 0; h < RPB; ++h) read_one(rbuf, rt, RPB * i + h, fa, nb);
             }
             if (load_stage >= 0) {
 #pragma unroll
@@ -274,6 +286,12 @@ gemm_mx8_kernel(GemmArgs args)
     };
 
     u8v fa[TM], fb[2][TN];
+    if constexpr (EB == 4) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i].hi = u4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[0][j].hi = fb[1][j].hi = u4{0, 0, 0, 0};
+    }
     // Stage 0 and its scales, drained completely (so that no scale load is
     // still counted as pending when the loop starts), then stage 1.
     if constexpr (!SDMA) {
@@ -339,15 +357,19 @@ typedef void (*KernelFn)(GemmArgs);
 
 struct Mx8Kernels {
     int id;
-    KernelFn fn[2][2][2];   // [scales through LDS][format of A][format of B]: 0 E4M3, 1 E5M2
+    KernelFn fn[2][2][2];   // 8-bit: [scales through LDS][format of A][format of B]: 0 E4M3, 1 E5M2
+    KernelFn fn4[2];        // E2M1: [scales through LDS]
     int threads;
 };
 
-#define SAM_MX8_FORMS(BM, BN, WM, WN, BK, SD)                                                             \
-    {{gemm_mx8_kernel<0, 0, BM, BN, WM, WN, BK, SD>, gemm_mx8_kernel<0, 1, BM, BN, WM, WN, BK, SD>},      \
-     {gemm_mx8_kernel<1, 0, BM, BN, WM, WN, BK, SD>, gemm_mx8_kernel<1, 1, BM, BN, WM, WN, BK, SD>}}
-#define SAM_MX8_ENTRY(id, name, BM, BN, WM, WN, BK, SD, gm, xr, ms, e8) \
-    {id, {SAM_MX8_FORMS(BM, BN, WM, WN, BK, false), SAM_MX8_FORMS(BM, BN, WM, WN, BK, SD != 0)}, WM * WN * 64},
+#define SAM_MX8_FORMS(BM, BN, WM, WN, BK, SD)                                                                   \
+    {{gemm_mx8_kernel<0, 0, BM, BN, WM, WN, BK, SD, 8>, gemm_mx8_kernel<0, 1, BM, BN, WM, WN, BK, SD, 8>},      \
+     {gemm_mx8_kernel<1, 0, BM, BN, WM, WN, BK, SD, 8>, gemm_mx8_kernel<1, 1, BM, BN, WM, WN, BK, SD, 8>}}
+// The E2M1 form runs twice the values of K per stage (same 128-byte rows).
+#define SAM_MX8_ENTRY(id, name, BM, BN, WM, WN, BK, SD, gm, xr, ms, e8, e4)                                  \
+    {id, {SAM_MX8_FORMS(BM, BN, WM, WN, BK, false), SAM_MX8_FORMS(BM, BN, WM, WN, BK, SD != 0)},               \
+     {gemm_mx8_kernel<4, 4, BM, BN, WM, WN, 2 * BK, false, 4>, gemm_mx8_kernel<4, 4, BM, BN, WM, WN, 2 * BK, SD != 0, 4>}, \
+     WM * WN * 64},
 
 const Mx8Kernels kMx8Table[] = {SAM_MX8_VARIANTS(SAM_MX8_ENTRY)};
 
@@ -355,11 +377,14 @@ const Mx8Kernels kMx8Table[] = {SAM_MX8_VARIANTS(SAM_MX8_ENTRY)};
 
 hipError_t launch_mx8(const Plan& p, const GemmArgs& a, hipStream_t s)
 {
-    if (a.fmt_a < 0 || a.fmt_a > 1 || a.fmt_b < 0 || a.fmt_b > 1) return hipErrorInvalidValue;
+    const bool fp4 = p.dtype == DT_MX4;
+    if (!fp4 && (a.fmt_a < 0 || a.fmt_a > 1 || a.fmt_b < 0 || a.fmt_b > 1)) return hipErrorInvalidValue;
     for (const Mx8Kernels& d : kMx8Table) {
         if (d.id != p.variant_id) continue;
         // The scale dwords are 4-byte aligned when K % 128 == 0.
-        hipLaunchKernelGGL(d.fn[a.K % 128 == 0][a.fmt_a][a.fmt_b], dim3((unsigned)p.grid), dim3(d.threads), 0, s, a);
+        const int sd = a.K % 128 == 0;
+        KernelFn fn = fp4 ? d.fn4[sd] : d.fn[sd][a.fmt_a][a.fmt_b];
+        hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(d.threads), 0, s, a);
         return hipGetLastError();
     }
     return hipErrorInvalidDeviceFunction;

@@ -48,8 +48,8 @@ namespace sam {
 #define SAM_F32RING_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32) \
     {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, BLK, NBUF, BK, gm, xr, ms, EL, e32, 0.0},
 
-#define SAM_MX8_ROW(id, name, BM, BN, WM, WN, BK, SD, gm, xr, ms, e8) \
-    {id, name, KIND_MX8, (1 << DT_MX8), BM, BN, WM, WN, 32, 2, BK, gm, xr, ms, 0, 0.0, 0.0, e8},
+#define SAM_MX8_ROW(id, name, BM, BN, WM, WN, BK, SD, gm, xr, ms, e8, e4) \
+    {id, name, KIND_MX8, (1 << DT_MX8) | (1 << DT_MX4), BM, BN, WM, WN, 32, 2, BK, gm, xr, ms, 0, 0.0, 0.0, e8, e4},
 
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
                                         SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)
@@ -66,13 +66,17 @@ const Variant* variant_get(int id)
 
 int k_stage(const Variant& v, int dtype)
 {
+    if (v.kind == KIND_MX8 && dtype == DT_MX4) return 2 * v.bk;   // E2M1: twice the values per LDS row
     if (v.kind != KIND_STAGED) return v.bk;
     return dtype == DT_F32 ? 32 : 64;   // one 128-byte LDS row
 }
 
-static int vec_elems(int dtype) { return dtype == DT_F32 ? 4 : (dtype == DT_MX8 ? 16 : 8); }
+static int vec_elems(int dtype) { return dtype == DT_F32 ? 4 : (dtype == DT_MX8 ? 16 : (dtype == DT_MX4 ? 32 : 8)); }
 
-static double in_bytes(int dtype) { return dtype == DT_F32 ? 4.0 : (dtype == DT_MX8 ? 1.0 : 2.0); }
+static double in_bytes(int dtype)
+{
+    return dtype == DT_F32 ? 4.0 : (dtype == DT_MX8 ? 1.0 : (dtype == DT_MX4 ? 0.5 : 2.0));
+}
 
 static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
@@ -101,12 +105,15 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
         return t;
     }
 
-    double eff = dtype == DT_F32 ? v.eff_f32 : (dtype == DT_MX8 ? v.eff_mx8 : v.eff_h16);
+    double eff = dtype == DT_F32 ? v.eff_f32
+                 : dtype == DT_MX8 ? v.eff_mx8
+                 : dtype == DT_MX4 ? v.eff_mx4 : v.eff_h16;
     if (!a_vec) eff *= 0.85;
     if (!b_vec) eff *= 0.85;
-    const double peak_cu = (dtype == DT_F32 ? kDev.f32_flop_per_clk_cu
-                                            : (dtype == DT_MX8 ? kDev.mx8_flop_per_clk_cu : kDev.h16_flop_per_clk_cu)) *
-                           kDev.clock_ghz * 1e3;              // FLOP per microsecond
+    const double flop_clk = dtype == DT_F32 ? kDev.f32_flop_per_clk_cu
+                            : dtype == DT_MX8 ? kDev.mx8_flop_per_clk_cu
+                            : dtype == DT_MX4 ? kDev.mx4_flop_per_clk_cu : kDev.h16_flop_per_clk_cu;
+    const double peak_cu = flop_clk * kDev.clock_ghz * 1e3;   // FLOP per microsecond
     const double t_wg = 2.0 * v.bm * v.bn * (double)kc / (peak_cu * eff);
     const double rounds = (double)cdiv(wgs, kDev.cus);
     // Every workgroup ends by writing its BM x BN FP32 tile (to C or to its
@@ -231,7 +238,7 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
                       Plan* out)
 {
     const Variant* v = variant_get(vid);
-    if (!v || dtype < DT_F32 || dtype > DT_MX8 || !(v->dtype_mask & (1 << dtype))) return false;
+    if (!v || dtype < DT_F32 || dtype > DT_MX4 || !(v->dtype_mask & (1 << dtype))) return false;
     if (M < 0 || N < 0 || K < 0) return false;
     // Block-scaled operands come in whole blocks of 32 values of K.
     if (v->kind == KIND_MX8 && K % 32 != 0) return false;
@@ -316,7 +323,7 @@ bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out)
 
 void plan_name(const Plan& p, char* buf, int n)
 {
-    static const char* dt[] = {"f32", "bf16", "f16", "mxfp8"};
+    static const char* dt[] = {"f32", "bf16", "f16", "mxfp8", "mxfp4"};
     const Variant* v = variant_get(p.variant_id);
     char sp[16];
     if (p.sk)

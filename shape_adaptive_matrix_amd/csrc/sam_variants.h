@@ -23,12 +23,7 @@
 // edge, 32 (32x32x2) or 16 (16x16x4, names "...b16"); EL = 1: the variant
 // also has an element-load form for K or N not a multiple of 4.
 //   F(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, group_m, xcd_remap, max_split, eff_f32)
-// Block-scaled 8-bit variants (sam_kernels_mx.hip): E4M3 / E5M2 elements
-// with E8M0 scales per 32 values of K, both operands K-contiguous, K % 32 ==
-// 0; a ring of two LDS stages of BK values of K. SD = 1: with K % 128 == 0
-// the scales travel through LDS with the operands (SD = 0, or other K: each
-// lane loads its own scale bytes).
-//   M8(id, name, BM, BN, WM, WN, BK, SD, group_m, xcd_remap, max_split, eff_mx8)
+// Block-scaled variants (ids 40..): sam_variants_mx.h.
 // eff_* is the fraction of the MFMA peak the variant sustains in steady
 // state, the calibration the cost model uses.
 #pragma once
@@ -81,9 +76,4 @@
     F(38, "f128x128_w4x2_k32n2_b16",   128, 128, 4, 2, 32, 2, 4, 1, 16, 1, 8, 1, 16, 0.88)   \
     F(39, "f128x128_w4x2_k32n2",       128, 128, 4, 2, 32, 2, 2, 1, 32, 1, 8, 1, 16, 0.87)
 
-#define SAM_MX8_VARIANTS(M8)                                                             \
-    M8(40, "x256x256_w2x2_k128", 256, 256, 2, 2, 128, 1, 8, 1,  8, 0.44)                 \
-    M8(41, "x256x128_w4x2_k128", 256, 128, 4, 2, 128, 1, 8, 1,  8, 0.30)                 \
-    M8(42, "x128x128_w2x2_k128", 128, 128, 2, 2, 128, 1, 8, 1, 16, 0.33)                 \
-    M8(43, "x128x128_w2x2_k256", 128, 128, 2, 2, 256, 1, 8, 1, 16, 0.28)                 \
-    M8(44, "x128x256_w2x4_k128", 128, 256, 2, 4, 128, 1, 8, 1,  8, 0.28)
+#include "sam_variants_mx.h"

@@ -40,10 +40,10 @@ __global__ void __launch_bounds__(256) mfma_loop(float* out, int iters, float se
     for (int i = 0; i < 8; ++i)
         av[i] = u4{__float_as_uint(x + i), __float_as_uint(x + 2 * i), __float_as_uint(x - i), __float_as_uint(x * i)};
     const u4 bv = {__float_as_uint(x), __float_as_uint(x + 1), __float_as_uint(x + 2), __float_as_uint(x + 3)};
-    // KIND 5: the block-scaled 8-bit 32x32x64 MFMA (E4M3 operands) with
+    // KIND 5 / 6: the block-scaled 32x32x64 MFMA with E4M3 / E2M1 operands and
     // per-lane scales in registers.
     const int sc = 120 + (threadIdx.x & 7);
-    if constexpr (KIND == 0 || KIND == 2 || KIND == 3 || KIND == 5) {   // 32x32 blocks: 16 acc regs
+    if constexpr (KIND == 0 || KIND == 2 || KIND == 3 || KIND == 5 || KIND == 6) {   // 32x32 blocks: 16 acc regs
         v16f acc[8];
         for (int i = 0; i < 8; ++i) for (int r = 0; r < 16; ++r) acc[i][r] = (float)(i * 16 + r);
         for (int it = 0; it < iters; ++it) {
@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(256) mfma_loop(float* out, int iters, float se
                     acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         __builtin_bit_cast(v8i, __builtin_shufflevector(av[i], bv, 0, 1, 2, 3, 4, 5, 6, 7)),
                         __builtin_bit_cast(v8i, __builtin_shufflevector(bv, av[i], 0, 1, 2, 3, 4, 5, 6, 7)), acc[i],
-                        0, 0, 0, sc, 0, sc + 1);
+                        KIND == 6 ? 4 : 0, KIND == 6 ? 4 : 0, 0, sc, 0, sc + 1);
             }
             asm volatile("" ::: "memory");
         }
@@ -124,9 +124,10 @@ int main(int argc, char** argv)
     struct { int kind; const char* name; double flops; } kinds[] = {
         {0, "f32_32x32x2", 32.0 * 32 * 2 * 2}, {1, "f32_16x16x4", 16.0 * 16 * 4 * 2},
         {2, "bf16_32x32x16", 32.0 * 32 * 16 * 2}, {3, "f16_32x32x16", 32.0 * 32 * 16 * 2},
-        {4, "bf16_16x16x32", 16.0 * 16 * 32 * 2}, {5, "mxfp8_32x32x64", 32.0 * 32 * 64 * 2}};
+        {4, "bf16_16x16x32", 16.0 * 16 * 32 * 2}, {5, "mxfp8_32x32x64", 32.0 * 32 * 64 * 2},
+        {6, "mxfp4_32x32x64", 32.0 * 32 * 64 * 2}};
     printf("{\"device\": \"%s\", \"cus\": %d, \"clock_khz\": %d, \"mfma\": {", prop.gcnArchName, cus, prop.clockRate);
-    for (int k = 0; k < 6; ++k) {
+    for (int k = 0; k < 7; ++k) {
         const int iters = kinds[k].kind <= 1 ? 2000 : 8000;
         for (int rep = 0; rep < 2; ++rep) {   // first pass warms the clocks
             CHECK(hipEventRecord(e0, 0));
@@ -136,7 +137,8 @@ int main(int argc, char** argv)
             case 2: hipLaunchKernelGGL(mfma_loop<2>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
             case 3: hipLaunchKernelGGL(mfma_loop<3>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
             case 4: hipLaunchKernelGGL(mfma_loop<4>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
-            default: hipLaunchKernelGGL(mfma_loop<5>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
+            case 5: hipLaunchKernelGGL(mfma_loop<5>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
+            default: hipLaunchKernelGGL(mfma_loop<6>, dim3(wgs), dim3(256), 0, 0, out, iters, 1.0f); break;
             }
             CHECK(hipGetLastError());
             CHECK(hipEventRecord(e1, 0));

@@ -28,7 +28,7 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 TUNED_H = PKG / "csrc" / "sam_tuned.h"
-DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "mxfp8": 3}
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2, "mxfp8": 3, "mxfp4": 4}
 
 # Shapes beyond the named workloads: square sizes between and around them,
 # K-heavy and K-light rectangles, skinny-ish panels, and the LLM-like shapes
@@ -43,6 +43,7 @@ EXTRA = {
     "f16": [(2048, 2048, 2048), (6144, 6144, 6144), (4096, 4096, 11008)],
     "mxfp8": [(2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144), (4096, 4096, 1024),
               (256, 11008, 4096), (4096, 4096, 11008), (2048, 8192, 2048)],
+    "mxfp4": [(2048, 2048, 2048), (6144, 6144, 6144), (4096, 4096, 11008), (256, 11008, 4096)],
 }
 
 SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
@@ -51,7 +52,7 @@ SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
 def shapes():
     import sam_inputs as si
     out = [(w.dtype, w.M, w.N, w.K, w.name) for w in si.WORKLOADS + si.MX_WORKLOADS
-           if (w.fmt_a, w.fmt_b) == ("e4m3", "e4m3")]
+           if (w.fmt_a, w.fmt_b) in (("e4m3", "e4m3"), ("e2m1", "e2m1"))]
     seen = {(d, m, n, k) for d, m, n, k, _ in out}
     for dt, lst in EXTRA.items():
         for (m, n, k) in lst:
@@ -121,9 +122,10 @@ def measure(record: Path, only=None):
         for (dt, M, N, K, name) in shapes():
             if only and name not in only:
                 continue
-            dist = {"f32": "uniform", "mxfp8": "mx_normal"}.get(dt, "normal16")
-            w = si.Workload(name, dt, M, N, K, dist, 77)
-            if dt == "mxfp8":
+            dist = {"f32": "uniform", "mxfp8": "mx_normal", "mxfp4": "mx_normal"}.get(dt, "normal16")
+            fmt = "e2m1" if dt == "mxfp4" else "e4m3"
+            w = si.Workload(name, dt, M, N, K, dist, 77, fmt_a=fmt, fmt_b=fmt)
+            if dt in ("mxfp8", "mxfp4"):
                 mx = [torch.from_numpy(x).cuda() for x in si.make_mx_operands(w)]
                 dA = mx[0]
             elif dt == "f32":
@@ -148,6 +150,9 @@ def measure(record: Path, only=None):
                 if dt == "mxfp8":   # E4M3 operands, scales as drawn
                     fn = sam.lib().sam_gemm_mxfp8_variant
                     args = (vid, split, 0, 0, *(ctypes.c_void_p(x.data_ptr()) for x in mx), *tail)
+                elif dt == "mxfp4":
+                    fn = sam.lib().sam_gemm_mxfp4_variant
+                    args = (vid, split, *(ctypes.c_void_p(x.data_ptr()) for x in mx), *tail)
                 else:
                     fn = sam.lib().sam_gemm_variant
                     args = (vid, sam.DTYPES[dt], split, ctypes.c_void_p(dA.data_ptr()), ctypes.c_void_p(dB.data_ptr()),
@@ -179,7 +184,7 @@ def measure(record: Path, only=None):
                 f.flush()
                 del ws
             del dA, C
-            if dt == "mxfp8":
+            if dt in ("mxfp8", "mxfp4"):
                 del mx
             else:
                 del dB

@@ -229,3 +229,21 @@ def test_mxfp8_plans_and_rejections_before_any_device_call():
     assert g(vid, -1, 0, 0, vp(A_), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -1
     assert g(0, 0, 0, 0, vp(A_), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -4   # not MX
     assert L.sam_gemm_variant(vid, sam.MXFP8, 0, vp(A_), vp(B_), vp(C_), 64, 64, 64, None, 0, None) == -1
+
+
+def test_mxfp4_plans_and_rejections():
+    """E2M1 plans come from the block-scaled variants with twice the values of
+    K per stage; K % 32 != 0 and the plain forced-variant entry point are
+    refused on the host."""
+    p8 = sam.plan(4096, 4096, 4096, "mxfp8")
+    p4 = sam.plan(4096, 4096, 4096, "mxfp4")
+    assert p4["name"].startswith("mxfp4_x") and p4["dtype"] == sam.MXFP4
+    assert sam.variant_plan(p8["variant_id"], 4096, 4096, 4096, "mxfp4", 1)["tile_k"] == 2 * p8["tile_k"]
+    with pytest.raises(sam.SamError):
+        sam.plan(64, 64, 48, "mxfp4")
+    vp = ctypes.c_void_p
+    A_, SA_, B_, SB_, C_ = 1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20
+    assert L.sam_gemm_mxfp4(vp(A_), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 48, None, 0, None) == -1
+    assert L.sam_gemm_mxfp4(vp(A_), None, vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -1
+    assert L.sam_gemm_mxfp4_variant(0, 0, vp(A_), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -4
+    assert L.sam_gemm_variant(p4["variant_id"], sam.MXFP4, 0, vp(A_), vp(B_), vp(C_), 64, 64, 64, None, 0, None) == -1

@@ -36,7 +36,7 @@ def test_table_covers_every_measured_shape():
 @pytest.mark.parametrize("row", _entries())
 def test_tuned_plan_is_returned(row):
     dt, M, N, K, vid, split = row
-    dtype = {0: "f32", 1: "bf16", 2: "f16", 3: "mxfp8"}[dt]
+    dtype = {0: "f32", 1: "bf16", 2: "f16", 3: "mxfp8", 4: "mxfp4"}[dt]
     p = sam.plan(M, N, K, dtype)
     assert (p["variant_id"], p["split_k"]) == (vid, split)
     assert p["name"].endswith("_tuned")
