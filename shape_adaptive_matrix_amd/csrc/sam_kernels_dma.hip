@@ -19,7 +19,11 @@
 //    within each 16-lane group, lane d receives, for k = kbase..kbase+3,
 //    the value at column (4 (source lane % 4) + d % 4) of the row that source
 //    lane 4 i + d / 4 points at. Two such loads give the eight consecutive K
-//    values of one column that the 32x32x16 MFMA takes per lane.
+//    values of one column that the MFMA takes per lane.
+//  * Two MFMA block shapes: 32x32x16 and 16x16x32. Both read the same bytes
+//    of LDS per FLOP; the 16x16 form issues twice the MFMAs of half the
+//    length and sustains about 7% more of the matrix peak on gfx950, at the
+//    cost of twice the fragment registers per k-step.
 //  * One barrier per stage, placed between the stage's two MFMA k-steps:
 //    before it every wave has finished reading the stage (so its buffer can
 //    be refilled) and has seen its own loads of the next stage land; after
@@ -33,6 +37,7 @@
 
 namespace sam {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -51,13 +56,33 @@ __device__ __forceinline__ unsigned pack_halves(unsigned x, unsigned y) {
     return __builtin_amdgcn_perm(y, x, H ? 0x07060302u : 0x05040100u);
 }
 
-template <int DT>
-__device__ __forceinline__ void mfma(v16f& c, const u4& a, const u4& b) {
-    if constexpr (DT == DT_BF16)
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
-    else
-        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
-}
+// The two MFMA block shapes. BLK 32: 32x32x16, lane l holds K values
+// 8 (l / 32) .. +7 of row / column l % 32, and accumulator value r is row
+// 8 (r / 4) + 4 (l / 32) + r % 4. BLK 16: 16x16x32, lane l holds K values
+// 8 (l / 16) .. +7 of row / column l % 16, and value r is row 4 (l / 16) + r.
+template <int DT, int BLK> struct Mf;
+template <int DT> struct Mf<DT, 32> {
+    typedef v16f T;
+    static constexpr int KSTEP = 16, NV = 16;
+    static __device__ __forceinline__ void mfma(T& c, const u4& a, const u4& b) {
+        if constexpr (DT == DT_BF16)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int lane, int r) { return ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3); }
+};
+template <int DT> struct Mf<DT, 16> {
+    typedef v4f T;
+    static constexpr int KSTEP = 32, NV = 4;
+    static __device__ __forceinline__ void mfma(T& c, const u4& a, const u4& b) {
+        if constexpr (DT == DT_BF16)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int lane, int r) { return ((lane >> 4) << 2) + r; }
+};
 
 }  // namespace dma
 
@@ -70,7 +95,7 @@ __device__ __forceinline__ void mfma(v16f& c, const u4& a, const u4& b) {
 //         transposed there (one v_perm per output dword) and stored
 //         K-contiguous, so its fragments are full-rate 128-bit LDS reads
 //         instead of half-rate transposing reads.
-template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE>
+template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK>
 __global__ void __launch_bounds__(WM * WN * 64)
 __attribute__((amdgpu_waves_per_eu(1, (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 > 0
                                            ? (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 : 1)))
@@ -81,12 +106,13 @@ gemm16_dma_kernel(GemmArgs args)
     static_assert(BK == 32 || BK == 64, "K per stage: 64- or 128-byte A rows");
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
+    typedef Mf<DT, BLK> MF;
+    constexpr int TM = WTM / BLK, TN = WTN / BLK;
     constexpr int A_ROW = BK * 2;              // bytes per A row in LDS
     constexpr int CPA = A_ROW / 16;            // 16-byte chunks per A row
     constexpr int RPA = 64 / CPA;              // A rows per wave load
     constexpr int RSW = 16 / CPA;              // A rows sharing one 256-byte bank sweep
-    constexpr int KSTEPS = BK / 16;            // MFMA k-steps per stage
+    constexpr int KSTEPS = BK / MF::KSTEP;     // MFMA k-steps per stage
     constexpr int A_BYTES = BM * A_ROW;
     constexpr int B_ROW = BN * 2;              // bytes per B row (MODE 0/1: N-contiguous rows)
     constexpr int B_BYTES = BK * B_ROW;
@@ -100,11 +126,12 @@ gemm16_dma_kernel(GemmArgs args)
     constexpr int LPS = MODE == 2 ? A_PW + 8 * NBS : A_PW + B_PW;   // loads per stage per lane
     constexpr int CPR = BN / 8;                // 16-byte chunks per B row
     constexpr int RPI = 64 / CPR;              // B rows per wave load
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(WTM % BLK == 0 && WTN % BLK == 0, "wave tile must be whole MFMA blocks");
+    static_assert(BLK == 32 || MODE == 0, "16x16 blocks: loads straight into LDS only");
     static_assert(A_INS % NW == 0 && B_INS % NW == 0, "loads must split evenly over waves");
     static_assert(CPR >= 16 && 64 % CPR == 0, "BN must be 128 or 256");
     static_assert(NBUF >= 2 && NBUF * STAGE <= 160 * 1024, "LDS ring");
-    static_assert(MODE == 0 || (NBUF == 2 && BK / 16 >= 3), "register-filled stages need NBUF 2, >= 3 k-steps");
+    static_assert(MODE == 0 || (NBUF == 2 && KSTEPS >= 3), "register-filled stages need NBUF 2, >= 3 k-steps");
     static_assert(MODE != 2 || NBS * NT == (BK / 8) * (BN / 8), "B blocks must split evenly over threads");
     static_assert((NBUF - 1) * LPS < 64, "vmcnt range");
 
@@ -219,29 +246,30 @@ gemm16_dma_kernel(GemmArgs args)
         *reinterpret_cast<u4*>(buf + dst + lane * 16) = R[q];
     };
 
-    const int lrow = lane & 31;
-    const int lgrp = lane >> 5;
+    const int lrow = lane % BLK;
+    const int lgrp = lane / BLK;               // K group of 8 values within a k-step
     const int g16 = lane >> 4, s16 = lane & 15;
     // Fragment reads, one LDS instruction each. Read r < TM: A block r;
     // read TM + 2 j + h: half h (K rows 4h..4h+3 of the lane's eight) of B block j.
-    //  A: row wm0 + 32 i + lrow, K 16 t + 8 lgrp .. +7, one 128-bit read.
-    //  B: column wn0 + 32 j + lrow, the same K, two transposing 64-bit reads.
+    //  A: row wm0 + BLK i + lrow, K KSTEP t + 8 lgrp .. +7, one 128-bit read.
+    //  B: column wn0 + BLK j + lrow, the same K, two transposing 64-bit reads;
+    //     the 16 lanes of a group address 4 K rows x 16 columns.
     auto read_one = [&](const unsigned char* buf, int t, int r, u4 (&fa)[TM], u2 (&fb)[TN][2]) {
         if (r < TM) {
-            const int row = wm0 + 32 * r + lrow;
-            const int c = (2 * t + lgrp) ^ ((row / RSW) % CPA);
+            const int row = wm0 + BLK * r + lrow;
+            const int c = ((MF::KSTEP / 8) * t + lgrp) ^ ((row / RSW) % CPA);
             fa[r] = *reinterpret_cast<const u4*>(buf + row * A_ROW + c * 16);
         } else if constexpr (MODE == 2) {
             const int j = r - TM;
-            const int row = wn0 + 32 * j + lrow;
-            const int c = (2 * t + lgrp) ^ ((row / RSW) % CPA);
+            const int row = wn0 + BLK * j + lrow;
+            const int c = ((MF::KSTEP / 8) * t + lgrp) ^ ((row / RSW) % CPA);
             const u4 v = *reinterpret_cast<const u4*>(buf + A_BYTES + row * A_ROW + c * 16);
             fb[j][0] = u2{v[0], v[1]};
             fb[j][1] = u2{v[2], v[3]};
         } else {
             const int j = (r - TM) >> 1, half = (r - TM) & 1;
-            const int col = wn0 + 32 * j + 16 * (g16 & 1) + 4 * (s16 & 3);
-            const int row = 16 * t + 8 * (g16 >> 1) + 4 * half + (s16 >> 2);
+            const int col = wn0 + BLK * j + (lrow & ~15) + 4 * (s16 & 3);
+            const int row = MF::KSTEP * t + 8 * lgrp + 4 * half + (s16 >> 2);
             const int c = (col >> 3) ^ (4 * (row & 3));
             const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 SAM_LDS4S(buf + A_BYTES + row * B_ROW + c * 16 + (col & 7) * 2));
@@ -249,23 +277,28 @@ gemm16_dma_kernel(GemmArgs args)
         }
     };
 
-    v16f acc[TM][TN];
+    typename MF::T acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < MF::NV; ++r) acc[i][j][r] = 0.0f;
 
     auto mfma_one = [&](int m, const u4 (&fa)[TM], const u2 (&fb)[TN][2]) {
         const int i = m / TN, j = m % TN;
         const u4 b = u4{fb[j][0][0], fb[j][0][1], fb[j][1][0], fb[j][1][1]};
-        mfma<DT>(acc[i][j], fa[i], b);
+        MF::mfma(acc[i][j], fa[i], b);
     };
 
     constexpr int NMF = TM * TN;          // MFMAs per k-step
     constexpr int NRD = MODE == 2 ? TM + TN : TM + 2 * TN;   // LDS reads per k-step
     constexpr int RPS = (NRD + NMF - 1) / NMF;   // reads per MFMA slot
+    // 16x16 blocks hold twice the fragment registers per k-step; their A
+    // fragments are single-buffered (each block's next read follows its last
+    // MFMA) so that eight waves fit 256 registers without spilling.
+    constexpr bool ASB = BLK == 16;
+    constexpr int FA = ASB ? 0 : 1;   // index mask of the A fragment set
 
     // One k-step: MFMA slot m issues MFMA m, then (while m < NRD) the next
     // step's read m into the other fragment set, then (in the second k-step)
@@ -276,9 +309,19 @@ gemm16_dma_kernel(GemmArgs args)
 #pragma unroll
         for (int m = 0; m < NMF; ++m) {
             mfma_one(m, fa, fb);
+            if constexpr (ASB) {
+                // A single-buffered: block i of the next k-step is read right
+                // after its last MFMA (m = TN i + TN - 1); the 2 TN B reads go
+                // to the other set, one every NMF / (2 TN) slots.
+                if (m % TN == TN - 1) read_one(rbuf, rt, m / TN, na, nb);
 #pragma unroll
-            for (int r = m * RPS; r < (m + 1) * RPS; ++r)
-                if (r < NRD) read_one(rbuf, rt, r, na, nb);
+                for (int q = 0; q < 2 * TN; ++q)
+                    if ((q * NMF) / (2 * TN) == m) read_one(rbuf, rt, TM + q, na, nb);
+            } else {
+#pragma unroll
+                for (int r = m * RPS; r < (m + 1) * RPS; ++r)
+                    if (r < NRD) read_one(rbuf, rt, r, na, nb);
+            }
             if constexpr (MODE == 2) {
                 // A: the A_PW straight-to-LDS loads; B: NBS blocks loaded (k-step 0)
                 // and transposed into LDS (next-to-last k-step), spread over slots.
@@ -356,10 +399,10 @@ gemm16_dma_kernel(GemmArgs args)
 #pragma unroll
         for (int t = 0; t + 1 < KSTEPS; ++t) {
             if constexpr (MODE == 2)
-                kstep(fa[t & 1], fb[t & 1], cur, t + 1, fa[(t + 1) & 1], fb[(t + 1) & 1], -1,
+                kstep(fa[t & FA], fb[t & 1], cur, t + 1, fa[(t + 1) & FA], fb[(t + 1) & 1], -1,
                       t == KSTEPS - 2 ? k + 1 : -1, t == 0 ? k + 1 : -1);
             else
-                kstep(fa[t & 1], fb[t & 1], cur, t + 1, fa[(t + 1) & 1], fb[(t + 1) & 1],
+                kstep(fa[t & FA], fb[t & 1], cur, t + 1, fa[(t + 1) & FA], fb[(t + 1) & 1],
                       (MODE == 1 && t == 0) ? k + 1 : -1, (MODE == 1 && t == KSTEPS - 2) ? k + 1 : -1);
         }
         // Stage k fully read by this wave; this wave's part of stage k+1 landed.
@@ -374,10 +417,10 @@ gemm16_dma_kernel(GemmArgs args)
         // LDS slot stage k leaves (MODE 0: whole stage k + NBUF; MODE 2: A of
         // stage k + 2).
         constexpr int L = (KSTEPS - 1) & 1;
-        kstep(fa[L], fb[L], nxt, 0, fa[L ^ 1], fb[L ^ 1], MODE == 0 ? k + NBUF : (MODE == 2 ? k + 2 : -1), -1);
+        kstep(fa[L & FA], fb[L], nxt, 0, fa[(L ^ 1) & FA], fb[L ^ 1], MODE == 0 ? k + NBUF : (MODE == 2 ? k + 2 : -1), -1);
         if constexpr (L == 0) {   // odd number of k-steps: next stage starts in set 1
 #pragma unroll
-            for (int i = 0; i < TM; ++i) fa[0][i] = fa[1][i];
+            for (int i = 0; i < TM; ++i) fa[0][i] = fa[FA][i];
 #pragma unroll
             for (int j = 0; j < TN; ++j) { fb[0][j][0] = fb[1][j][0]; fb[0][j][1] = fb[1][j][1]; }
         }
@@ -390,10 +433,10 @@ gemm16_dma_kernel(GemmArgs args)
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = wn0 + 32 * j + lrow;
+            const int col = wn0 + BLK * j + lrow;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm0 + 32 * i + ((r >> 2) << 3) + (lgrp << 2) + (r & 3);
+            for (int r = 0; r < MF::NV; ++r) {
+                const int row = wm0 + BLK * i + MF::row(lane, r);
                 const bool ok = m0 + row < M && n0 + col < N;
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rC,
                                                       ok ? (row * N + col) * 4 : kOOB, 0, 0);
@@ -410,11 +453,11 @@ struct DmaKernels {
     int threads;
 };
 
-#define SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, MODE, gm, xr, ms, e16)                \
-    {id, {nullptr, gemm16_dma_kernel<DT_BF16, BM, BN, WM, WN, BK, NBUF, MODE>,                   \
-          gemm16_dma_kernel<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE>}, WM * WN * 64},
+#define SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, gm, xr, ms, e16)           \
+    {id, {nullptr, gemm16_dma_kernel<DT_BF16, BM, BN, WM, WN, BK, NBUF, MODE, BLK>,              \
+          gemm16_dma_kernel<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE, BLK>}, WM * WN * 64},
 
-static const DmaKernels kDmaTable[] = {SAM_DMA_VARIANTS(SAM_DMA_ENTRY)};
+static const DmaKernels kDmaTable[] = {SAM_DMA_VARIANTS(SAM_DMA_ENTRY) SAM_DMA16_VARIANTS(SAM_DMA_ENTRY)};
 
 hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s)
 {

@@ -39,8 +39,8 @@ namespace sam {
 
 #define SAM_STAGED_ROW(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16, pf32, pf16) \
     {id, name, KIND_STAGED, 7, BM, BN, WM, WN, BLK, 2, 0, gm, xr, ms, 1, e32, e16},
-#define SAM_DMA_ROW(id, name, BM, BN, WM, WN, BK, NBUF, MODE, gm, xr, ms, e16) \
-    {id, name, KIND_DMA, (1 << DT_BF16) | (1 << DT_F16), BM, BN, WM, WN, 32, NBUF, BK, gm, xr, ms, 0, 0.0, e16},
+#define SAM_DMA_ROW(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, gm, xr, ms, e16) \
+    {id, name, KIND_DMA, (1 << DT_BF16) | (1 << DT_F16), BM, BN, WM, WN, BLK, NBUF, BK, gm, xr, ms, 0, 0.0, e16},
 
 #define SAM_STREAM_ROW(id, name, BM, BN, KB, ms, eff) \
     {id, name, KIND_STREAM, (1 << DT_F32), BM, BN, 1, 1, 16, 1, KB, 1, 0, ms, 1, eff, 0.0},
@@ -53,7 +53,7 @@ namespace sam {
 
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
                                         SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)
-                                            SAM_MX8_VARIANTS(SAM_MX8_ROW)};
+                                            SAM_MX8_VARIANTS(SAM_MX8_ROW) SAM_DMA16_VARIANTS(SAM_DMA_ROW)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

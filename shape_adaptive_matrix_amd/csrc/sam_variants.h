@@ -7,7 +7,9 @@
 //   X(id, name, BM, BN, WM, WN, BLK, group_m, xcd_remap, max_split, eff_f32, eff_h16, pf_f32, pf_h16)
 // LDS-ring variants (sam_kernels_dma.hip): 16-bit operands with K % 8 == 0
 // and N % 8 == 0 only; loads write LDS directly into a ring of NBUF stages.
-//   D(id, name, BM, BN, WM, WN, BK, NBUF, MODE, group_m, xcd_remap, max_split, eff_h16)
+//   D(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, group_m, xcd_remap, max_split, eff_h16)
+// BLK is the MFMA block edge: 32 (32x32x16) or 16 (16x16x32, names "..._b16",
+// ids 45.., listed after the block-scaled variants).
 // MODE 0 loads straight into LDS; MODE 1 loads into registers and writes LDS
 // (names start with "q"); MODE 2 loads A straight into LDS and B through
 // registers, transposed to K-contiguous rows (names start with "h").
@@ -39,18 +41,18 @@
     X(7, "t256x256_w2x4_b32", 256, 256, 2, 4, 32, 8, 1,  8, 0.88, 0.35, 1, 1)
 
 #define SAM_DMA_VARIANTS(D)                                                              \
-    D(8, "r256x256_w2x2_k32n4",  256, 256, 2, 2, 32, 4, 0, 8, 1, 8, 0.45)                   \
-    D(9, "r128x256_w2x2_k32n4",  128, 256, 2, 2, 32, 4, 0, 8, 1, 8, 0.37)                   \
-    D(10, "r256x128_w2x2_k32n4", 256, 128, 2, 2, 32, 4, 0, 8, 1, 8, 0.36)                   \
-    D(11, "r128x128_w2x2_k32n4", 128, 128, 2, 2, 32, 4, 0, 8, 1, 16, 0.34)                  \
-    D(12, "r256x256_w2x2_k64n2", 256, 256, 2, 2, 64, 2, 0, 8, 1, 8, 0.47)                   \
-    D(13, "r256x128_w2x2_k64n3", 256, 128, 2, 2, 64, 3, 0, 8, 1, 8, 0.38)                   \
-    D(14, "r128x256_w2x2_k64n3", 128, 256, 2, 2, 64, 3, 0, 8, 1, 8, 0.37)                \
-    D(15, "q256x256_w2x2_k64",   256, 256, 2, 2, 64, 2, 1, 8, 1, 8, 0.44)                \
-    D(16, "h256x256_w2x2_k64",   256, 256, 2, 2, 64, 2, 2, 8, 1, 8, 0.36)                \
-    D(17, "r256x256_w2x4_k64n2", 256, 256, 2, 4, 64, 2, 0, 8, 1, 8, 0.50)                \
-    D(18, "r256x256_w4x2_k64n2", 256, 256, 4, 2, 64, 2, 0, 8, 1, 8, 0.495)                \
-    D(19, "r256x256_w2x4_k32n4", 256, 256, 2, 4, 32, 4, 0, 8, 1, 8, 0.47)
+    D(8, "r256x256_w2x2_k32n4", 256, 256, 2, 2, 32, 4, 0, 32, 8, 1, 8, 0.45)                   \
+    D(9, "r128x256_w2x2_k32n4", 128, 256, 2, 2, 32, 4, 0, 32, 8, 1, 8, 0.37)                   \
+    D(10, "r256x128_w2x2_k32n4", 256, 128, 2, 2, 32, 4, 0, 32, 8, 1, 8, 0.36)                   \
+    D(11, "r128x128_w2x2_k32n4", 128, 128, 2, 2, 32, 4, 0, 32, 8, 1, 16, 0.34)                  \
+    D(12, "r256x256_w2x2_k64n2", 256, 256, 2, 2, 64, 2, 0, 32, 8, 1, 8, 0.47)                   \
+    D(13, "r256x128_w2x2_k64n3", 256, 128, 2, 2, 64, 3, 0, 32, 8, 1, 8, 0.38)                   \
+    D(14, "r128x256_w2x2_k64n3", 128, 256, 2, 2, 64, 3, 0, 32, 8, 1, 8, 0.37)                \
+    D(15, "q256x256_w2x2_k64", 256, 256, 2, 2, 64, 2, 1, 32, 8, 1, 8, 0.44)                \
+    D(16, "h256x256_w2x2_k64", 256, 256, 2, 2, 64, 2, 2, 32, 8, 1, 8, 0.36)                \
+    D(17, "r256x256_w2x4_k64n2", 256, 256, 2, 4, 64, 2, 0, 32, 8, 1, 8, 0.50)                \
+    D(18, "r256x256_w4x2_k64n2", 256, 256, 4, 2, 64, 2, 0, 32, 8, 1, 8, 0.495)                \
+    D(19, "r256x256_w2x4_k32n4", 256, 256, 2, 4, 32, 4, 0, 32, 8, 1, 8, 0.47)
 
 #define SAM_STREAM_VARIANTS(S)                                                           \
     S(20, "sm16x64_k2048", 16, 64, 2048, 32, 0.92)                                       \
@@ -77,3 +79,8 @@
     F(39, "f128x128_w4x2_k32n2",       128, 128, 4, 2, 32, 2, 2, 1, 32, 1, 8, 1, 16, 0.87)
 
 #include "sam_variants_mx.h"
+
+#define SAM_DMA16_VARIANTS(D)                                                            \
+    D(45, "r256x256_w2x4_k64n2_b16", 256, 256, 2, 4, 64, 2, 0, 16, 8, 1, 8, 0.52)         \
+    D(46, "r256x256_w4x2_k64n2_b16", 256, 256, 4, 2, 64, 2, 0, 16, 8, 1, 8, 0.51)         \
+    D(47, "r128x128_w2x2_k64n2_b16", 128, 128, 2, 2, 64, 2, 0, 16, 8, 1, 16, 0.34)
