@@ -51,9 +51,13 @@ namespace sam {
 #define SAM_MX8_ROW(id, name, BM, BN, WM, WN, BK, SD, gm, xr, ms, e8, e4) \
     {id, name, KIND_MX8, (1 << DT_MX8) | (1 << DT_MX4), BM, BN, WM, WN, 32, 2, BK, gm, xr, ms, 0, 0.0, 0.0, e8, e4},
 
+#define SAM_KQ_ROW(id, name, TB, gm, xr, e32) \
+    {id, name, KIND_KQ, (1 << DT_F32), 16 * TB, 16 * TB, 1, 1, 16, 3, 16, gm, xr, 1, 1, e32, 0.0},
+
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
                                         SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)
-                                            SAM_MX8_VARIANTS(SAM_MX8_ROW) SAM_DMA16_VARIANTS(SAM_DMA_ROW)};
+                                            SAM_MX8_VARIANTS(SAM_MX8_ROW) SAM_DMA16_VARIANTS(SAM_DMA_ROW)
+                                                SAM_KQ_VARIANTS(SAM_KQ_ROW)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -109,7 +113,7 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
                  : dtype == DT_MX8 ? v.eff_mx8
                  : dtype == DT_MX4 ? v.eff_mx4 : v.eff_h16;
     if (!a_vec) eff *= 0.85;
-    if (!b_vec) eff *= 0.85;
+    if (!b_vec && v.kind != KIND_KQ) eff *= 0.85;   // the single-launch kernels read B per value anyway
     const double flop_clk = dtype == DT_F32 ? kDev.f32_flop_per_clk_cu
                             : dtype == DT_MX8 ? kDev.mx8_flop_per_clk_cu
                             : dtype == DT_MX4 ? kDev.mx4_flop_per_clk_cu : kDev.h16_flop_per_clk_cu;
@@ -160,6 +164,7 @@ static void fill_plan(const Variant& v, long long M, long long N, long long K, i
     p->blk = v.blk;
     p->split = split;
     p->k_chunk = (int)(cdiv(cdiv(K, bk), split) * bk);
+    if (v.kind == KIND_KQ) p->k_chunk = (int)(cdiv(cdiv(K, 64), 4) * 64);   // K per wave (four waves), whole 4-chunk trips
     p->group_m = v.group_m;
     p->xcd_remap = v.xcd_remap;
     p->a_vec = (K % ve) == 0;
@@ -247,6 +252,13 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     // FP32 ring kernels take rows that are not 16-byte pieces only in their
     // element-load form, which not every variant has.
     if (v->kind == KIND_F32RING && (K % 4 != 0 || N % 4 != 0) && !v->elem_loads) return false;
+    // The single-launch small-tile kernels split K inside the workgroup only,
+    // and address A's tile rows and all of B with 32-bit byte offsets.
+    // Prefetches run up to 48 values of K past a wave's range (the plan's
+    // K per wave may itself end up to 63 values past K).
+    if (v->kind == KIND_KQ && (split_req > 1 || (long long)v->bm * (K + 128) * 4 >= 0x7FFFFFF0ll ||
+                               (K + 128) * N * 4 >= 0x7FFFFFF0ll))
+        return false;
     // The streaming kernels cover at most 16 rows (16 x 64 tile) or 16
     // columns (64 x 16 tile) of C.
     if (v->kind == KIND_STREAM && (v->bm == 16 ? M > 16 : N > 16)) return false;

@@ -84,3 +84,12 @@
     D(45, "r256x256_w2x4_k64n2_b16", 256, 256, 2, 4, 64, 2, 0, 16, 8, 1, 8, 0.52)         \
     D(46, "r256x256_w4x2_k64n2_b16", 256, 256, 4, 2, 64, 2, 0, 16, 8, 1, 8, 0.51)         \
     D(47, "r128x128_w2x2_k64n2_b16", 128, 128, 2, 2, 64, 2, 0, 16, 8, 1, 16, 0.34)
+
+// Single-launch small-tile variants (sam_kernels_kq.hip): FP32 only, a
+// 16 TB x 16 TB tile per workgroup whose four waves each take a quarter of
+// K and sum their partial tiles in LDS in a fixed order; any K and N.
+//   Q(id, name, TB, group_m, xcd_remap, eff_f32)
+#define SAM_KQ_VARIANTS(Q)                                                               \
+    Q(48, "kq32x32", 2, 8, 1, 0.55)                                                      \
+    Q(49, "kq48x48", 3, 8, 1, 0.65)                                                      \
+    Q(50, "kq64x64", 4, 8, 1, 0.70)
