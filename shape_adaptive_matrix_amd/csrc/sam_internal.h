@@ -29,7 +29,7 @@ struct DeviceModel {
 };
 
 // Static description of a tile/schedule variant.
-enum Kind : int { KIND_STAGED = 0, KIND_DMA = 1, KIND_STREAM = 2, KIND_F32RING = 3, KIND_MX8 = 4, KIND_KQ = 5 };
+enum Kind : int { KIND_STAGED = 0, KIND_DMA = 1, KIND_STREAM = 2, KIND_F32RING = 3, KIND_MX8 = 4, KIND_KQ = 5, KIND_KP = 6 };
 
 struct Variant {
     int id;
@@ -111,6 +111,7 @@ hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mx8(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_kq(const Plan& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_kp(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const float* parts, int split, long long part_stride,
                          float* C, long long count, hipStream_t s);
 hipError_t launch_zero(float* C, long long count, hipStream_t s);

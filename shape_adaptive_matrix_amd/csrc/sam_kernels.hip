@@ -538,6 +538,7 @@ hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s)
     if (p.kind == KIND_F32RING) return launch_f32_ring(p, a, s);
     if (p.kind == KIND_MX8) return launch_mx8(p, a, s);
     if (p.kind == KIND_KQ) return launch_kq(p, a, s);
+    if (p.kind == KIND_KP) return launch_kp(p, a, s);
     const VariantKernels& vk = kTable[p.variant_id];
     KernelFn fn = vk.fn[p.dtype][p.a_vec][p.b_vec];
     hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(vk.threads), 0, s, a);

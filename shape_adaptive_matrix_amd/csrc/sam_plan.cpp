@@ -54,10 +54,13 @@ namespace sam {
 #define SAM_KQ_ROW(id, name, TB, gm, xr, e32) \
     {id, name, KIND_KQ, (1 << DT_F32), 16 * TB, 16 * TB, 1, 1, 16, 3, 16, gm, xr, 1, 1, e32, 0.0},
 
+#define SAM_KP_ROW(id, name, KP, gm, xr, e32) \
+    {id, name, KIND_KP, (1 << DT_F32), 128, 128, 4, 2, 16, 2, KP, gm, xr, 1, 0, e32, 0.0},
+
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
                                         SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)
                                             SAM_MX8_VARIANTS(SAM_MX8_ROW) SAM_DMA16_VARIANTS(SAM_DMA_ROW)
-                                                SAM_KQ_VARIANTS(SAM_KQ_ROW)};
+                                                SAM_KQ_VARIANTS(SAM_KQ_ROW) SAM_KP_VARIANTS(SAM_KP_ROW)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -97,6 +100,16 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
     const double in_b = in_bytes(dtype);
     const double mb = 1e-6;                                   // bytes -> MB; GB/s = MB/ms
 
+    if (v.kind == KIND_KP) {
+        // Resident workgroups (one per CU for the 64-value panel, two for
+        // 32) walk the tiles; each tile's multiplies overlap the previous
+        // tile's C write, so a round of 256 tiles costs the larger of the two.
+        const double peak_cu = kDev.f32_flop_per_clk_cu * kDev.clock_ghz * 1e3;
+        const double t_mfma = 2.0 * v.bm * v.bn * (double)v.bk / (peak_cu * v.eff_f32);
+        const double t_write = kDev.cus * v.bm * v.bn * 4.0 * mb / kDev.hbm_write_gbs * 1e3;
+        const double t_fill = 2.0 * v.bm * v.bk * 4.0 * kDev.cus * mb / kDev.hbm_gbs * 1e3;
+        return (double)cdiv(tiles_m * tiles_n, kDev.cus) * fmax(t_mfma, t_write) + t_fill + kDev.launch_us;
+    }
     if (v.kind == KIND_STREAM) {
         // HBM-bound: the operands cross HBM once at the variant's share of the
         // read rate, scaled down while fewer than two 8-wave workgroups per CU
@@ -172,6 +185,12 @@ static void fill_plan(const Variant& v, long long M, long long N, long long K, i
     p->tiles_m = (int)cdiv(M, v.bm);
     p->tiles_n = (int)cdiv(N, v.bn);
     p->grid = (long long)p->tiles_m * p->tiles_n * split;
+    if (v.kind == KIND_KP) {   // resident workgroups: as many as fit the CUs' LDS, at most one per tile
+        const long long per_cu = kDev.lds_bytes / (2 * 2 * v.bm * v.bk * 4);
+        const long long g = kDev.cus * per_cu;
+        p->grid = p->grid < g ? p->grid : g;
+        p->k_chunk = (int)K;
+    }
     p->ws_bytes = split > 1 ? (unsigned long long)split * (unsigned long long)(M * N) * 4ull : 0ull;
     p->est_us = estimate_us(v, M, N, K, dtype, split, p->a_vec, p->b_vec);
 }
@@ -259,6 +278,9 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     if (v->kind == KIND_KQ && (split_req > 1 || (long long)v->bm * (K + 128) * 4 >= 0x7FFFFFF0ll ||
                                (K + 128) * N * 4 >= 0x7FFFFFF0ll))
         return false;
+    // The persistent short-K kernels hold a whole K panel per tile in LDS and
+    // load A and B rows as 16-byte pieces.
+    if (v->kind == KIND_KP && (split_req > 1 || K > v->bk || K % 4 != 0 || N % 4 != 0)) return false;
     // The streaming kernels cover at most 16 rows (16 x 64 tile) or 16
     // columns (64 x 16 tile) of C.
     if (v->kind == KIND_STREAM && (v->bm == 16 ? M > 16 : N > 16)) return false;

@@ -93,3 +93,12 @@
     Q(48, "kq32x32", 2, 8, 1, 0.55)                                                      \
     Q(49, "kq48x48", 3, 8, 1, 0.65)                                                      \
     Q(50, "kq64x64", 4, 8, 1, 0.70)
+
+// Persistent short-K variants (sam_kernels_kp.hip): FP32 only, K <= KP,
+// K % 4 == 0 and N % 4 == 0; 128 x 128 tiles, resident workgroups walk their
+// tiles with the next tile's panels loading and the last tile's stores
+// draining while the current one is multiplied.
+//   P(id, name, KP, group_m, xcd_remap, eff_f32)
+#define SAM_KP_VARIANTS(P)                                                               \
+    P(51, "kp128x128_k32", 32, 8, 1, 0.80)                                              \
+    P(52, "kp128x128_k64", 64, 8, 1, 0.85)

@@ -34,7 +34,9 @@ def test_device_is_gfx950():
 RAGGED = [(1, 1, 1), (17, 33, 45), (64, 64, 64), (70, 130, 100), (129, 257, 200), (16, 300, 96),
           (300, 16, 96), (256, 256, 256),
           # K and N multiples of 8 (the LDS-ring variants' domain), ragged M/N/K tiles
-          (129, 136, 200), (257, 392, 328), (33, 520, 72), (1000, 264, 40)]
+          (129, 136, 200), (257, 392, 328), (33, 520, 72), (1000, 264, 40),
+          # short K with N % 4 == 0 (the persistent short-K variants' domain too)
+          (70, 132, 28)]
 
 
 def _supported(vid, M, N, K, dtype, split=0):
@@ -156,6 +158,44 @@ def test_stream_k_random_and_repeatable():
     assert vids
     for vid in vids:
         outs = [run(A, B, "f32", variant=vid, split=-1) for _ in range(3)]
+        assert rel_rms(outs[0], ref) <= 1e-5
+        for o in outs[1:]:
+            assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), vid
+
+
+def test_persistent_short_k():
+    """The persistent short-K variants on grids with more tiles than resident
+    workgroups, so that workgroups walk several tiles with the next panels
+    loading and the last stores draining; ragged M and N tails, K not a
+    multiple of the 16-value step. Small integers: bit-exact. Random inputs:
+    within the FP32 bound and bitwise repeatable."""
+    kp = [v for v in range(sam.variant_count()) if sam.variant_info(v)["name"].startswith("kp")]
+    assert len(kp) == 2
+    cases = [(2341, 2324, 60), (3100, 3000, 28), (130, 260, 4)]
+    ran = 0
+    for (M, N, K) in cases:
+        A, B = ints_operands(M, N, K, "f32", seed=M + N + K)
+        ref = orc().gemm("f32", A, B)
+        for vid in kp:
+            if not _supported(vid, M, N, K, "f32"):
+                continue
+            plan = sam.variant_plan(vid, M, N, K, "f32", 0)
+            C = run(A, B, "f32", variant=vid)
+            bad = bitexact_mismatches(C, ref)
+            assert bad == 0, f"variant {vid} {(M, N, K)} grid {plan['grid_wgs']}: {bad} mismatches"
+            ran += 1
+    assert ran >= 4
+    # More tiles than resident workgroups for both variants.
+    assert sam.variant_plan(kp[0], 3100, 3000, 28, "f32", 0)["grid_wgs"] < 25 * 24
+    assert sam.variant_plan(kp[1], 2341, 2324, 60, "f32", 0)["grid_wgs"] < 19 * 19
+    M, N, K = 1500, 1000, 64
+    rng = np.random.default_rng(11)
+    A, B = si.uniform_pm1(rng, (M, K)), si.uniform_pm1(rng, (K, N))
+    ref = orc().gemm("f32", A, B)
+    for vid in kp:
+        if not _supported(vid, M, N, K, "f32"):
+            continue
+        outs = [run(A, B, "f32", variant=vid) for _ in range(3)]
         assert rel_rms(outs[0], ref) <= 1e-5
         for o in outs[1:]:
             assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), vid
