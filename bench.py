@@ -37,18 +37,19 @@ PEAK_HBM_GBS = 8000.0
 
 
 KERNEL_SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_kernels_stream.hip", "sam_kernels_f32ring.hip",
-                  "sam_kernels_mx.hip", "sam_kernels_kq.hip", "sam_dma.h", "sam_internal.h", "sam_variants.h",
-                  "sam_variants_mx.h"]
+                  "sam_kernels_mx.hip", "sam_kernels_kq.hip", "sam_kernels_kp.hip", "sam_dma.h", "sam_internal.h",
+                  "sam_variants.h", "sam_variants_mx.h"]
 
-# Kernel function of a plan, by the first letter of its variant name.
+# Kernel function of a plan, by the leading letters of its variant name.
 KERNEL_OF = {"t": "sam::gemm_kernel", "r": "sam::gemm16_dma_kernel", "q": "sam::gemm16_dma_kernel",
              "h": "sam::gemm16_dma_kernel", "s": "sam::stream_m_kernel / sam::stream_n_kernel",
-             "f": "sam::gemm_f32_ring_kernel", "x": "sam::gemm_mx8_kernel", "k": "sam::gemm_f32_kq_kernel"}
+             "f": "sam::gemm_f32_ring_kernel", "x": "sam::gemm_mx8_kernel", "kq": "sam::gemm_f32_kq_kernel",
+             "kp": "sam::gemm_f32_kp_kernel"}
 
 
 def kernel_name(plan) -> str:
     variant = plan["name"].split("_", 1)[1]
-    return KERNEL_OF.get(variant[0], "?")
+    return KERNEL_OF.get(variant[:2], KERNEL_OF.get(variant[0], "?"))
 
 
 def src_digest() -> str:
