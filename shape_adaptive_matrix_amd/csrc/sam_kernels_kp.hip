@@ -1,12 +1,13 @@
 // FP32 GEMM for short K (K <= 64): C = A*B, row-major A[M][K], B[K][N].
 //
 // With K this short a 128 x 128 tile is 2 MFLOP of multiplies against 64 KB
-// of C to write, and at 8192 x 8192 the C write alone (268 MB) takes as long
-// as the MFMAs (P2, "Scale coverage exposes a remaining GEMM gap": its
-// K-light shapes; P4 names the K-loop prologue and drain as the cost of
-// short loops). A data-parallel launch runs each tile's fill, multiplies and
-// store one after the other. Here each workgroup stays resident and walks
-// its tiles t = g, g + G, ...:
+// of C to write: at 8192 x 8192 the C write (268 MB) is a large share of the
+// time, and the per-tile fill and drain of the K loop (counted as a fixed
+// cost per tile on page "Measured data point on fixed-tile vs shape-adaptive
+// GEMM", section "The wall, and why we think it's structural") are paid once
+// for only two K stages. A data-parallel launch runs each tile's fill,
+// multiplies and store one after the other. Here each workgroup stays
+// resident and walks its tiles t = g, g + G, ...:
 //
 //  * Two LDS buffers, each holding one tile's whole A panel (128 rows x KP
 //    values of K) and B panel (KP rows x 128 columns). While tile t is

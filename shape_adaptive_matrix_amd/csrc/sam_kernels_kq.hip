@@ -1,12 +1,13 @@
 // FP32 GEMM in one launch for products too small to fill the machine:
 // C = A*B, row-major A[M][K], B[K][N], FP32 in and out.
 //
-// Page "Measured data point on fixed-tile vs shape-adaptive GEMM" (its D=768
-// row) and page "Post-mortem: a GPU stack without nvcc, cuBLAS, or LLVM"
-// (the K-loop prologue and drain it names as the cost of small shapes): at
-// D <= ~1000 the work per CU is a few microseconds, so a split-K plan that
-// ends in a second, reducing launch pays a launch gap as large as the
-// product itself. Here the K split stays inside the workgroup instead:
+// Page "Measured data point on fixed-tile vs shape-adaptive GEMM" lists a
+// D=768 configuration ("What we measured"); it and page "Post-mortem: a GPU
+// stack without nvcc, cuBLAS, or LLVM" (section 2.1) count the K-loop drain
+// as a fixed cost per tile. At D <= ~1000 the work per CU is a few
+// microseconds, so a split-K plan that ends in a second, reducing launch
+// pays fixed costs as large as the product itself. Here the K split stays
+// inside the workgroup instead:
 //
 //  * A workgroup owns one 16 TB x 16 TB tile of C and runs four waves, one
 //    per SIMD; wave w takes K values [w kq, (w + 1) kq), kq a multiple of 64.
