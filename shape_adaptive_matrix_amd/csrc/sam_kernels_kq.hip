@@ -10,10 +10,11 @@
 // inside the workgroup instead:
 //
 //  * A workgroup owns one 16 TB x 16 TB tile of C and runs four waves, one
-//    per SIMD; wave w takes K values [w kq, (w + 1) kq), kq a multiple of 64.
+//    per SIMD, or eight, two per SIMD; wave w takes K values
+//    [w kq, (w + 1) kq), kq a multiple of 64 (four waves) or 32 (eight).
 //  * Each wave streams its K range straight from memory into registers, 16
-//    values of K per chunk with three chunks in flight ahead of the one being
-//    multiplied, and runs 16x16x4 FP32 MFMAs on them. Lane l carries row /
+//    values of K per chunk with three chunks (four waves) or one (eight) in
+//    flight ahead of the one being multiplied, and runs 16x16x4 FP32 MFMAs on them. Lane l carries row /
 //    column l % 16 and the K values 4 (l / 16) + e, e = 0..3, of a chunk, in
 //    A and in B alike, so every product pairs the same K index. A is read as
 //    one 16-byte piece per row and chunk when K % 4 == 0, else per value; B
@@ -21,9 +22,9 @@
 //  * Every read stays inside A or B (buffer loads; offsets past an operand
 //    read zero). Values past the wave's K range are zeroed in both operands,
 //    so a value beyond K (an Inf in the next row, say) is never multiplied.
-//  * The four partial tiles meet in LDS and each element of C is stored as
-//    ((P0 + P1) + P2) + P3: a fixed order, so repeated runs give the same
-//    bits, with no atomics and no second launch.
+//  * The partial tiles meet in LDS and each element of C is stored as
+//    ((P0 + P1) + P2) + ... in wave order: a fixed order, so repeated runs
+//    give the same bits, with no atomics and no second launch.
 #include "sam_dma.h"
 #include "sam_internal.h"
 #include "sam_variants.h"
@@ -35,14 +36,20 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 }  // namespace kq
 
-template <int TB, bool VA>
-__global__ void __launch_bounds__(256) gemm_f32_kq_kernel(GemmArgs args)
+// NW waves split K: 4 (one per SIMD, four register sets: three chunks in
+// flight) or 8 (two per SIMD, two sets: one chunk in flight, the other wave
+// on the SIMD covering the wait).
+template <int NW> constexpr int kq_sets() { return NW == 4 ? 4 : 2; }
+
+template <int TB, bool VA, int NW>
+__global__ void __launch_bounds__(64 * NW) gemm_f32_kq_kernel(GemmArgs args)
 {
     using namespace kq;
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     constexpr int BT = 16 * TB;                // tile edge
     constexpr int LS = BT + 4;                 // LDS row stride (floats): conflict-free partial stores
-    constexpr int NSET = 4;                    // register sets: one in use, three in flight
-    __shared__ float part[4][BT * LS];
+    constexpr int NSET = kq_sets<NW>();        // register sets: one in use, NSET - 1 in flight
+    __shared__ float part[NW][BT * LS];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: the loop below is not divergent
@@ -114,20 +121,20 @@ __global__ void __launch_bounds__(256) gemm_f32_kq_kernel(GemmArgs args)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[set][i][e], b[set][j][e], acc[i][j], 0, 0, 0);
     };
 
-    // Four chunks per trip, with no branch inside it (a branch makes the
+    // NSET chunks per trip, with no branch inside it (a branch makes the
     // compiler wait for every load in flight). Chunks past this wave's range
     // hold zeros in both operands, so multiplying them leaves the partial
     // tile unchanged (its values start at +0 and never become -0); the plan
-    // makes kq a multiple of 64, so only the last wave can run such chunks.
+    // makes kq a multiple of 16 NSET, so only the last wave can run such
+    // chunks.
     // The scheduling barriers keep each set's loads ahead of the multiplies
     // they are to overlap: left alone, the scheduler sinks loads to their
     // uses to shorten live ranges, and every chunk would wait for its data.
-    load(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load(1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load(2, 2);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u + 1 < NSET; ++u) {
+        load(u, u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int c = 0; c < nch; c += NSET) {
 #pragma unroll
         for (int u = 0; u < NSET; ++u) {
@@ -149,15 +156,15 @@ __global__ void __launch_bounds__(256) gemm_f32_kq_kernel(GemmArgs args)
                 part[wave][(16 * i + 4 * q + r) * LS + 16 * j + r16] = acc[i][j][r];
     __syncthreads();
 
-    // ((P0 + P1) + P2) + P3, one element per thread and pass, row-major so
-    // that consecutive threads store consecutive columns.
+    // (((P0 + P1) + P2) + ...) in wave order, one element per thread and
+    // pass, row-major so that consecutive threads store consecutive columns.
     float* crow = args.out + (long long)m0 * N + n0;
-    for (int x = threadIdx.x; x < BT * BT; x += 256) {
+    for (int x = threadIdx.x; x < BT * BT; x += 64 * NW) {
         const int row = x / BT, col = x % BT;
         const int o = row * LS + col;
-        float v = part[0][o] + part[1][o];
-        v = v + part[2][o];
-        v = v + part[3][o];
+        float v = part[0][o];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v = v + part[w][o];
         if (m0 + row < M && n0 + col < N) crow[(long long)row * N + col] = v;
     }
 }
@@ -167,17 +174,19 @@ typedef void (*KqFn)(GemmArgs);
 struct KqKernels {
     int id;
     KqFn fn[2];   // [A rows are whole 16-byte pieces]
+    int waves;
 };
 
-#define SAM_KQ_ENTRY(id, name, TB, gm, xr, e32) {id, {gemm_f32_kq_kernel<TB, false>, gemm_f32_kq_kernel<TB, true>}},
+#define SAM_KQ_ENTRY(id, name, TB, NW, gm, xr, e32) \
+    {id, {gemm_f32_kq_kernel<TB, false, NW>, gemm_f32_kq_kernel<TB, true, NW>}, NW},
 
-static const KqKernels kKqTable[] = {SAM_KQ_VARIANTS(SAM_KQ_ENTRY)};
+static const KqKernels kKqTable[] = {SAM_KQ_VARIANTS(SAM_KQ_ENTRY) SAM_KQ8_VARIANTS(SAM_KQ_ENTRY)};
 
 hipError_t launch_kq(const Plan& p, const GemmArgs& a, hipStream_t s)
 {
     for (const KqKernels& k : kKqTable) {
         if (k.id != p.variant_id) continue;
-        hipLaunchKernelGGL(k.fn[p.a_vec ? 1 : 0], dim3((unsigned)p.grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k.fn[p.a_vec ? 1 : 0], dim3((unsigned)p.grid), dim3(64 * k.waves), 0, s, a);
         return hipGetLastError();
     }
     return hipErrorInvalidDeviceFunction;

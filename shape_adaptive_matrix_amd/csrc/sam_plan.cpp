@@ -51,8 +51,8 @@ namespace sam {
 #define SAM_MX8_ROW(id, name, BM, BN, WM, WN, BK, SD, gm, xr, ms, e8, e4) \
     {id, name, KIND_MX8, (1 << DT_MX8) | (1 << DT_MX4), BM, BN, WM, WN, 32, 2, BK, gm, xr, ms, 0, 0.0, 0.0, e8, e4},
 
-#define SAM_KQ_ROW(id, name, TB, gm, xr, e32) \
-    {id, name, KIND_KQ, (1 << DT_F32), 16 * TB, 16 * TB, 1, 1, 16, 3, 16, gm, xr, 1, 1, e32, 0.0},
+#define SAM_KQ_ROW(id, name, TB, NW, gm, xr, e32) \
+    {id, name, KIND_KQ, (1 << DT_F32), 16 * TB, 16 * TB, 1, NW, 16, NW == 4 ? 4 : 2, 16, gm, xr, 1, 1, e32, 0.0},
 
 #define SAM_KP_ROW(id, name, KP, gm, xr, e32) \
     {id, name, KIND_KP, (1 << DT_F32), 128, 128, 4, 2, 16, 2, KP, gm, xr, 1, 0, e32, 0.0},
@@ -60,7 +60,8 @@ namespace sam {
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
                                         SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)
                                             SAM_MX8_VARIANTS(SAM_MX8_ROW) SAM_DMA16_VARIANTS(SAM_DMA_ROW)
-                                                SAM_KQ_VARIANTS(SAM_KQ_ROW) SAM_KP_VARIANTS(SAM_KP_ROW)};
+                                                SAM_KQ_VARIANTS(SAM_KQ_ROW) SAM_KP_VARIANTS(SAM_KP_ROW)
+                                                    SAM_KQ8_VARIANTS(SAM_KQ_ROW)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -177,7 +178,10 @@ static void fill_plan(const Variant& v, long long M, long long N, long long K, i
     p->blk = v.blk;
     p->split = split;
     p->k_chunk = (int)(cdiv(cdiv(K, bk), split) * bk);
-    if (v.kind == KIND_KQ) p->k_chunk = (int)(cdiv(cdiv(K, 64), 4) * 64);   // K per wave (four waves), whole 4-chunk trips
+    if (v.kind == KIND_KQ) {   // K per wave: NW waves (v.wn), whole trips of nbuf 16-value chunks
+        const long long trip = 16ll * v.nbuf;
+        p->k_chunk = (int)(cdiv(cdiv(K, trip), v.wn) * trip);
+    }
     p->group_m = v.group_m;
     p->xcd_remap = v.xcd_remap;
     p->a_vec = (K % ve) == 0;

@@ -86,13 +86,14 @@
     D(47, "r128x128_w2x2_k64n2_b16", 128, 128, 2, 2, 64, 2, 0, 16, 8, 1, 16, 0.34)
 
 // Single-launch small-tile variants (sam_kernels_kq.hip): FP32 only, a
-// 16 TB x 16 TB tile per workgroup whose four waves each take a quarter of
-// K and sum their partial tiles in LDS in a fixed order; any K and N.
-//   Q(id, name, TB, group_m, xcd_remap, eff_f32)
+// 16 TB x 16 TB tile per workgroup whose NW waves (4 or 8, names "..._w8")
+// each take a share of K and sum their partial tiles in LDS in a fixed
+// order; any K and N.
+//   Q(id, name, TB, NW, group_m, xcd_remap, eff_f32)
 #define SAM_KQ_VARIANTS(Q)                                                               \
-    Q(48, "kq32x32", 2, 8, 1, 0.55)                                                      \
-    Q(49, "kq48x48", 3, 8, 1, 0.65)                                                      \
-    Q(50, "kq64x64", 4, 8, 1, 0.70)
+    Q(48, "kq32x32", 2, 4, 8, 1, 0.55)                                                   \
+    Q(49, "kq48x48", 3, 4, 8, 1, 0.65)                                                   \
+    Q(50, "kq64x64", 4, 4, 8, 1, 0.70)
 
 // Persistent short-K variants (sam_kernels_kp.hip): FP32 only, K <= KP,
 // K % 4 == 0 and N % 4 == 0; 128 x 128 tiles, resident workgroups walk their
@@ -102,3 +103,9 @@
 #define SAM_KP_VARIANTS(P)                                                               \
     P(51, "kp128x128_k32", 32, 8, 1, 0.80)                                              \
     P(52, "kp128x128_k64", 64, 8, 1, 0.85)
+
+// Eight-wave forms of the single-launch small-tile variants (same list format).
+#define SAM_KQ8_VARIANTS(Q)                                                              \
+    Q(53, "kq32x32_w8", 2, 8, 8, 1, 0.62)                                                \
+    Q(54, "kq48x48_w8", 3, 8, 8, 1, 0.73)                                                \
+    Q(55, "kq64x64_w8", 4, 8, 8, 1, 0.78)
