@@ -252,6 +252,37 @@ def test_inf_beyond_k_tail_is_not_read(shape):
     assert ran > 0
 
 
+@pytest.mark.parametrize("dtype,shape", [("f32", (130, 132, 60)), ("f32", (70, 136, 45)), ("f32", (37, 64, 1037)),
+                                         ("bf16", (130, 136, 200)), ("f16", (70, 264, 40))])
+def test_inf_at_start_of_next_row_is_not_read(dtype, shape):
+    """A row's K tail is the start of the next row in memory. Inf there (A
+    rows 1 and 3 start with Inf) must reach only those rows' outputs: rows 0
+    and 2, whose last K stage or chunk ends inside the Inf, must come out
+    exactly K. Run on every variant that takes the shape."""
+    M, N, K = shape
+    A = np.ones((M, K), np.float32)
+    A[1, 0] = np.inf
+    A[3, 0:4] = np.inf
+    B = np.ones((K, N), np.float32)
+    if dtype == "f32":
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    else:
+        t = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+        dA, dB = torch.from_numpy(A).cuda().to(t), torch.from_numpy(B).cuda().to(t)
+    ran = 0
+    for vid in range(sam.variant_count()):
+        if not _supported(vid, M, N, K, dtype):
+            continue
+        C = sam.gemm_variant(vid, dA, dB).cpu().numpy()
+        torch.cuda.synchronize()
+        for r in (0, 2, 4, M - 1):
+            assert np.all(C[r] == K), (vid, r)
+        for r in (1, 3):
+            assert np.all(np.isposinf(C[r])), (vid, r)
+        ran += 1
+    assert ran > 0
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_inf_beyond_k_tail_16bit(dtype):
     """Same for 16-bit operands, K a multiple of 8 but not of any stage depth:
