@@ -6,6 +6,14 @@
 //    traffic); FLOP/s = waves x iterations x 8 x FLOPs per MFMA / time.
 //  * HBM: a 16-byte-per-lane streaming copy and a streaming read-reduce over
 //    buffers far larger than the 256 MB Infinity Cache.
+//  * Operand delivery into a CU: one workgroup of 8 waves per CU streams
+//    32 KB blocks of a source region into a ring of D LDS buffers with the
+//    direct-to-LDS buffer loads the GEMM kernels use (D - 1 blocks in
+//    flight, a barrier per block, no arithmetic), and, for comparison, into
+//    registers with ordinary 16-byte buffer loads (16 KB in flight per
+//    wave). Regions of 2 MB (resident in each XCD's 4 MB L2), 64 MB (beyond
+//    L2, inside the Infinity Cache) and 1 GB. Reported as GB/s over the chip
+//    and bytes per clock per CU at the reported clock.
 // Prints one JSON object. Timing uses HIP events on one stream.
 #include <hip/hip_runtime.h>
 #include <stdio.h>
@@ -17,6 +25,8 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+
+#include "../csrc/sam_dma.h"
 
 #define CHECK(x)                                                                      \
     do {                                                                              \
@@ -102,6 +112,60 @@ __global__ void __launch_bounds__(256) read16(const u4* __restrict__ src, unsign
     if (acc == 0x9E3779B9u) out[0] = acc;   // practically never true; keeps the loads alive
 }
 
+// D-deep LDS ring of 32 KB blocks; block b of workgroup g is source block
+// (7 g + b) mod (region / 32 KB). Every offset is inside the region.
+template <int D>
+__global__ void __launch_bounds__(512) lds_stream(const char* src, int region_bytes, int iters, unsigned* sink)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[D * 32768];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const sam::dma::i4 r0 = sam::dma::rsrc_words(src, region_bytes);
+    // Wave-uniform by construction; said explicitly so that the resource
+    // stays in scalar registers, as the load instruction requires.
+    const sam::dma::i4 r = {__builtin_amdgcn_readfirstlane(r0[0]), __builtin_amdgcn_readfirstlane(r0[1]),
+                            __builtin_amdgcn_readfirstlane(r0[2]), __builtin_amdgcn_readfirstlane(r0[3])};
+    const int blocks = region_bytes / 32768;
+    auto issue = [&](int b) {
+        const int blk = (int)(((long long)blockIdx.x * 7 + b) % blocks);
+        unsigned char* buf = lds + (b % D) * 32768;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int I = wave + q * 8;   // 1 KB piece of the block
+            sam::dma::lds_load16(r, sam::dma::lds_addr(buf + I * 1024), blk * 32768 + I * 1024 + lane * 16);
+        }
+    };
+#pragma unroll
+    for (int b = 0; b < D - 1; ++b) issue(b);
+    for (int it = 0; it < iters; ++it) {
+        issue(it + D - 1);   // its slot held block it - 1, released by the last barrier
+        sam::dma::wait_cnt<(D - 1) * 4, 15>();   // block `it` has landed
+        sam::dma::barrier();
+    }
+    sam::dma::wait_cnt<0, 0>();
+    if (lds[threadIdx.x] == 0xAB && lds[threadIdx.x + 512] == 0xCD) sink[0] = 1;   // keeps the loads live
+}
+
+// The same blocks into registers: 16 loads of 16 bytes per lane in flight.
+__global__ void __launch_bounds__(512) vgpr_stream(const char* src, int region_bytes, int iters, unsigned* sink)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const __amdgpu_buffer_rsrc_t r = sam::dma::make_rsrc(src, region_bytes);
+    const int blocks = region_bytes / 32768;
+    unsigned acc = 0;
+    for (int it = 0; it < iters; it += 4) {
+        u4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {   // blocks it .. it + 3, 4 pieces each
+            const int blk = (int)(((long long)blockIdx.x * 7 + it + u / 4) % blocks);
+            const int I = wave + (u % 4) * 8;
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, blk * 32768 + I * 1024 + lane * 16, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 static float time_ms(hipEvent_t a, hipEvent_t b) {
     float ms = 0;
     CHECK(hipEventElapsedTime(&ms, a, b));
@@ -174,8 +238,43 @@ int main(int argc, char** argv)
         CHECK(hipEventSynchronize(e1));
         if (rep) best_read = fminf(best_read, time_ms(e0, e1));
     }
-    printf("\"hbm\": {\"copy_gbs\": %.1f, \"read_gbs\": %.1f, \"bytes_each_way\": %lld}}\n",
+    printf("\"hbm\": {\"copy_gbs\": %.1f, \"read_gbs\": %.1f, \"bytes_each_way\": %lld}, ",
            2.0 * bytes / (best_copy * 1e-3) / 1e9, bytes / (best_read * 1e-3) / 1e9, bytes);
+    // Operand delivery: 32 KB blocks into LDS (ring depth D) or registers.
+    {
+        const double clk_ghz = prop.clockRate * 1e-6;
+        const int regions[3] = {2 << 20, 64 << 20, 1 << 30};
+        const char* rnames[3] = {"l2_2MB", "mall_64MB", "hbm_1GB"};
+        printf("\"delivery\": {");
+        for (int ri = 0; ri < 3; ++ri) {
+            const int rb = regions[ri];
+            const int iters = 512;
+            printf("%s\"%s\": {", ri ? ", " : "", rnames[ri]);
+            for (int kind = 0; kind < 4; ++kind) {
+                float best = 1e30f;
+                for (int rep = 0; rep < 4; ++rep) {
+                    CHECK(hipEventRecord(e0, 0));
+                    switch (kind) {
+                    case 0: hipLaunchKernelGGL(lds_stream<2>, dim3(cus), dim3(512), 0, 0, (const char*)src, rb, iters, sink); break;
+                    case 1: hipLaunchKernelGGL(lds_stream<3>, dim3(cus), dim3(512), 0, 0, (const char*)src, rb, iters, sink); break;
+                    case 2: hipLaunchKernelGGL(lds_stream<4>, dim3(cus), dim3(512), 0, 0, (const char*)src, rb, iters, sink); break;
+                    default: hipLaunchKernelGGL(vgpr_stream, dim3(cus), dim3(512), 0, 0, (const char*)src, rb, iters, sink); break;
+                    }
+                    CHECK(hipGetLastError());
+                    CHECK(hipEventRecord(e1, 0));
+                    CHECK(hipEventSynchronize(e1));
+                    if (rep) best = fminf(best, time_ms(e0, e1));
+                }
+                const double bytes = (double)cus * iters * 32768.0;
+                const double gbs = bytes / (best * 1e-3) / 1e9;
+                const char* kn[4] = {"lds_ring2", "lds_ring3", "lds_ring4", "vgpr_16"};
+                printf("%s\"%s\": {\"gbs\": %.1f, \"bytes_per_clk_cu\": %.1f}", kind ? ", " : "", kn[kind], gbs,
+                       gbs / cus / clk_ghz);
+            }
+            printf("}");
+        }
+        printf("}}\n");
+    }
     CHECK(hipFree(src));
     CHECK(hipFree(dst));
     CHECK(hipFree(sink));
