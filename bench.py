@@ -4,12 +4,14 @@
 One step = one GEMM call (dispatcher, main kernel, and the split-K reduce
 when the plan has one) on resident device operands. The headline workload is
 FP32 M = N = K = 2048 (uniform [-1, 1) from seed 2); ``--workload`` picks
-another from the table in ``sam_inputs``. After the headline line's timing,
-``--sweep`` (default on) times every workload with the batch protocol of
-page "Scale coverage exposes a remaining GEMM gap" (section "GEMM: frozen
+another from the table in ``sam_inputs``. Before the headline is timed, the
+sweep (on unless ``--no-sweep``) times every workload with the batch protocol
+of page "Scale coverage exposes a remaining GEMM gap" (section "GEMM: frozen
 schedules at larger dimensions": warmup, several rounds of batched launches,
 median of round medians), plus a cold-cache single-launch time for the
-HBM-bound skinny shapes.
+HBM-bound skinny shapes; each entry carries its own roofline record. Running
+it first also lets the clock settle under load, so that a short timed region
+measures the kernel and not the clock ramp.
 
 Prints one JSON line (rank 0, N = 1 only: this path runs on one GPU).
 
@@ -19,6 +21,7 @@ as it stands) on a bounded slab of rows of the same workload.
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
 import hashlib
 import json
@@ -173,6 +176,50 @@ def prepare_ex(w, torch, sam, si, ta: bool, tb: bool, alpha: float, beta: float,
     return {"step": step, "plan": sam.plan(w.M, w.N, w.K, w.dtype), "keep": (dA, dB, C, ws), "stream": stream}
 
 
+def profile_kernel_avg_us(workload: str, kernel: str):
+    """Average duration (us) of `kernel` in the committed rocprofv3
+    kernel-trace summary of `workload` (profiles/<kernel>_<workload>.txt,
+    the kernel_stats.csv row it quotes), with the file's name; None if there
+    is none."""
+    short = kernel.split("::")[-1]
+    p = ROOT / "profiles" / f"{short}_{workload}.txt"
+    if not p.exists():
+        return None
+    for line in p.read_text().splitlines():
+        if line.startswith('"') and short + "<" in line.split(",")[0]:
+            cells = next(csv.reader([line]))
+            return {"file": str(p.relative_to(ROOT)), "kernel": cells[0], "calls": int(cells[1]),
+                    "avg_us": round(float(cells[3]) / 1e3, 3)}
+    return None
+
+
+def roofline_of(w, t_ms: float, plan, digest: str) -> dict:
+    """Roofline record of one timed workload: MFMA-bound for the dense
+    shapes (2MNK FLOP against the dtype's peak), HBM-bound for the skinny ones
+    (algorithmic bytes against 8 TB/s)."""
+    skinny = min(w.M, w.N) <= 16
+    split = plan["split_k"] > 1
+    if skinny:
+        achieved = w.alg_bytes / t_ms / 1e6
+        rec = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+               "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = w.flops / t_ms / 1e9
+        rec = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+               "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4)}
+    rec["traffic"] = None if split else load_traffic(w.name, digest)
+    rec["kernel"] = kernel_name(plan) + (" + sam::splitk_reduce_kernel" if split else "") + \
+        (" + sam::sk_fixup_kernel" if plan["split_k"] == -1 else "")
+    if plan["split_k"] == 1:
+        prof = profile_kernel_avg_us(w.name, kernel_name(plan))
+        if prof is not None:
+            prof["frac_at_profile_avg"] = round(
+                (w.flops / (prof["avg_us"] * 1e-6) / 1e12 / PEAK_TFLOPS[w.dtype]) if not skinny else
+                (w.alg_bytes / (prof["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS), 4)
+            rec["profile"] = prof
+    return rec
+
+
 def time_steps(torch, step, steps: int) -> float:
     """Milliseconds for `steps` back-to-back calls, HIP events on the stream the
     kernels run on (torch's current stream, which the calls are given)."""
@@ -186,12 +233,12 @@ def time_steps(torch, step, steps: int) -> float:
     return s.elapsed_time(e)
 
 
-def sweep(torch, sam, si, rounds: int = 5):
+def sweep(torch, sam, si, digest: str, rounds: int = 5):
     """Every workload: median over rounds of the per-launch time of a batch
     lasting >= 20 ms; cold-cache single launches for the skinny shapes."""
     out = []
     flush = None
-    for w in si.WORKLOADS + si.MX_WORKLOADS:
+    for w in si.WORKLOADS + si.MX_WORKLOADS + si.LLM_WORKLOADS + si.LLM_MX_WORKLOADS:
         g = prepare(w, torch, sam, si)
         step = g["step"]
         for _ in range(3):
@@ -211,6 +258,7 @@ def sweep(torch, sam, si, rounds: int = 5):
             "tflops": round(w.flops / t_ms / 1e9, 2),
             "pct_mfma_peak": round(100 * w.flops / t_ms / 1e9 / PEAK_TFLOPS[w.dtype], 1),
             "alg_gbs": round(w.alg_bytes / t_ms / 1e6, 1),
+            "roofline": roofline_of(w, t_ms, g["plan"], digest),
         }
         if min(w.M, w.N) <= 16:
             # Evict the operands by reading 1 GiB: a read leaves clean lines,
@@ -268,7 +316,18 @@ def cpu_baseline(w, si, seconds: float):
     flops = 2.0 * target * w.N * w.K * reps
     what = (f"rows 0..{target - 1}" if target < w.M else "all rows") + f" of {w.name}"
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{what} (N={w.N}, K={w.K}) x{reps}, {elapsed:.1f} s, double-precision i-k-j loop"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def load_traffic(workload: str, digest: str):
@@ -343,6 +402,12 @@ def main():
     else:
         g = prepare(w, torch, sam, si, args.variant, args.split)
     step = g["step"]
+    digest = src_digest()
+    # The sweep runs first: after it the clock has settled under load, so a
+    # short timed region measures the kernel rather than the clock ramp.
+    sweep_rec = None
+    if not args.no_sweep:
+        sweep_rec = sweep(torch, sam, si, digest)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -353,8 +418,13 @@ def main():
     ms_step = ms / args.steps
     tflops = w.flops / ms_step / 1e9
 
-    digest = src_digest()
     split = g["plan"]["split_k"] > 1
+    prof = None if (args.ex or args.variant is not None or args.shape or split) else \
+        profile_kernel_avg_us(w.name, kernel_name(g["plan"]))
+    if prof is not None:
+        # The committed kernel trace of the same command: the fraction at its
+        # average kernel duration, next to the event-timed one above.
+        prof["frac_at_profile_avg"] = round(w.flops / (prof["avg_us"] * 1e-6) / 1e12 / PEAK_TFLOPS[w.dtype], 4)
     line = {
         "metric": "GEMM TFLOP/s and % of MFMA peak on 1 MI355X, fp32 and bf16, D=2048-8192",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -372,13 +442,16 @@ def main():
             "traffic": None if split else load_traffic(w.name, digest),
             "kernel": kernel_name(g["plan"]) + (" + sam::splitk_reduce_kernel" if split else ""),
             "per_launch_flops": w.flops, "src_digest": digest,
+            "timing": f"HIP events on the launch stream around {args.steps} back-to-back calls, "
+                      f"after {args.warmup} warm-up calls" + (" and the sweep" if sweep_rec else ""),
+            "profile": prof,
         },
         "build": sam.build_info(),
     }
     del g
     torch.cuda.empty_cache()
-    if not args.no_sweep:
-        line["sweep"] = sweep(torch, sam, si)
+    if sweep_rec is not None:
+        line["sweep"] = sweep_rec
     if args.ceilings:
         import subprocess
         exe = ROOT / "shape_adaptive_matrix_amd" / "microbench" / "sam_ceilings"

@@ -41,7 +41,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "MX_WORKLOADS", "by_name", "uniform_pm1", "small_ints",
+__all__ = ["Workload", "WORKLOADS", "MX_WORKLOADS", "LLM_WORKLOADS", "LLM_MX_WORKLOADS", "LLM_SHAPES", "by_name", "uniform_pm1", "small_ints",
            "normal16", "make_operands", "sample_points", "bf16_rne_bits",
            "mx_codes", "mx_scales", "make_mx_operands", "MX_BLOCK"]
 
@@ -172,7 +172,36 @@ MX_WORKLOADS = [
     Workload("mxfp4_8192", "mxfp4", 8192, 8192, 8192, "mx_normal", 20, tol=5e-5, fmt_a="e2m1", fmt_b="e2m1"),
 ]
 
-_BY_NAME = {w.name: w for w in WORKLOADS + MX_WORKLOADS}
+# A second, LLM-like workload: the projection shapes of page "Scale coverage
+# exposes a remaining GEMM gap", section "GEMM: frozen schedules at larger
+# dimensions" (256 x 11008 x 4096, 4096 x 4096 x 11008 and the ragged
+# 2049 x 4097 x 1025), in FP32, bfloat16 and binary16, plus the two shapes
+# that also have block-scaled plans.
+LLM_SHAPES = [(256, 11008, 4096), (4096, 4096, 11008), (2049, 4097, 1025)]
+
+
+def _llm(dtype, seed0):
+    out = []
+    for i, (M, N, K) in enumerate(LLM_SHAPES):
+        name = f"llm_{dtype}_{M}x{N}x{K}"
+        if dtype == "f32":
+            out.append(Workload(name, "f32", M, N, K, "uniform", seed0 + i))
+        else:
+            out.append(Workload(name, dtype, M, N, K, "normal16", seed0 + i, tol=1e-2))
+    return out
+
+
+LLM_WORKLOADS = _llm("f32", 21) + _llm("bf16", 24) + _llm("f16", 27)
+LLM_MX_WORKLOADS = [
+    Workload("llm_mxfp8_256x11008x4096", "mxfp8", 256, 11008, 4096, "mx_normal", 30, tol=5e-5),
+    Workload("llm_mxfp8_4096x4096x11008", "mxfp8", 4096, 4096, 11008, "mx_normal", 31, tol=5e-5),
+    Workload("llm_mxfp4_256x11008x4096", "mxfp4", 256, 11008, 4096, "mx_normal", 32, tol=5e-5,
+             fmt_a="e2m1", fmt_b="e2m1"),
+    Workload("llm_mxfp4_4096x4096x11008", "mxfp4", 4096, 4096, 11008, "mx_normal", 33, tol=5e-5,
+             fmt_a="e2m1", fmt_b="e2m1"),
+]
+
+_BY_NAME = {w.name: w for w in WORKLOADS + MX_WORKLOADS + LLM_WORKLOADS + LLM_MX_WORKLOADS}
 
 
 def by_name(name: str) -> Workload:

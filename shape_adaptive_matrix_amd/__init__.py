@@ -185,6 +185,23 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else None
 
 
+def _on_device(tensors, names, device=None):
+    """Every tensor lives on one GPU (the first one's unless `device` is
+    given): the library is handed raw device pointers, and a host pointer or
+    another GPU's memory must never reach a kernel."""
+    dev = device
+    for t, name in zip(tensors, names):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {dev}")
+    return dev
+
+
 def _operands(A, B, dtype):
     code = _torch_dtype_code(A, dtype)
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
@@ -197,26 +214,56 @@ def _operands(A, B, dtype):
     return code
 
 
-def workspace_for(plan_dict: dict, device):
+def _output(C, M, N, others, names, workspace=None):
+    """Checks, before anything reaches the library, that the caller's C is a
+    compact float32 [M][N] matrix and that C, the workspace and the operands
+    (`others`) all live on one GPU; returns C, or a new one on that GPU."""
+    import torch
+    if C is not None:
+        if C.dtype != torch.float32:
+            raise TypeError(f"C must be float32 (got {C.dtype})")
+        if tuple(C.shape) != (M, N):
+            raise ValueError(f"C must have shape ({M}, {N}) (got {tuple(C.shape)})")
+        if not C.is_contiguous():
+            raise ValueError("C must be contiguous row-major")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    dev = _on_device((*others, C, workspace), (*names, "C", "workspace"))
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    return C
+
+
+def _workspace_bytes(workspace) -> int:
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def workspace_for(plan_dict: dict, device, stream=None):
+    """A workspace of the plan's size, allocated on `stream` (torch's current
+    stream when None). The caching allocator hands freed memory only to later
+    work on the stream it was allocated on, so a workspace that goes out of
+    scope when the call returns is not reused while the call's kernels, queued
+    on that stream, still use it."""
     import torch
     n = int(plan_dict["workspace_bytes"])
     if n == 0:
         return None
-    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
+    if stream is None:
+        return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
 
 
 def gemm(A, B, C=None, dtype=None, workspace=None, stream=None):
     """C = A·B on the tensors' device through the dispatcher; returns C (FP32)."""
-    import torch
     code = _operands(A, B, dtype)
     M, K = A.shape
     N = B.shape[1]
-    if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    C = _output(C, M, N, (A, B), ("A", "B"), workspace)
     p = plan(M, N, K, code)
     if workspace is None:
-        workspace = workspace_for(p, A.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = workspace_for(p, A.device, stream)
+    ws_bytes = _workspace_bytes(workspace)
     fn = {F32: lib().sam_gemm_f32, BF16: lib().sam_gemm_bf16, F16: lib().sam_gemm_f16}[code]
     _check(fn(_ptr(A), _ptr(B), _ptr(C), M, N, K, _ptr(workspace), ws_bytes, _stream_ptr(stream)))
     return C
@@ -224,16 +271,14 @@ def gemm(A, B, C=None, dtype=None, workspace=None, stream=None):
 
 def gemm_variant(vid: int, A, B, C=None, split_k: int = 0, dtype=None, workspace=None, stream=None):
     """C = A·B with a forced variant (and split; 0 = the variant's own pick)."""
-    import torch
     code = _operands(A, B, dtype)
     M, K = A.shape
     N = B.shape[1]
-    if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    C = _output(C, M, N, (A, B), ("A", "B"), workspace)
     p = variant_plan(vid, M, N, K, code, split_k)
     if workspace is None:
-        workspace = workspace_for(p, A.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = workspace_for(p, A.device, stream)
+    ws_bytes = _workspace_bytes(workspace)
     _check(lib().sam_gemm_variant(vid, code, p["split_k"], _ptr(A), _ptr(B), _ptr(C), M, N, K,
                                   _ptr(workspace), ws_bytes, _stream_ptr(stream)))
     return C
@@ -269,17 +314,20 @@ def gemm_ex(A, B, C=None, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, dty
     Kb, N = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
     if Kb != K:
         raise ValueError(f"op(A) is {M}x{K} but op(B) is {Kb}x{N}")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    dev = _on_device((A, B, C, workspace), ("A", "B", "C", "workspace"))
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs C")
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
     if tuple(C.shape) != (M, N) or C.dtype != torch.float32:
         raise ValueError(f"C must be float32 [{M}, {N}]")
     ldc = _rows(C, "C")
     if workspace is None:
         n = ex_workspace_bytes(M, N, K, trans_a, trans_b, lda, ldb, ldc, alpha, beta, code)
-        workspace = torch.empty((n + 3) // 4, dtype=torch.float32, device=A.device) if n else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = workspace_for({"workspace_bytes": n}, dev, stream)
+    ws_bytes = _workspace_bytes(workspace)
     _check(lib().sam_gemm_ex(code, int(trans_a), int(trans_b), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
                              float(beta), _ptr(C), ldc, _ptr(workspace), ws_bytes, _stream_ptr(stream)))
     return C
@@ -305,11 +353,10 @@ def gemm_mxfp8(A, SA, Bt, SB, fmt_a="e4m3", fmt_b="e4m3", C=None, workspace=None
     device; returns C [M][N] FP32."""
     import torch
     M, N, K, fa, fb = _mx_operands(A, SA, Bt, SB, fmt_a, fmt_b)
-    if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    C = _output(C, M, N, (A, SA, Bt, SB), ("A", "scale_a", "Bt", "scale_b"), workspace)
     if workspace is None:
-        workspace = workspace_for(plan(M, N, K, MXFP8), A.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = workspace_for(plan(M, N, K, MXFP8), A.device, stream)
+    ws_bytes = _workspace_bytes(workspace)
     _check(lib().sam_gemm_mxfp8(fa, fb, _ptr(A), _ptr(SA), _ptr(Bt), _ptr(SB), _ptr(C), M, N, K, _ptr(workspace),
                                 ws_bytes, _stream_ptr(stream)))
     return C
@@ -320,12 +367,11 @@ def gemm_mxfp8_variant(vid: int, A, SA, Bt, SB, fmt_a="e4m3", fmt_b="e4m3", C=No
     """gemm_mxfp8 with a forced variant and split (0 = the variant's pick)."""
     import torch
     M, N, K, fa, fb = _mx_operands(A, SA, Bt, SB, fmt_a, fmt_b)
-    if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    C = _output(C, M, N, (A, SA, Bt, SB), ("A", "scale_a", "Bt", "scale_b"), workspace)
     p = variant_plan(vid, M, N, K, MXFP8, split_k)
     if workspace is None:
-        workspace = workspace_for(p, A.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = workspace_for(p, A.device, stream)
+    ws_bytes = _workspace_bytes(workspace)
     _check(lib().sam_gemm_mxfp8_variant(vid, p["split_k"], fa, fb, _ptr(A), _ptr(SA), _ptr(Bt), _ptr(SB), _ptr(C),
                                         M, N, K, _ptr(workspace), ws_bytes, _stream_ptr(stream)))
     return C
@@ -350,11 +396,10 @@ def gemm_mxfp4(A, SA, Bt, SB, C=None, workspace=None, stream=None):
     [N][K/32] E8M0 scale codes, all uint8 on the device; returns C [M][N] FP32."""
     import torch
     M, N, K = _mx4_operands(A, SA, Bt, SB)
-    if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    C = _output(C, M, N, (A, SA, Bt, SB), ("A", "scale_a", "Bt", "scale_b"), workspace)
     if workspace is None:
-        workspace = workspace_for(plan(M, N, K, MXFP4), A.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = workspace_for(plan(M, N, K, MXFP4), A.device, stream)
+    ws_bytes = _workspace_bytes(workspace)
     _check(lib().sam_gemm_mxfp4(_ptr(A), _ptr(SA), _ptr(Bt), _ptr(SB), _ptr(C), M, N, K, _ptr(workspace), ws_bytes,
                                 _stream_ptr(stream)))
     return C
@@ -364,12 +409,11 @@ def gemm_mxfp4_variant(vid: int, A, SA, Bt, SB, C=None, split_k: int = 0, worksp
     """gemm_mxfp4 with a forced variant and split (0 = the variant's pick)."""
     import torch
     M, N, K = _mx4_operands(A, SA, Bt, SB)
-    if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    C = _output(C, M, N, (A, SA, Bt, SB), ("A", "scale_a", "Bt", "scale_b"), workspace)
     p = variant_plan(vid, M, N, K, MXFP4, split_k)
     if workspace is None:
-        workspace = workspace_for(p, A.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = workspace_for(p, A.device, stream)
+    ws_bytes = _workspace_bytes(workspace)
     _check(lib().sam_gemm_mxfp4_variant(vid, p["split_k"], _ptr(A), _ptr(SA), _ptr(Bt), _ptr(SB), _ptr(C), M, N, K,
                                         _ptr(workspace), ws_bytes, _stream_ptr(stream)))
     return C

@@ -37,3 +37,22 @@ def rel_rms(gpu: np.ndarray, ref64: np.ndarray) -> float:
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / den)
+
+
+# Gate of the block-scaled random-input tests: every element within this
+# fraction of sum_k |a_k b_k| of the oracle's exact sum. The scaled matrix
+# instruction sums each group of products with fewer bits than FP32, so the
+# block-scaled path is not held to the FP32 bound; a wrong scale or a dropped
+# 32-value block moves an element by a block's partial sum, far beyond it.
+MX_ELEMENT_BOUND = 2.0 ** -12
+MX_REL_RMS = 5e-5
+
+
+def mx_bound_excess(gpu: np.ndarray, ref64: np.ndarray, absum: np.ndarray) -> float:
+    """Largest |gpu - ref| - MX_ELEMENT_BOUND * absum over the elements
+    (positive: the gate rejects); +inf when any GPU value is not finite."""
+    g = np.asarray(gpu, dtype=np.float64)
+    if not np.all(np.isfinite(g)):
+        return float("inf")
+    err = np.abs(g - np.asarray(ref64, dtype=np.float64))
+    return float(np.max(err - MX_ELEMENT_BOUND * np.asarray(absum, dtype=np.float64)))

@@ -564,6 +564,35 @@ def pin_mx4_packing_closed_form(o):
     assert got.tolist() == [[0.5, 1.0, 6.0]], got
 
 
+def pin_mx4_points(o):
+    """Single MXFP4 points equal the full product's sums bit for bit, at
+    corners, interior positions and with an odd number of 32-value blocks;
+    with scales near 1 they also equal the exact rational sum of the
+    independently unpacked and decoded values. M != N, and rows and cols are
+    drawn apart, so a row/column mix-up or a nibble picked from the wrong half
+    of a byte on one operand changes the result."""
+    rng = np.random.default_rng(132)
+    for (M, N, K, slo, shi) in [(7, 5, 96, 100, 154), (6, 9, 160, 126, 128), (5, 4, 32, 120, 134)]:
+        A, SA, Bt, SB = _mx4_random(rng, M, N, K, slo, shi)
+        full = o.gemm_mxfp4(A, SA, Bt, SB)
+        lim = min(M, N)
+        rows = np.array([0, lim - 1, 1, lim - 1, 2, 0, lim - 2], dtype=np.int64)
+        cols = np.array([0, lim - 1, 3 % lim, 0, 1, lim - 1, 2], dtype=np.int64)
+        pts = o.gemm_mxfp4_points(A, SA, Bt, SB, rows, cols)
+        assert np.array_equal(_bits(pts), _bits(full[rows, cols])), (M, N, K)
+        if shi - slo <= 2:
+            a, b = _e2m1_values(_unpack4(A)), _e2m1_values(_unpack4(Bt))
+            sa, sb = _torch_values("e8m0", SA), _torch_values("e8m0", SB)
+            for p, (i, j) in enumerate(zip(rows, cols)):
+                want = sum((Fraction(float(a[i, k])) * Fraction(float(sa[i, k // 32])) *
+                            Fraction(float(b[j, k])) * Fraction(float(sb[j, k // 32])) for k in range(K)),
+                           Fraction(0))
+                assert Fraction(pts[p]) == want, (M, N, K, i, j)
+    z = o.gemm_mxfp4_points(np.zeros((2, 0), np.uint8), np.zeros((2, 0), np.uint8), np.zeros((3, 0), np.uint8),
+                            np.zeros((3, 0), np.uint8), [1], [2])
+    assert z.tolist() == [0.0] and not np.signbit(z).any()
+
+
 ALL_PINS = [pin_golden_small, pin_decode_table, pin_decode_library,
             pin_bruteforce_ints, pin_bruteforce_16bit, pin_fsum_bound,
             pin_closed_forms, pin_identity_permutation,
@@ -571,4 +600,5 @@ ALL_PINS = [pin_golden_small, pin_decode_table, pin_decode_library,
             pin_rows_points_consistent, pin_degenerate, pin_ex_bruteforce, pin_ex_inexact_scales,
             pin_mx_decode_table, pin_mx_decode_library, pin_mx_bruteforce,
             pin_mx_unit_scales, pin_mx_scale_closed_form, pin_mx_points_and_degenerate,
-            pin_mx4_decode_via_e4m3, pin_mx4_bruteforce, pin_mx4_unit_scales, pin_mx4_packing_closed_form]
+            pin_mx4_decode_via_e4m3, pin_mx4_bruteforce, pin_mx4_unit_scales, pin_mx4_packing_closed_form,
+            pin_mx4_points]

@@ -253,3 +253,36 @@ def test_mxfp4_plans_and_rejections():
     assert L.sam_gemm_mxfp4(vp(A_), None, vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -1
     assert L.sam_gemm_mxfp4_variant(0, 0, vp(A_), vp(SA_), vp(B_), vp(SB_), vp(C_), 64, 64, 64, None, 0, None) == -4
     assert L.sam_gemm_variant(p4["variant_id"], sam.MXFP4, 0, vp(A_), vp(B_), vp(C_), 64, 64, 64, None, 0, None) == -1
+
+
+def test_binding_rejects_host_tensors_and_bad_c():
+    """The binding checks C (shape, float32, contiguity) and that every tensor
+    is a GPU tensor before it calls into the library: a host pointer or a
+    short C must never reach a kernel."""
+    import torch
+    A = torch.ones(4, 3)
+    B = torch.ones(3, 5)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sam.gemm(A, B)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sam.gemm_variant(0, A, B, torch.empty(4, 5))
+    with pytest.raises(ValueError, match="shape"):
+        sam.gemm(A, B, torch.empty(4, 4))
+    with pytest.raises(ValueError, match="shape"):
+        sam.gemm_variant(0, A, B, torch.empty(5, 4))
+    with pytest.raises(TypeError, match="float32"):
+        sam.gemm(A, B, torch.empty(4, 5, dtype=torch.float64))
+    with pytest.raises(ValueError, match="contiguous"):
+        sam.gemm(A, B, torch.empty(5, 4).t())
+    with pytest.raises(ValueError, match="contiguous"):
+        sam.gemm(A, B, torch.empty(4, 5), workspace=torch.empty(8, 2).t())
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sam.gemm_ex(A, B)
+    u8 = torch.zeros(4, 32, dtype=torch.uint8)
+    s8 = torch.zeros(4, 1, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="shape"):
+        sam.gemm_mxfp8(u8, s8, u8, s8, C=torch.empty(3, 4))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sam.gemm_mxfp8(u8, s8, u8, s8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sam.gemm_mxfp4(u8[:, :16].contiguous(), s8, u8[:, :16].contiguous(), s8)

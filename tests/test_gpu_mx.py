@@ -19,7 +19,7 @@ import torch
 import oracle
 import sam_inputs as si
 import shape_adaptive_matrix_amd as sam
-from tests.compare import bitexact_mismatches, rel_rms
+from tests.compare import bitexact_mismatches, mx_bound_excess, rel_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -67,9 +67,7 @@ def _abs_sum(ops, fa, fb):
 
 def _check_bound(C, ref, absum, K):
     assert np.isfinite(C).all()
-    err = np.abs(C.astype(np.float64) - ref)
-    bound = 2.0 ** -12 * absum
-    worst = np.max(err - bound)
+    worst = mx_bound_excess(C, ref, absum)
     assert worst <= 0, f"error exceeds the instruction-precision bound by {worst}"
 
 
@@ -132,7 +130,7 @@ def test_mx_auto_plans_random_shapes():
         assert bitexact_mismatches(C, ref) == 0, (M, N, K, fa, fb)
 
 
-@pytest.mark.parametrize("name", [w.name for w in si.MX_WORKLOADS if w.dtype == "mxfp8"])
+@pytest.mark.parametrize("name", [w.name for w in si.MX_WORKLOADS + si.LLM_MX_WORKLOADS if w.dtype == "mxfp8"])
 def test_mx_workload_sampled(name):
     """Full-size workloads in the launch configuration the benchmark times:
     sampled outputs (random points plus the corners and tail rows/columns)
@@ -265,7 +263,7 @@ def test_mx4_auto_plans_random_shapes():
         assert bitexact_mismatches(_run4(ops), orc().gemm_mxfp4(*ops)) == 0, (M, N, K)
 
 
-@pytest.mark.parametrize("name", [w.name for w in si.MX_WORKLOADS if w.dtype == "mxfp4"])
+@pytest.mark.parametrize("name", [w.name for w in si.MX_WORKLOADS + si.LLM_MX_WORKLOADS if w.dtype == "mxfp4"])
 def test_mx4_workload_sampled(name):
     w = si.by_name(name)
     ops = si.make_mx_operands(w)

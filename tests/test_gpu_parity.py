@@ -125,7 +125,10 @@ def test_every_variant_dyadic_skinny(vid):
 # (300x300x4096: ~28 shares per tile), ragged and odd-K/N ones, and a range
 # that touches three tiles.
 SK_SHAPES = [(300, 300, 4096), (768, 768, 768), (129, 257, 2000), (1000, 1000, 1000), (17, 2000, 3000),
-             (1536, 1536, 1536), (260, 1030, 2052)]
+             (1536, 1536, 1536), (260, 1030, 2052),
+             # K % 4 != 0 (and N % 4 != 0): the element-load forms inside stream-K segments,
+             # shapes for which the dispatcher itself picks a stream-K plan
+             (1500, 1500, 2047), (260, 1030, 2051), (3000, 3000, 3001)]
 _SK_REF = {}
 
 
@@ -147,11 +150,13 @@ def test_every_variant_stream_k_dyadic(vid):
         pytest.skip(f"variant {vid} has no stream-K form for these shapes")
 
 
-def test_stream_k_random_and_repeatable():
+@pytest.mark.parametrize("shape", [(300, 300, 4096), (1500, 1500, 2047)], ids=str)
+def test_stream_k_random_and_repeatable(shape):
     """Random inputs: within the FP32 bound, and bitwise identical on repeats
-    (the shares of a tile are always added in the same order)."""
-    M, N, K = 300, 300, 4096
-    rng = np.random.default_rng(5)
+    (the shares of a tile are always added in the same order); K % 4 != 0
+    runs the element-load form inside the segments."""
+    M, N, K = shape
+    rng = np.random.default_rng(5 + K)
     A, B = si.uniform_pm1(rng, (M, K)), si.uniform_pm1(rng, (K, N))
     ref = orc().gemm("f32", A, B)
     vids = [v for v in range(sam.variant_count()) if _supported(v, M, N, K, "f32", -1)]
@@ -161,6 +166,14 @@ def test_stream_k_random_and_repeatable():
         assert rel_rms(outs[0], ref) <= 1e-5
         for o in outs[1:]:
             assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), vid
+
+
+def test_dispatcher_picks_stream_k_on_odd_k():
+    """The shapes above with K % 4 != 0 are ones the dispatcher itself sends
+    to stream-K, so those segments are the automatic path, not only forced."""
+    picked = [s for s in [(1500, 1500, 2047), (3000, 3000, 3001), (260, 1030, 2051)]
+              if sam.plan(*s, "f32")["split_k"] == -1]
+    assert picked, "no odd-K shape goes to stream-K any more; pick new shapes"
 
 
 def test_persistent_short_k():
@@ -303,27 +316,16 @@ def test_inf_beyond_k_tail_16bit(dtype):
 
 
 # -- the workloads at their real sizes ------------------------------------------------
-def _check_workload(w, C):
-    A, B = si.make_operands(w)
-    M, N = w.M, w.N
-    o = orc()
-    if w.M * w.N * w.K <= 2048 ** 3:
-        ref = o.gemm(w.dtype, A, B)
-        got = C
-    else:
-        # A slab of leading and trailing rows plus sampled points (corners and
-        # tail-adjacent elements included).
-        rows = min(32, M)
-        top = o.gemm_rows(w.dtype, A, B, 0, rows)
-        bot = o.gemm_rows(w.dtype, A, B, M - rows, rows)
-        r, c = si.sample_points(M, N, 4096, seed=w.seed + 7)
-        pts = o.gemm_points(w.dtype, A, B, r, c)
-        ref = np.concatenate([top.ravel(), bot.ravel(), pts])
-        got = np.concatenate([C[:rows].ravel(), C[M - rows:].ravel(), C[r, c]])
+def _check_workload(w, C, A=None, B=None):
+    """Every element of C against the full oracle (the FP64 product of the
+    whole workload, computed on the host's cores in seconds even at 8192^3)."""
+    if A is None:
+        A, B = si.make_operands(w)
+    ref = orc().gemm(w.dtype, A, B)
     if w.check == "bitexact":
-        assert bitexact_mismatches(got, ref) == 0
+        assert bitexact_mismatches(C, ref) == 0
     else:
-        e = rel_rms(got, ref)
+        e = rel_rms(C, ref)
         assert e <= w.tol, e
         if w.dtype != "f32":
             # FP32 accumulation of exact products: anything near the 1e-2 gate
@@ -331,13 +333,28 @@ def _check_workload(w, C):
             assert e <= 1e-4, e
 
 
-@pytest.mark.parametrize("name", [w.name for w in si.WORKLOADS])
+@pytest.mark.parametrize("name", [w.name for w in si.WORKLOADS + si.LLM_WORKLOADS])
 def test_workload_parity(name):
+    """The dispatcher's own plan (the launch configuration the benchmark
+    times) at the workload's full size, every element against the oracle."""
     w = si.by_name(name)
     A, B = si.make_operands(w)
     print(f"[parity] {name} plan={sam.plan(w.M, w.N, w.K, w.dtype)['name']}", flush=True)
     C = run(A, B, w.dtype)
-    _check_workload(w, C)
+    _check_workload(w, C, A, B)
+
+
+@pytest.mark.parametrize("shape", si.LLM_SHAPES, ids=str)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_llm_shapes_dyadic(shape, dtype):
+    """The LLM-like shapes in their frozen (or modelled) plans on small
+    integers: every partial sum is exact, so every element must equal the
+    oracle bit for bit."""
+    M, N, K = shape
+    A, B = ints_operands(M, N, K, dtype, seed=M + N + K, lo=-2, hi=2)
+    print(f"[llm] {dtype} {shape} plan={sam.plan(M, N, K, dtype)['name']}", flush=True)
+    C = run(A, B, dtype)
+    assert bitexact_mismatches(C, orc().gemm(dtype, A, B)) == 0
 
 
 @pytest.mark.parametrize("name", ["f32_2048", "bf16_4096", "f32_16x8192x8192", "f32_768"])

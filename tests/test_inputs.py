@@ -35,7 +35,7 @@ def test_workloads_match_the_stated_configs():
     for s in [(768, 768, 768), (4097, 3071, 8191), (8191, 8193, 4096), (16, 8192, 8192),
               (8192, 16, 8192), (8192, 8192, 64)]:
         assert s in shapes
-    every = si.WORKLOADS + si.MX_WORKLOADS
+    every = si.WORKLOADS + si.MX_WORKLOADS + si.LLM_WORKLOADS + si.LLM_MX_WORKLOADS
     assert len({w.seed for w in every}) == len(every)
 
 

@@ -60,6 +60,10 @@ MUTANTS = {
                                 "(uint8_t)(byte & 0xF)"),
     "mx4_scale_row_ignored": ("return oracle_decode_fp4(code) * oracle_decode_e8m0(scales[row * (K / 32) + k / 32]);",
                               "return oracle_decode_fp4(code) * oracle_decode_e8m0(scales[k / 32]);"),
+    "mx4_points_rows_cols_swapped": ("s = s + mx4_val(A, SA, rows[p], K, k) * mx4_val(Bt, SB, cols[p], K, k);",
+                                     "s = s + mx4_val(A, SA, cols[p], K, k) * mx4_val(Bt, SB, rows[p], K, k);"),
+    "mx4_points_b_nibble_inverted": ("s = s + mx4_val(A, SA, rows[p], K, k) * mx4_val(Bt, SB, cols[p], K, k);",
+                                     "s = s + mx4_val(A, SA, rows[p], K, k) * mx4_val(Bt, SB, cols[p], K, k ^ 1);"),
     "mx_last_block_dropped": ("for (int64_t k = 0; k < K; ++k)\n                s = s + mx_val(fmt_a, A, SA, i, K, k)",
                               "for (int64_t k = 0; k < K - 32; ++k)\n                s = s + mx_val(fmt_a, A, SA, i, K, k)"),
 }
