@@ -241,6 +241,27 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k,
                             int64_t N, int64_t K, void* workspace,
                             uint64_t workspace_bytes, void* stream);
 
+/* Bytes of the device scratch array behind sam_gemm_noalloc (64 MiB per GPU). */
+#define SAM_SCRATCH_BYTES (64ull << 20)
+
+/* C = A*B exactly as sam_gemm_f32 / sam_gemm_bf16 / sam_gemm_f16 (`dtype`
+ * SAM_F32, SAM_BF16 or SAM_F16; the same plan, kernels and bits) without a
+ * caller workspace and without any allocation: for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Split-K partials and stream-K slots go to
+ * a file-scope device array of SAM_SCRATCH_BYTES that each GPU holds from
+ * its first such call until the process ends. A plan whose workspace_bytes
+ * exceeds SAM_SCRATCH_BYTES is refused with SAM_ERR_WORKSPACE (use
+ * sam_gemm_<dtype> with a workspace for it). Nothing in the array needs to
+ * start at zero: every plan writes each workspace value before reading it.
+ * Every call on one GPU shares that GPU's array, so calls that overlap in
+ * time on one GPU (on different streams, or from different threads without
+ * ordering) race and may return wrong results; calls in order on one stream
+ * are safe. Other arguments, alignment and errors as for sam_gemm_f32. */
+sam_status sam_gemm_noalloc(sam_dtype dtype, const void* A, const void* B,
+                            float* C, int64_t M, int64_t N, int64_t K,
+                            void* stream);
+
 /* Checks once per process that the current device is gfx950 and that the
  * library's kernels are loadable on it. SAM_ERR_UNSUPPORTED_DEVICE if not. */
 sam_status sam_device_check(void);

@@ -98,6 +98,7 @@ def lib() -> ctypes.CDLL:
                                     u64, vp], ctypes.c_int),
         "sam_gemm_mxfp4": ([vp, vp, vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
         "sam_gemm_mxfp4_variant": ([i32, i32, vp, vp, vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
+        "sam_gemm_noalloc": ([ctypes.c_int, vp, vp, vp, i64, i64, i64, vp], ctypes.c_int),
         "sam_device_check": ([], ctypes.c_int),
         "sam_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "sam_last_error": ([], ctypes.c_char_p),
@@ -281,6 +282,21 @@ def gemm_variant(vid: int, A, B, C=None, split_k: int = 0, dtype=None, workspace
     ws_bytes = _workspace_bytes(workspace)
     _check(lib().sam_gemm_variant(vid, code, p["split_k"], _ptr(A), _ptr(B), _ptr(C), M, N, K,
                                   _ptr(workspace), ws_bytes, _stream_ptr(stream)))
+    return C
+
+
+SCRATCH_BYTES = 64 << 20   # SAM_SCRATCH_BYTES of include/sam.h
+
+
+def gemm_noalloc(A, B, C=None, dtype=None, stream=None):
+    """C = A·B through sam_gemm_noalloc: the plan of gemm(), with its
+    workspace in the library's per-GPU scratch array (no allocation in the
+    library; C is allocated here only when not given)."""
+    code = _operands(A, B, dtype)
+    M, K = A.shape
+    N = B.shape[1]
+    C = _output(C, M, N, (A, B), ("A", "B"))
+    _check(lib().sam_gemm_noalloc(code, _ptr(A), _ptr(B), _ptr(C), M, N, K, _stream_ptr(stream)))
     return C
 
 

@@ -17,6 +17,13 @@
 #define SAM_BUILD_STAMP "sam (unstamped build)"
 #endif
 
+// Workspace of sam_gemm_noalloc: split-K partials and stream-K slots live in
+// this array instead of caller memory. Each GPU the library runs on holds its
+// own copy until the process ends. In host code `scratch` only names the
+// symbol; its device address, which differs per GPU, comes from
+// hipGetSymbolAddress with that GPU current and is kept per device below.
+static __device__ __align__(256) unsigned char scratch[SAM_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -110,6 +117,33 @@ void to_public(const sam::Plan& p, sam_plan* out)
     out->grid_wgs = p.grid;
     out->workspace_bytes = p.ws_bytes;
     out->est_us = p.est_us;
+}
+
+std::atomic<void*> g_scratch[kMaxDevices];
+
+sam_status scratch_address(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return fail(SAM_ERR_UNSUPPORTED_DEVICE, "no usable HIP device");
+    }
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return fail(SAM_ERR_INTERNAL, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                            hipGetErrorString(e));
+            }
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SAM_OK;
 }
 
 // Block-scaled operands: scale codes and element formats (B is then given
@@ -484,6 +518,31 @@ sam_status sam_gemm_mxfp4_variant(int32_t id, int32_t split_k, const uint8_t* A,
     if (id < 0) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);
     return gemm_mx_impl(sam::DT_MX4, id, split_k, 0, 0, A, scale_a, Bt, scale_b, C, M, N, K, workspace,
                         workspace_bytes, stream);
+}
+
+sam_status sam_gemm_noalloc(sam_dtype dtype, const void* A, const void* B, float* C, int64_t M, int64_t N,
+                            int64_t K, void* stream)
+{
+    if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+    sam_status st = check_shape(M, N, K);
+    if (st != SAM_OK) return st;
+    sam::Plan p{};
+    if (!sam::plan_auto(M, N, K, dtype, &p)) return fail(SAM_ERR_INTERNAL, "no admissible plan");
+    if (p.ws_bytes > SAM_SCRATCH_BYTES) {
+        char name[64];
+        sam::plan_name(p, name, sizeof(name));
+        return fail(SAM_ERR_WORKSPACE,
+                    "plan %s needs %llu workspace bytes; the scratch array of sam_gemm_noalloc holds %llu",
+                    name, (unsigned long long)p.ws_bytes, (unsigned long long)SAM_SCRATCH_BYTES);
+    }
+    void* ws = nullptr;
+    if (p.ws_bytes > 0 && M > 0 && N > 0 && K > 0) {
+        st = device_check_impl();
+        if (st != SAM_OK) return st;
+        st = scratch_address(&ws);
+        if (st != SAM_OK) return st;
+    }
+    return run(p, A, B, C, M, N, K, ws, p.ws_bytes, stream);
 }
 
 sam_status sam_device_check(void) { return device_check_impl(); }

@@ -286,3 +286,19 @@ def test_binding_rejects_host_tensors_and_bad_c():
         sam.gemm_mxfp8(u8, s8, u8, s8)
     with pytest.raises(ValueError, match="GPU tensor"):
         sam.gemm_mxfp4(u8[:, :16].contiguous(), s8, u8[:, :16].contiguous(), s8)
+
+
+def test_noalloc_refusals_before_any_device_call():
+    """sam_gemm_noalloc refuses, on the host, a plan whose workspace exceeds
+    its scratch array (SAM_ERR_WORKSPACE) and bad dtypes or sizes; without a
+    GPU an ordinary call reports the missing device."""
+    vp = ctypes.c_void_p
+    big = sam.plan(4097, 3071, 8191, "f32")["workspace_bytes"]
+    assert big > sam.SCRATCH_BYTES
+    assert L.sam_gemm_noalloc(sam.F32, vp(16), vp(1 << 40), vp(1 << 41), 4097, 3071, 8191, None) == -3
+    assert "scratch" in sam.last_error()
+    assert L.sam_gemm_noalloc(sam.MXFP8, vp(16), vp(32), vp(48), 4, 4, 32, None) == -1
+    assert L.sam_gemm_noalloc(sam.F32, vp(16), vp(32), vp(48), -1, 4, 4, None) == -1
+    assert L.sam_gemm_noalloc(sam.F32, None, None, None, 0, 4, 4, None) == 0
+    rc = L.sam_gemm_noalloc(sam.F32, vp(16), vp(1 << 40), vp(1 << 41), 16, 8192, 8192, None)
+    assert rc == -5, rc
