@@ -166,6 +166,62 @@ __global__ void __launch_bounds__(512) vgpr_stream(const char* src, int region_b
     if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// LDS read rate of one CU: one workgroup of 8 waves per CU (the 96 KB array
+// keeps a second one off the CU), every lane issuing 16 independent reads per
+// iteration; read j of wave w covers the contiguous 64 x BYTES bytes at
+// ((16 w + j) x 64 x BYTES) mod 64 KB, so every address is inside the array
+// and the lanes of one read hit consecutive banks. KIND 0: 128-bit reads,
+// 1: 64-bit reads, 2: the transposing 64-bit read of 16-bit values. The
+// shader clock counter and the constant 100 MHz counter bracket the loop, so
+// the rate comes out per clock of the clock the CU actually ran at.
+template <int KIND>
+__global__ void __launch_bounds__(512) lds_read_rate(int iters, unsigned* sink, unsigned long long* ticks)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[96 * 1024];
+    for (int i = threadIdx.x; i < 65536 / 4; i += 512) reinterpret_cast<unsigned*>(lds)[i] = i * 2654435761u;
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int BYTES = KIND == 0 ? 16 : 8;
+    unsigned acc = 0;
+    const unsigned long long c0 = clock64(), r0 = wall_clock64();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int off = (((wave * 16 + j) * 64 * BYTES) & 65535) + lane * BYTES;
+            if constexpr (KIND == 0) {
+                const u4 v = *reinterpret_cast<const u4*>(lds + off);
+                acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+            } else if constexpr (KIND == 1) {
+                const unsigned long long v = *reinterpret_cast<const unsigned long long*>(lds + off);
+                acc ^= (unsigned)v ^ (unsigned)(v >> 32);
+            } else {
+                typedef short v4s __attribute__((ext_vector_type(4)));
+                const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s*)(lds + off));
+                acc ^= (unsigned)(unsigned short)v[0] ^ ((unsigned)(unsigned short)v[1] << 16) ^
+                       (unsigned)(unsigned short)v[2] ^ ((unsigned)(unsigned short)v[3] << 16);
+            }
+        }
+        asm volatile("" ::: "memory");   // the reads stay inside the loop
+    }
+    __syncthreads();
+    const unsigned long long c1 = clock64(), r1 = wall_clock64();
+    if (threadIdx.x == 0) {
+        ticks[2 * blockIdx.x] = c1 - c0;
+        ticks[2 * blockIdx.x + 1] = r1 - r0;
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+// Which SIMD each wave of a 512-thread workgroup runs on: the SIMD field of
+// the HW_ID hardware register (bits 5:4 on gfx9-family parts), one entry per
+// wave of every workgroup.
+__global__ void __launch_bounds__(512) wave_simd(int* out)
+{
+    const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);
+    if ((threadIdx.x & 63) == 0) out[blockIdx.x * 8 + (threadIdx.x >> 6)] = (int)((hw >> 4) & 3);
+}
+
 static float time_ms(hipEvent_t a, hipEvent_t b) {
     float ms = 0;
     CHECK(hipEventElapsedTime(&ms, a, b));
@@ -273,7 +329,61 @@ int main(int argc, char** argv)
             }
             printf("}");
         }
-        printf("}}\n");
+        printf("}, ");
+    }
+    // LDS read rate per CU, bytes per shader clock (mean over CUs).
+    {
+        unsigned long long* ticks;
+        CHECK(hipMalloc(&ticks, (size_t)cus * 2 * sizeof(unsigned long long)));
+        const int iters = 4096;
+        const char* kn[3] = {"ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16"};
+        const int bytes_per_lane[3] = {16, 8, 8};
+        printf("\"lds_read\": {");
+        for (int kind = 0; kind < 3; ++kind) {
+            double bpc = 0, ghz = 0;
+            for (int rep = 0; rep < 3; ++rep) {
+                switch (kind) {
+                case 0: hipLaunchKernelGGL(lds_read_rate<0>, dim3(cus), dim3(512), 0, 0, iters, sink, ticks); break;
+                case 1: hipLaunchKernelGGL(lds_read_rate<1>, dim3(cus), dim3(512), 0, 0, iters, sink, ticks); break;
+                default: hipLaunchKernelGGL(lds_read_rate<2>, dim3(cus), dim3(512), 0, 0, iters, sink, ticks); break;
+                }
+                CHECK(hipGetLastError());
+                CHECK(hipDeviceSynchronize());
+            }
+            unsigned long long* h = (unsigned long long*)malloc((size_t)cus * 2 * sizeof(unsigned long long));
+            CHECK(hipMemcpy(h, ticks, (size_t)cus * 2 * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+            const double per_cu = 8.0 * iters * 16 * 64 * bytes_per_lane[kind];
+            for (int c = 0; c < cus; ++c) {
+                bpc += per_cu / (double)h[2 * c];
+                ghz += (double)h[2 * c] / (double)h[2 * c + 1] * 0.1;   // wall clock counter runs at 100 MHz
+            }
+            free(h);
+            printf("%s\"%s\": {\"bytes_per_clk_cu\": %.1f, \"clock_ghz\": %.3f}", kind ? ", " : "", kn[kind],
+                   bpc / cus, ghz / cus);
+        }
+        printf("}, ");
+        CHECK(hipFree(ticks));
+    }
+    // SIMD of each wave: how often wave w of a workgroup sits on SIMD w % 4.
+    {
+        int* d;
+        CHECK(hipMalloc(&d, (size_t)cus * 8 * sizeof(int)));
+        hipLaunchKernelGGL(wave_simd, dim3(cus), dim3(512), 0, 0, d);
+        CHECK(hipGetLastError());
+        int* h = (int*)malloc((size_t)cus * 8 * sizeof(int));
+        CHECK(hipMemcpy(h, d, (size_t)cus * 8 * sizeof(int), hipMemcpyDeviceToHost));
+        int match = 0, pair_split = 0;
+        for (int b = 0; b < cus; ++b) {
+            for (int w = 0; w < 8; ++w) match += h[b * 8 + w] == w % 4;
+            int ok = 1;   // waves w and w + 4 on one SIMD, the four SIMDs all used
+            for (int w = 0; w < 4; ++w) ok &= h[b * 8 + w] == h[b * 8 + w + 4];
+            pair_split += ok;
+        }
+        printf("\"wave_simd\": {\"block0\": [%d, %d, %d, %d, %d, %d, %d, %d], \"waves_on_simd_w_mod_4\": %d, "
+               "\"blocks_with_w_and_w_plus_4_together\": %d, \"blocks\": %d}}\n",
+               h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7], match, pair_split, cus);
+        free(h);
+        CHECK(hipFree(d));
     }
     CHECK(hipFree(src));
     CHECK(hipFree(dst));
