@@ -89,6 +89,17 @@ typedef struct {
     int64_t grid_wgs;          /* workgroups of the main kernel              */
     uint64_t workspace_bytes;  /* device workspace the call needs (0 if none) */
     double est_us;             /* the dispatcher's cost estimate, microseconds */
+    int32_t raster_n;          /* 0: groups of group_m tile rows sweep the tile
+                                  columns (M-major); 1: groups of group_m tile
+                                  columns sweep the rows (N-major)           */
+    int32_t operand_swap;      /* 1: the MFMA takes B's fragment as its first
+                                  operand, so accumulators hold the transposed
+                                  block (stored 16 bytes per lane)           */
+    int64_t sk_dp_tiles;       /* stream-K: leading tiles run one per
+                                  workgroup before the shared ones (16-bit)  */
+    int32_t tuned;             /* 0 cost model, 1 frozen table (this shape),
+                                  2 frozen table (a measured shape in the same
+                                  half-octave bucket)                        */
 } sam_plan;
 
 /* The plan sam_gemm_<dtype> would run for this shape. Host only: touches no
@@ -228,9 +239,29 @@ sam_status sam_variant_info(int32_t id, sam_plan* out);
  * variants with tiles up to 128 x 256, when the shape has at least as many K
  * iterations as resident workgroups). SAM_ERR_UNSUPPORTED if the variant does
  * not take `dtype` or the split is not admissible for the shape;
- * SAM_ERR_INVALID_ARG for split_k < -1. */
+ * SAM_ERR_INVALID_ARG for split_k < -1. The 16-bit 16x16x32 ring variants
+ * have a stream-K form too: whole waves of tiles run one per workgroup and
+ * the tiles of the last, partial wave share their K iterations. */
 sam_status sam_variant_plan(int32_t id, int64_t M, int64_t N, int64_t K,
                             sam_dtype dtype, int32_t split_k, sam_plan* out);
+
+/* The same with a forced raster order: raster_n = 0 (M-major), 1 (N-major)
+ * or -1 (the one the cost model prefers for this variant and split; ties go
+ * to M-major). The raster order decides which tiles run together and so how
+ * much of each A and B panel the XCD's L2 serves to several of them (page
+ * "fix(fp4_gemm autotune) SM107 kernel family excluded from autotune
+ * candidates and heuristics update - #4856", section "Swap × raster
+ * experiment: tile reuse root cause"). SAM_ERR_INVALID_ARG for other
+ * raster_n; SAM_ERR_UNSUPPORTED where the variant has no tiles (the streaming
+ * skinny kernels) and raster_n is 1. */
+sam_status sam_variant_plan_r(int32_t id, int64_t M, int64_t N, int64_t K,
+                              sam_dtype dtype, int32_t split_k, int32_t raster_n,
+                              sam_plan* out);
+
+/* The cost model's own plan for this shape, ignoring the frozen table of
+ * measured shapes (host only; for calibration reports and tests). */
+sam_status sam_gemm_plan_model(int64_t M, int64_t N, int64_t K, sam_dtype dtype,
+                               sam_plan* out);
 
 /* Run a forced variant (tests, profiling and calibration). Operands as for
  * sam_gemm_<dtype> (16-bit ones as uint16_t patterns). SAM_MXFP8 and
@@ -261,6 +292,14 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k,
 sam_status sam_gemm_noalloc(sam_dtype dtype, const void* A, const void* B,
                             float* C, int64_t M, int64_t N, int64_t K,
                             void* stream);
+
+/* sam_gemm_variant with a forced raster order (raster_n as for
+ * sam_variant_plan_r). */
+sam_status sam_gemm_variant_r(int32_t id, sam_dtype dtype, int32_t split_k,
+                              int32_t raster_n, const void* A, const void* B,
+                              float* C, int64_t M, int64_t N, int64_t K,
+                              void* workspace, uint64_t workspace_bytes,
+                              void* stream);
 
 /* Checks once per process that the current device is gfx950 and that the
  * library's kernels are loadable on it. SAM_ERR_UNSUPPORTED_DEVICE if not. */

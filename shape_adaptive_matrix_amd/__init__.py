@@ -49,7 +49,8 @@ class SamPlan(ctypes.Structure):
         ("split_k", ctypes.c_int32), ("group_m", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
         ("a_vector", ctypes.c_int32), ("b_vector", ctypes.c_int32),
         ("grid_wgs", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
-        ("est_us", ctypes.c_double),
+        ("est_us", ctypes.c_double), ("raster_n", ctypes.c_int32), ("operand_swap", ctypes.c_int32),
+        ("sk_dp_tiles", ctypes.c_int64), ("tuned", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -88,6 +89,9 @@ def lib() -> ctypes.CDLL:
         "sam_variant_info": ([i32, P], ctypes.c_int),
         "sam_variant_plan": ([i32, i64, i64, i64, ctypes.c_int, i32, P], ctypes.c_int),
         "sam_gemm_variant": ([i32, ctypes.c_int, i32, vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
+        "sam_variant_plan_r": ([i32, i64, i64, i64, ctypes.c_int, i32, i32, P], ctypes.c_int),
+        "sam_gemm_variant_r": ([i32, ctypes.c_int, i32, i32, vp, vp, vp, i64, i64, i64, vp, u64, vp], ctypes.c_int),
+        "sam_gemm_plan_model": ([i64, i64, i64, ctypes.c_int, P], ctypes.c_int),
         "sam_gemm_ex": ([ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, ctypes.c_float, vp, i64, vp, i64,
                          ctypes.c_float, vp, i64, vp, u64, vp], ctypes.c_int),
         "sam_gemm_ex_workspace": ([ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i64, i64,
@@ -147,9 +151,18 @@ def variant_info(vid: int) -> dict:
     return p.as_dict()
 
 
-def variant_plan(vid: int, M: int, N: int, K: int, dtype="f32", split_k: int = 0) -> dict:
+def variant_plan(vid: int, M: int, N: int, K: int, dtype="f32", split_k: int = 0, raster: int = -1) -> dict:
+    """Plan of a forced variant and split (0: its own choice, -1: stream-K)
+    and raster order (-1: the cost model's choice, 0 M-major, 1 N-major)."""
     p = SamPlan()
-    _check(lib().sam_variant_plan(vid, M, N, K, _dt(dtype), split_k, ctypes.byref(p)))
+    _check(lib().sam_variant_plan_r(vid, M, N, K, _dt(dtype), split_k, raster, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def plan_model(M: int, N: int, K: int, dtype="f32") -> dict:
+    """The cost model's own plan, ignoring the frozen table (host only)."""
+    p = SamPlan()
+    _check(lib().sam_gemm_plan_model(M, N, K, _dt(dtype), ctypes.byref(p)))
     return p.as_dict()
 
 
@@ -270,18 +283,20 @@ def gemm(A, B, C=None, dtype=None, workspace=None, stream=None):
     return C
 
 
-def gemm_variant(vid: int, A, B, C=None, split_k: int = 0, dtype=None, workspace=None, stream=None):
-    """C = A·B with a forced variant (and split; 0 = the variant's own pick)."""
+def gemm_variant(vid: int, A, B, C=None, split_k: int = 0, dtype=None, workspace=None, stream=None,
+                 raster: int = -1):
+    """C = A·B with a forced variant (and split; 0 = the variant's own pick;
+    raster -1 = the cost model's raster order, 0 M-major, 1 N-major)."""
     code = _operands(A, B, dtype)
     M, K = A.shape
     N = B.shape[1]
     C = _output(C, M, N, (A, B), ("A", "B"), workspace)
-    p = variant_plan(vid, M, N, K, code, split_k)
+    p = variant_plan(vid, M, N, K, code, split_k, raster)
     if workspace is None:
         workspace = workspace_for(p, A.device, stream)
     ws_bytes = _workspace_bytes(workspace)
-    _check(lib().sam_gemm_variant(vid, code, p["split_k"], _ptr(A), _ptr(B), _ptr(C), M, N, K,
-                                  _ptr(workspace), ws_bytes, _stream_ptr(stream)))
+    _check(lib().sam_gemm_variant_r(vid, code, p["split_k"], p["raster_n"], _ptr(A), _ptr(B), _ptr(C), M, N, K,
+                                    _ptr(workspace), ws_bytes, _stream_ptr(stream)))
     return C
 
 

@@ -117,6 +117,10 @@ void to_public(const sam::Plan& p, sam_plan* out)
     out->grid_wgs = p.grid;
     out->workspace_bytes = p.ws_bytes;
     out->est_us = p.est_us;
+    out->raster_n = p.raster_n;
+    out->operand_swap = p.swap;
+    out->sk_dp_tiles = p.sk ? p.sk_dp : 0;
+    out->tuned = p.tuned;
 }
 
 std::atomic<void*> g_scratch[kMaxDevices];
@@ -211,6 +215,7 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         a.tiles_n = p.tiles_n;
         a.group_m = p.group_m;
         a.xcd_remap = p.xcd_remap;
+        a.raster_n = p.raster_n;
         a.part_stride = M * N;
         if (mx) {
             a.sa = mx->sa;
@@ -221,7 +226,8 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         if (p.sk) {
             a.ws = static_cast<float*>(ws);
             a.sk_iters = (int)((K + p.bk - 1) / p.bk);
-            a.sk_grid = (int)p.grid;
+            a.sk_grid = p.sk_g;
+            a.sk_dp = p.sk_dp;
         }
         e = sam::launch_gemm(p, a, s);
         if (e == hipSuccess && p.split > 1)
@@ -426,16 +432,24 @@ sam_status sam_variant_info(int32_t id, sam_plan* out)
 sam_status sam_variant_plan(int32_t id, int64_t M, int64_t N, int64_t K, sam_dtype dtype,
                             int32_t split_k, sam_plan* out)
 {
+    return sam_variant_plan_r(id, M, N, K, dtype, split_k, -1, out);
+}
+
+sam_status sam_variant_plan_r(int32_t id, int64_t M, int64_t N, int64_t K, sam_dtype dtype, int32_t split_k,
+                              int32_t raster_n, sam_plan* out)
+{
     if (!out) return fail(SAM_ERR_INVALID_ARG, "out is null");
+    if (raster_n < -1 || raster_n > 1)
+        return fail(SAM_ERR_INVALID_ARG, "raster_n %d (-1 the dispatcher's choice, 0 M-major, 1 N-major)", raster_n);
     if (dtype < SAM_F32 || dtype > SAM_MXFP4) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
     if (split_k < -1) return fail(SAM_ERR_INVALID_ARG, "split %d (-1 is stream-K, 0 the variant's choice)", split_k);
     sam_status st = check_shape(M, N, K);
     if (st != SAM_OK) return st;
     if (!sam::variant_get(id)) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);
     sam::Plan p{};
-    if (!sam::plan_for_variant(id, M, N, K, dtype, split_k, &p))
-        return fail(SAM_ERR_UNSUPPORTED, "variant %d cannot run dtype %d with split %d for K=%lld", id,
-                    (int)dtype, split_k, (long long)K);
+    if (!sam::plan_for_variant(id, M, N, K, dtype, split_k, &p, raster_n))
+        return fail(SAM_ERR_UNSUPPORTED, "variant %d cannot run dtype %d with split %d, raster %d for K=%lld", id,
+                    (int)dtype, split_k, raster_n, (long long)K);
     to_public(p, out);
     return SAM_OK;
 }
@@ -444,6 +458,15 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k, const 
                             float* C, int64_t M, int64_t N, int64_t K, void* workspace,
                             uint64_t workspace_bytes, void* stream)
 {
+    return sam_gemm_variant_r(id, dtype, split_k, -1, A, B, C, M, N, K, workspace, workspace_bytes, stream);
+}
+
+sam_status sam_gemm_variant_r(int32_t id, sam_dtype dtype, int32_t split_k, int32_t raster_n, const void* A,
+                              const void* B, float* C, int64_t M, int64_t N, int64_t K, void* workspace,
+                              uint64_t workspace_bytes, void* stream)
+{
+    if (raster_n < -1 || raster_n > 1)
+        return fail(SAM_ERR_INVALID_ARG, "raster_n %d (-1 the dispatcher's choice, 0 M-major, 1 N-major)", raster_n);
     if (dtype == SAM_MXFP8 || dtype == SAM_MXFP4)
         return fail(SAM_ERR_INVALID_ARG, "block-scaled operands go through sam_gemm_mxfp8_variant / sam_gemm_mxfp4_variant");
     if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
@@ -452,10 +475,22 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k, const 
     if (st != SAM_OK) return st;
     if (!sam::variant_get(id)) return fail(SAM_ERR_INVALID_ARG, "no variant %d", id);
     sam::Plan p{};
-    if (!sam::plan_for_variant(id, M, N, K, dtype, split_k, &p))
-        return fail(SAM_ERR_UNSUPPORTED, "variant %d cannot run dtype %d with split %d for K=%lld", id,
-                    (int)dtype, split_k, (long long)K);
+    if (!sam::plan_for_variant(id, M, N, K, dtype, split_k, &p, raster_n))
+        return fail(SAM_ERR_UNSUPPORTED, "variant %d cannot run dtype %d with split %d, raster %d for K=%lld", id,
+                    (int)dtype, split_k, raster_n, (long long)K);
     return run(p, A, B, C, M, N, K, workspace, workspace_bytes, stream);
+}
+
+sam_status sam_gemm_plan_model(int64_t M, int64_t N, int64_t K, sam_dtype dtype, sam_plan* out)
+{
+    if (!out) return fail(SAM_ERR_INVALID_ARG, "out is null");
+    if (dtype < SAM_F32 || dtype > SAM_MXFP4) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+    sam_status st = check_shape(M, N, K);
+    if (st != SAM_OK) return st;
+    sam::Plan p{};
+    if (!sam::plan_model(M, N, K, dtype, &p)) return fail(SAM_ERR_INTERNAL, "no admissible plan");
+    to_public(p, out);
+    return SAM_OK;
 }
 
 // dtype DT_MX8 (formats fmt_a / fmt_b) or DT_MX4 (E2M1; formats ignored).

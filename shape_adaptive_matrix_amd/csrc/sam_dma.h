@@ -72,16 +72,24 @@ __device__ __forceinline__ int logical_wg(int wg, int total, int remap) {
     return (x < rem) ? x * (q + 1) + y : rem * (q + 1) + (x - rem) * q + y;
 }
 
-// Tile index -> (tile row, tile column) in grouped-raster order: group_m tile
-// rows sweep the tile columns together.
+// Tile index -> (tile row, tile column) in grouped-raster order. M-major
+// (raster_n = 0): group_m tile rows sweep the tile columns together, the
+// rows of a group taking consecutive indices. N-major (raster_n = 1): the
+// same with rows and columns exchanged, group_m tile columns sweeping the
+// rows (the raster-order choice of page "fix(fp4_gemm autotune) SM107 kernel
+// family excluded from autotune candidates and heuristics update - #4856",
+// section "Swap × raster experiment: tile reuse root cause").
 __device__ __forceinline__ void tile_of(int t, const GemmArgs& a, int& tm, int& tn) {
-    const int per_group = a.group_m * a.tiles_n;
+    const int lead = a.raster_n ? a.tiles_n : a.tiles_m;    // the grouped dimension
+    const int other = a.raster_n ? a.tiles_m : a.tiles_n;
+    const int per_group = a.group_m * other;
     const int grp = t / per_group;
-    const int first_m = grp * a.group_m;
-    const int gsz = min(a.tiles_m - first_m, a.group_m);
+    const int first = grp * a.group_m;
+    const int gsz = min(lead - first, a.group_m);
     const int r = t - grp * per_group;
-    tm = first_m + r % gsz;
-    tn = r / gsz;
+    const int x = first + r % gsz, y = r / gsz;
+    tm = a.raster_n ? y : x;
+    tn = a.raster_n ? x : y;
 }
 
 // Workgroup id -> (tile row, tile column, split); the split index is the

@@ -24,7 +24,8 @@ struct DeviceModel {
     double hbm_gbs = 5900.0;       // measured streaming read rate
     double tiled_hbm_frac = 0.75;  // share of it the LDS-tiled kernels reach when HBM-bound (calibrated)
     double hbm_write_gbs = 6000.0; // rate the epilogue write phase drains at (calibrated)
-    double l2_gbs = 20000.0;       // aggregate L2/MALL delivery, rough
+    double l2_gbs = 16000.0;       // operand delivery from L2 into LDS, chip-wide (calibrated)
+    double fabric_gbs = 7000.0;    // L2 misses: delivery from beyond L2, chip-wide (measured)
     double launch_us = 4.0;        // per kernel launch, rough
 };
 
@@ -46,6 +47,7 @@ struct Variant {
     int xcd_remap;       // 1: remap workgroup ids so each XCD gets a contiguous range
     int max_split;       // largest split-K the variant is planned with
     int elem_loads;      // takes rows that are not whole 16-byte pieces (K or N odd for FP32)
+    int swap;            // MFMA operands exchanged: the accumulators hold the transposed block
     double eff_f32;      // calibrated fraction of MFMA peak it sustains in steady state
                          // (streaming variants: fraction of the HBM read rate)
     double eff_h16;
@@ -70,7 +72,9 @@ struct GemmArgs {
     long long part_stride;  // M*N (elements between consecutive partials)
     float* ws;           // stream-K: partial-tile slots (2 per workgroup, BM*BN floats each)
     int sk_iters;        // stream-K: K iterations per tile (0: data-parallel launch)
-    int sk_grid;         // stream-K: workgroups of the main kernel
+    int sk_grid;         // stream-K: workgroups sharing the stream-K tiles' iterations
+    int sk_dp;           // stream-K: leading tiles run one per workgroup before them (16-bit form)
+    int raster_n;        // 1: raster groups of group_m tile columns walk the rows (N-major)
     const unsigned char* sa;   // block-scaled operands: scale codes of A (M x K/32)
     const unsigned char* sb;   // ... and of B (N x K/32); B is then N rows of K codes
     int fmt_a, fmt_b;    // element formats: 0 E4M3, 1 E5M2
@@ -94,12 +98,19 @@ struct Plan {
     double est_us;
     int tuned;           // 1: taken from the frozen table of measured shapes
     int sk;              // 1: stream-K (grid = persistent workgroups, split == 1)
+    int sk_dp;           // stream-K: tiles run one per workgroup ahead of the shared ones
+    int sk_g;            // stream-K: workgroups sharing the remaining tiles' iterations
+    int raster_n;        // 0: groups of group_m tile rows sweep the columns; 1: the transpose
+    int swap;            // 1: MFMA operands exchanged (accumulators hold the transposed block)
 };
 
 // Dispatcher (sam_plan.cpp). Host only, pure.
+// raster_req: -1 lets the cost model pick the raster order, 0 / 1 forces it.
 bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
-                      int split_req, Plan* out);
+                      int split_req, Plan* out, int raster_req = -1);
 bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out);
+// The cost model's own choice, ignoring the frozen table.
+bool plan_model(long long M, long long N, long long K, int dtype, Plan* out);
 void plan_name(const Plan& p, char* buf, int n);
 int k_stage(const Variant& v, int dtype);   // K per LDS stage
 
@@ -109,6 +120,7 @@ hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_stream(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s);
+hipError_t launch_sk_fixup_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mx8(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_kq(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_kp(const Plan& p, const GemmArgs& a, hipStream_t s);

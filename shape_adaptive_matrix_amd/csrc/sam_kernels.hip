@@ -26,6 +26,7 @@
 // No atomics: the K order of every output is fixed, which makes repeated
 // runs bitwise identical (page "Measured data point on fixed-tile vs
 // shape-adaptive GEMM", question 2).
+#include "sam_dma.h"
 #include "sam_internal.h"
 #include "sam_variants.h"
 
@@ -117,22 +118,7 @@ template <> __device__ __forceinline__ int acc_row<16>(int lane, int r) {
 }
 
 __device__ __forceinline__ void tile_coords(int wg, const GemmArgs& a, int& tm, int& tn, int& s) {
-    const int total = a.tiles_m * a.tiles_n * a.split;
-    int L = wg;
-    if (a.xcd_remap) {
-        const int q = total >> 3, rem = total & 7, x = wg & 7, y = wg >> 3;
-        L = (x < rem) ? x * (q + 1) + y : rem * (q + 1) + (x - rem) * q + y;
-    }
-    const int tiles = a.tiles_m * a.tiles_n;
-    s = L / tiles;
-    const int t = L - s * tiles;
-    const int per_group = a.group_m * a.tiles_n;
-    const int g = t / per_group;
-    const int first_m = g * a.group_m;
-    const int gsz = min(a.tiles_m - first_m, a.group_m);
-    const int r = t - g * per_group;
-    tm = first_m + r % gsz;
-    tn = r / gsz;
+    dma::tile_coords(wg, a, tm, tn, s);
 }
 
 // 16-bit lane select: half `h` (0 low, 1 high) of x and y -> (x_h | y_h << 16).

@@ -33,6 +33,7 @@
 // bits.
 #include "sam_dma.h"
 #include "sam_internal.h"
+#include "sam_sk.h"
 #include "sam_variants.h"
 
 namespace sam {
@@ -95,11 +96,24 @@ template <int DT> struct Mf<DT, 16> {
 //         transposed there (one v_perm per output dword) and stored
 //         K-contiguous, so its fragments are full-rate 128-bit LDS reads
 //         instead of half-rate transposing reads.
-template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK>
-__global__ void __launch_bounds__(WM * WN * 64)
-__attribute__((amdgpu_waves_per_eu(1, (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 > 0
-                                           ? (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 : 1)))
-gemm16_dma_kernel(GemmArgs args)
+//
+// SWAP (16x16x32 blocks only): the MFMA takes the B fragment as its first
+// operand and the A fragment as its second, so it computes the transposed
+// block (C^T = B^T A^T on the block) and each lane's four accumulator values
+// are four adjacent columns of one row of C, stored with one 16-byte store
+// instead of four 4-byte ones (the operand-swap schedule of page
+// "fix(fp4_gemm autotune) SM107 kernel family excluded from autotune
+// candidates and heuristics update - #4856", section "Swap microbenchmarks
+// across M, N, and K", in its form for a symmetric matrix instruction).
+//
+// One output tile over K values [kbeg, kend). SEG = false: the tile goes to C
+// or to split `ostride`'s partial slice; SEG = true (a segment of a stream-K
+// workgroup): to `outp` with row stride `ostride`, of which `orows` x `ocols`
+// are stored. The ring is this function's own LDS array, so a kernel that
+// instantiates it once holds one ring.
+template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK, int SWAP, bool SEG>
+__device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int tn, int kbeg, int kend, float* outp,
+                                               int ostride, int orows, int ocols)
 {
     using namespace dma;
     static_assert(DT == DT_BF16 || DT == DT_F16, "16-bit operands only");
@@ -134,18 +148,19 @@ gemm16_dma_kernel(GemmArgs args)
     static_assert(MODE == 0 || (NBUF == 2 && KSTEPS >= 3), "register-filled stages need NBUF 2, >= 3 k-steps");
     static_assert(MODE != 2 || NBS * NT == (BK / 8) * (BN / 8), "B blocks must split evenly over threads");
     static_assert((NBUF - 1) * LPS < 64, "vmcnt range");
+    static_assert(SWAP == 0 || BLK == 16, "operand swap: 16x16x32 blocks");
+    static_assert(!SEG || MODE == 0, "stream-K segments: loads straight into LDS");
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    int tm, tn, s;
-    tile_coords(blockIdx.x, args, tm, tn, s);
+    // Uniform across the wave: held in a scalar register, so everything
+    // derived from it alone stays out of the vector registers (at 256 VGPRs
+    // the difference decides whether addresses spill inside the K loop).
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int M = args.M, N = args.N, K = args.K;
     const int m0 = tm * BM, n0 = tn * BN;
-    const int kbeg = s * args.k_chunk;
-    const int kend = min(K, kbeg + args.k_chunk);
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
     const int wm0 = (wave / WN) * WTM;
     const int wn0 = (wave % WN) * WTN;
@@ -288,7 +303,10 @@ gemm16_dma_kernel(GemmArgs args)
     auto mfma_one = [&](int m, const u4 (&fa)[TM], const u2 (&fb)[TN][2]) {
         const int i = m / TN, j = m % TN;
         const u4 b = u4{fb[j][0][0], fb[j][0][1], fb[j][1][0], fb[j][1][1]};
-        MF::mfma(acc[i][j], fa[i], b);
+        if constexpr (SWAP)
+            MF::mfma(acc[i][j], b, fa[i]);
+        else
+            MF::mfma(acc[i][j], fa[i], b);
     };
 
     constexpr int NMF = TM * TN;          // MFMAs per k-step
@@ -425,23 +443,119 @@ gemm16_dma_kernel(GemmArgs args)
             for (int j = 0; j < TN; ++j) { fb[0][j][0] = fb[1][j][0]; fb[0][j][1] = fb[1][j][1]; }
         }
     }
-    wait_cnt<0, 0>();   // no LDS load may still be in flight when the workgroup ends
+    wait_cnt<0, 0>();   // no LDS load may still be in flight when the segment ends
 
-    float* outp = args.out + (long long)s * args.part_stride + (long long)m0 * N + n0;
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(outp, ((long long)(M - m0) * N - n0) * 4);
+    // The data-parallel form stores to C or to split `ostride`'s partial
+    // slice, at (m0, n0) with row stride N (formed here, so nothing of it is
+    // live through the K loop).
+    if constexpr (!SEG) {
+        outp = args.out + (long long)ostride * args.part_stride + (long long)m0 * N + n0;
+        orows = M - m0;
+        ocols = N - n0;
+        ostride = N;
+    }
+    const __amdgpu_buffer_rsrc_t rC =
+        SEG ? make_rsrc(outp, orows > 0 && ocols > 0 ? ((long long)(orows - 1) * ostride + ocols) * 4 : 0)
+            : make_rsrc(outp, ((long long)(M - m0) * N - n0) * 4);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = wn0 + BLK * j + lrow;
+            if constexpr (SWAP) {
+                // Transposed block: lane l holds row l % 16 of the block,
+                // columns 4 (l / 16) .. + 3 (N % 8 == 0, so the four are all
+                // inside C or all past it).
+                const int row = wm0 + BLK * i + lrow;
+                const int col = wn0 + BLK * j + 4 * lgrp;
+                const bool ok = row < orows && col < ocols;
+                const u4 v = {__float_as_uint(acc[i][j][0]), __float_as_uint(acc[i][j][1]),
+                              __float_as_uint(acc[i][j][2]), __float_as_uint(acc[i][j][3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, rC, ok ? (row * ostride + col) * 4 : kOOB, 0, 0);
+            } else {
+                const int col = wn0 + BLK * j + lrow;
 #pragma unroll
-            for (int r = 0; r < MF::NV; ++r) {
-                const int row = wm0 + BLK * i + MF::row(lane, r);
-                const bool ok = m0 + row < M && n0 + col < N;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rC,
-                                                      ok ? (row * N + col) * 4 : kOOB, 0, 0);
+                for (int r = 0; r < MF::NV; ++r) {
+                    const int row = wm0 + BLK * i + MF::row(lane, r);
+                    const bool ok = row < orows && col < ocols;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rC,
+                                                          ok ? (row * ostride + col) * 4 : kOOB, 0, 0);
+                }
             }
         }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NBUF>
+constexpr int ring16_waves_per_eu()
+{
+    return (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 > 0
+               ? (160 * 1024 / (NBUF * (BM + BN) * BK * 2)) * WM * WN / 4 : 1;
+}
+
+// Data-parallel form: one workgroup per (tile, split).
+template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK, int SWAP>
+__global__ void __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(1, ring16_waves_per_eu<BM, BN, WM, WN, BK, NBUF>())))
+gemm16_dma_kernel(GemmArgs args)
+{
+    int tm, tn, s;
+    dma::tile_coords(blockIdx.x, args, tm, tn, s);
+    const int kbeg = s * args.k_chunk;
+    const int kend = min(args.K, kbeg + args.k_chunk);
+    ring16_segment<DT, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SWAP, false>(args, tm, tn, kbeg, kend, nullptr, s, 0, 0);
+}
+
+// Data-parallel + stream-K form (page "fix(fp4_gemm autotune) SM107 kernel
+// family excluded from autotune candidates and heuristics update - #4856",
+// section "Swap microbenchmarks across M, N, and K": a last wave of tiles
+// that leaves CUs idle). The first sk_dp tiles (whole waves of resident
+// workgroups) run one per workgroup; the remaining T_sk tiles x I
+// K-iterations form W = T_sk I iterations shared by sk_grid workgroups in
+// equal ranges [floor(W g / G), floor(W (g + 1) / G)). Since T_sk < G, a
+// range spans at most two tiles. A tile wholly inside one range goes to C; a
+// shared tile leaves each share in a workspace slot (a range's first segment
+// in slot 2 g, its second in slot 2 g + 1) and the fix-up kernel adds them in
+// range order. All split points depend on the plan alone.
+template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK, int SWAP>
+__global__ void __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(1, ring16_waves_per_eu<BM, BN, WM, WN, BK, NBUF>())))
+gemm16_dma_sk_kernel(GemmArgs args)
+{
+    const long long I = args.sk_iters, dp = args.sk_dp;
+    const long long T = (long long)args.tiles_m * args.tiles_n;
+    const long long G = args.sk_grid, W = (T - dp) * I;
+    // Workgroups are dispatched in id order, so ids below sk_dp (whole waves)
+    // run the data-parallel tiles and the last wave the stream-K ranges. Each
+    // part is remapped onto the XCDs on its own: one remap over the whole
+    // grid would put stream-K ranges into the first wave and push
+    // data-parallel tiles into the last.
+    const bool is_dp = blockIdx.x < dp;
+    const long long L = is_dp ? dma::logical_wg(blockIdx.x, (int)dp, args.xcd_remap)
+                              : dp + dma::logical_wg(blockIdx.x - (int)dp, (int)G, args.xcd_remap);
+    // A data-parallel workgroup runs one job (its whole tile); a stream-K
+    // one runs the segments of its range. One copy of the tile pipeline
+    // serves every job (the loop is not unrolled), so nothing is held in
+    // registers from one job to the next.
+    const long long g = L - dp;
+    long long it = is_dp ? 0 : W * g / G;
+    const long long end = is_dp ? I : W * (g + 1) / G;
+#pragma clang loop unroll(disable)
+    for (int seg = 0; seg < 2; ++seg) {
+        if (it >= end) break;
+        const long long t = is_dp ? L : dp + it / I;
+        const int k0 = (int)(is_dp ? 0 : it - (t - dp) * I);
+        const int k1 = (int)min(I, (long long)k0 + (end - it));
+        int tm, tn;
+        dma::tile_of((int)t, args, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        if (seg > 0) dma::barrier();   // the previous segment's last LDS reads are done
+        const bool whole = k0 == 0 && k1 == I;
+        float* outp = whole ? args.out + (long long)m0 * args.N + n0
+                            : args.ws + (2 * g + seg) * (long long)(BM * BN);
+        ring16_segment<DT, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SWAP, true>(
+            args, tm, tn, k0 * BK, min(args.K, k1 * BK), outp, whole ? args.N : BN, whole ? args.M - m0 : BM,
+            whole ? args.N - n0 : BN);
+        it += k1 - k0;
     }
 }
 
@@ -450,25 +564,58 @@ typedef void (*KernelFn)(GemmArgs);
 struct DmaKernels {
     int id;
     KernelFn fn[3];
+    KernelFn sk[3];      // stream-K form (16x16x32 variants only)
+    KernelFn fixup;
+    int fixup_wgs;
     int threads;
 };
 
-#define SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, gm, xr, ms, e16)           \
-    {id, {nullptr, gemm16_dma_kernel<DT_BF16, BM, BN, WM, WN, BK, NBUF, MODE, BLK>,              \
-          gemm16_dma_kernel<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE, BLK>}, WM * WN * 64},
+template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK, int SWAP>
+constexpr KernelFn ring16_sk()
+{
+    if constexpr (MODE == 0 && BLK == 16)
+        return gemm16_dma_sk_kernel<DT, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SWAP>;
+    else
+        return nullptr;
+}
 
-static const DmaKernels kDmaTable[] = {SAM_DMA_VARIANTS(SAM_DMA_ENTRY) SAM_DMA16_VARIANTS(SAM_DMA_ENTRY)};
+#define SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW, gm, xr, ms, e16)                  \
+    {id,                                                                                               \
+     {nullptr, gemm16_dma_kernel<DT_BF16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW>,                    \
+      gemm16_dma_kernel<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW>},                             \
+     {nullptr, ring16_sk<DT_BF16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW>(),                          \
+      ring16_sk<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW>()},                                   \
+     sk_fixup_kernel<BM, BN>, sk_fixup_wgs<BM, BN>(), WM * WN * 64},
+#define SAM_DMA_ENTRY0(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, gm, xr, ms, e16) \
+    SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, 0, gm, xr, ms, e16)
+
+static const DmaKernels kDmaTable[] = {SAM_DMA_VARIANTS(SAM_DMA_ENTRY0) SAM_DMA16_VARIANTS(SAM_DMA_ENTRY0)
+                                           SAM_DMA16S_VARIANTS(SAM_DMA_ENTRY)};
+
+static const DmaKernels* dma_entry(int id)
+{
+    for (const DmaKernels& d : kDmaTable)
+        if (d.id == id) return &d;
+    return nullptr;
+}
 
 hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s)
 {
-    for (const DmaKernels& d : kDmaTable) {
-        if (d.id != p.variant_id) continue;
-        KernelFn fn = d.fn[p.dtype];
-        if (!fn) return hipErrorInvalidDeviceFunction;
-        hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(d.threads), 0, s, a);
-        return hipGetLastError();
-    }
-    return hipErrorInvalidDeviceFunction;
+    const DmaKernels* d = dma_entry(p.variant_id);
+    if (!d) return hipErrorInvalidDeviceFunction;
+    KernelFn fn = p.sk ? d->sk[p.dtype] : d->fn[p.dtype];
+    if (!fn) return hipErrorInvalidDeviceFunction;
+    hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(d->threads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sk_fixup_dma(const Plan& p, const GemmArgs& a, hipStream_t s)
+{
+    const DmaKernels* d = dma_entry(p.variant_id);
+    if (!d) return hipErrorInvalidDeviceFunction;
+    const long long tiles = (long long)p.tiles_m * p.tiles_n - p.sk_dp;
+    hipLaunchKernelGGL(d->fixup, dim3((unsigned)(tiles * d->fixup_wgs)), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace sam

@@ -42,6 +42,7 @@
 // bits.
 #include "sam_dma.h"
 #include "sam_internal.h"
+#include "sam_sk.h"
 #include "sam_variants.h"
 
 namespace sam {
@@ -466,56 +467,6 @@ gemm_f32_ring_sk_kernel(GemmArgs args)
     }
 }
 
-// Stream-K fix-up: sk_fixup_wgs workgroups per tile. A tile that lies in one
-// range was written by the main kernel; otherwise its shares are added in
-// range order, (((share of range g0) + share of g0 + 1) + ...), and the sum
-// is stored.
-__device__ __forceinline__ long long sk_start(long long W, long long G, long long g) { return W * g / G; }
-
-__device__ __forceinline__ long long sk_range_of(long long W, long long G, long long x) {
-    long long g = x * G / W;
-    while (g + 1 < G && sk_start(W, G, g + 1) <= x) ++g;
-    while (g > 0 && sk_start(W, G, g) > x) --g;
-    return g;
-}
-
-// Workgroups per tile in the fix-up: one float4 of the tile per thread.
-template <int BM, int BN>
-constexpr int sk_fixup_wgs() { return BM * BN / (256 * 4); }
-
-template <int BM, int BN>
-__global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs args)
-{
-    typedef float v4f __attribute__((ext_vector_type(4)));
-    constexpr int CH = sk_fixup_wgs<BM, BN>();
-    const long long I = args.sk_iters, T = (long long)args.tiles_m * args.tiles_n;
-    const long long W = T * I, G = args.sk_grid, t = blockIdx.x / CH;
-    const long long lo = t * I, hi = (t + 1) * I - 1;
-    const long long g0 = sk_range_of(W, G, lo), g1 = sk_range_of(W, G, hi);
-    if (g0 == g1) return;
-    int tm, tn;
-    dma::tile_of((int)t, args, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int e4 = (blockIdx.x % CH) * 256 + threadIdx.x;
-    const int r = e4 / (BN / 4), c = (e4 % (BN / 4)) * 4;
-    if (m0 + r >= args.M || n0 + c >= args.N) return;
-    const long long first_slot = sk_start(W, G, g0) == lo ? 2 * g0 : 2 * g0 + 1;
-    v4f sum = reinterpret_cast<const v4f*>(args.ws + first_slot * (BM * BN))[e4];
-#pragma unroll 4
-    for (long long g = g0 + 1; g <= g1; ++g) {
-        if (sk_start(W, G, g) == sk_start(W, G, g + 1)) continue;   // empty range
-        const v4f x = reinterpret_cast<const v4f*>(args.ws + 2 * g * (BM * BN))[e4];
-        sum[0] = sum[0] + x[0];
-        sum[1] = sum[1] + x[1];
-        sum[2] = sum[2] + x[2];
-        sum[3] = sum[3] + x[3];
-    }
-    float* crow = args.out + (long long)(m0 + r) * args.N + n0 + c;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (n0 + c + q < args.N) crow[q] = sum[q];
-}
-
 typedef void (*F32RingFn)(GemmArgs);
 
 // Stream-K forms exist for tiles up to 128 x 256: larger tiles run out of
@@ -578,6 +529,7 @@ hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s)
 
 hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s)
 {
+    if (p.kind == KIND_DMA) return launch_sk_fixup_dma(p, a, s);
     for (const F32RingKernel& k : kF32RingTable) {
         if (k.id != p.variant_id) continue;
         hipLaunchKernelGGL(k.fixup, dim3((unsigned)((long long)p.tiles_m * p.tiles_n * k.fixup_wgs)), dim3(256), 0, s,

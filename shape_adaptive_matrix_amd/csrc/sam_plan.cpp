@@ -31,6 +31,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "sam_internal.h"
 #include "sam_tuned.h"
 #include "sam_variants.h"
@@ -38,30 +40,32 @@
 namespace sam {
 
 #define SAM_STAGED_ROW(id, name, BM, BN, WM, WN, BLK, gm, xr, ms, e32, e16, pf32, pf16) \
-    {id, name, KIND_STAGED, 7, BM, BN, WM, WN, BLK, 2, 0, gm, xr, ms, 1, e32, e16},
+    {id, name, KIND_STAGED, 7, BM, BN, WM, WN, BLK, 2, 0, gm, xr, ms, 1, 0, e32, e16},
+#define SAM_DMA_ROWS(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW, gm, xr, ms, e16) \
+    {id, name, KIND_DMA, (1 << DT_BF16) | (1 << DT_F16), BM, BN, WM, WN, BLK, NBUF, BK, gm, xr, ms, 0, SW, 0.0, e16},
 #define SAM_DMA_ROW(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, gm, xr, ms, e16) \
-    {id, name, KIND_DMA, (1 << DT_BF16) | (1 << DT_F16), BM, BN, WM, WN, BLK, NBUF, BK, gm, xr, ms, 0, 0.0, e16},
+    SAM_DMA_ROWS(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, 0, gm, xr, ms, e16)
 
 #define SAM_STREAM_ROW(id, name, BM, BN, KB, ms, eff) \
-    {id, name, KIND_STREAM, (1 << DT_F32), BM, BN, 1, 1, 16, 1, KB, 1, 0, ms, 1, eff, 0.0},
+    {id, name, KIND_STREAM, (1 << DT_F32), BM, BN, 1, 1, 16, 1, KB, 1, 0, ms, 1, 0, eff, 0.0},
 
 #define SAM_F32RING_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32) \
-    {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, BLK, NBUF, BK, gm, xr, ms, EL, e32, 0.0},
+    {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, BLK, NBUF, BK, gm, xr, ms, EL, 0, e32, 0.0},
 
 #define SAM_MX8_ROW(id, name, BM, BN, WM, WN, BK, SD, gm, xr, ms, e8, e4) \
-    {id, name, KIND_MX8, (1 << DT_MX8) | (1 << DT_MX4), BM, BN, WM, WN, 32, 2, BK, gm, xr, ms, 0, 0.0, 0.0, e8, e4},
+    {id, name, KIND_MX8, (1 << DT_MX8) | (1 << DT_MX4), BM, BN, WM, WN, 32, 2, BK, gm, xr, ms, 0, 0, 0.0, 0.0, e8, e4},
 
 #define SAM_KQ_ROW(id, name, TB, NW, gm, xr, e32) \
-    {id, name, KIND_KQ, (1 << DT_F32), 16 * TB, 16 * TB, 1, NW, 16, NW == 4 ? 4 : 2, 16, gm, xr, 1, 1, e32, 0.0},
+    {id, name, KIND_KQ, (1 << DT_F32), 16 * TB, 16 * TB, 1, NW, 16, NW == 4 ? 4 : 2, 16, gm, xr, 1, 1, 0, e32, 0.0},
 
 #define SAM_KP_ROW(id, name, KP, gm, xr, e32) \
-    {id, name, KIND_KP, (1 << DT_F32), 128, 128, 4, 2, 16, 2, KP, gm, xr, 1, 0, e32, 0.0},
+    {id, name, KIND_KP, (1 << DT_F32), 128, 128, 4, 2, 16, 2, KP, gm, xr, 1, 0, 0, e32, 0.0},
 
 static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_VARIANTS(SAM_DMA_ROW)
                                         SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)
                                             SAM_MX8_VARIANTS(SAM_MX8_ROW) SAM_DMA16_VARIANTS(SAM_DMA_ROW)
                                                 SAM_KQ_VARIANTS(SAM_KQ_ROW) SAM_KP_VARIANTS(SAM_KP_ROW)
-                                                    SAM_KQ8_VARIANTS(SAM_KQ_ROW)};
+                                                    SAM_KQ8_VARIANTS(SAM_KQ_ROW) SAM_DMA16S_VARIANTS(SAM_DMA_ROWS)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -90,8 +94,44 @@ static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
 static const DeviceModel kDev;
 
+// Share of a tile kernel's operand requests that miss the XCD's L2: the
+// first tiles the XCD runs at once (one workgroup per CU, 32 per XCD, taken
+// in the raster order of tile_of: groups of group_m rows, or with raster_n of
+// group_m columns) request their A and B panels; panels shared by several of
+// them are fetched from beyond L2 once. Exact for the first wave of XCD 0,
+// representative of the rest.
+static double reuse_miss_frac(const Variant& v, long long tiles_m, long long tiles_n, int raster_n)
+{
+    const long long c = std::min<long long>(kDev.cus / kDev.xcds, tiles_m * tiles_n);
+    if (c <= 0) return 1.0;
+    const long long lead = raster_n ? tiles_n : tiles_m, other = raster_n ? tiles_m : tiles_n;
+    const long long gm = v.group_m > 0 ? v.group_m : 1;
+    // Tiles 0 .. c-1: whole groups of gm x other, then part of the next.
+    long long lead_used = 0, other_used = 0;
+    for (long long first = 0, left = c; left > 0 && first < lead; first += gm) {
+        const long long gsz = std::min(gm, lead - first);
+        const long long take = std::min(left, gsz * other);
+        lead_used += std::min(gsz, take);
+        other_used = std::max(other_used, cdiv(take, gsz));
+        left -= take;
+    }
+    const double rows = (double)(raster_n ? other_used : lead_used);
+    const double cols = (double)(raster_n ? lead_used : other_used);
+    return (rows * v.bm + cols * v.bn) / ((double)c * (v.bm + v.bn));
+}
+
+// Rounds of workgroups over the CUs. A last, partial round costs less than a
+// full one (its workgroups share the memory system with fewer others):
+// 0.7 + 0.3 x its fill, fitted to bf16 5120^3 and 6144^3 on the 256 x 256
+// 16-bit tiles (0.56 and 0.25 full).
+static double wave_rounds(long long wgs)
+{
+    const long long full = wgs / kDev.cus, rem = wgs - full * kDev.cus;
+    return (double)full + (rem > 0 ? 0.7 + 0.3 * (double)rem / kDev.cus : 0.0);
+}
+
 static double estimate_us(const Variant& v, long long M, long long N, long long K, int dtype,
-                          int split, int a_vec, int b_vec)
+                          int split, int a_vec, int b_vec, int raster_n)
 {
     const int bk = k_stage(v, dtype);
     const long long nkb = cdiv(K, bk);
@@ -133,7 +173,7 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
                             : dtype == DT_MX4 ? kDev.mx4_flop_per_clk_cu : kDev.h16_flop_per_clk_cu;
     const double peak_cu = flop_clk * kDev.clock_ghz * 1e3;   // FLOP per microsecond
     const double t_wg = 2.0 * v.bm * v.bn * (double)kc / (peak_cu * eff);
-    const double rounds = (double)cdiv(wgs, kDev.cus);
+    const double rounds = wave_rounds(wgs);
     // Every workgroup ends by writing its BM x BN FP32 tile (to C or to its
     // split's partials). Workgroups of one round finish together, so that
     // write is an HBM-bound phase of its own rather than hidden under MFMA.
@@ -144,10 +184,14 @@ static double estimate_us(const Variant& v, long long M, long long N, long long 
     const double alg = in_b * (double)(M * K + K * N) + 4.0 * (double)(M * N);
     const double part = split > 1 ? 4.0 * (double)(M * N) * split : 0.0;
     const double t_hbm = (alg + part) * mb / (kDev.hbm_gbs * kDev.tiled_hbm_frac) * 1e3;
+    // Operand delivery: every tile reads its A and B panels; the share that
+    // misses L2 (set by how the tiles running together share panels, i.e. by
+    // the raster order) comes from beyond L2 at the fabric rate.
     const double tile_traffic = in_b * ((double)M * K * tiles_n + (double)K * N * tiles_m);
-    const double t_l2 = tile_traffic * mb / kDev.l2_gbs * 1e3;
+    const double miss = reuse_miss_frac(v, tiles_m, tiles_n, raster_n);
+    const double t_deliver = tile_traffic * mb * ((1.0 - miss) / kDev.l2_gbs + miss / kDev.fabric_gbs) * 1e3;
 
-    double t = fmax(t_mfma, fmax(t_hbm, t_l2)) + kDev.launch_us;
+    double t = fmax(t_mfma, fmax(t_hbm, t_deliver)) + kDev.launch_us;
     if (split > 1) t += (part + 4.0 * M * N) * mb / kDev.hbm_gbs * 1e3 + kDev.launch_us;
     return t;
 }
@@ -163,7 +207,7 @@ static bool split_admissible(const Variant& v, long long K, int dtype, int split
 }
 
 static void fill_plan(const Variant& v, long long M, long long N, long long K, int dtype, int split,
-                      Plan* p)
+                      int raster_n, Plan* p)
 {
     const int bk = k_stage(v, dtype);
     const int ve = vec_elems(dtype);
@@ -196,57 +240,104 @@ static void fill_plan(const Variant& v, long long M, long long N, long long K, i
         p->k_chunk = (int)K;
     }
     p->ws_bytes = split > 1 ? (unsigned long long)split * (unsigned long long)(M * N) * 4ull : 0ull;
-    p->est_us = estimate_us(v, M, N, K, dtype, split, p->a_vec, p->b_vec);
+    p->raster_n = raster_n;
+    p->swap = v.swap;
+    p->sk = 0;
+    p->sk_dp = 0;
+    p->sk_g = 0;
+    p->est_us = estimate_us(v, M, N, K, dtype, split, p->a_vec, p->b_vec, raster_n);
 }
 
-// Stream-K (split_k = -1 in the ABI): FP32 ring variants with tiles of at
-// most 128 x 256, G = resident workgroups (256 CUs x those that fit one CU's
-// LDS), W = tiles x I K-iterations with W >= G (no empty range) and at most
-// 2 I iterations per range (a range then touches at most three tiles).
+// Stream-K (split_k = -1 in the ABI).
+//  * FP32 ring variants with tiles of at most 128 x 256: G = resident
+//    workgroups (256 CUs x those that fit one CU's LDS) share all tiles x I
+//    K-iterations, W >= G (no empty range) and at most 2 I iterations per
+//    range (a range then touches at most three tiles).
+//  * 16-bit ring variants with 16x16x32 blocks: whole waves of tiles (sk_dp,
+//    a multiple of the resident count R) run one per workgroup, and the
+//    T_sk < R tiles of the last, partial wave share their T_sk x I
+//    iterations over G = min(R, W) workgroups (a range then touches at most
+//    two tiles).
 static int sk_wgs_per_cu(const Variant& v)
 {
-    const int lds = v.nbuf * (v.bm + v.bn) * v.bk * 4;
+    const int es = v.kind == KIND_F32RING ? 4 : 2;
+    const int lds = v.nbuf * (v.bm + v.bn) * v.bk * es;
     const int w = kDev.lds_bytes / lds;
     return w < 1 ? 1 : w;
 }
 
-static bool sk_geometry(const Variant& v, long long M, long long N, long long K, long long* G, long long* I)
+struct SkGeom {
+    long long G, I, dp;
+};
+
+static bool sk_geometry(const Variant& v, long long M, long long N, long long K, SkGeom* g)
 {
-    if (v.kind != KIND_F32RING || (long long)v.bm * v.bn > 128 * 256 || K == 0 || M == 0 || N == 0) return false;
+    if (K == 0 || M == 0 || N == 0) return false;
     const long long tiles = cdiv(M, v.bm) * cdiv(N, v.bn);
-    *I = cdiv(K, v.bk);
-    *G = (long long)kDev.cus * sk_wgs_per_cu(v);
-    const long long W = tiles * *I;
-    return W >= *G && cdiv(W, *G) <= 2 * *I && tiles < (1ll << 31);
+    if (tiles >= (1ll << 31)) return false;
+    if (v.kind == KIND_F32RING && (long long)v.bm * v.bn <= 128 * 256) {
+        g->I = cdiv(K, v.bk);
+        g->G = (long long)kDev.cus * sk_wgs_per_cu(v);
+        g->dp = 0;
+        const long long W = tiles * g->I;
+        return W >= g->G && cdiv(W, g->G) <= 2 * g->I;
+    }
+    if (v.kind == KIND_DMA && v.blk == 16) {
+        g->I = cdiv(K, v.bk);
+        const long long R = (long long)kDev.cus * sk_wgs_per_cu(v);
+        g->dp = tiles / R * R;
+        const long long W = (tiles - g->dp) * g->I;
+        g->G = std::min(R, W);
+        return W > 0;
+    }
+    return false;
 }
 
-static double estimate_sk_us(const Variant& v, long long M, long long N, long long K, int dtype, long long G,
-                             long long I, int a_vec, int b_vec)
+static double estimate_sk_us(const Variant& v, long long M, long long N, long long K, int dtype, const SkGeom& g,
+                             int a_vec, int b_vec, int raster_n)
 {
     double eff = dtype == DT_F32 ? v.eff_f32 : v.eff_h16;
     if (!a_vec) eff *= 0.85;
     if (!b_vec) eff *= 0.85;
-    const double peak_cu = kDev.f32_flop_per_clk_cu * kDev.clock_ghz * 1e3;   // FLOP per microsecond
+    const double flop_clk = dtype == DT_F32 ? kDev.f32_flop_per_clk_cu : kDev.h16_flop_per_clk_cu;
+    const double peak_cu = flop_clk * kDev.clock_ghz * 1e3;   // FLOP per microsecond
     const double t_iter = 2.0 * v.bm * v.bn * v.bk / (peak_cu * eff);
-    const long long W = cdiv(M, v.bm) * cdiv(N, v.bn) * I;
+    const long long T = cdiv(M, v.bm) * cdiv(N, v.bn);
+    const long long W = (T - g.dp) * g.I;
+    const long long per_cu = sk_wgs_per_cu(v);
     const double mb = 1e-6;
-    // Every range runs ceil(W / G) iterations with the CU shared by the
-    // workgroups resident on it, and ends up to three segments with a tile
-    // store; the fix-up reads at most two slots per range and writes C.
-    const double t_main = (double)cdiv(W, G) * t_iter * sk_wgs_per_cu(v);
-    const double t_epi = 3.0 * kDev.cus * v.bm * v.bn * 4.0 * mb / kDev.hbm_write_gbs * 1e3;
-    const double fix = (2.0 * G * v.bm * v.bn * 4.0 + 4.0 * M * N) * mb / kDev.hbm_gbs * 1e3;
-    return t_main + t_epi + fix + 2 * kDev.launch_us;
+    const double t_round_epi = kDev.cus * per_cu * v.bm * v.bn * 4.0 * mb / kDev.hbm_write_gbs * 1e3;
+    // Whole waves of data-parallel tiles, each ending with its tile store;
+    // then every range runs ceil(W / G) iterations with the CU shared by the
+    // workgroups resident on it, and ends up to three (FP32) or two (16-bit)
+    // segments with a tile store; the fix-up reads at most two slots per
+    // range and writes C.
+    const double t_dp = (double)(g.dp / (kDev.cus * per_cu)) * (g.I * t_iter * per_cu + t_round_epi);
+    const double t_main = (double)cdiv(W, g.G) * t_iter * per_cu;
+    const double segs = v.kind == KIND_F32RING ? 3.0 : 2.0;
+    // Each segment ends with a tile store of the whole round and starts by
+    // filling the LDS ring (about 5 us of load latency before its first MFMA).
+    const double t_epi = segs * (t_round_epi + 5.0);
+    const double fix = (2.0 * g.G * v.bm * v.bn * 4.0 + 4.0 * (double)(T - g.dp) * v.bm * v.bn) * mb / kDev.hbm_gbs * 1e3;
+    // Operand delivery as for the data-parallel form.
+    const double in_b = dtype == DT_F32 ? 4.0 : 2.0;
+    const long long tiles_m = cdiv(M, v.bm), tiles_n = cdiv(N, v.bn);
+    const double tile_traffic = in_b * ((double)M * K * tiles_n + (double)K * N * tiles_m);
+    const double miss = reuse_miss_frac(v, tiles_m, tiles_n, raster_n);
+    const double t_deliver = tile_traffic * mb * ((1.0 - miss) / kDev.l2_gbs + miss / kDev.fabric_gbs) * 1e3;
+    return fmax(t_dp + t_main + t_epi, t_deliver) + fix + 2 * kDev.launch_us;
 }
 
-static void fill_plan_sk(const Variant& v, long long M, long long N, long long K, int dtype, long long G, long long I,
-                         Plan* p)
+static void fill_plan_sk(const Variant& v, long long M, long long N, long long K, int dtype, const SkGeom& g,
+                         int raster_n, Plan* p)
 {
-    fill_plan(v, M, N, K, dtype, 1, p);
+    fill_plan(v, M, N, K, dtype, 1, raster_n, p);
     p->sk = 1;
-    p->grid = G;
-    p->ws_bytes = 2ull * (unsigned long long)G * (unsigned long long)(v.bm * v.bn) * 4ull;
-    p->est_us = estimate_sk_us(v, M, N, K, dtype, G, I, p->a_vec, p->b_vec);
+    p->sk_dp = (int)g.dp;
+    p->sk_g = (int)g.G;
+    p->grid = g.dp + g.G;
+    p->ws_bytes = 2ull * (unsigned long long)g.G * (unsigned long long)(v.bm * v.bn) * 4ull;
+    p->est_us = estimate_sk_us(v, M, N, K, dtype, g, p->a_vec, p->b_vec, raster_n);
 }
 
 static const int kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
@@ -263,8 +354,9 @@ static bool split_wanted(const Plan& p)
 }
 
 bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype, int split_req,
-                      Plan* out)
+                      Plan* out, int raster_req)
 {
+    if (raster_req < -1 || raster_req > 1) return false;
     const Variant* v = variant_get(vid);
     if (!v || dtype < DT_F32 || dtype > DT_MX4 || !(v->dtype_mask & (1 << dtype))) return false;
     if (M < 0 || N < 0 || K < 0) return false;
@@ -288,37 +380,50 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     // The streaming kernels cover at most 16 rows (16 x 64 tile) or 16
     // columns (64 x 16 tile) of C.
     if (v->kind == KIND_STREAM && (v->bm == 16 ? M > 16 : N > 16)) return false;
-    long long G = 0, I = 0;
-    const bool sk_ok = sk_geometry(*v, M, N, K, &G, &I);
-    if (split_req == -1) {
-        if (!sk_ok) return false;
-        fill_plan_sk(*v, M, N, K, dtype, G, I, out);
-        return true;
-    }
-    if (split_req > 0) {
-        if (split_req > 1 && (K == 0 || !split_admissible(*v, K, dtype, split_req))) return false;
-        fill_plan(*v, M, N, K, dtype, split_req, out);
-        return out->grid < (1ll << 31);
-    }
+    // Raster orders to consider: the requested one, or both (M-major first,
+    // so it wins ties). Only tiled kernels walk tiles in raster order.
+    const bool tiled = v->kind != KIND_STREAM;
+    const int r_lo = raster_req >= 0 ? raster_req : 0;
+    const int r_hi = raster_req >= 0 ? raster_req : (tiled ? 1 : 0);
+    if (!tiled && raster_req == 1) return false;
+    SkGeom g{};
+    const bool sk_ok = sk_geometry(*v, M, N, K, &g);
     bool found = false;
     Plan best{};
-    for (int s : kSplits) {
-        if (s > v->max_split) break;
-        if (s > 1 && (K == 0 || !split_admissible(*v, K, dtype, s))) continue;
-        Plan p{};
-        fill_plan(*v, M, N, K, dtype, s, &p);
-        if (p.grid >= (1ll << 31) || !split_wanted(p)) continue;
-        if (!found || p.est_us < best.est_us) {
+    auto consider = [&](const Plan& p) {
+        if (!found || p.est_us < best.est_us) {   // strict: ties keep the earlier candidate
             best = p;
             found = true;
         }
-    }
-    if (sk_ok) {
-        Plan p{};
-        fill_plan_sk(*v, M, N, K, dtype, G, I, &p);
-        if (!found || p.est_us < best.est_us) {
-            best = p;
-            found = true;
+    };
+    for (int r = r_lo; r <= r_hi; ++r) {
+        if (split_req == -1) {
+            if (!sk_ok) return false;
+            Plan p{};
+            fill_plan_sk(*v, M, N, K, dtype, g, r, &p);
+            consider(p);
+            continue;
+        }
+        if (split_req > 0) {
+            if (split_req > 1 && (K == 0 || !split_admissible(*v, K, dtype, split_req))) return false;
+            Plan p{};
+            fill_plan(*v, M, N, K, dtype, split_req, r, &p);
+            if (p.grid >= (1ll << 31)) return false;
+            consider(p);
+            continue;
+        }
+        for (int s : kSplits) {
+            if (s > v->max_split) break;
+            if (s > 1 && (K == 0 || !split_admissible(*v, K, dtype, s))) continue;
+            Plan p{};
+            fill_plan(*v, M, N, K, dtype, s, r, &p);
+            if (p.grid >= (1ll << 31) || !split_wanted(p)) continue;
+            consider(p);
+        }
+        if (sk_ok) {
+            Plan p{};
+            fill_plan_sk(*v, M, N, K, dtype, g, r, &p);
+            consider(p);
         }
     }
     if (found) *out = best;
@@ -328,29 +433,87 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
 struct TunedPlan {
     int dtype;
     long long M, N, K;
-    int variant, split;
+    int variant, split, raster;
 };
 
-#define SAM_TUNED_ROW(dt, M, N, K, v, s) {dt, M, N, K, v, s},
-static const TunedPlan kTuned[] = {SAM_TUNED_PLANS(SAM_TUNED_ROW){-1, 0, 0, 0, 0, 0}};
+#define SAM_TUNED_ROW(dt, M, N, K, v, s, r) {dt, M, N, K, v, s, r},
+static const TunedPlan kTuned[] = {SAM_TUNED_PLANS(SAM_TUNED_ROW){-1, 0, 0, 0, 0, 0, 0}};
+
+// Half-octave bucket of a size: round(2 log2 x). Sizes within a factor of
+// about 1.19 of each other share a bucket edge-to-edge.
+static int bucket_of(long long x) { return x <= 0 ? -1 : (int)lround(2.0 * log2((double)x)); }
+
+// Distance between two shapes in log2 units, summed over M, N and K.
+static double shape_distance(long long M, long long N, long long K, const TunedPlan& t)
+{
+    return fabs(log2((double)M / t.M)) + fabs(log2((double)N / t.N)) + fabs(log2((double)K / t.K));
+}
 
 bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out)
 {
+    // 1. A shape measured offline: its fastest (variant, split, raster).
     for (const TunedPlan& t : kTuned) {
         if (t.dtype != dtype || t.M != M || t.N != N || t.K != K) continue;
         Plan p{};
-        if (plan_for_variant(t.variant, M, N, K, dtype, t.split, &p)) {
+        if (plan_for_variant(t.variant, M, N, K, dtype, t.split, &p, t.raster)) {
             p.tuned = 1;
             *out = p;
             return true;
         }
     }
+    // 2. A measured shape in the same half-octave bucket in M, N and K (the
+    //    nearest one, ties to the earlier table row): its variant and raster
+    //    order, with its split when that is admissible here and otherwise
+    //    the variant's own choice. The bucketed fallback of page
+    //    "fix(fp4_gemm autotune) SM107 kernel family excluded from autotune
+    //    candidates and heuristics update - #4856", description item 4.
+    if (M > 0 && N > 0 && K > 0) {
+        const TunedPlan* near = nullptr;
+        double dist = 0.0;
+        for (const TunedPlan& t : kTuned) {
+            if (t.dtype != dtype || bucket_of(t.M) != bucket_of(M) || bucket_of(t.N) != bucket_of(N) ||
+                bucket_of(t.K) != bucket_of(K))
+                continue;
+            Plan probe{};
+            if (!plan_for_variant(t.variant, M, N, K, dtype, 0, &probe, t.raster)) continue;
+            const double d = shape_distance(M, N, K, t);
+            if (!near || d < dist) {
+                near = &t;
+                dist = d;
+            }
+        }
+        if (near) {
+            Plan p{};
+            if (!plan_for_variant(near->variant, M, N, K, dtype, near->split, &p, near->raster))
+                plan_for_variant(near->variant, M, N, K, dtype, 0, &p, near->raster);
+            p.tuned = 2;
+            *out = p;
+            return true;
+        }
+    }
+    // 3. The cost model over every admissible variant.
     bool found = false;
     Plan best{};
     for (int id = 0; id < kVariantCount; ++id) {
         Plan p{};
-        if (!plan_for_variant(id, M, N, K, dtype, 0, &p)) continue;
+        if (!plan_for_variant(id, M, N, K, dtype, 0, &p, -1)) continue;
         if (!found || p.est_us < best.est_us) {   // strict: ties keep the lower id
+            best = p;
+            found = true;
+        }
+    }
+    if (found) *out = best;
+    return found;
+}
+
+bool plan_model(long long M, long long N, long long K, int dtype, Plan* out)
+{
+    bool found = false;
+    Plan best{};
+    for (int id = 0; id < kVariantCount; ++id) {
+        Plan p{};
+        if (!plan_for_variant(id, M, N, K, dtype, 0, &p, -1)) continue;
+        if (!found || p.est_us < best.est_us) {
             best = p;
             found = true;
         }
@@ -368,8 +531,8 @@ void plan_name(const Plan& p, char* buf, int n)
         snprintf(sp, sizeof(sp), "sk");
     else
         snprintf(sp, sizeof(sp), "s%d", p.split);
-    snprintf(buf, n, "%s_%s_%s%s%s%s", dt[p.dtype], v ? v->name : "?", sp, p.a_vec ? "" : "_ua",
-             p.b_vec ? "" : "_ub", p.tuned ? "_tuned" : "");
+    snprintf(buf, n, "%s_%s_%s%s%s%s%s", dt[p.dtype], v ? v->name : "?", sp, p.raster_n ? "_rn" : "",
+             p.a_vec ? "" : "_ua", p.b_vec ? "" : "_ub", p.tuned == 1 ? "_tuned" : (p.tuned == 2 ? "_bucket" : ""));
 }
 
 }  // namespace sam

@@ -81,8 +81,8 @@
 #include "sam_variants_mx.h"
 
 #define SAM_DMA16_VARIANTS(D)                                                            \
-    D(45, "r256x256_w2x4_k64n2_b16", 256, 256, 2, 4, 64, 2, 0, 16, 8, 1, 8, 0.52)         \
-    D(46, "r256x256_w4x2_k64n2_b16", 256, 256, 4, 2, 64, 2, 0, 16, 8, 1, 8, 0.51)         \
+    D(45, "r256x256_w2x4_k64n2_b16", 256, 256, 2, 4, 64, 2, 0, 16, 8, 1, 8, 0.58)         \
+    D(46, "r256x256_w4x2_k64n2_b16", 256, 256, 4, 2, 64, 2, 0, 16, 8, 1, 8, 0.575)         \
     D(47, "r128x128_w2x2_k64n2_b16", 128, 128, 2, 2, 64, 2, 0, 16, 8, 1, 16, 0.34)
 
 // Single-launch small-tile variants (sam_kernels_kq.hip): FP32 only, a
@@ -109,3 +109,12 @@
     Q(53, "kq32x32_w8", 2, 8, 8, 1, 0.62)                                                \
     Q(54, "kq48x48_w8", 3, 8, 8, 1, 0.73)                                                \
     Q(55, "kq64x64_w8", 4, 8, 8, 1, 0.78)
+
+// Operand-swap forms of the 16x16x32 ring variants (same list format as
+// SAM_DMA16_VARIANTS plus SW = 1): the MFMA computes the transposed block, so
+// each lane stores four adjacent columns of C with one 16-byte store.
+//   D(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW, group_m, xcd_remap, max_split, eff_h16)
+#define SAM_DMA16S_VARIANTS(D)                                                           \
+    D(56, "r256x256_w2x4_k64n2_b16_sw", 256, 256, 2, 4, 64, 2, 0, 16, 1, 8, 1, 8, 0.575)  \
+    D(57, "r256x256_w4x2_k64n2_b16_sw", 256, 256, 4, 2, 64, 2, 0, 16, 1, 8, 1, 8, 0.57)  \
+    D(58, "r128x128_w2x2_k64n2_b16_sw", 128, 128, 2, 2, 64, 2, 0, 16, 1, 8, 1, 16, 0.34)

@@ -63,47 +63,46 @@ def shapes():
 
 
 def candidates(sam, dt, M, N, K):
-    """(variant, split) pairs: every admissible variant with its own split
-    choice and its stream-K form (split -1) where it has one, plus the other
-    admissible splits of the four variants the cost model ranks best, when
-    their tile count leaves CUs idle."""
+    """(variant, split, raster) triples: every admissible variant with its
+    own split and raster choice and its stream-K form (split -1) where it has
+    one; for the four variants the cost model ranks best, the other raster
+    order (M-major 0 / N-major 1) too, and, when their tile count leaves CUs
+    idle, the other admissible splits."""
     own = []
     for vid in range(sam.variant_count()):
         try:
             own.append(sam.variant_plan(vid, M, N, K, dt, 0))
         except sam.SamError:
             continue
-    out = {(p["variant_id"], p["split_k"]) for p in own}
+    out = {(p["variant_id"], p["split_k"], p["raster_n"]) for p in own}
     for p in own:   # stream-K forms (split -1) where the variant has one
         try:
-            sam.variant_plan(p["variant_id"], M, N, K, dt, -1)
-            out.add((p["variant_id"], -1))
+            q = sam.variant_plan(p["variant_id"], M, N, K, dt, -1)
+            out.add((p["variant_id"], -1, q["raster_n"]))
         except sam.SamError:
             pass
+    mx = dt in ("mxfp8", "mxfp4")   # block-scaled calls take the cost model's raster order
     for p in sorted(own, key=lambda p: (p["est_us"], p["variant_id"]))[:4]:
-        if p["grid_wgs"] // p["split_k"] >= 256:
+        if not mx:
+            try:
+                sam.variant_plan(p["variant_id"], M, N, K, dt, p["split_k"], 1 - p["raster_n"])
+                out.add((p["variant_id"], p["split_k"], 1 - p["raster_n"]))
+            except sam.SamError:
+                pass
+        if p["grid_wgs"] // max(p["split_k"], 1) >= 256:
             continue
         for s in SPLITS:
             try:
-                sam.variant_plan(p["variant_id"], M, N, K, dt, s)
-                out.add((p["variant_id"], s))
+                q = sam.variant_plan(p["variant_id"], M, N, K, dt, s)
+                out.add((p["variant_id"], s, q["raster_n"]))
             except sam.SamError:
                 pass
     return sorted(out)
 
 
 def model_plan(sam, dt, M, N, K):
-    """The cost model's own pick, ignoring the frozen table: the lowest
-    estimate over every variant's own plan, ties to the lower id."""
-    best = None
-    for vid in range(sam.variant_count()):
-        try:
-            p = sam.variant_plan(vid, M, N, K, dt, 0)
-        except sam.SamError:
-            continue
-        if best is None or p["est_us"] < best["est_us"]:
-            best = p
-    return best
+    """The cost model's own pick, ignoring the frozen table."""
+    return sam.plan_model(M, N, K, dt)
 
 
 def measure(record: Path, only=None):
@@ -117,7 +116,7 @@ def measure(record: Path, only=None):
     if record.exists():
         for line in record.read_text().splitlines():
             r = json.loads(line)
-            done.add((r["dtype"], r["M"], r["N"], r["K"], r["variant"], r["split"]))
+            done.add((r["dtype"], r["M"], r["N"], r["K"], r["variant"], r["split"], r.get("raster", 0)))
     with record.open("a") as f:
         for (dt, M, N, K, name) in shapes():
             if only and name not in only:
@@ -140,10 +139,10 @@ def measure(record: Path, only=None):
             stream = torch.cuda.current_stream()
             auto = model_plan(sam, dt, M, N, K)
             print(f"[tune] {name}: {len(candidates(sam, dt, M, N, K))} candidates", flush=True)
-            for (vid, split) in candidates(sam, dt, M, N, K):
-                if (dt, M, N, K, vid, split) in done:
+            for (vid, split, raster) in candidates(sam, dt, M, N, K):
+                if (dt, M, N, K, vid, split, raster) in done:
                     continue
-                p = sam.variant_plan(vid, M, N, K, dt, split)
+                p = sam.variant_plan(vid, M, N, K, dt, split, raster if dt not in ("mxfp8", "mxfp4") else -1)
                 ws = sam.workspace_for(p, dA.device)
                 tail = (ctypes.c_void_p(C.data_ptr()), M, N, K, ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
                         ws.numel() * 4 if ws is not None else 0, ctypes.c_void_p(stream.cuda_stream))
@@ -154,9 +153,9 @@ def measure(record: Path, only=None):
                     fn = sam.lib().sam_gemm_mxfp4_variant
                     args = (vid, split, *(ctypes.c_void_p(x.data_ptr()) for x in mx), *tail)
                 else:
-                    fn = sam.lib().sam_gemm_variant
-                    args = (vid, sam.DTYPES[dt], split, ctypes.c_void_p(dA.data_ptr()), ctypes.c_void_p(dB.data_ptr()),
-                            *tail)
+                    fn = sam.lib().sam_gemm_variant_r
+                    args = (vid, sam.DTYPES[dt], split, raster, ctypes.c_void_p(dA.data_ptr()),
+                            ctypes.c_void_p(dB.data_ptr()), *tail)
                 for _ in range(3):
                     rc = fn(*args)
                     if rc != 0:
@@ -177,10 +176,11 @@ def measure(record: Path, only=None):
                     samples.append(e0.elapsed_time(e1) / n)
                 ms = statistics.median(samples)
                 f.write(json.dumps({"shape": name, "dtype": dt, "M": M, "N": N, "K": K, "variant": vid,
-                                    "split": split, "plan": p["name"], "ms": round(ms, 5),
+                                    "split": split, "raster": p["raster_n"], "plan": p["name"], "ms": round(ms, 5),
                                     "tflops": round(2.0 * M * N * K / ms / 1e9, 2),
                                     "est_us": round(p["est_us"], 1),
-                                    "model_pick": vid == auto["variant_id"] and split == auto["split_k"]}) + "\n")
+                                    "model_pick": (vid, split, p["raster_n"]) == (auto["variant_id"], auto["split_k"],
+                                                                                  auto["raster_n"])}) + "\n")
                 f.flush()
                 del ws
             del dA, C
@@ -193,21 +193,24 @@ def measure(record: Path, only=None):
 
 def load(record: Path):
     """Per shape: the measured candidates, fastest first (ties: lower id, then
-    lower split)."""
+    lower split, then M-major). Records without a raster field were taken
+    when every plan was M-major."""
     by = {}
     for line in record.read_text().splitlines():
         r = json.loads(line)
-        by.setdefault((r["dtype"], r["M"], r["N"], r["K"]), {})[(r["variant"], r["split"])] = r
-    return {k: sorted(v.values(), key=lambda r: (r["ms"], r["variant"], r["split"])) for k, v in by.items()}
+        r.setdefault("raster", 0)
+        by.setdefault((r["dtype"], r["M"], r["N"], r["K"]), {})[(r["variant"], r["split"], r["raster"])] = r
+    return {k: sorted(v.values(), key=lambda r: (r["ms"], r["variant"], r["split"], r["raster"]))
+            for k, v in by.items()}
 
 
 def emit(record: Path, out: Path = TUNED_H) -> str:
     table = load(record)
     lines = [
-        "// Frozen dispatch table: the fastest measured (variant, split-K) per shape.",
+        "// Frozen dispatch table: the fastest measured (variant, split-K, raster order) per shape.",
         "// Generated by shape_adaptive_matrix_amd/tune.py from tuning/" + record.name + ";",
         "// regenerate with `python -m shape_adaptive_matrix_amd.tune emit <record>`, do not edit.",
-        "//   T(dtype, M, N, K, variant, split)   dtype: 0 f32, 1 bf16, 2 f16",
+        "//   T(dtype, M, N, K, variant, split, raster_n)   dtype: 0 f32, 1 bf16, 2 f16, 3 mxfp8, 4 mxfp4",
         "#pragma once",
         "",
         "#define SAM_TUNED_PLANS(T) \\",
@@ -215,7 +218,7 @@ def emit(record: Path, out: Path = TUNED_H) -> str:
     rows = []
     for (dt, M, N, K), rs in sorted(table.items(), key=lambda kv: (DTYPE_CODE[kv[0][0]], kv[0][1:])):
         best = rs[0]
-        rows.append(f"    T({DTYPE_CODE[dt]}, {M}, {N}, {K}, {best['variant']}, {best['split']})")
+        rows.append(f"    T({DTYPE_CODE[dt]}, {M}, {N}, {K}, {best['variant']}, {best['split']}, {best['raster']})")
     lines += [r + " \\" for r in rows[:-1]] + rows[-1:]
     text = "\n".join(lines) + "\n"
     out.write_text(text)
@@ -230,7 +233,8 @@ def report(record: Path) -> str:
     for (dt, M, N, K), rs in sorted(table.items(), key=lambda kv: (DTYPE_CODE[kv[0][0]], kv[0][1:])):
         best = rs[0]
         mp = model_plan(sam, dt, M, N, K)
-        model = next((r for r in rs if (r["variant"], r["split"]) == (mp["variant_id"], mp["split_k"])), None)
+        model = next((r for r in rs if (r["variant"], r["split"], r["raster"]) ==
+                      (mp["variant_id"], mp["split_k"], mp["raster_n"])), None)
         out.append(f"| {M}x{N}x{K} | {dt} | {best['plan']} | {best['tflops']} | "
                    f"{model['plan'] if model else '-'} | {model['tflops'] if model else '-'} | {len(rs)} |")
     return "\n".join(out) + "\n"

@@ -168,6 +168,73 @@ def test_stream_k_random_and_repeatable(shape):
             assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), vid
 
 
+# 16-bit stream-K (data-parallel waves, then the last wave's tiles shared):
+# no data-parallel part (few tiles), ranges crossing tile boundaries, M, N
+# and K tails, one or two iterations per range.
+SK16_SHAPES = [(300, 264, 2048), (1000, 1000, 1000), (4352, 4352, 512), (2304, 8192, 1024),
+               (4400, 4104, 520)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("vid", range(sam.variant_count()))
+def test_every_16bit_variant_stream_k_dyadic(vid, dtype):
+    ran = 0
+    for (M, N, K) in SK16_SHAPES:
+        if not _supported(vid, M, N, K, dtype, -1):
+            continue
+        p = sam.variant_plan(vid, M, N, K, dtype, -1)
+        A, B = ints_operands(M, N, K, dtype, seed=M + 5 * N + 3 * K)
+        print(f"[sk16] variant {vid} {dtype} {(M, N, K)} dp={p['sk_dp_tiles']} grid={p['grid_wgs']}", flush=True)
+        C = run(A, B, dtype, variant=vid, split=-1)
+        bad = bitexact_mismatches(C, orc().gemm(dtype, A, B))
+        assert bad == 0, f"variant {vid} {dtype} {(M, N, K)} stream-K: {bad} mismatches"
+        ran += 1
+    if ran == 0:
+        pytest.skip(f"variant {vid} has no 16-bit stream-K form")
+
+
+def test_16bit_stream_k_random_and_repeatable():
+    M, N, K = 2304, 8192, 1024
+    rng = np.random.default_rng(17)
+    A, B = si.normal16(rng, (M, K), "bf16"), si.normal16(rng, (K, N), "bf16")
+    ref = orc().gemm("bf16", A, B)
+    vids = [v for v in range(sam.variant_count()) if _supported(v, M, N, K, "bf16", -1)]
+    assert vids
+    for vid in vids:
+        outs = [run(A, B, "bf16", variant=vid, split=-1) for _ in range(3)]
+        assert rel_rms(outs[0], ref) <= 1e-5
+        for o in outs[1:]:
+            assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)), vid
+
+
+# N-major raster (groups of tile columns sweep the rows): every tiled variant
+# on shapes with several tile rows and columns, ragged in M, N and K.
+RASTER_SHAPES = [(1000, 1096, 200), (520, 2056, 136), (2056, 520, 72)]
+
+
+@pytest.mark.parametrize("vid", range(sam.variant_count()))
+def test_every_variant_n_major_raster_dyadic(vid):
+    ran = 0
+    for (M, N, K) in RASTER_SHAPES:
+        for dtype in ("f32", "bf16"):
+            try:
+                p = sam.variant_plan(vid, M, N, K, dtype, 0, 1)
+            except sam.SamError:
+                continue
+            assert p["raster_n"] == 1
+            A, B = ints_operands(M, N, K, dtype, seed=M + N + 11 * K)
+            dA, dB = to_dev(A, dtype), to_dev(B, dtype)
+            C = torch.full((M, N), float("nan"), device="cuda")
+            print(f"[raster] variant {vid} {dtype} {(M, N, K)} {p['name']}", flush=True)
+            sam.gemm_variant(vid, dA, dB, C, raster=1)
+            torch.cuda.synchronize()
+            bad = bitexact_mismatches(C.cpu().numpy(), orc().gemm(dtype, A, B))
+            assert bad == 0, f"variant {vid} {dtype} {(M, N, K)} N-major: {bad} mismatches"
+            ran += 1
+    if ran == 0:
+        pytest.skip(f"variant {vid} takes none of the raster shapes")
+
+
 def test_dispatcher_picks_stream_k_on_odd_k():
     """The shapes above with K % 4 != 0 are ones the dispatcher itself sends
     to stream-K, so those segments are the automatic path, not only forced."""

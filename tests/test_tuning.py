@@ -33,19 +33,33 @@ def test_table_covers_every_measured_shape():
     assert len(_entries()) == len(tune.load(RECORD)) > 0
 
 
+DTN = {0: "f32", 1: "bf16", 2: "f16", 3: "mxfp8", 4: "mxfp4"}
+
+
 @pytest.mark.parametrize("row", _entries())
 def test_tuned_plan_is_returned(row):
-    dt, M, N, K, vid, split = row
-    dtype = {0: "f32", 1: "bf16", 2: "f16", 3: "mxfp8", 4: "mxfp4"}[dt]
+    dt, M, N, K, vid, split, raster = row
+    dtype = DTN[dt]
     p = sam.plan(M, N, K, dtype)
-    assert (p["variant_id"], p["split_k"]) == (vid, split)
-    assert p["name"].endswith("_tuned")
+    assert (p["variant_id"], p["split_k"], p["raster_n"]) == (vid, split, raster)
+    assert p["name"].endswith("_tuned") and p["tuned"] == 1
     # the fastest measured candidate is what the table holds
     best = tune.load(RECORD)[(dtype, M, N, K)][0]
-    assert (best["variant"], best["split"]) == (vid, split)
+    assert (best["variant"], best["split"], best["raster"]) == (vid, split, raster)
 
 
-def test_untuned_shape_uses_the_cost_model():
+def test_shape_in_a_measured_bucket_takes_its_plan():
+    """2040 x 2056 x 2064 shares the half-octave buckets of the measured
+    2048^3: it takes that shape's variant and raster order."""
     p = sam.plan(2040, 2056, 2064, "f32")
-    assert not p["name"].endswith("_tuned")
+    ref = sam.plan(2048, 2048, 2048, "f32")
+    assert p["tuned"] == 2 and p["name"].endswith("_bucket")
+    assert (p["variant_id"], p["raster_n"]) == (ref["variant_id"], ref["raster_n"])
     assert sam.plan(2040, 2056, 2064, "f32") == p   # pure function of the shape
+
+
+def test_shape_outside_every_bucket_uses_the_cost_model():
+    p = sam.plan(2040, 2056, 700, "f32")
+    assert p["tuned"] == 0 and not p["name"].endswith(("_tuned", "_bucket"))
+    assert p == sam.plan_model(2040, 2056, 700, "f32")
+    assert sam.plan(2040, 2056, 700, "f32") == p
