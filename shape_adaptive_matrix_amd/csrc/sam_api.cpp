@@ -198,13 +198,29 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
     if (d != SAM_OK) return d;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
+    hipError_t e = hipSuccess;
     if (K == 0) {
         e = sam::launch_zero(C, M * N, s);
     } else {
+        // 16-bit operands whose rows are not whole 16-byte pieces: padded
+        // copies in front of the plan's own workspace.
+        char* wsb = static_cast<char*>(ws);
+        if (p.pad_a) {
+            e = sam::launch_pad16(A, K, wsb, p.lda, M, K, s);
+            A = wsb;
+        }
+        if (e == hipSuccess && p.pad_b) {
+            char* bb = wsb + (p.pad_a ? ((unsigned long long)(M * p.lda) * 2ull + 255ull) & ~255ull : 0ull);
+            e = sam::launch_pad16(B, N, bb, p.ldb, K, N, s);
+            B = bb;
+        }
+        if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+        ws = p.ws_bytes > 0 ? wsb + p.ws_inner : ws;
         sam::GemmArgs a{};
         a.A = A;
         a.B = B;
+        a.lda = (int)p.lda;
+        a.ldb = (int)p.ldb;
         a.out = p.split > 1 ? static_cast<float*>(ws) : C;
         a.M = (int)M;
         a.N = (int)N;

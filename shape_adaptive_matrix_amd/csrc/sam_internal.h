@@ -75,6 +75,7 @@ struct GemmArgs {
     int sk_grid;         // stream-K: workgroups sharing the stream-K tiles' iterations
     int sk_dp;           // stream-K: leading tiles run one per workgroup before them (16-bit form)
     int raster_n;        // 1: raster groups of group_m tile columns walk the rows (N-major)
+    int lda, ldb;        // row strides of A and B in elements (16-bit ring kernel; K and N otherwise)
     const unsigned char* sa;   // block-scaled operands: scale codes of A (M x K/32)
     const unsigned char* sb;   // ... and of B (N x K/32); B is then N rows of K codes
     int fmt_a, fmt_b;    // element formats: 0 E4M3, 1 E5M2
@@ -102,6 +103,14 @@ struct Plan {
     int sk_g;            // stream-K: workgroups sharing the remaining tiles' iterations
     int raster_n;        // 0: groups of group_m tile rows sweep the columns; 1: the transpose
     int swap;            // 1: MFMA operands exchanged (accumulators hold the transposed block)
+    // 16-bit operands whose rows are not whole 16-byte pieces: A (K % 8 != 0)
+    // and / or B (N % 8 != 0) are first copied into the workspace with row
+    // strides lda / ldb rounded up to a multiple of 8 and zeros in the gap,
+    // then the ring kernel reads the copies. ws_inner is where the plan's own
+    // split-K / stream-K workspace starts.
+    int pad_a, pad_b;
+    long long lda, ldb;
+    unsigned long long ws_inner;
 };
 
 // Dispatcher (sam_plan.cpp). Host only, pure.
@@ -133,6 +142,10 @@ hipError_t launch_pack(const void* in, long long ld, void* out, long long rows, 
                        int trans, hipStream_t s);
 hipError_t launch_axpby(const float* T, long long ldt, float* C, long long ldc, long long M, long long N, float alpha,
                         float beta, hipStream_t s);
+// 16-bit rows x cols (row stride lds elements) into dst with row stride ldd
+// (a multiple of 8, dst 16-byte aligned), zeros in columns cols .. ldd - 1.
+hipError_t launch_pad16(const void* src, long long lds, void* dst, long long ldd, long long rows, long long cols,
+                        hipStream_t s);
 // A representative kernel symbol for loadability checks.
 const void* probe_kernel();
 

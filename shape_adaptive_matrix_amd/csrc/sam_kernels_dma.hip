@@ -165,11 +165,14 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
     const int wm0 = (wave / WN) * WTM;
     const int wn0 = (wave % WN) * WTN;
 
-    const i4 rA = rsrc_words(static_cast<const char*>(args.A) + (long long)m0 * K * 2,
-                             (long long)(M - m0) * K * 2);
-    const __amdgpu_buffer_rsrc_t rAb = make_rsrc(static_cast<const char*>(args.A) + (long long)m0 * K * 2,
-                                                 (long long)(M - m0) * K * 2);
-    const long long b_bytes = (long long)K * N * 2;
+    // Row strides of A and B in elements (K and N for compact operands; a
+    // padded copy's stride when a row is not whole 16-byte pieces).
+    const int lda = args.lda, ldb = args.ldb;
+    const i4 rA = rsrc_words(static_cast<const char*>(args.A) + (long long)m0 * lda * 2,
+                             (long long)(M - m0) * lda * 2);
+    const __amdgpu_buffer_rsrc_t rAb = make_rsrc(static_cast<const char*>(args.A) + (long long)m0 * lda * 2,
+                                                 (long long)(M - m0) * lda * 2);
+    const long long b_bytes = (long long)K * ldb * 2;
 
     // One 1 KB wave load of stage `st` (relative to this split): loads
     // 0 .. A_PW-1 fetch A rows, the rest B rows. Slot layout in LDS is the
@@ -184,7 +187,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
             const int c = (lane % CPA) ^ ((row / RSW) % CPA);   // logical chunk stored at this slot
             const int gk = k0 + c * 8;
             const bool ok = m0 + row < M && gk < kend;
-            const int off = ok ? (row * K + gk) * 2 : kOOB;
+            const int off = ok ? (row * lda + gk) * 2 : kOOB;
             if constexpr (MODE != 1)
                 lds_load16(rA, lds_addr(buf + I * 1024), off);
             else
@@ -194,8 +197,8 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
             const int row = I * RPI + lane / CPR;
             const int c = (lane % CPR) ^ (4 * (row & 3));
             const bool ok = k0 + row < kend && n0 + c * 8 < N;
-            const long long bbase = ((long long)k0 * N + n0) * 2;
-            const int off = ok ? (row * N + c * 8) * 2 : kOOB;
+            const long long bbase = ((long long)k0 * ldb + n0) * 2;
+            const int off = ok ? (row * ldb + c * 8) * 2 : kOOB;
             if constexpr (MODE == 0) {
                 const i4 rB = rsrc_words(static_cast<const char*>(args.B) + bbase, b_bytes - bbase);
                 lds_load16(rB, lds_addr(buf + A_BYTES + I * 1024), off);
@@ -213,7 +216,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
         const int sb = tid + q * NT;
         const int kc = sb % (BK / 8);
         const int nb = (sb / (BK / 8)) * 8;
-        const long long bbase = ((long long)k0 * N + n0) * 2;
+        const long long bbase = ((long long)k0 * ldb + n0) * 2;
         const __amdgpu_buffer_rsrc_t rB = make_rsrc(static_cast<const char*>(args.B) + bbase, b_bytes - bbase);
         // Only K rows past the split's end must read zero. Columns past N read
         // the next row's values (or zero past the end of B): they only reach
@@ -221,7 +224,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const bool ok = k0 + kc * 8 + r < kend;
-            RB[q][r] = __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? ((kc * 8 + r) * N + nb) * 2 : kOOB, 0, 0);
+            RB[q][r] = __builtin_amdgcn_raw_buffer_load_b128(rB, ok ? ((kc * 8 + r) * ldb + nb) * 2 : kOOB, 0, 0);
         }
     };
     // MODE 2: transpose block q and store column nb + c as chunk kc of LDS

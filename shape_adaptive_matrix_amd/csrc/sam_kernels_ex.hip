@@ -43,6 +43,29 @@ pack_kernel(const T* __restrict__ in, long long ld, T* __restrict__ out, long lo
     }
 }
 
+// dst[r][c] = c < cols ? src[r][c] : 0 for 16-bit values, c < ldd: the
+// copy of an operand whose rows are not whole 16-byte pieces into rows that
+// are (ldd a multiple of 8, dst 16-byte aligned), so the ring kernel can load
+// it 16 bytes at a time. One thread per 16-byte piece of dst; the source is
+// read one value at a time (its rows start at any 2-byte boundary).
+__global__ void __launch_bounds__(256)
+pad16_kernel(const unsigned short* __restrict__ src, long long lds, unsigned short* __restrict__ dst, long long ldd,
+             long long rows, long long cols)
+{
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const long long per_row = ldd / 8, total = rows * per_row;
+    const long long step = (long long)gridDim.x * blockDim.x;
+    for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += step) {
+        const long long r = e / per_row, c0 = (e - r * per_row) * 8;
+        unsigned short v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = c0 + q < cols ? src[r * lds + c0 + q] : (unsigned short)0;
+        const u4 w = {v[0] | ((unsigned)v[1] << 16), v[2] | ((unsigned)v[3] << 16), v[4] | ((unsigned)v[5] << 16),
+                      v[6] | ((unsigned)v[7] << 16)};
+        *reinterpret_cast<u4*>(dst + r * ldd + c0) = w;
+    }
+}
+
 // C[i][j] (row stride ldc) = alpha T[i][j] + beta C[i][j], evaluated as
 // fmaf(alpha, t, beta * c) in FP32. T is the product with row stride ldt, or
 // absent (alpha == 0 or K == 0: it counts as zero). C is read only when
@@ -64,6 +87,18 @@ axpby_kernel(const float* T, long long ldt, float* C, long long ldc, long long M
 }
 
 }  // namespace
+
+hipError_t launch_pad16(const void* src, long long lds, void* dst, long long ldd, long long rows, long long cols,
+                        hipStream_t s)
+{
+    const long long total = rows * (ldd / 8);
+    long long blocks = (total + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(pad16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const unsigned short*>(src),
+                       lds, static_cast<unsigned short*>(dst), ldd, rows, cols);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack(const void* in, long long ld, void* out, long long rows, long long cols, int elem_bytes,
                        int trans, hipStream_t s)

@@ -206,6 +206,38 @@ static bool split_admissible(const Variant& v, long long K, int dtype, int split
     return cdiv(nkb, per) == split;                           // no empty split
 }
 
+static unsigned long long align256(unsigned long long x) { return (x + 255ull) & ~255ull; }
+
+// The 16-bit ring kernels load whole 16-byte pieces of A and B rows. When K
+// (A's rows) or N (B's rows) is not a multiple of 8, that operand is first
+// copied into the workspace with its row stride rounded up to a multiple of
+// 8 and zeros in the gap; the kernel reads the copy, whose K and N tails it
+// masks as always. C is written in place. p->ws_bytes holds the plan's own
+// workspace on entry; the copies go in front of it.
+static void apply_pad(const Variant& v, long long M, long long N, long long K, Plan* p)
+{
+    p->pad_a = p->pad_b = 0;
+    p->lda = K;
+    p->ldb = N;
+    p->ws_inner = 0;
+    if (v.kind != KIND_DMA || (K % 8 == 0 && N % 8 == 0)) return;
+    p->pad_a = K % 8 != 0;
+    p->pad_b = N % 8 != 0;
+    p->lda = p->pad_a ? (K + 7) / 8 * 8 : K;
+    p->ldb = p->pad_b ? (N + 7) / 8 * 8 : N;
+    unsigned long long off = 0;
+    if (p->pad_a) off = align256((unsigned long long)(M * p->lda) * 2ull);
+    if (p->pad_b) off = align256(off + (unsigned long long)(K * p->ldb) * 2ull);
+    p->ws_inner = off;
+    p->ws_bytes += off;
+    // The copies read the operand one value at a time (about half the
+    // streaming rate) and write it 16 bytes at a time; one launch each.
+    const double mb = 1e-6;
+    const double bytes_a = p->pad_a ? 2.0 * M * K + 2.0 * M * p->lda : 0.0;
+    const double bytes_b = p->pad_b ? 2.0 * K * N + 2.0 * K * p->ldb : 0.0;
+    p->est_us += (bytes_a + bytes_b) * mb / (0.5 * kDev.hbm_gbs) * 1e3 + (p->pad_a + p->pad_b) * kDev.launch_us;
+}
+
 static void fill_plan(const Variant& v, long long M, long long N, long long K, int dtype, int split,
                       int raster_n, Plan* p)
 {
@@ -245,7 +277,9 @@ static void fill_plan(const Variant& v, long long M, long long N, long long K, i
     p->sk = 0;
     p->sk_dp = 0;
     p->sk_g = 0;
+    if (v.kind == KIND_DMA) p->a_vec = p->b_vec = 1;   // always 16-byte pieces (of a padded copy if need be)
     p->est_us = estimate_us(v, M, N, K, dtype, split, p->a_vec, p->b_vec, raster_n);
+    apply_pad(v, M, N, K, p);
 }
 
 // Stream-K (split_k = -1 in the ABI).
@@ -338,6 +372,7 @@ static void fill_plan_sk(const Variant& v, long long M, long long N, long long K
     p->grid = g.dp + g.G;
     p->ws_bytes = 2ull * (unsigned long long)g.G * (unsigned long long)(v.bm * v.bn) * 4ull;
     p->est_us = estimate_sk_us(v, M, N, K, dtype, g, p->a_vec, p->b_vec, raster_n);
+    apply_pad(v, M, N, K, p);
 }
 
 static const int kSplits[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
@@ -362,8 +397,11 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     if (M < 0 || N < 0 || K < 0) return false;
     // Block-scaled operands come in whole blocks of 32 values of K.
     if (v->kind == KIND_MX8 && K % 32 != 0) return false;
-    // The LDS-ring kernels take whole 16-byte pieces of A and B rows.
-    if (v->kind == KIND_DMA && (K % 8 != 0 || N % 8 != 0)) return false;
+    // The LDS-ring kernels take whole 16-byte pieces of A and B rows (of a
+    // padded copy when K or N is not a multiple of 8, see apply_pad); the
+    // operand-swap forms store four adjacent columns of C at once, so C's
+    // rows must be whole 16-byte pieces.
+    if (v->kind == KIND_DMA && v->swap && N % 4 != 0) return false;
     // FP32 ring kernels take rows that are not 16-byte pieces only in their
     // element-load form, which not every variant has.
     if (v->kind == KIND_F32RING && (K % 4 != 0 || N % 4 != 0) && !v->elem_loads) return false;

@@ -55,7 +55,7 @@ def test_plan_is_audited_argmin(shape, dtype):
     M, N, K = shape
     p = sam.plan(M, N, K, dtype)
     assert p == sam.plan(M, N, K, dtype)
-    if not p["name"].endswith("_tuned"):
+    if p["tuned"] == 0:
         best = None
         for vid in range(sam.variant_count()):
             try:
@@ -65,19 +65,41 @@ def test_plan_is_audited_argmin(shape, dtype):
             if best is None or q["est_us"] < best["est_us"]:
                 best = q
         assert best is not None
-        assert p["variant_id"] == best["variant_id"]
-        assert p["split_k"] == best["split_k"]
+        assert (p["variant_id"], p["split_k"], p["raster_n"]) == \
+            (best["variant_id"], best["split_k"], best["raster_n"])
+        assert p == sam.plan_model(M, N, K, dtype)
     tiles = -(-M // p["tile_m"]) * -(-N // p["tile_n"])
     if "_kp" in p["name"]:
         # Persistent short-K plans launch the resident workgroups only: one
         # per CU with a 64-value K panel (128 KB of LDS), two with 32.
         assert p["grid_wgs"] == min(tiles, 256 * (1 if p["tile_k"] == 64 else 2))
+    elif p["split_k"] == -1:
+        # Stream-K: data-parallel tiles (16-bit form) plus the sharing workgroups.
+        assert p["sk_dp_tiles"] <= p["grid_wgs"] and p["sk_dp_tiles"] <= tiles
     else:
         assert p["grid_wgs"] == tiles * p["split_k"]
+    assert p["workspace_bytes"] == expected_workspace(p, M, N, K, dtype)
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+def expected_workspace(p, M, N, K, dtype):
+    """Padded 16-bit operand copies (ring kernels with K or N not a multiple
+    of 8), then split-K partials or stream-K slots."""
+    pad = 0
+    if dtype in ("bf16", "f16") and p["name"].split("_", 1)[1][0] in "rqh":
+        if K % 8:
+            pad = _a256(M * ((K + 7) // 8 * 8) * 2)
+        if N % 8:
+            pad = _a256(pad + K * ((N + 7) // 8 * 8) * 2)
     if p["split_k"] > 1:
-        assert p["workspace_bytes"] == p["split_k"] * M * N * 4
-    else:
-        assert p["workspace_bytes"] == 0
+        return pad + p["split_k"] * M * N * 4
+    if p["split_k"] == -1:
+        G = p["grid_wgs"] - p["sk_dp_tiles"]
+        return pad + 2 * G * p["tile_m"] * p["tile_n"] * 4
+    return pad
 
 
 def test_large_d_picks_other_tile_than_2048():

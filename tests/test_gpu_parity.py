@@ -333,7 +333,9 @@ def test_inf_beyond_k_tail_is_not_read(shape):
 
 
 @pytest.mark.parametrize("dtype,shape", [("f32", (130, 132, 60)), ("f32", (70, 136, 45)), ("f32", (37, 64, 1037)),
-                                         ("bf16", (130, 136, 200)), ("f16", (70, 264, 40))])
+                                         ("bf16", (130, 136, 200)), ("f16", (70, 264, 40)),
+                                         # rows that are not whole 16-byte pieces (padded copies)
+                                         ("bf16", (130, 133, 201)), ("f16", (70, 261, 45))])
 def test_inf_at_start_of_next_row_is_not_read(dtype, shape):
     """A row's K tail is the start of the next row in memory. Inf there (A
     rows 1 and 3 start with Inf) must reach only those rows' outputs: rows 0
