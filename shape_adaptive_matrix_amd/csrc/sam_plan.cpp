@@ -117,7 +117,12 @@ static double reuse_miss_frac(const Variant& v, long long tiles_m, long long til
     }
     const double rows = (double)(raster_n ? other_used : lead_used);
     const double cols = (double)(raster_n ? lead_used : other_used);
-    return (rows * v.bm + cols * v.bn) / ((double)c * (v.bm + v.bn));
+    // A B panel is K rows of BN values (short row pieces), an A panel BM rows
+    // of K values: re-fetching B costs more per byte (loads of B alone took
+    // 1.2x those of A alone for the same bytes, 256 x 256 16-bit tiles), so
+    // its misses are weighted by that.
+    constexpr double kBWeight = 1.2;
+    return (rows * v.bm + kBWeight * cols * v.bn) / ((double)c * (v.bm + v.bn));
 }
 
 // Rounds of workgroups over the CUs. A last, partial round costs less than a
@@ -412,6 +417,10 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     if (v->kind == KIND_KQ && (split_req > 1 || (long long)v->bm * (K + 128) * 4 >= 0x7FFFFFF0ll ||
                                (K + 128) * N * 4 >= 0x7FFFFFF0ll))
         return false;
+    // They are for products that 128 x 128 tiles cannot spread over the
+    // CUs: with enough such tiles their small tiles only re-read operands
+    // (a 64 x 64 tile reads twice the bytes per FLOP of a 128 x 128 one).
+    if (v->kind == KIND_KQ && split_req <= 0 && cdiv(M, 128) * cdiv(N, 128) >= kDev.cus) return false;
     // The persistent short-K kernels hold a whole K panel per tile in LDS and
     // load A and B rows as 16-byte pieces.
     if (v->kind == KIND_KP && (split_req > 1 || K > v->bk || K % 4 != 0 || N % 4 != 0)) return false;

@@ -16,7 +16,9 @@ always gets the same plan):
 
 Timing protocol per candidate: 3 warm-up calls, then the median of 5
 batches of back-to-back calls lasting at least 15 ms each, HIP events on the
-launch stream. Inputs are the seeded generators of ``sam_inputs``.
+launch stream; skinny shapes (at most 16 rows or columns of C, HBM-bound)
+instead take the median of 15 single launches, each after a 1 GiB read that
+evicts the operands. Inputs are the seeded generators of ``sam_inputs``.
 """
 from __future__ import annotations
 
@@ -39,14 +41,21 @@ EXTRA = {
             (2048, 2048, 8192), (4096, 4096, 1024), (64, 4096, 4096), (4096, 64, 4096),
             (32, 8192, 8192), (256, 11008, 4096), (4096, 4096, 11008), (2049, 4097, 1025)],
     "bf16": [(1024, 1024, 1024), (2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144),
-             (4096, 4096, 1024), (2048, 8192, 2048), (256, 11008, 4096), (4096, 4096, 11008)],
-    "f16": [(2048, 2048, 2048), (6144, 6144, 6144), (4096, 4096, 11008)],
+             (4096, 4096, 1024), (2048, 8192, 2048), (256, 11008, 4096), (4096, 4096, 11008),
+             (2049, 4097, 1025), (5120, 5120, 5120), (8192, 8192, 8190)],
+    "f16": [(2048, 2048, 2048), (6144, 6144, 6144), (4096, 4096, 11008), (256, 11008, 4096), (2049, 4097, 1025)],
     "mxfp8": [(2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144), (4096, 4096, 1024),
               (256, 11008, 4096), (4096, 4096, 11008), (2048, 8192, 2048)],
     "mxfp4": [(2048, 2048, 2048), (6144, 6144, 6144), (4096, 4096, 11008), (256, 11008, 4096)],
 }
 
 SPLITS = (1, 2, 3, 4, 6, 8, 12, 16)
+
+# Shapes with at most this many rows or columns of C are bound by reading
+# the large operand from HBM once; they are timed cold (operands evicted
+# before each launch), the condition under which such a product runs when
+# its large operand is a weight matrix streamed from memory.
+COLD_EDGE = 16
 
 
 def shapes():
@@ -112,6 +121,7 @@ def measure(record: Path, only=None):
     import shape_adaptive_matrix_amd as sam
 
     sam.device_check()
+    flush = None
     done = set()
     if record.exists():
         for line in record.read_text().splitlines():
@@ -138,6 +148,9 @@ def measure(record: Path, only=None):
             C = torch.empty((M, N), dtype=torch.float32, device="cuda")
             stream = torch.cuda.current_stream()
             auto = model_plan(sam, dt, M, N, K)
+            cold = min(M, N) <= COLD_EDGE
+            if cold and flush is None:
+                flush = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
             print(f"[tune] {name}: {len(candidates(sam, dt, M, N, K))} candidates", flush=True)
             for (vid, split, raster) in candidates(sam, dt, M, N, K):
                 if (dt, M, N, K, vid, split, raster) in done:
@@ -161,22 +174,37 @@ def measure(record: Path, only=None):
                     if rc != 0:
                         raise RuntimeError(f"{name} variant {vid} split {split}: {sam.last_error()}")
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn(*args)
-                e1.record()
-                e1.synchronize()
-                n = max(3, int(15.0 / max(e0.elapsed_time(e1), 1e-3)))
-                samples = []
-                for _ in range(5):
-                    e0.record()
-                    for _ in range(n):
+                if cold:
+                    # HBM-bound skinny shape: single launches, each after a
+                    # 1 GiB read that evicts the operands (a read leaves clean
+                    # lines, so no write-back lands in the timed launch).
+                    samples = []
+                    for _ in range(15):
+                        flush.sum()
+                        e0.record()
                         fn(*args)
+                        e1.record()
+                        e1.synchronize()
+                        samples.append(e0.elapsed_time(e1))
+                    ms = statistics.median(samples)
+                else:
+                    e0.record()
+                    fn(*args)
                     e1.record()
                     e1.synchronize()
-                    samples.append(e0.elapsed_time(e1) / n)
-                ms = statistics.median(samples)
+                    n = max(3, int(15.0 / max(e0.elapsed_time(e1), 1e-3)))
+                    samples = []
+                    for _ in range(5):
+                        e0.record()
+                        for _ in range(n):
+                            fn(*args)
+                        e1.record()
+                        e1.synchronize()
+                        samples.append(e0.elapsed_time(e1) / n)
+                    ms = statistics.median(samples)
                 f.write(json.dumps({"shape": name, "dtype": dt, "M": M, "N": N, "K": K, "variant": vid,
                                     "split": split, "raster": p["raster_n"], "plan": p["name"], "ms": round(ms, 5),
+                                    "timing": "cold" if cold else "batch",
                                     "tflops": round(2.0 * M * N * K / ms / 1e9, 2),
                                     "est_us": round(p["est_us"], 1),
                                     "model_pick": (vid, split, p["raster_n"]) == (auto["variant_id"], auto["split_k"],

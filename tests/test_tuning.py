@@ -63,3 +63,21 @@ def test_shape_outside_every_bucket_uses_the_cost_model():
     assert p["tuned"] == 0 and not p["name"].endswith(("_tuned", "_bucket"))
     assert p == sam.plan_model(2040, 2056, 700, "f32")
     assert sam.plan(2040, 2056, 700, "f32") == p
+
+
+# The cost model alone (no frozen table) against the measured record: on
+# every recorded shape its pick was measured too (it is one of the
+# candidates), and it must be within this factor of the fastest one.
+MODEL_MARGIN = 1.30
+
+
+def test_cost_model_pick_is_near_the_measured_best():
+    worst = []
+    for (dtype, M, N, K), rs in tune.load(RECORD).items():
+        mp = sam.plan_model(M, N, K, dtype)
+        key = (mp["variant_id"], mp["split_k"], mp["raster_n"])
+        mine = next((r for r in rs if (r["variant"], r["split"], r["raster"]) == key), None)
+        assert mine is not None, f"{dtype} {(M, N, K)}: the model's pick {mp['name']} was never measured"
+        worst.append((mine["ms"] / rs[0]["ms"], dtype, (M, N, K), mp["name"], rs[0]["plan"]))
+    worst.sort(reverse=True)
+    assert worst[0][0] <= MODEL_MARGIN, worst[:3]
