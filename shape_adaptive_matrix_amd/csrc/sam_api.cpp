@@ -159,19 +159,29 @@ struct MxExtra {
 };
 
 // Shared body of every GEMM entry point once a plan is known.
+// lda / ldb: row strides of A and B in elements; 0 means compact rows (K
+// and N). Only the 16-bit ring kernels read strided rows, so any other
+// stride reaching here is an internal error.
 sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long long M, long long N,
-               long long K, void* ws, unsigned long long ws_bytes, void* stream, const MxExtra* mx = nullptr)
+               long long K, void* ws, unsigned long long ws_bytes, void* stream, const MxExtra* mx = nullptr,
+               long long lda = 0, long long ldb = 0)
 {
     const bool blockscaled = p.dtype == sam::DT_MX8 || p.dtype == sam::DT_MX4;
     // Bytes per element (E2M1: counted as one here; the operand sizes below halve it).
     const unsigned long long es = p.dtype == sam::DT_F32 ? 4 : (blockscaled ? 1 : 2);
     const unsigned long long half = p.dtype == sam::DT_MX4 ? 2 : 1;
     if (blockscaled != (mx != nullptr)) return fail(SAM_ERR_INTERNAL, "scale arguments mismatch");
+    if (lda <= 0) lda = K;
+    if (ldb <= 0) ldb = N;
+    // (A padded copy reads its source at any stride.)
+    if (lda < K || ldb < N || (lda != K && (p.kind != sam::KIND_DMA || (!p.pad_a && lda % 8))) ||
+        (ldb != N && (p.kind != sam::KIND_DMA || (!p.pad_b && ldb % 8))))
+        return fail(SAM_ERR_INTERNAL, "strided operands on a plan that cannot read them");
     if (M == 0 || N == 0) return SAM_OK;
     // Kernels address a workgroup's operand panels with 32-bit byte offsets:
-    // up to 257 rows of A (K elements each), 129 rows of B and 257 rows of C.
+    // up to 257 rows of A (lda elements each), 129 rows of B and 257 rows of C.
     const long long lim = 0x7FFFFFF0ll;
-    if ((long long)K * (long long)es * 257 >= lim || (long long)N * (long long)es * 129 >= lim ||
+    if ((long long)lda * (long long)es * 257 >= lim || (long long)ldb * (long long)es * 129 >= lim ||
         N * 4ll * 257 >= lim)
         return fail(SAM_ERR_INVALID_ARG, "K=%lld or N=%lld beyond the supported offset range", K, N);
     if (!C) return fail(SAM_ERR_INVALID_ARG, "C is null");
@@ -180,8 +190,9 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
     if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))) || (ws && !aligned16(ws)))
         return fail(SAM_ERR_MISALIGNED, "A, B, C and workspace must be 16-byte aligned");
     const unsigned long long cbytes = (unsigned long long)(M * N) * 4ull;
-    if (ranges_overlap(C, cbytes, A, (unsigned long long)(M * K) * es / half) ||
-        ranges_overlap(C, cbytes, B, (unsigned long long)(K * N) * es / half))
+    const unsigned long long abytes = K ? (unsigned long long)((M - 1) * lda + K) * es / half : 0;
+    const unsigned long long bbytes = K ? (unsigned long long)((K - 1) * ldb + N) * es / half : 0;
+    if (ranges_overlap(C, cbytes, A, abytes) || ranges_overlap(C, cbytes, B, bbytes))
         return fail(SAM_ERR_INVALID_ARG, "C overlaps A or B");
     if (mx && (ranges_overlap(C, cbytes, mx->sa, (unsigned long long)(M * (K / 32))) ||
                ranges_overlap(C, cbytes, mx->sb, (unsigned long long)(N * (K / 32)))))
@@ -190,8 +201,8 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         if (!ws || ws_bytes < p.ws_bytes)
             return fail(SAM_ERR_WORKSPACE, "plan %d needs %llu workspace bytes, got %llu", p.variant_id,
                         (unsigned long long)p.ws_bytes, (unsigned long long)(ws ? ws_bytes : 0));
-        if (ranges_overlap(C, cbytes, ws, p.ws_bytes) || ranges_overlap(A, (unsigned long long)(M * K) * es / half, ws, p.ws_bytes) ||
-            ranges_overlap(B, (unsigned long long)(K * N) * es / half, ws, p.ws_bytes))
+        if (ranges_overlap(C, cbytes, ws, p.ws_bytes) || ranges_overlap(A, abytes, ws, p.ws_bytes) ||
+            ranges_overlap(B, bbytes, ws, p.ws_bytes))
             return fail(SAM_ERR_INVALID_ARG, "workspace overlaps A, B or C");
     }
     sam_status d = device_check_impl();
@@ -206,12 +217,12 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         // copies in front of the plan's own workspace.
         char* wsb = static_cast<char*>(ws);
         if (p.pad_a) {
-            e = sam::launch_pad16(A, K, wsb, p.lda, M, K, s);
+            e = sam::launch_pad16(A, lda, wsb, p.lda, M, K, s);
             A = wsb;
         }
         if (e == hipSuccess && p.pad_b) {
             char* bb = wsb + (p.pad_a ? ((unsigned long long)(M * p.lda) * 2ull + 255ull) & ~255ull : 0ull);
-            e = sam::launch_pad16(B, N, bb, p.ldb, K, N, s);
+            e = sam::launch_pad16(B, ldb, bb, p.ldb, K, N, s);
             B = bb;
         }
         if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
@@ -219,8 +230,8 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         sam::GemmArgs a{};
         a.A = A;
         a.B = B;
-        a.lda = (int)p.lda;
-        a.ldb = (int)p.ldb;
+        a.lda = (int)(p.pad_a ? p.lda : lda);
+        a.ldb = (int)(p.pad_b ? p.ldb : ldb);
         a.out = p.split > 1 ? static_cast<float*>(ws) : C;
         a.M = (int)M;
         a.N = (int)N;
@@ -271,6 +282,7 @@ struct ExLayout {
     bool fast;            // plain C = A*B: straight to the GEMM path
     bool product;         // alpha != 0 and K > 0
     bool pack_a, pack_b;  // op(A) / op(B) copied into compact rows first
+    bool direct_a, direct_b;  // strided A / B read in place by the 16-bit ring kernel
     bool use_t;           // product into a temporary, then C = alpha T + beta C
     unsigned long long off_a, off_b, off_t, off_w, total;
     sam::Plan plan;
@@ -304,8 +316,11 @@ sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long l
         L->total = L->plan.ws_bytes;
         return SAM_OK;
     }
-    L->pack_a = L->product && (ta || lda != K);
-    L->pack_b = L->product && (tb || ldb != N);
+    const bool ring16 = L->product && L->plan.kind == sam::KIND_DMA;
+    L->direct_a = ring16 && !ta && lda != K && (L->plan.pad_a || lda % 8 == 0);
+    L->direct_b = ring16 && !tb && ldb != N && (L->plan.pad_b || ldb % 8 == 0);
+    L->pack_a = L->product && (ta || lda != K) && !L->direct_a;
+    L->pack_b = L->product && (tb || ldb != N) && !L->direct_b;
     L->use_t = L->product && !(ldc == N && beta == 0.0f);
     L->off_a = 0;
     L->off_b = align256(L->off_a + (L->pack_a ? (unsigned long long)(M * K) * es : 0));
@@ -376,7 +391,8 @@ sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t 
         }
         if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
         float* out = L.use_t ? reinterpret_cast<float*>(ws + L.off_t) : C;
-        st = run(L.plan, a, b, out, M, N, K, L.plan.ws_bytes ? ws + L.off_w : nullptr, L.plan.ws_bytes, stream);
+        st = run(L.plan, a, b, out, M, N, K, L.plan.ws_bytes ? ws + L.off_w : nullptr, L.plan.ws_bytes, stream,
+                 nullptr, L.direct_a ? lda : 0, L.direct_b ? ldb : 0);
         if (st != SAM_OK) return st;
         if (L.use_t)
             e = sam::launch_axpby(out, N, C, ldc, M, N, alpha, beta, s);

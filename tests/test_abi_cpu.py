@@ -226,6 +226,28 @@ def test_gemm_ex_rejections_before_any_device_call():
     assert sam.ex_workspace_bytes(64, 64, 64, False, False, 64, 64, 64, 1.0, 0.0, "f32") == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_ex_strided_rows_on_a_16bit_ring_plan_need_no_packed_copy(dtype):
+    """A 16-bit ring plan reads padded rows in place when the stride keeps
+    16-byte rows, and through its own padded copy when the plan makes one:
+    the workspace is then the plan's alone. Other strides, transposes and
+    other plan kinds still reserve a packed copy."""
+    M, N, K = 1024, 768, 200
+    p = sam.plan(M, N, K, dtype)
+    assert p["name"].startswith(dtype + "_r")
+    ws = lambda ta, tb, lda, ldb: sam.ex_workspace_bytes(M, N, K, ta, tb, lda, ldb, N, 1.0, 0.0, dtype)
+    assert ws(False, False, K + 8, N + 16) == p["workspace_bytes"]
+    assert ws(False, False, K + 3, N) >= M * K * 2                      # misaligned rows: packed
+    assert ws(True, False, M, N) >= M * K * 2                           # transposed: packed
+    q = sam.plan(2049, 4097, 1025, dtype)                               # plan pads both operands
+    assert q["name"].startswith(dtype + "_r") and q["workspace_bytes"] > 0
+    assert sam.ex_workspace_bytes(2049, 4097, 1025, False, False, 1028, 4102, 4097, 1.0, 0.0,
+                                  dtype) == q["workspace_bytes"]
+    r = sam.plan(512, 512, 512, dtype)                                  # staged plan: packed
+    assert not r["name"].startswith(dtype + "_r")
+    assert sam.ex_workspace_bytes(512, 512, 512, False, False, 520, 520, 512, 1.0, 0.0, dtype) >= 512 * 512 * 4
+
+
 def test_mxfp8_plans_and_rejections_before_any_device_call():
     """Block-scaled plans come from the block-scaled variants only; K not a
     multiple of 32, bad formats, a negative split, null scales and the plain

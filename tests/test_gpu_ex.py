@@ -109,3 +109,33 @@ def test_ex_k_zero_and_alpha_zero():
     sam.gemm_ex(A, B, Cd, alpha=0.0, beta=0.5)
     torch.cuda.synchronize()
     assert np.array_equal(Cd.cpu().numpy(), 0.5 * C0)
+
+
+# Operands with padded rows read in place by the 16-bit ring kernel (no
+# packed copy): row strides that keep 16-byte rows, and misaligned ones on a
+# shape whose plan copies both operands into zero-padded rows anyway (the
+# copy then reads the caller's stride). Every case's plan is a ring plan.
+RING16_STRIDED = [((1024, 768, 200), 8, 16), ((1500, 1200, 1032), 64, 8), ((2048, 2048, 2048), 24, 40),
+                  ((2049, 4097, 1025), 3, 5)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", RING16_STRIDED, ids=lambda c: "x".join(map(str, c[0])) + f"_p{c[1]}_{c[2]}")
+def test_ex_ring16_strided_in_place(dtype, case):
+    (M, N, K), pa, pb = case
+    plan = sam.plan(M, N, K, dtype)
+    assert plan["name"].startswith(dtype + "_r"), plan["name"]
+    lda, ldb = K + pa, N + pb
+    # no region for a packed copy: the workspace is the plan's own
+    assert sam.ex_workspace_bytes(M, N, K, False, False, lda, ldb, N, 1.0, 0.0, dtype) == plan["workspace_bytes"]
+    rng = np.random.default_rng(M + 7 * N + 11 * K + pa)
+    Av = rng.integers(-3, 4, size=(M, lda)).astype(np.float32)
+    Bv = rng.integers(-3, 4, size=(K, ldb)).astype(np.float32)
+    Av[:, K:] = np.inf                                                # gaps: never read
+    Bv[:, N:] = np.inf
+    Cd = torch.full((M, N), float("nan"), device="cuda")
+    sam.gemm_ex(_dev(dtype, _enc(dtype, Av))[:, :K], _dev(dtype, _enc(dtype, Bv))[:, :N], Cd)
+    torch.cuda.synchronize()
+    ref = orc().gemm(dtype, np.ascontiguousarray(_enc(dtype, Av)[:, :K]),
+                     np.ascontiguousarray(_enc(dtype, Bv)[:, :N]), nthreads=orc().max_threads())
+    assert bitexact_mismatches(Cd.cpu().numpy(), ref) == 0
