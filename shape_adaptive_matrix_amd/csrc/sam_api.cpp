@@ -159,37 +159,62 @@ struct MxExtra {
 };
 
 // Shared body of every GEMM entry point once a plan is known.
-// lda / ldb: row strides of A and B in elements; 0 means compact rows (K
-// and N). Only the 16-bit ring kernels read strided rows, so any other
-// stride reaching here is an internal error.
+// The general entry point's strides of A, B and C (elements) and its
+// alpha / beta, taken inside a ring plan's loads and stores.
+struct ExTail {
+    long long lda, ldb, ldc;
+    float alpha, beta;
+};
+
+// Whether a plan can take A rows with stride lda != K in place: a 16-bit
+// ring plan whose rows stay 16-byte pieces or which copies A into padded
+// rows anyway (the copy reads any stride); an FP32 ring plan whose rows stay
+// 16-byte pieces or which reads A one value at a time. Likewise B.
+bool reads_strided(const sam::Plan& p, bool a_side, long long ld)
+{
+    if (p.kind == sam::KIND_DMA) return (a_side ? p.pad_a : p.pad_b) || ld % 8 == 0;
+    if (p.kind == sam::KIND_F32RING) return !(a_side ? p.a_vec : p.b_vec) || ld % 4 == 0;
+    return false;
+}
+
+// Ring plans store C with row stride ldc (a multiple of 4: 16-byte stores)
+// and through the alpha / beta epilogue, in the kernel or the split-K /
+// stream-K pass that writes C.
+bool writes_general_c(const sam::Plan& p, long long ldc)
+{
+    return (p.kind == sam::KIND_DMA || p.kind == sam::KIND_F32RING) && ldc % 4 == 0;
+}
+
+// x: null for compact operands and C = A B; otherwise what the plan must
+// honour, which the caller has checked with reads_strided / writes_general_c.
 sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long long M, long long N,
                long long K, void* ws, unsigned long long ws_bytes, void* stream, const MxExtra* mx = nullptr,
-               long long lda = 0, long long ldb = 0)
+               const ExTail* x = nullptr)
 {
     const bool blockscaled = p.dtype == sam::DT_MX8 || p.dtype == sam::DT_MX4;
     // Bytes per element (E2M1: counted as one here; the operand sizes below halve it).
     const unsigned long long es = p.dtype == sam::DT_F32 ? 4 : (blockscaled ? 1 : 2);
     const unsigned long long half = p.dtype == sam::DT_MX4 ? 2 : 1;
     if (blockscaled != (mx != nullptr)) return fail(SAM_ERR_INTERNAL, "scale arguments mismatch");
-    if (lda <= 0) lda = K;
-    if (ldb <= 0) ldb = N;
-    // (A padded copy reads its source at any stride.)
-    if (lda < K || ldb < N || (lda != K && (p.kind != sam::KIND_DMA || (!p.pad_a && lda % 8))) ||
-        (ldb != N && (p.kind != sam::KIND_DMA || (!p.pad_b && ldb % 8))))
-        return fail(SAM_ERR_INTERNAL, "strided operands on a plan that cannot read them");
+    const long long lda = x ? x->lda : K, ldb = x ? x->ldb : N, ldc = x ? x->ldc : N;
+    const float alpha = x ? x->alpha : 1.0f, beta = x ? x->beta : 0.0f;
+    const bool gen = alpha != 1.0f || beta != 0.0f;
+    if (x && (K == 0 || lda < K || ldb < N || ldc < N || (lda != K && !reads_strided(p, true, lda)) ||
+              (ldb != N && !reads_strided(p, false, ldb)) || ((ldc != N || gen) && !writes_general_c(p, ldc))))
+        return fail(SAM_ERR_INTERNAL, "strides or alpha / beta on a plan that cannot take them");
     if (M == 0 || N == 0) return SAM_OK;
     // Kernels address a workgroup's operand panels with 32-bit byte offsets:
     // up to 257 rows of A (lda elements each), 129 rows of B and 257 rows of C.
     const long long lim = 0x7FFFFFF0ll;
     if ((long long)lda * (long long)es * 257 >= lim || (long long)ldb * (long long)es * 129 >= lim ||
-        N * 4ll * 257 >= lim)
+        ldc * 4ll * 257 >= lim)
         return fail(SAM_ERR_INVALID_ARG, "K=%lld or N=%lld beyond the supported offset range", K, N);
     if (!C) return fail(SAM_ERR_INVALID_ARG, "C is null");
     if (K > 0 && (!A || !B)) return fail(SAM_ERR_INVALID_ARG, "A or B is null");
     if (mx && K > 0 && (!mx->sa || !mx->sb)) return fail(SAM_ERR_INVALID_ARG, "a scale array is null");
     if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))) || (ws && !aligned16(ws)))
         return fail(SAM_ERR_MISALIGNED, "A, B, C and workspace must be 16-byte aligned");
-    const unsigned long long cbytes = (unsigned long long)(M * N) * 4ull;
+    const unsigned long long cbytes = (unsigned long long)((M - 1) * ldc + N) * 4ull;
     const unsigned long long abytes = K ? (unsigned long long)((M - 1) * lda + K) * es / half : 0;
     const unsigned long long bbytes = K ? (unsigned long long)((K - 1) * ldb + N) * es / half : 0;
     if (ranges_overlap(C, cbytes, A, abytes) || ranges_overlap(C, cbytes, B, bbytes))
@@ -233,6 +258,10 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         a.lda = (int)(p.pad_a ? p.lda : lda);
         a.ldb = (int)(p.pad_b ? p.ldb : ldb);
         a.out = p.split > 1 ? static_cast<float*>(ws) : C;
+        a.ldc = (int)(p.split > 1 ? N : ldc);   // split-K: the reduce pass writes C
+        a.epi = p.split > 1 ? 0 : (int)gen;
+        a.alpha = alpha;
+        a.beta = beta;
         a.M = (int)M;
         a.N = (int)N;
         a.K = (int)K;
@@ -258,7 +287,9 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         }
         e = sam::launch_gemm(p, a, s);
         if (e == hipSuccess && p.split > 1)
-            e = sam::launch_reduce(static_cast<const float*>(ws), p.split, M * N, C, M * N, s);
+            e = ldc != N || gen
+                    ? sam::launch_reduce_ex(static_cast<const float*>(ws), p.split, M * N, C, M, N, ldc, alpha, beta, s)
+                    : sam::launch_reduce(static_cast<const float*>(ws), p.split, M * N, C, M * N, s);
         if (e == hipSuccess && p.sk) e = sam::launch_sk_fixup(p, a, s);
     }
     if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
@@ -282,7 +313,8 @@ struct ExLayout {
     bool fast;            // plain C = A*B: straight to the GEMM path
     bool product;         // alpha != 0 and K > 0
     bool pack_a, pack_b;  // op(A) / op(B) copied into compact rows first
-    bool direct_a, direct_b;  // strided A / B read in place by the 16-bit ring kernel
+    bool direct_a, direct_b;  // strided A / B read in place by a ring plan
+    bool fused_c;         // a ring plan stores C itself (stride ldc, alpha / beta)
     bool use_t;           // product into a temporary, then C = alpha T + beta C
     unsigned long long off_a, off_b, off_t, off_w, total;
     sam::Plan plan;
@@ -316,12 +348,12 @@ sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long l
         L->total = L->plan.ws_bytes;
         return SAM_OK;
     }
-    const bool ring16 = L->product && L->plan.kind == sam::KIND_DMA;
-    L->direct_a = ring16 && !ta && lda != K && (L->plan.pad_a || lda % 8 == 0);
-    L->direct_b = ring16 && !tb && ldb != N && (L->plan.pad_b || ldb % 8 == 0);
+    L->direct_a = L->product && !ta && lda != K && reads_strided(L->plan, true, lda);
+    L->direct_b = L->product && !tb && ldb != N && reads_strided(L->plan, false, ldb);
+    L->fused_c = L->product && writes_general_c(L->plan, ldc);
     L->pack_a = L->product && (ta || lda != K) && !L->direct_a;
     L->pack_b = L->product && (tb || ldb != N) && !L->direct_b;
-    L->use_t = L->product && !(ldc == N && beta == 0.0f);
+    L->use_t = L->product && !L->fused_c && !(ldc == N && beta == 0.0f);
     L->off_a = 0;
     L->off_b = align256(L->off_a + (L->pack_a ? (unsigned long long)(M * K) * es : 0));
     L->off_t = align256(L->off_b + (L->pack_b ? (unsigned long long)(K * N) * es : 0));
@@ -391,10 +423,14 @@ sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t 
         }
         if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
         float* out = L.use_t ? reinterpret_cast<float*>(ws + L.off_t) : C;
+        const ExTail x{L.direct_a ? lda : K, L.direct_b ? ldb : N, L.fused_c ? ldc : N, L.fused_c ? alpha : 1.0f,
+                       L.fused_c ? beta : 0.0f};
         st = run(L.plan, a, b, out, M, N, K, L.plan.ws_bytes ? ws + L.off_w : nullptr, L.plan.ws_bytes, stream,
-                 nullptr, L.direct_a ? lda : 0, L.direct_b ? ldb : 0);
+                 nullptr, &x);
         if (st != SAM_OK) return st;
-        if (L.use_t)
+        if (L.fused_c) {
+            // alpha / beta and the stride of C were applied where C was written
+        } else if (L.use_t)
             e = sam::launch_axpby(out, N, C, ldc, M, N, alpha, beta, s);
         else if (alpha != 1.0f)
             e = sam::launch_axpby(C, ldc, C, ldc, M, N, alpha, 0.0f, s);   // in place: C = alpha C

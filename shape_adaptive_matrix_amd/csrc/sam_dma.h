@@ -102,5 +102,58 @@ __device__ __forceinline__ void tile_coords(int wg, const GemmArgs& a, int& tm, 
     tile_of(L - s * tiles, a, tm, tn);
 }
 
+// Stores of C with the general entry point's epilogue. With gen, each
+// product value t becomes alpha t + beta c, evaluated as fmaf(alpha, t,
+// beta c) in FP32 with c the value C holds at that place, read first and only
+// when beta != 0 (so values in C never reach a beta == 0 result); without
+// gen, t is stored as it is. An out-of-range offset reads zero and drops the
+// store, as for the plain stores.
+__device__ __forceinline__ float epi_value(float t, float c, const GemmArgs& a) {
+    return a.beta != 0.0f ? __fmaf_rn(a.alpha, t, a.beta * c) : a.alpha * t;
+}
+
+template <int W>
+struct StoreC;
+
+template <>
+struct StoreC<4> {
+    typedef unsigned int V __attribute__((ext_vector_type(4)));
+    static __device__ __forceinline__ void run(V v, __amdgpu_buffer_rsrc_t rC, int off, const GemmArgs& a, bool gen) {
+        if (gen) {
+            V c = {0u, 0u, 0u, 0u};
+            if (a.beta != 0.0f) c = __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = __float_as_uint(epi_value(__uint_as_float(v[q]), __uint_as_float(c[q]), a));
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, 0);
+    }
+};
+
+template <>
+struct StoreC<2> {
+    typedef unsigned int V __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ void run(V v, __amdgpu_buffer_rsrc_t rC, int off, const GemmArgs& a, bool gen) {
+        if (gen) {
+            V c = {0u, 0u};
+            if (a.beta != 0.0f) c = __builtin_amdgcn_raw_buffer_load_b64(rC, off, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) v[q] = __float_as_uint(epi_value(__uint_as_float(v[q]), __uint_as_float(c[q]), a));
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
+    }
+};
+
+template <>
+struct StoreC<1> {
+    typedef unsigned int V;
+    static __device__ __forceinline__ void run(V v, __amdgpu_buffer_rsrc_t rC, int off, const GemmArgs& a, bool gen) {
+        if (gen) {
+            const V c = a.beta != 0.0f ? __builtin_amdgcn_raw_buffer_load_b32(rC, off, 0, 0) : 0u;
+            v = __float_as_uint(epi_value(__uint_as_float(v), __uint_as_float(c), a));
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(v, rC, off, 0, 0);
+    }
+};
+
 }  // namespace dma
 }  // namespace sam

@@ -75,7 +75,15 @@ struct GemmArgs {
     int sk_grid;         // stream-K: workgroups sharing the stream-K tiles' iterations
     int sk_dp;           // stream-K: leading tiles run one per workgroup before them (16-bit form)
     int raster_n;        // 1: raster groups of group_m tile columns walk the rows (N-major)
-    int lda, ldb;        // row strides of A and B in elements (16-bit ring kernel; K and N otherwise)
+    int lda, ldb;        // row strides of A and B in elements (ring kernels; K and N otherwise)
+    // Final store of C (not of split-K partials; ring kernels and their
+    // stream-K fix-up only): row stride ldc, and with epi = 1 the stored
+    // value is alpha t + beta C for the product t, as the general entry
+    // point defines it (C read only when beta != 0). Otherwise ldc = N,
+    // epi = 0.
+    int ldc;
+    int epi;
+    float alpha, beta;
     const unsigned char* sa;   // block-scaled operands: scale codes of A (M x K/32)
     const unsigned char* sb;   // ... and of B (N x K/32); B is then N rows of K codes
     int fmt_a, fmt_b;    // element formats: 0 E4M3, 1 E5M2
@@ -135,6 +143,10 @@ hipError_t launch_kq(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_kp(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const float* parts, int split, long long part_stride,
                          float* C, long long count, hipStream_t s);
+// Split-K sum into C with row stride ldc through the general entry point's
+// epilogue (alpha t + beta C).
+hipError_t launch_reduce_ex(const float* parts, int split, long long part_stride, float* C, long long M, long long N,
+                            long long ldc, float alpha, float beta, hipStream_t s);
 hipError_t launch_zero(float* C, long long count, hipStream_t s);
 // General entry point (sam_kernels_ex.hip): pack an operand (transposing
 // when `trans`) into compact rows, and C = alpha T + beta C.

@@ -113,7 +113,7 @@ template <int DT> struct Mf<DT, 16> {
 // instantiates it once holds one ring.
 template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK, int SWAP, bool SEG>
 __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int tn, int kbeg, int kend, float* outp,
-                                               int ostride, int orows, int ocols)
+                                               int ostride, int orows, int ocols, bool to_c)
 {
     using namespace dma;
     static_assert(DT == DT_BF16 || DT == DT_F16, "16-bit operands only");
@@ -449,43 +449,51 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
     wait_cnt<0, 0>();   // no LDS load may still be in flight when the segment ends
 
     // The data-parallel form stores to C or to split `ostride`'s partial
-    // slice, at (m0, n0) with row stride N (formed here, so nothing of it is
-    // live through the K loop).
+    // slice, at (m0, n0) with row stride ldc (N for partials; formed here,
+    // so nothing of it is live through the K loop).
     if constexpr (!SEG) {
-        outp = args.out + (long long)ostride * args.part_stride + (long long)m0 * N + n0;
+        outp = args.out + (long long)ostride * args.part_stride + (long long)m0 * args.ldc + n0;
         orows = M - m0;
         ocols = N - n0;
-        ostride = N;
+        ostride = args.ldc;
     }
     const __amdgpu_buffer_rsrc_t rC =
-        SEG ? make_rsrc(outp, orows > 0 && ocols > 0 ? ((long long)(orows - 1) * ostride + ocols) * 4 : 0)
-            : make_rsrc(outp, ((long long)(M - m0) * N - n0) * 4);
+        make_rsrc(outp, orows > 0 && ocols > 0 ? ((long long)(orows - 1) * ostride + ocols) * 4 : 0);
+    const bool gen = to_c && args.epi;       // the general entry point's alpha / beta
+    // The plain and the alpha / beta stores are separate straight-line loops.
+    auto store_all = [&](auto genc) {
+        constexpr bool GEN = decltype(genc)::value;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (SWAP) {
-                // Transposed block: lane l holds row l % 16 of the block,
-                // columns 4 (l / 16) .. + 3 (N % 8 == 0, so the four are all
-                // inside C or all past it).
-                const int row = wm0 + BLK * i + lrow;
-                const int col = wn0 + BLK * j + 4 * lgrp;
-                const bool ok = row < orows && col < ocols;
-                const u4 v = {__float_as_uint(acc[i][j][0]), __float_as_uint(acc[i][j][1]),
-                              __float_as_uint(acc[i][j][2]), __float_as_uint(acc[i][j][3])};
-                __builtin_amdgcn_raw_buffer_store_b128(v, rC, ok ? (row * ostride + col) * 4 : kOOB, 0, 0);
-            } else {
-                const int col = wn0 + BLK * j + lrow;
-#pragma unroll
-                for (int r = 0; r < MF::NV; ++r) {
-                    const int row = wm0 + BLK * i + MF::row(lane, r);
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (SWAP) {
+                    // Transposed block: lane l holds row l % 16 of the block,
+                    // columns 4 (l / 16) .. + 3 (N % 8 == 0, so the four are
+                    // all inside C or all past it).
+                    const int row = wm0 + BLK * i + lrow;
+                    const int col = wn0 + BLK * j + 4 * lgrp;
                     const bool ok = row < orows && col < ocols;
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rC,
-                                                          ok ? (row * ostride + col) * 4 : kOOB, 0, 0);
+                    const u4 v = {__float_as_uint(acc[i][j][0]), __float_as_uint(acc[i][j][1]),
+                                  __float_as_uint(acc[i][j][2]), __float_as_uint(acc[i][j][3])};
+                    StoreC<4>::run(v, rC, ok ? (row * ostride + col) * 4 : kOOB, args, GEN);
+                } else {
+                    const int col = wn0 + BLK * j + lrow;
+#pragma unroll
+                    for (int r = 0; r < MF::NV; ++r) {
+                        const int row = wm0 + BLK * i + MF::row(lane, r);
+                        const bool ok = row < orows && col < ocols;
+                        StoreC<1>::run(__float_as_uint(acc[i][j][r]), rC, ok ? (row * ostride + col) * 4 : kOOB,
+                                       args, GEN);
+                    }
                 }
             }
         }
-    }
+    };
+    if (gen)
+        store_all(std::true_type{});
+    else
+        store_all(std::false_type{});
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NBUF>
@@ -505,7 +513,8 @@ gemm16_dma_kernel(GemmArgs args)
     dma::tile_coords(blockIdx.x, args, tm, tn, s);
     const int kbeg = s * args.k_chunk;
     const int kend = min(args.K, kbeg + args.k_chunk);
-    ring16_segment<DT, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SWAP, false>(args, tm, tn, kbeg, kend, nullptr, s, 0, 0);
+    ring16_segment<DT, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SWAP, false>(args, tm, tn, kbeg, kend, nullptr, s, 0, 0,
+                                                                        true);
 }
 
 // Data-parallel + stream-K form (page "fix(fp4_gemm autotune) SM107 kernel
@@ -553,11 +562,11 @@ gemm16_dma_sk_kernel(GemmArgs args)
         const int m0 = tm * BM, n0 = tn * BN;
         if (seg > 0) dma::barrier();   // the previous segment's last LDS reads are done
         const bool whole = k0 == 0 && k1 == I;
-        float* outp = whole ? args.out + (long long)m0 * args.N + n0
+        float* outp = whole ? args.out + (long long)m0 * args.ldc + n0
                             : args.ws + (2 * g + seg) * (long long)(BM * BN);
         ring16_segment<DT, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SWAP, true>(
-            args, tm, tn, k0 * BK, min(args.K, k1 * BK), outp, whole ? args.N : BN, whole ? args.M - m0 : BM,
-            whole ? args.N - n0 : BN);
+            args, tm, tn, k0 * BK, min(args.K, k1 * BK), outp, whole ? args.ldc : BN, whole ? args.M - m0 : BM,
+            whole ? args.N - n0 : BN, whole);
         it += k1 - k0;
     }
 }

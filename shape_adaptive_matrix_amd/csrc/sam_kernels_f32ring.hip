@@ -86,7 +86,7 @@ constexpr int ring_lds_bytes() { return NBUF * (BM + BN) * BK * 4; }
 // to C or to the partial slice of split `ostride`.
 template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool SEG>
 __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int tn, int kbeg, int kend, float* outp,
-                                             int ostride, int orows, int ocols)
+                                             int ostride, int orows, int ocols, bool to_c)
 {
     using namespace dma;
     using namespace f32ring;
@@ -139,9 +139,10 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
     const int wn0 = (pos % WN) * WTN;
     const int tbase = half * KH;               // this wave's first chunk step of a stage
 
-    const i4 rA = rsrc_words(reinterpret_cast<const char*>(args.A) + (long long)m0 * K * 4,
-                             (long long)(M - m0) * K * 4);
-    const long long b_bytes = (long long)K * N * 4;
+    const int lda = args.lda, ldb = args.ldb;    // operand row strides (elements)
+    const i4 rA = rsrc_words(reinterpret_cast<const char*>(args.A) + (long long)m0 * lda * 4,
+                             (long long)(M - m0) * lda * 4);
+    const long long b_bytes = (long long)K * ldb * 4;
 
     // Wave load q of stage `st`: the first A_PW LA loads fetch A rows into
     // 1 KB blocks (RPA rows per block, chunks placed swizzled: physical chunk
@@ -161,7 +162,7 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
             const int p = ((4 * d) % A_ROW) / 16;
             const int gk = k0 + 4 * (p ^ ((row / RSW) % CPA)) + (d & 3);
             const bool ok = m0 + row < M && gk < kend;
-            lds_load4(rA, lds_addr(buf + I * 1024 + 256 * (q % 4)), ok ? (row * K + gk) * 4 : kOOB);
+            lds_load4(rA, lds_addr(buf + I * 1024 + 256 * (q % 4)), ok ? (row * lda + gk) * 4 : kOOB);
         } else {
             const int qq = q - A_PW * LA;
             const int qb = qq / 4, d = 64 * (qq % 4) + lane;
@@ -169,9 +170,9 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
             const int byte = I * 1024 + 4 * d;
             const int row = byte / B_ROW, col = (byte % B_ROW) / 4;
             const bool ok = k0 + row < kend && n0 + col < N;
-            const long long bbase = ((long long)k0 * N + n0) * 4;
+            const long long bbase = ((long long)k0 * ldb + n0) * 4;
             const i4 rB = rsrc_words(reinterpret_cast<const char*>(args.B) + bbase, b_bytes - bbase);
-            lds_load4(rB, lds_addr(buf + A_BYTES + I * 1024 + 256 * (qq % 4)), ok ? (row * N + col) * 4 : kOOB);
+            lds_load4(rB, lds_addr(buf + A_BYTES + I * 1024 + 256 * (qq % 4)), ok ? (row * ldb + col) * 4 : kOOB);
         }
     };
     auto issue_one = [&](int st, int q) {
@@ -195,15 +196,15 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
             const int c = (lane % CPA) ^ ((row / RSW) % CPA);
             const int gk = k0 + 4 * c;
             const bool ok = m0 + row < M && gk < kend;
-            lds_load16(rA, lds_addr(buf + I * 1024), ok ? (row * K + gk) * 4 : kOOB);
+            lds_load16(rA, lds_addr(buf + I * 1024), ok ? (row * lda + gk) * 4 : kOOB);
         } else {
             const int I = wave + (q - A_PW) * NW;
             const int byte = I * 1024 + 16 * lane;
             const int row = byte / B_ROW, col = (byte % B_ROW) / 4;
             const bool ok = k0 + row < kend && n0 + col < N;
-            const long long bbase = ((long long)k0 * N + n0) * 4;
+            const long long bbase = ((long long)k0 * ldb + n0) * 4;
             const i4 rB = rsrc_words(reinterpret_cast<const char*>(args.B) + bbase, b_bytes - bbase);
-            lds_load16(rB, lds_addr(buf + A_BYTES + I * 1024), ok ? (row * N + col) * 4 : kOOB);
+            lds_load16(rB, lds_addr(buf + A_BYTES + I * 1024), ok ? (row * ldb + col) * 4 : kOOB);
         }
     };
 
@@ -317,17 +318,18 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
     // tail is instantiated per half so every accumulator index is static.
     constexpr int I0 = KS == 2 ? TM / 2 : TM;  // row blocks each wave stores
     // Data-parallel form (outp carries nothing): the tile goes to C, or to
-    // split `ostride`'s partial slice, at (m0, n0) with row stride N. Formed
-    // here rather than by the caller, so it is not live through the K loop.
+    // split `ostride`'s partial slice, at (m0, n0) with row stride ldc (N
+    // for partials). Formed here rather than by the caller, so it is not live
+    // through the K loop.
     if constexpr (!SEG) {
-        outp = args.out + (long long)ostride * args.part_stride + (long long)m0 * N + n0;
+        outp = args.out + (long long)ostride * args.part_stride + (long long)m0 * args.ldc + n0;
         orows = M - m0;
         ocols = N - n0;
-        ostride = N;
+        ostride = args.ldc;
     }
     const __amdgpu_buffer_rsrc_t rC =
-        SEG ? make_rsrc(outp, orows > 0 && ocols > 0 ? ((long long)(orows - 1) * ostride + ocols) * 4 : 0)
-            : make_rsrc(outp, ((long long)(M - m0) * N - n0) * 4);
+        make_rsrc(outp, orows > 0 && ocols > 0 ? ((long long)(orows - 1) * ostride + ocols) * 4 : 0);
+    const bool gen = to_c && args.epi;       // the general entry point's alpha / beta
     auto finish = [&](auto hc) {
         constexpr int H = decltype(hc)::value;
         constexpr int IB = KS == 2 ? H * I0 : 0;
@@ -366,40 +368,48 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
                         }
         }
         // Accumulator element r of acc[i][j][v], lane (lrow, g): row wm0 +
-        // BLK i + MF::row(lane, r), column wn0 + CG j + V lrow + v.
+        // BLK i + MF::row(lane, r), column wn0 + CG j + V lrow + v. The
+        // plain and the alpha / beta stores are separate straight-line loops.
+        auto store_all = [&](auto genc) {
+            constexpr bool GEN = decltype(genc)::value;
 #pragma unroll
-        for (int ii = 0; ii < I0; ++ii)
+            for (int ii = 0; ii < I0; ++ii)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int i = IB + ii;
-                const int col = wn0 + CG * j + V * lrow;
+                for (int j = 0; j < TN; ++j) {
+                    const int col = wn0 + CG * j + V * lrow;
 #pragma unroll
-                for (int r = 0; r < MF::N; ++r) {
-                    const int row = wm0 + BLK * i + MF::row(lane, r);
-                    if constexpr (ELB) {
-                        // Rows need not be 16-byte pieces: one float per store,
-                        // each column checked against N.
+                    for (int r = 0; r < MF::N; ++r) {
+                        const int row = wm0 + BLK * (IB + ii) + MF::row(lane, r);
+                        if constexpr (ELB) {
+                            // Rows need not be 16-byte pieces: one float per
+                            // store, each column checked against N.
 #pragma unroll
-                        for (int v = 0; v < V; ++v) {
-                            const bool okv = row < orows && col + v < ocols;
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[IB + ii][j][v][r]), rC,
-                                                                  okv ? (row * ostride + col + v) * 4 : kOOB, 0, 0);
+                            for (int v = 0; v < V; ++v) {
+                                const bool okv = row < orows && col + v < ocols;
+                                StoreC<1>::run(__float_as_uint(acc[IB + ii][j][v][r]), rC,
+                                               okv ? (row * ostride + col + v) * 4 : kOOB, args, GEN);
+                            }
+                            continue;
                         }
-                        continue;
-                    }
-                    const bool ok = row < orows && col < ocols;
-                    const int off = ok ? (row * ostride + col) * 4 : kOOB;
-                    if constexpr (V == 4) {
-                        const u4 v = {__float_as_uint(acc[IB + ii][j][0][r]), __float_as_uint(acc[IB + ii][j][1][r]),
-                                      __float_as_uint(acc[IB + ii][j][2][r]), __float_as_uint(acc[IB + ii][j][3][r])};
-                        __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, 0);
-                    } else {
-                        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-                        const u2 v = {__float_as_uint(acc[IB + ii][j][0][r]), __float_as_uint(acc[IB + ii][j][1][r])};
-                        __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, 0);
+                        const bool ok = row < orows && col < ocols;
+                        const int off = ok ? (row * ostride + col) * 4 : kOOB;
+                        if constexpr (V == 4) {
+                            const u4 v = {__float_as_uint(acc[IB + ii][j][0][r]), __float_as_uint(acc[IB + ii][j][1][r]),
+                                          __float_as_uint(acc[IB + ii][j][2][r]), __float_as_uint(acc[IB + ii][j][3][r])};
+                            StoreC<4>::run(v, rC, off, args, GEN);
+                        } else {
+                            typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+                            const u2 v = {__float_as_uint(acc[IB + ii][j][0][r]),
+                                          __float_as_uint(acc[IB + ii][j][1][r])};
+                            StoreC<2>::run(v, rC, off, args, GEN);
+                        }
                     }
                 }
-            }
+        };
+        if (gen)
+            store_all(std::true_type{});
+        else
+            store_all(std::false_type{});
     };
     if (KS == 1 || half == 0)
         finish(std::integral_constant<int, 0>{});
@@ -419,7 +429,8 @@ gemm_f32_ring_kernel(GemmArgs args)
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = s * args.k_chunk;
     const int kend = min(args.K, kbeg + args.k_chunk);
-    ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, false>(args, tm, tn, kbeg, kend, nullptr, s, 0, 0);
+    ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, false>(args, tm, tn, kbeg, kend, nullptr, s, 0, 0,
+                                                                       true);
 }
 
 // Stream-K form (page "fix(fp4_gemm autotune) SM107 kernel family excluded
@@ -458,11 +469,11 @@ gemm_f32_ring_sk_kernel(GemmArgs args)
         if (!first) dma::barrier();   // the previous segment's last LDS reads are done
         const int kbeg = k0 * BK, kend = min(args.K, k1 * BK);
         const bool whole = k0 == 0 && k1 == I;
-        float* outp = whole ? args.out + (long long)m0 * args.N + n0
+        float* outp = whole ? args.out + (long long)m0 * args.ldc + n0
                             : args.ws + (2 * g + (first ? 0 : 1)) * (long long)(BM * BN);
         ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, true>(
-            args, tm, tn, kbeg, kend, outp, whole ? args.N : BN, whole ? args.M - m0 : BM,
-            whole ? args.N - n0 : BN);
+            args, tm, tn, kbeg, kend, outp, whole ? args.ldc : BN, whole ? args.M - m0 : BM,
+            whole ? args.N - n0 : BN, whole);
         it += k1 - k0;
     }
 }

@@ -7,7 +7,8 @@
 // segment's share in slot 2 g + 1 (BM x BN floats each) when the tile is not
 // wholly inside it. This kernel, sk_fixup_wgs() workgroups per stream-K
 // tile, adds a shared tile's shares in range order,
-// (((share of range g0) + share of g0 + 1) + ...), and stores the sum to C;
+// (((share of range g0) + share of g0 + 1) + ...), and stores the sum to C
+// (through the general entry point's epilogue when args.epi is set);
 // tiles that lie in one range were stored by the main kernel.
 #pragma once
 
@@ -57,10 +58,11 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs args)
         sum[2] = sum[2] + x[2];
         sum[3] = sum[3] + x[3];
     }
-    float* crow = args.out + (long long)(m0 + r) * args.N + n0 + c;
+    float* crow = args.out + (long long)(m0 + r) * args.ldc + n0 + c;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        if (n0 + c + q < args.N) crow[q] = sum[q];
+        if (n0 + c + q < args.N)
+            crow[q] = args.epi ? dma::epi_value(sum[q], args.beta != 0.0f ? crow[q] : 0.0f, args) : sum[q];
 }
 
 }  // namespace sam

@@ -248,6 +248,22 @@ def test_ex_strided_rows_on_a_16bit_ring_plan_need_no_packed_copy(dtype):
     assert sam.ex_workspace_bytes(512, 512, 512, False, False, 520, 520, 512, 1.0, 0.0, dtype) >= 512 * 512 * 4
 
 
+def test_ex_on_a_ring_plan_writes_c_itself():
+    """Ring plans apply ldc and alpha / beta where they store C: no
+    temporary product is reserved unless ldc breaks 16-byte stores; other
+    plan kinds still take the temporary and the separate pass."""
+    M, N, K = 1792, 1792, 256
+    p = sam.plan(M, N, K, "f32")
+    assert p["name"].startswith("f32_f")
+    ws = lambda ldc, a, b: sam.ex_workspace_bytes(M, N, K, False, False, K, N, ldc, a, b, "f32")
+    assert ws(N + 8, 0.5, -1.0) == p["workspace_bytes"]
+    assert ws(N, 2.0, 0.0) == p["workspace_bytes"]
+    assert ws(N + 3, 0.5, -1.0) >= p["workspace_bytes"] + M * N * 4     # ldc % 4 != 0: temporary
+    q = sam.plan(256, 256, 256, "f32")
+    assert not q["name"].startswith("f32_f")
+    assert sam.ex_workspace_bytes(256, 256, 256, False, False, 256, 256, 264, 0.5, -1.0, "f32") >= 256 * 256 * 4
+
+
 def test_mxfp8_plans_and_rejections_before_any_device_call():
     """Block-scaled plans come from the block-scaled variants only; K not a
     multiple of 32, bad formats, a negative split, null scales and the plain
@@ -346,3 +362,17 @@ def test_noalloc_refusals_before_any_device_call():
     assert L.sam_gemm_noalloc(sam.F32, None, None, None, 0, 4, 4, None) == 0
     rc = L.sam_gemm_noalloc(sam.F32, vp(16), vp(1 << 40), vp(1 << 41), 16, 8192, 8192, None)
     assert rc == -5, rc
+
+
+def test_no_alloc_pairs_still_need_scratch():
+    """The allocation-free entry point's GPU test compares calls whose
+    plans use the scratch array (split-K or stream-K workspace within its
+    size); planner changes must not turn any of them into a plan without."""
+    from tests.test_zz_no_alloc import PAIRS
+    for pair in PAIRS:
+        for (M, N, K, dtype) in pair:
+            p = sam.plan(M, N, K, dtype)
+            assert 0 < p["workspace_bytes"] <= sam.SCRATCH_BYTES, (M, N, K, dtype, p["name"])
+    firsts = [sam.plan(*pair[0][:3], pair[0][3])["workspace_bytes"] for pair in PAIRS]
+    seconds = [sam.plan(*pair[1][:3], pair[1][3])["workspace_bytes"] for pair in PAIRS]
+    assert any(b < a for a, b in zip(firsts, seconds))        # a smaller second call is covered

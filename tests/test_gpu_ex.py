@@ -139,3 +139,80 @@ def test_ex_ring16_strided_in_place(dtype, case):
     ref = orc().gemm(dtype, np.ascontiguousarray(_enc(dtype, Av)[:, :K]),
                      np.ascontiguousarray(_enc(dtype, Bv)[:, :N]), nthreads=orc().max_threads())
     assert bitexact_mismatches(Cd.cpu().numpy(), ref) == 0
+
+
+# Ring plans take strided operands in place and store C themselves: row
+# stride ldc and alpha / beta in the kernel that writes C (the data-parallel
+# epilogue, the split-K reduce or the stream-K fix-up), with no packed copy
+# of a non-transposed operand, no temporary product and no separate pass
+# over C. Each case names the plan form its shape takes.
+FUSED = [
+    ("f32", (1792, 1792, 256), False, False, 4, 8, 8, 0.5, -1.0, "f32_f", "s1"),
+    ("f32", (1792, 1792, 256), True, True, 0, 0, 4, 2.0, 0.0, "f32_f", "s1"),
+    ("f32", (256, 1536, 3072), False, False, 0, 0, 12, -1.0, 0.25, "f32_f", "s8"),
+    ("f32", (2304, 2560, 1536), False, False, 4, 4, 4, 0.5, 2.0, "f32_f", "sk"),
+    ("f32", (2049, 4097, 1025), False, False, 3, 1, 3, 1.0, 1.0, "f32_f", "s3_ua_ub"),
+    ("bf16", (640, 1792, 256), False, False, 8, 8, 4, 0.5, -1.0, "bf16_r", "s1"),
+    ("bf16", (256, 384, 3072), True, False, 0, 0, 8, 1.0, 1.0, "bf16_r", "s12"),
+    ("f16", (640, 1792, 256), False, True, 0, 0, 4, -2.0, 0.5, "f16_r", "s1"),
+]
+
+
+def _fused_case(dtype, M, N, K, ta, tb, pa, pb, pc, alpha, beta, seed):
+    rng = np.random.default_rng(seed)
+    ra, ca = (K, M) if ta else (M, K)
+    rb, cb = (N, K) if tb else (K, N)
+    lda, ldb, ldc = ca + pa, cb + pb, N + pc
+    Av = rng.integers(-3, 4, size=(ra, lda)).astype(np.float32)
+    Bv = rng.integers(-3, 4, size=(rb, ldb)).astype(np.float32)
+    Av[:, ca:] = np.inf
+    Bv[:, cb:] = np.inf
+    C0 = rng.integers(-3, 4, size=(M, ldc)).astype(np.float32)
+    if beta == 0.0:
+        C0[:, :N] = np.nan                       # must never reach the result
+    C0[:, N:] = 12345.0                          # padding columns: untouched
+    return Av, Bv, C0, lda, ldb, ldc
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: f"{c[0]}_{'x'.join(map(str, c[1]))}_{'T' if c[2] else 'N'}"
+                         f"{'T' if c[3] else 'N'}_{c[10]}")
+def test_ex_fused_epilogue_on_ring_plans(case):
+    dtype, (M, N, K), ta, tb, pa, pb, pc, alpha, beta, prefix, form = case
+    plan = sam.plan(M, N, K, dtype)
+    assert plan["name"].startswith(prefix) and f"_{form}" in plan["name"], plan["name"]
+    Av, Bv, C0, lda, ldb, ldc = _fused_case(dtype, M, N, K, ta, tb, pa, pb, pc, alpha, beta, M + N + K + pc)
+    if not ta and not tb:       # nothing but the plan's own workspace
+        assert sam.ex_workspace_bytes(M, N, K, ta, tb, lda, ldb, ldc, alpha, beta, dtype) == plan["workspace_bytes"]
+    ca, cb = (M if ta else K), (K if tb else N)
+    Cd = torch.from_numpy(C0.copy()).cuda()
+    sam.gemm_ex(_dev(dtype, _enc(dtype, Av))[:, :ca], _dev(dtype, _enc(dtype, Bv))[:, :cb], Cd[:, :N],
+                trans_a=ta, trans_b=tb, alpha=alpha, beta=beta)
+    torch.cuda.synchronize()
+    got = Cd.cpu().numpy()
+    ref = orc().gemm_ex(dtype, M, N, K, _enc(dtype, Av), lda, _enc(dtype, Bv), ldb, ta, tb, alpha, beta,
+                        np.ascontiguousarray(C0[:, :N]), nthreads=orc().max_threads())
+    assert bitexact_mismatches(got[:, :N], ref) == 0
+    assert np.all(got[:, N:] == 12345.0)
+
+
+# The 16-bit stream-K and operand-swap forms at the sizes that take them:
+# the product against the oracle's plain GEMM of the compact operands,
+# then alpha P + beta C0 (exact here: small integers, dyadic alpha / beta).
+@pytest.mark.parametrize("dtype,shape,form", [("bf16", (6144, 6144, 6144), "_sk"),
+                                              ("f16", (4096, 4096, 11008), "_sw_")])
+def test_ex_fused_epilogue_16bit_stream_k_and_swap(dtype, shape, form):
+    M, N, K = shape
+    plan = sam.plan(M, N, K, dtype)
+    assert form in plan["name"], plan["name"]
+    alpha, beta = 0.5, -1.0
+    Av, Bv, C0, lda, ldb, ldc = _fused_case(dtype, M, N, K, False, False, 8, 16, 4, alpha, beta, 5)
+    Cd = torch.from_numpy(C0.copy()).cuda()
+    sam.gemm_ex(_dev(dtype, _enc(dtype, Av))[:, :K], _dev(dtype, _enc(dtype, Bv))[:, :N], Cd[:, :N],
+                alpha=alpha, beta=beta)
+    torch.cuda.synchronize()
+    got = Cd.cpu().numpy()
+    P = orc().gemm(dtype, np.ascontiguousarray(_enc(dtype, Av)[:, :K]), np.ascontiguousarray(_enc(dtype, Bv)[:, :N]),
+                   nthreads=orc().max_threads())
+    ref = alpha * P + beta * C0[:, :N].astype(np.float64)
+    assert bitexact_mismatches(got[:, :N], ref) == 0
+    assert np.all(got[:, N:] == 12345.0)

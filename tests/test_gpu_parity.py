@@ -128,7 +128,7 @@ SK_SHAPES = [(300, 300, 4096), (768, 768, 768), (129, 257, 2000), (1000, 1000, 1
              (1536, 1536, 1536), (260, 1030, 2052),
              # K % 4 != 0 (and N % 4 != 0): the element-load forms inside stream-K segments,
              # shapes for which the dispatcher itself picks a stream-K plan
-             (1500, 1500, 2047), (260, 1030, 2051), (3000, 3000, 3001)]
+             (1500, 1500, 2047), (260, 1030, 2051), (3000, 3000, 3001), (1500, 3000, 2047)]
 _SK_REF = {}
 
 
@@ -238,7 +238,7 @@ def test_every_variant_n_major_raster_dyadic(vid):
 def test_dispatcher_picks_stream_k_on_odd_k():
     """The shapes above with K % 4 != 0 are ones the dispatcher itself sends
     to stream-K, so those segments are the automatic path, not only forced."""
-    picked = [s for s in [(1500, 1500, 2047), (3000, 3000, 3001), (260, 1030, 2051)]
+    picked = [s for s in [(1500, 1500, 2047), (3000, 3000, 3001), (260, 1030, 2051), (1500, 3000, 2047)]
               if sam.plan(*s, "f32")["split_k"] == -1]
     assert picked, "no odd-K shape goes to stream-K any more; pick new shapes"
 
