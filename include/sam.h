@@ -208,10 +208,20 @@ typedef enum { SAM_OP_N = 0, SAM_OP_T = 1 } sam_op;
  * fmaf(alpha, P, beta * C) with P the FP32 product of the GEMM path (alpha * P
  * when beta == 0).
  * How: a call with SAM_OP_N, SAM_OP_N, compact strides, alpha 1 and beta 0 is
- * exactly sam_gemm_<dtype>. Otherwise op(A) and op(B) are first copied into
- * compact rows in the workspace (transposing where asked), the GEMM path runs
- * on them (into a workspace temporary unless ldc == N and beta == 0), and a
- * last pass applies alpha and beta; the copies cost extra HBM traffic.
+ * exactly sam_gemm_<dtype>. Otherwise the plan for (M, N, K, dtype) decides:
+ *  - ring plans (FP32 "f..." and 16-bit "r..." variants) read A and B rows
+ *    with their strides in place when each row stays whole 16-byte pieces
+ *    (or the plan reads that operand one value at a time, or copies it into
+ *    padded rows anyway), and store C themselves with row stride ldc (a
+ *    multiple of 4) and alpha / beta applied where C is written: in the
+ *    kernel, the split-K reduce or the stream-K fix-up. 16-bit 16x16x32 ring
+ *    plans also read a transposed B (SAM_OP_T) straight, when K, N and ldb
+ *    are multiples of 8;
+ *  - whatever remains (a transposed operand the plan cannot read, other
+ *    strides, other plan kinds) is copied into compact rows in the
+ *    workspace first, the product goes to a workspace temporary unless the
+ *    plan stores C itself or ldc == N and beta == 0, and a last pass applies
+ *    alpha and beta; those copies cost extra HBM traffic.
  * Base pointers must be 16-byte aligned; the workspace must hold
  * sam_gemm_ex_workspace() bytes (SAM_ERR_WORKSPACE otherwise).
  * Asynchronous on `stream`, like the other entry points. */
@@ -227,6 +237,28 @@ sam_status sam_gemm_ex_workspace(sam_dtype dtype, sam_op trans_a,
                                  int64_t K, int64_t lda, int64_t ldb,
                                  int64_t ldc, float alpha, float beta,
                                  uint64_t* bytes);
+
+/* sam_gemm_ex with a forced plan: variant `id`, split_k and raster_n as for
+ * sam_gemm_variant_r (SAM_ERR_UNSUPPORTED / SAM_ERR_INVALID_ARG likewise);
+ * everything else as for sam_gemm_ex, with the workspace from
+ * sam_gemm_ex_variant_workspace. For tests and tuning of the general forms. */
+sam_status sam_gemm_ex_variant(int32_t id, int32_t split_k, int32_t raster_n,
+                               sam_dtype dtype, sam_op trans_a,
+                               sam_op trans_b, int64_t M, int64_t N,
+                               int64_t K, float alpha, const void* A,
+                               int64_t lda, const void* B, int64_t ldb,
+                               float beta, float* C, int64_t ldc,
+                               void* workspace, uint64_t workspace_bytes,
+                               void* stream);
+
+/* Workspace bytes sam_gemm_ex_variant needs for these arguments (host only). */
+sam_status sam_gemm_ex_variant_workspace(int32_t id, int32_t split_k,
+                                         int32_t raster_n, sam_dtype dtype,
+                                         sam_op trans_a, sam_op trans_b,
+                                         int64_t M, int64_t N, int64_t K,
+                                         int64_t lda, int64_t ldb, int64_t ldc,
+                                         float alpha, float beta,
+                                         uint64_t* bytes);
 
 /* Number of entries in the variant table (ids 0 .. count-1). */
 int32_t sam_variant_count(void);

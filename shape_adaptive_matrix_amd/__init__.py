@@ -96,6 +96,12 @@ def lib() -> ctypes.CDLL:
                          ctypes.c_float, vp, i64, vp, u64, vp], ctypes.c_int),
         "sam_gemm_ex_workspace": ([ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i64, i64,
                                    ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
+        "sam_gemm_ex_variant": ([i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                 ctypes.c_float, vp, i64, vp, i64, ctypes.c_float, vp, i64, vp, u64, vp],
+                                ctypes.c_int),
+        "sam_gemm_ex_variant_workspace": ([i32, i32, i32, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                           i64, i64, i64, ctypes.c_float, ctypes.c_float,
+                                           ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
         "sam_gemm_mxfp8": ([ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, vp, u64, vp],
                            ctypes.c_int),
         "sam_gemm_mxfp8_variant": ([i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, vp,
@@ -323,18 +329,25 @@ def _rows(t, name):
     return max(int(t.stride(0)), int(t.shape[1]), 1)
 
 
-def ex_workspace_bytes(M, N, K, trans_a, trans_b, lda, ldb, ldc, alpha, beta, dtype="f32") -> int:
+def ex_workspace_bytes(M, N, K, trans_a, trans_b, lda, ldb, ldc, alpha, beta, dtype="f32", variant=None,
+                       split=0, raster=-1) -> int:
     n = ctypes.c_uint64()
-    _check(lib().sam_gemm_ex_workspace(_dt(dtype), int(trans_a), int(trans_b), M, N, K, lda, ldb, ldc,
-                                       float(alpha), float(beta), ctypes.byref(n)))
+    if variant is None:
+        _check(lib().sam_gemm_ex_workspace(_dt(dtype), int(trans_a), int(trans_b), M, N, K, lda, ldb, ldc,
+                                           float(alpha), float(beta), ctypes.byref(n)))
+    else:
+        _check(lib().sam_gemm_ex_variant_workspace(int(variant), int(split), int(raster), _dt(dtype), int(trans_a),
+                                                   int(trans_b), M, N, K, lda, ldb, ldc, float(alpha), float(beta),
+                                                   ctypes.byref(n)))
     return int(n.value)
 
 
 def gemm_ex(A, B, C=None, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, dtype=None, workspace=None,
-            stream=None):
+            stream=None, variant=None, split=0, raster=-1):
     """C = alpha·op(A)·op(B) + beta·C (sam_gemm_ex); returns C. op(A) is A or
     A.T as stored (A is K x M when trans_a), likewise B; A, B and C may be
-    views with padded rows (their row stride is the leading dimension)."""
+    views with padded rows (their row stride is the leading dimension).
+    variant: a forced plan (sam_gemm_ex_variant, with split and raster)."""
     import torch
     code = _torch_dtype_code(A, dtype)
     want = 4 if code == F32 else 2
@@ -356,11 +369,16 @@ def gemm_ex(A, B, C=None, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, dty
         raise ValueError(f"C must be float32 [{M}, {N}]")
     ldc = _rows(C, "C")
     if workspace is None:
-        n = ex_workspace_bytes(M, N, K, trans_a, trans_b, lda, ldb, ldc, alpha, beta, code)
+        n = ex_workspace_bytes(M, N, K, trans_a, trans_b, lda, ldb, ldc, alpha, beta, code, variant, split, raster)
         workspace = workspace_for({"workspace_bytes": n}, dev, stream)
     ws_bytes = _workspace_bytes(workspace)
-    _check(lib().sam_gemm_ex(code, int(trans_a), int(trans_b), M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
-                             float(beta), _ptr(C), ldc, _ptr(workspace), ws_bytes, _stream_ptr(stream)))
+    tail = (M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc, _ptr(workspace), ws_bytes,
+            _stream_ptr(stream))
+    if variant is None:
+        _check(lib().sam_gemm_ex(code, int(trans_a), int(trans_b), *tail))
+    else:
+        _check(lib().sam_gemm_ex_variant(int(variant), int(split), int(raster), code, int(trans_a), int(trans_b),
+                                         *tail))
     return C
 
 

@@ -164,6 +164,7 @@ struct MxExtra {
 struct ExTail {
     long long lda, ldb, ldc;
     float alpha, beta;
+    bool bt;   // B given transposed: N rows of K values with stride ldb
 };
 
 // Whether a plan can take A rows with stride lda != K in place: a 16-bit
@@ -175,6 +176,15 @@ bool reads_strided(const sam::Plan& p, bool a_side, long long ld)
     if (p.kind == sam::KIND_DMA) return (a_side ? p.pad_a : p.pad_b) || ld % 8 == 0;
     if (p.kind == sam::KIND_F32RING) return !(a_side ? p.a_vec : p.b_vec) || ld % 4 == 0;
     return false;
+}
+
+// Whether a 16-bit ring plan can read a transposed B (N x K, stride ldb)
+// straight: its variant has the transposed-B kernels, and neither operand
+// needs a padded copy (K and N multiples of 8, 16-byte rows).
+bool reads_transposed_b(const sam::Plan& p, long long K, long long ldb)
+{
+    return p.kind == sam::KIND_DMA && !p.pad_a && !p.pad_b && K % 8 == 0 && ldb % 8 == 0 &&
+           sam::dma_has_bt(p.variant_id, p.dtype);
 }
 
 // Ring plans store C with row stride ldc (a multiple of 4: 16-byte stores)
@@ -196,12 +206,14 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
     const unsigned long long es = p.dtype == sam::DT_F32 ? 4 : (blockscaled ? 1 : 2);
     const unsigned long long half = p.dtype == sam::DT_MX4 ? 2 : 1;
     if (blockscaled != (mx != nullptr)) return fail(SAM_ERR_INTERNAL, "scale arguments mismatch");
+    const bool bt = x && x->bt;
     const long long lda = x ? x->lda : K, ldb = x ? x->ldb : N, ldc = x ? x->ldc : N;
     const float alpha = x ? x->alpha : 1.0f, beta = x ? x->beta : 0.0f;
     const bool gen = alpha != 1.0f || beta != 0.0f;
-    if (x && (K == 0 || lda < K || ldb < N || ldc < N || (lda != K && !reads_strided(p, true, lda)) ||
-              (ldb != N && !reads_strided(p, false, ldb)) || ((ldc != N || gen) && !writes_general_c(p, ldc))))
-        return fail(SAM_ERR_INTERNAL, "strides or alpha / beta on a plan that cannot take them");
+    if (x && (K == 0 || lda < K || ldb < (bt ? K : N) || ldc < N || (lda != K && !reads_strided(p, true, lda)) ||
+              (bt ? !reads_transposed_b(p, K, ldb) : (ldb != N && !reads_strided(p, false, ldb))) ||
+              ((ldc != N || gen) && !writes_general_c(p, ldc))))
+        return fail(SAM_ERR_INTERNAL, "strides, a transposed B or alpha / beta on a plan that cannot take them");
     if (M == 0 || N == 0) return SAM_OK;
     // Kernels address a workgroup's operand panels with 32-bit byte offsets:
     // up to 257 rows of A (lda elements each), 129 rows of B and 257 rows of C.
@@ -216,7 +228,8 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         return fail(SAM_ERR_MISALIGNED, "A, B, C and workspace must be 16-byte aligned");
     const unsigned long long cbytes = (unsigned long long)((M - 1) * ldc + N) * 4ull;
     const unsigned long long abytes = K ? (unsigned long long)((M - 1) * lda + K) * es / half : 0;
-    const unsigned long long bbytes = K ? (unsigned long long)((K - 1) * ldb + N) * es / half : 0;
+    const unsigned long long bbytes =
+        K ? (unsigned long long)(bt ? (N - 1) * ldb + K : (K - 1) * ldb + N) * es / half : 0;
     if (ranges_overlap(C, cbytes, A, abytes) || ranges_overlap(C, cbytes, B, bbytes))
         return fail(SAM_ERR_INVALID_ARG, "C overlaps A or B");
     if (mx && (ranges_overlap(C, cbytes, mx->sa, (unsigned long long)(M * (K / 32))) ||
@@ -285,7 +298,9 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
             a.sk_grid = p.sk_g;
             a.sk_dp = p.sk_dp;
         }
-        e = sam::launch_gemm(p, a, s);
+        sam::Plan q = p;
+        q.bt = bt;
+        e = sam::launch_gemm(q, a, s);
         if (e == hipSuccess && p.split > 1)
             e = ldc != N || gen
                     ? sam::launch_reduce_ex(static_cast<const float*>(ws), p.split, M * N, C, M, N, ldc, alpha, beta, s)
@@ -315,6 +330,7 @@ struct ExLayout {
     bool pack_a, pack_b;  // op(A) / op(B) copied into compact rows first
     bool direct_a, direct_b;  // strided A / B read in place by a ring plan
     bool fused_c;         // a ring plan stores C itself (stride ldc, alpha / beta)
+    bool bt;              // a transposed B read straight by a 16-bit ring plan
     bool use_t;           // product into a temporary, then C = alpha T + beta C
     unsigned long long off_a, off_b, off_t, off_w, total;
     sam::Plan plan;
@@ -322,8 +338,14 @@ struct ExLayout {
 
 unsigned long long align256(unsigned long long x) { return (x + 255ull) & ~255ull; }
 
+// A forced plan for the general entry point: variant, split and raster as
+// for sam_gemm_variant_r.
+struct ExForced {
+    int id, split, raster;
+};
+
 sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long long K, long long lda, long long ldb,
-                     long long ldc, float alpha, float beta, ExLayout* L)
+                     long long ldc, float alpha, float beta, ExLayout* L, const ExForced* f = nullptr)
 {
     if (dtype < SAM_F32 || dtype > SAM_F16) return fail(SAM_ERR_INVALID_ARG, "bad dtype %d", dtype);
     if ((ta != SAM_OP_N && ta != SAM_OP_T) || (tb != SAM_OP_N && tb != SAM_OP_T))
@@ -341,7 +363,14 @@ sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long l
     *L = ExLayout{};
     L->product = alpha != 0.0f && K > 0 && M > 0 && N > 0;
     L->fast = !ta && !tb && lda == K && ldb == N && ldc == N && alpha == 1.0f && beta == 0.0f;
-    if (L->product || L->fast) {
+    if ((L->product || L->fast) && f) {
+        if (f->raster < -1 || f->raster > 1 || f->split < -1)
+            return fail(SAM_ERR_INVALID_ARG, "split %d / raster %d out of range", f->split, f->raster);
+        if (!sam::variant_get(f->id)) return fail(SAM_ERR_INVALID_ARG, "no variant %d", f->id);
+        if (!sam::plan_for_variant(f->id, M, N, K, dtype, f->split, &L->plan, f->raster))
+            return fail(SAM_ERR_UNSUPPORTED, "variant %d cannot run dtype %d with split %d, raster %d for K=%lld",
+                        f->id, dtype, f->split, f->raster, K);
+    } else if (L->product || L->fast) {
         if (!sam::plan_auto(M, N, K, dtype, &L->plan)) return fail(SAM_ERR_INTERNAL, "no admissible plan");
     }
     if (L->fast) {
@@ -350,9 +379,10 @@ sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long l
     }
     L->direct_a = L->product && !ta && lda != K && reads_strided(L->plan, true, lda);
     L->direct_b = L->product && !tb && ldb != N && reads_strided(L->plan, false, ldb);
+    L->bt = L->product && tb && reads_transposed_b(L->plan, K, ldb);
     L->fused_c = L->product && writes_general_c(L->plan, ldc);
     L->pack_a = L->product && (ta || lda != K) && !L->direct_a;
-    L->pack_b = L->product && (tb || ldb != N) && !L->direct_b;
+    L->pack_b = L->product && (tb || ldb != N) && !L->direct_b && !L->bt;
     L->use_t = L->product && !L->fused_c && !(ldc == N && beta == 0.0f);
     L->off_a = 0;
     L->off_b = align256(L->off_a + (L->pack_a ? (unsigned long long)(M * K) * es : 0));
@@ -362,28 +392,12 @@ sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long l
     return SAM_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-sam_status sam_gemm_ex_workspace(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t M, int64_t N, int64_t K,
-                                 int64_t lda, int64_t ldb, int64_t ldc, float alpha, float beta, uint64_t* bytes)
+// The general entry point once its layout (and plan) is known.
+sam_status gemm_ex_run(const ExLayout& L, sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t M, int64_t N,
+                       int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                       float* C, int64_t ldc, void* workspace, uint64_t workspace_bytes, void* stream)
 {
-    if (!bytes) return fail(SAM_ERR_INVALID_ARG, "bytes is null");
-    ExLayout L;
-    sam_status st = ex_layout(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc, alpha, beta, &L);
-    if (st != SAM_OK) return st;
-    *bytes = L.total;
-    return SAM_OK;
-}
-
-sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t M, int64_t N, int64_t K, float alpha,
-                       const void* A, int64_t lda, const void* B, int64_t ldb, float beta, float* C, int64_t ldc,
-                       void* workspace, uint64_t workspace_bytes, void* stream)
-{
-    ExLayout L;
-    sam_status st = ex_layout(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc, alpha, beta, &L);
-    if (st != SAM_OK) return st;
+    sam_status st = SAM_OK;
     if (L.fast) return run(L.plan, A, B, C, M, N, K, workspace, workspace_bytes, stream);
     if (M == 0 || N == 0) return SAM_OK;
     if (!C) return fail(SAM_ERR_INVALID_ARG, "C is null");
@@ -423,8 +437,8 @@ sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t 
         }
         if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
         float* out = L.use_t ? reinterpret_cast<float*>(ws + L.off_t) : C;
-        const ExTail x{L.direct_a ? lda : K, L.direct_b ? ldb : N, L.fused_c ? ldc : N, L.fused_c ? alpha : 1.0f,
-                       L.fused_c ? beta : 0.0f};
+        const ExTail x{L.direct_a ? lda : K, (L.direct_b || L.bt) ? ldb : N, L.fused_c ? ldc : N,
+                       L.fused_c ? alpha : 1.0f, L.fused_c ? beta : 0.0f, L.bt};
         st = run(L.plan, a, b, out, M, N, K, L.plan.ws_bytes ? ws + L.off_w : nullptr, L.plan.ws_bytes, stream,
                  nullptr, &x);
         if (st != SAM_OK) return st;
@@ -438,6 +452,58 @@ sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t 
     if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
     g_err[0] = '\0';
     return SAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sam_status sam_gemm_ex_workspace(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t M, int64_t N, int64_t K,
+                                 int64_t lda, int64_t ldb, int64_t ldc, float alpha, float beta, uint64_t* bytes)
+{
+    if (!bytes) return fail(SAM_ERR_INVALID_ARG, "bytes is null");
+    ExLayout L;
+    sam_status st = ex_layout(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc, alpha, beta, &L);
+    if (st != SAM_OK) return st;
+    *bytes = L.total;
+    return SAM_OK;
+}
+
+sam_status sam_gemm_ex(sam_dtype dtype, sam_op trans_a, sam_op trans_b, int64_t M, int64_t N, int64_t K, float alpha,
+                       const void* A, int64_t lda, const void* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                       void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    ExLayout L;
+    sam_status st = ex_layout(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc, alpha, beta, &L);
+    if (st != SAM_OK) return st;
+    return gemm_ex_run(L, dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                       workspace_bytes, stream);
+}
+
+sam_status sam_gemm_ex_variant_workspace(int32_t id, int32_t split_k, int32_t raster_n, sam_dtype dtype,
+                                         sam_op trans_a, sam_op trans_b, int64_t M, int64_t N, int64_t K, int64_t lda,
+                                         int64_t ldb, int64_t ldc, float alpha, float beta, uint64_t* bytes)
+{
+    if (!bytes) return fail(SAM_ERR_INVALID_ARG, "bytes is null");
+    ExLayout L;
+    const ExForced f{id, split_k, raster_n};
+    sam_status st = ex_layout(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc, alpha, beta, &L, &f);
+    if (st != SAM_OK) return st;
+    *bytes = L.total;
+    return SAM_OK;
+}
+
+sam_status sam_gemm_ex_variant(int32_t id, int32_t split_k, int32_t raster_n, sam_dtype dtype, sam_op trans_a,
+                               sam_op trans_b, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                               int64_t lda, const void* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                               void* workspace, uint64_t workspace_bytes, void* stream)
+{
+    ExLayout L;
+    const ExForced f{id, split_k, raster_n};
+    sam_status st = ex_layout(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc, alpha, beta, &L, &f);
+    if (st != SAM_OK) return st;
+    return gemm_ex_run(L, dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                       workspace_bytes, stream);
 }
 
 

@@ -119,6 +119,9 @@ struct Plan {
     int pad_a, pad_b;
     long long lda, ldb;
     unsigned long long ws_inner;
+    // 16-bit ring plans of the general entry point: B given transposed
+    // (N rows of K values, row stride ldb), read straight by the kernel.
+    int bt;
 };
 
 // Dispatcher (sam_plan.cpp). Host only, pure.
@@ -137,6 +140,8 @@ hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_stream(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s);
+// Whether a 16-bit ring variant has the transposed-B kernels.
+bool dma_has_bt(int variant_id, int dtype);
 hipError_t launch_sk_fixup_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mx8(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_kq(const Plan& p, const GemmArgs& a, hipStream_t s);

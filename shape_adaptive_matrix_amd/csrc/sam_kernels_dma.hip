@@ -96,6 +96,11 @@ template <int DT> struct Mf<DT, 16> {
 //         transposed there (one v_perm per output dword) and stored
 //         K-contiguous, so its fragments are full-rate 128-bit LDS reads
 //         instead of half-rate transposing reads.
+// MODE 3: B given transposed (op(B) = B^T with B stored N x K, K-contiguous
+//         rows, row stride ldb): both operands load straight into LDS the
+//         same way, and B's fragments are 128-bit reads like A's (the layout
+//         both MFMA operands take natively). Used by the general entry point
+//         for a transposed B; the ring and the schedule are MODE 0's.
 //
 // SWAP (16x16x32 blocks only): the MFMA takes the B fragment as its first
 // operand and the A fragment as its second, so it computes the transposed
@@ -138,18 +143,20 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
     constexpr int NT = NW * 64;
     constexpr int NBS = MODE == 2 ? (BK / 8) * (BN / 8) / NT : 0;
     constexpr int LPS = MODE == 2 ? A_PW + 8 * NBS : A_PW + B_PW;   // loads per stage per lane
+    constexpr bool DIRECT = MODE == 0 || MODE == 3;   // every load straight into LDS
+    constexpr bool BKC = MODE == 2 || MODE == 3;      // B K-contiguous in LDS (rows of BK values)
     constexpr int CPR = BN / 8;                // 16-byte chunks per B row
     constexpr int RPI = 64 / CPR;              // B rows per wave load
     static_assert(WTM % BLK == 0 && WTN % BLK == 0, "wave tile must be whole MFMA blocks");
-    static_assert(BLK == 32 || MODE == 0, "16x16 blocks: loads straight into LDS only");
+    static_assert(BLK == 32 || DIRECT, "16x16 blocks: loads straight into LDS only");
     static_assert(A_INS % NW == 0 && B_INS % NW == 0, "loads must split evenly over waves");
     static_assert(CPR >= 16 && 64 % CPR == 0, "BN must be 128 or 256");
     static_assert(NBUF >= 2 && NBUF * STAGE <= 160 * 1024, "LDS ring");
-    static_assert(MODE == 0 || (NBUF == 2 && KSTEPS >= 3), "register-filled stages need NBUF 2, >= 3 k-steps");
+    static_assert(DIRECT || (NBUF == 2 && KSTEPS >= 3), "register-filled stages need NBUF 2, >= 3 k-steps");
     static_assert(MODE != 2 || NBS * NT == (BK / 8) * (BN / 8), "B blocks must split evenly over threads");
     static_assert((NBUF - 1) * LPS < 64, "vmcnt range");
     static_assert(SWAP == 0 || BLK == 16, "operand swap: 16x16x32 blocks");
-    static_assert(!SEG || MODE == 0, "stream-K segments: loads straight into LDS");
+    static_assert(!SEG || DIRECT, "stream-K segments: loads straight into LDS");
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * STAGE];
 
@@ -192,6 +199,16 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
                 lds_load16(rA, lds_addr(buf + I * 1024), off);
             else
                 R[q] = __builtin_amdgcn_raw_buffer_load_b128(rAb, off, 0, 0);
+        } else if constexpr (MODE == 3) {
+            // B^T rows n0 + row (K-contiguous), placed and swizzled as A's.
+            const int I = wave + (q - A_PW) * NW;
+            const int row = I * RPA + lane / CPA;
+            const int c = (lane % CPA) ^ ((row / RSW) % CPA);
+            const int gk = k0 + c * 8;
+            const bool ok = n0 + row < N && gk < kend;
+            const i4 rBt = rsrc_words(static_cast<const char*>(args.B) + (long long)n0 * ldb * 2,
+                                      (long long)(N - n0) * ldb * 2);
+            lds_load16(rBt, lds_addr(buf + A_BYTES + I * 1024), ok ? (row * ldb + gk) * 2 : kOOB);
         } else {
             const int I = wave + (q - A_PW) * NW;
             const int row = I * RPI + lane / CPR;
@@ -277,7 +294,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
             const int row = wm0 + BLK * r + lrow;
             const int c = ((MF::KSTEP / 8) * t + lgrp) ^ ((row / RSW) % CPA);
             fa[r] = *reinterpret_cast<const u4*>(buf + row * A_ROW + c * 16);
-        } else if constexpr (MODE == 2) {
+        } else if constexpr (BKC) {
             const int j = r - TM;
             const int row = wn0 + BLK * j + lrow;
             const int c = ((MF::KSTEP / 8) * t + lgrp) ^ ((row / RSW) % CPA);
@@ -313,7 +330,8 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
     };
 
     constexpr int NMF = TM * TN;          // MFMAs per k-step
-    constexpr int NRD = MODE == 2 ? TM + TN : TM + 2 * TN;   // LDS reads per k-step
+    constexpr int NBR = BKC ? TN : 2 * TN;                  // B reads per k-step
+    constexpr int NRD = TM + NBR;                            // LDS reads per k-step
     constexpr int RPS = (NRD + NMF - 1) / NMF;   // reads per MFMA slot
     // 16x16 blocks hold twice the fragment registers per k-step; their A
     // fragments are single-buffered (each block's next read follows its last
@@ -332,12 +350,12 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
             mfma_one(m, fa, fb);
             if constexpr (ASB) {
                 // A single-buffered: block i of the next k-step is read right
-                // after its last MFMA (m = TN i + TN - 1); the 2 TN B reads go
-                // to the other set, one every NMF / (2 TN) slots.
+                // after its last MFMA (m = TN i + TN - 1); the NBR B reads go
+                // to the other set, one every NMF / NBR slots.
                 if (m % TN == TN - 1) read_one(rbuf, rt, m / TN, na, nb);
 #pragma unroll
-                for (int q = 0; q < 2 * TN; ++q)
-                    if ((q * NMF) / (2 * TN) == m) read_one(rbuf, rt, TM + q, na, nb);
+                for (int q = 0; q < NBR; ++q)
+                    if ((q * NMF) / NBR == m) read_one(rbuf, rt, TM + q, na, nb);
             } else {
 #pragma unroll
                 for (int r = m * RPS; r < (m + 1) * RPS; ++r)
@@ -380,7 +398,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
 
     u4 fa[2][TM];
     u2 fb[2][TN][2];
-    if constexpr (MODE == 0) {
+    if constexpr (DIRECT) {
         // Fill the whole ring, then wait for stage 0.
 #pragma unroll
         for (int st = 0; st < NBUF; ++st)
@@ -427,7 +445,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
                       (MODE == 1 && t == 0) ? k + 1 : -1, (MODE == 1 && t == KSTEPS - 2) ? k + 1 : -1);
         }
         // Stage k fully read by this wave; this wave's part of stage k+1 landed.
-        if constexpr (MODE == 0)
+        if constexpr (DIRECT)
             wait_cnt<(NBUF - 2) * LPS, 0>();
         else if constexpr (MODE == 1)
             wait_cnt<63, 0>();
@@ -438,7 +456,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
         // LDS slot stage k leaves (MODE 0: whole stage k + NBUF; MODE 2: A of
         // stage k + 2).
         constexpr int L = (KSTEPS - 1) & 1;
-        kstep(fa[L & FA], fb[L], nxt, 0, fa[(L ^ 1) & FA], fb[L ^ 1], MODE == 0 ? k + NBUF : (MODE == 2 ? k + 2 : -1), -1);
+        kstep(fa[L & FA], fb[L], nxt, 0, fa[(L ^ 1) & FA], fb[L ^ 1], DIRECT ? k + NBUF : (MODE == 2 ? k + 2 : -1), -1);
         if constexpr (L == 0) {   // odd number of k-steps: next stage starts in set 1
 #pragma unroll
             for (int i = 0; i < TM; ++i) fa[0][i] = fa[FA][i];
@@ -577,6 +595,8 @@ struct DmaKernels {
     int id;
     KernelFn fn[3];
     KernelFn sk[3];      // stream-K form (16x16x32 variants only)
+    KernelFn nt[3];      // B given transposed (MODE 3; 16x16x32 straight-load variants only)
+    KernelFn nt_sk[3];
     KernelFn fixup;
     int fixup_wgs;
     int threads;
@@ -585,10 +605,25 @@ struct DmaKernels {
 template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK, int SWAP>
 constexpr KernelFn ring16_sk()
 {
-    if constexpr (MODE == 0 && BLK == 16)
+    if constexpr ((MODE == 0 || MODE == 3) && BLK == 16)
         return gemm16_dma_sk_kernel<DT, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SWAP>;
     else
         return nullptr;
+}
+
+// The transposed-B form of a straight-load 16x16x32 variant (data-parallel
+// or stream-K), else none.
+template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK, int SWAP, bool SK>
+constexpr KernelFn ring16_nt()
+{
+    if constexpr (MODE == 0 && BLK == 16) {
+        if constexpr (SK)
+            return ring16_sk<DT, BM, BN, WM, WN, BK, NBUF, 3, BLK, SWAP>();
+        else
+            return gemm16_dma_kernel<DT, BM, BN, WM, WN, BK, NBUF, 3, BLK, SWAP>;
+    } else {
+        return nullptr;
+    }
 }
 
 #define SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW, gm, xr, ms, e16)                  \
@@ -597,6 +632,10 @@ constexpr KernelFn ring16_sk()
       gemm16_dma_kernel<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW>},                             \
      {nullptr, ring16_sk<DT_BF16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW>(),                          \
       ring16_sk<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW>()},                                   \
+     {nullptr, ring16_nt<DT_BF16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW, false>(),                   \
+      ring16_nt<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW, false>()},                            \
+     {nullptr, ring16_nt<DT_BF16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW, true>(),                    \
+      ring16_nt<DT_F16, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SW, true>()},                             \
      sk_fixup_kernel<BM, BN>, sk_fixup_wgs<BM, BN>(), WM * WN * 64},
 #define SAM_DMA_ENTRY0(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, gm, xr, ms, e16) \
     SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, 0, gm, xr, ms, e16)
@@ -615,10 +654,16 @@ hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s)
 {
     const DmaKernels* d = dma_entry(p.variant_id);
     if (!d) return hipErrorInvalidDeviceFunction;
-    KernelFn fn = p.sk ? d->sk[p.dtype] : d->fn[p.dtype];
+    KernelFn fn = p.bt ? (p.sk ? d->nt_sk[p.dtype] : d->nt[p.dtype]) : (p.sk ? d->sk[p.dtype] : d->fn[p.dtype]);
     if (!fn) return hipErrorInvalidDeviceFunction;
     hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(d->threads), 0, s, a);
     return hipGetLastError();
+}
+
+bool dma_has_bt(int variant_id, int dtype)
+{
+    const DmaKernels* d = dma_entry(variant_id);
+    return d && dtype >= 1 && dtype <= 2 && d->nt[dtype] && d->nt_sk[dtype];
 }
 
 hipError_t launch_sk_fixup_dma(const Plan& p, const GemmArgs& a, hipStream_t s)
