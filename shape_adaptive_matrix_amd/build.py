@@ -27,7 +27,7 @@ BUILD_DIR = ROOT / "_build" / "sam"
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_kernels_stream.hip", "sam_kernels_f32ring.hip", "sam_kernels_ex.hip", "sam_kernels_mx.hip", "sam_kernels_kq.hip", "sam_kernels_kp.hip", "sam_plan.cpp", "sam_api.cpp"]
+SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_kernels_dma_t.hip", "sam_kernels_stream.hip", "sam_kernels_f32ring.hip", "sam_kernels_ex.hip", "sam_kernels_mx.hip", "sam_kernels_kq.hip", "sam_kernels_kp.hip", "sam_plan.cpp", "sam_api.cpp"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -164,7 +164,7 @@ struct MxExtra {
 struct ExTail {
     long long lda, ldb, ldc;
     float alpha, beta;
-    bool bt;   // B given transposed: N rows of K values with stride ldb
+    int tr;    // operands given transposed, read straight: bit 0 B (N rows of K), bit 1 A (K rows of M)
 };
 
 // Whether a plan can take A rows with stride lda != K in place: a 16-bit
@@ -178,13 +178,15 @@ bool reads_strided(const sam::Plan& p, bool a_side, long long ld)
     return false;
 }
 
-// Whether a 16-bit ring plan can read a transposed B (N x K, stride ldb)
-// straight: its variant has the transposed-B kernels, and neither operand
-// needs a padded copy (K and N multiples of 8, 16-byte rows).
-bool reads_transposed_b(const sam::Plan& p, long long K, long long ldb)
+// Whether a 16-bit ring plan can read operands given transposed straight
+// (tr: bit 0 B as N rows of K values, bit 1 A as K rows of M values): its
+// variant has the kernels of that layout, neither operand needs a padded
+// copy (K and N multiples of 8), and each transposed operand's rows are
+// whole 16-byte pieces.
+bool reads_transposed(const sam::Plan& p, int tr, long long lda, long long ldb)
 {
-    return p.kind == sam::KIND_DMA && !p.pad_a && !p.pad_b && K % 8 == 0 && ldb % 8 == 0 &&
-           sam::dma_has_bt(p.variant_id, p.dtype);
+    return p.kind == sam::KIND_DMA && !p.pad_a && !p.pad_b && (!(tr & 1) || ldb % 8 == 0) &&
+           (!(tr & 2) || lda % 8 == 0) && sam::dma_has_layout(p.variant_id, tr, p.dtype);
 }
 
 // Ring plans store C with row stride ldc (a multiple of 4: 16-byte stores)
@@ -206,14 +208,15 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
     const unsigned long long es = p.dtype == sam::DT_F32 ? 4 : (blockscaled ? 1 : 2);
     const unsigned long long half = p.dtype == sam::DT_MX4 ? 2 : 1;
     if (blockscaled != (mx != nullptr)) return fail(SAM_ERR_INTERNAL, "scale arguments mismatch");
-    const bool bt = x && x->bt;
-    const long long lda = x ? x->lda : K, ldb = x ? x->ldb : N, ldc = x ? x->ldc : N;
+    const int tr = x ? x->tr : 0;
+    const bool at = tr & 2, bt = tr & 1;
+    const long long lda = x ? x->lda : (at ? M : K), ldb = x ? x->ldb : (bt ? K : N), ldc = x ? x->ldc : N;
     const float alpha = x ? x->alpha : 1.0f, beta = x ? x->beta : 0.0f;
     const bool gen = alpha != 1.0f || beta != 0.0f;
-    if (x && (K == 0 || lda < K || ldb < (bt ? K : N) || ldc < N || (lda != K && !reads_strided(p, true, lda)) ||
-              (bt ? !reads_transposed_b(p, K, ldb) : (ldb != N && !reads_strided(p, false, ldb))) ||
-              ((ldc != N || gen) && !writes_general_c(p, ldc))))
-        return fail(SAM_ERR_INTERNAL, "strides, a transposed B or alpha / beta on a plan that cannot take them");
+    if (x && (K == 0 || lda < (at ? M : K) || ldb < (bt ? K : N) || ldc < N ||
+              (tr && !reads_transposed(p, tr, lda, ldb)) || (!at && lda != K && !reads_strided(p, true, lda)) ||
+              (!bt && ldb != N && !reads_strided(p, false, ldb)) || ((ldc != N || gen) && !writes_general_c(p, ldc))))
+        return fail(SAM_ERR_INTERNAL, "strides, transposed operands or alpha / beta on a plan that cannot take them");
     if (M == 0 || N == 0) return SAM_OK;
     // Kernels address a workgroup's operand panels with 32-bit byte offsets:
     // up to 257 rows of A (lda elements each), 129 rows of B and 257 rows of C.
@@ -227,7 +230,8 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
     if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))) || (ws && !aligned16(ws)))
         return fail(SAM_ERR_MISALIGNED, "A, B, C and workspace must be 16-byte aligned");
     const unsigned long long cbytes = (unsigned long long)((M - 1) * ldc + N) * 4ull;
-    const unsigned long long abytes = K ? (unsigned long long)((M - 1) * lda + K) * es / half : 0;
+    const unsigned long long abytes =
+        K ? (unsigned long long)(at ? (K - 1) * lda + M : (M - 1) * lda + K) * es / half : 0;
     const unsigned long long bbytes =
         K ? (unsigned long long)(bt ? (N - 1) * ldb + K : (K - 1) * ldb + N) * es / half : 0;
     if (ranges_overlap(C, cbytes, A, abytes) || ranges_overlap(C, cbytes, B, bbytes))
@@ -299,7 +303,7 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
             a.sk_dp = p.sk_dp;
         }
         sam::Plan q = p;
-        q.bt = bt;
+        q.tr = tr;
         e = sam::launch_gemm(q, a, s);
         if (e == hipSuccess && p.split > 1)
             e = ldc != N || gen
@@ -330,7 +334,7 @@ struct ExLayout {
     bool pack_a, pack_b;  // op(A) / op(B) copied into compact rows first
     bool direct_a, direct_b;  // strided A / B read in place by a ring plan
     bool fused_c;         // a ring plan stores C itself (stride ldc, alpha / beta)
-    bool bt;              // a transposed B read straight by a 16-bit ring plan
+    int tr;               // operands given transposed read straight by a 16-bit ring plan (bit 0 B, bit 1 A)
     bool use_t;           // product into a temporary, then C = alpha T + beta C
     unsigned long long off_a, off_b, off_t, off_w, total;
     sam::Plan plan;
@@ -379,10 +383,19 @@ sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long l
     }
     L->direct_a = L->product && !ta && lda != K && reads_strided(L->plan, true, lda);
     L->direct_b = L->product && !tb && ldb != N && reads_strided(L->plan, false, ldb);
-    L->bt = L->product && tb && reads_transposed_b(L->plan, K, ldb);
+    // Transposed operands read straight where the plan can (both, else B
+    // alone, else A alone); the rest is packed.
+    L->tr = 0;
+    if (L->product) {
+        for (int tr : {3, 1, 2})
+            if ((tr & 1) <= (tb ? 1 : 0) && (tr & 2) <= (ta ? 2 : 0) && reads_transposed(L->plan, tr, lda, ldb)) {
+                L->tr = tr;
+                break;
+            }
+    }
     L->fused_c = L->product && writes_general_c(L->plan, ldc);
-    L->pack_a = L->product && (ta || lda != K) && !L->direct_a;
-    L->pack_b = L->product && (tb || ldb != N) && !L->direct_b && !L->bt;
+    L->pack_a = L->product && (ta || lda != K) && !L->direct_a && !(L->tr & 2);
+    L->pack_b = L->product && (tb || ldb != N) && !L->direct_b && !(L->tr & 1);
     L->use_t = L->product && !L->fused_c && !(ldc == N && beta == 0.0f);
     L->off_a = 0;
     L->off_b = align256(L->off_a + (L->pack_a ? (unsigned long long)(M * K) * es : 0));
@@ -437,8 +450,8 @@ sam_status gemm_ex_run(const ExLayout& L, sam_dtype dtype, sam_op trans_a, sam_o
         }
         if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
         float* out = L.use_t ? reinterpret_cast<float*>(ws + L.off_t) : C;
-        const ExTail x{L.direct_a ? lda : K, (L.direct_b || L.bt) ? ldb : N, L.fused_c ? ldc : N,
-                       L.fused_c ? alpha : 1.0f, L.fused_c ? beta : 0.0f, L.bt};
+        const ExTail x{(L.direct_a || (L.tr & 2)) ? lda : K, (L.direct_b || (L.tr & 1)) ? ldb : N,
+                       L.fused_c ? ldc : N, L.fused_c ? alpha : 1.0f, L.fused_c ? beta : 0.0f, L.tr};
         st = run(L.plan, a, b, out, M, N, K, L.plan.ws_bytes ? ws + L.off_w : nullptr, L.plan.ws_bytes, stream,
                  nullptr, &x);
         if (st != SAM_OK) return st;

@@ -119,9 +119,10 @@ struct Plan {
     int pad_a, pad_b;
     long long lda, ldb;
     unsigned long long ws_inner;
-    // 16-bit ring plans of the general entry point: B given transposed
-    // (N rows of K values, row stride ldb), read straight by the kernel.
-    int bt;
+    // 16-bit ring plans of the general entry point: operands given
+    // transposed and read straight by the kernel, bit 0 B (N rows of K
+    // values, row stride ldb), bit 1 A (K rows of M values, row stride lda).
+    int tr;
 };
 
 // Dispatcher (sam_plan.cpp). Host only, pure.
@@ -140,8 +141,11 @@ hipError_t launch_gemm_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_stream(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s);
-// Whether a 16-bit ring variant has the transposed-B kernels.
-bool dma_has_bt(int variant_id, int dtype);
+typedef void (*KernelFn)(GemmArgs);
+// 16-bit ring kernels for operands given transposed (layout: bit 0 B,
+// bit 1 A), and whether a variant has both forms of a layout.
+KernelFn dma_t_kernel(int variant_id, int layout, bool stream_k, int dtype);
+bool dma_has_layout(int variant_id, int layout, int dtype);
 hipError_t launch_sk_fixup_dma(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_mx8(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_kq(const Plan& p, const GemmArgs& a, hipStream_t s);

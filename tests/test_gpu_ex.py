@@ -219,18 +219,20 @@ def test_ex_fused_epilogue_16bit_stream_k_and_swap(dtype, shape, form):
     assert np.all(got[:, N:] == 12345.0)
 
 
-# A transposed B (N rows of K values) read straight by every 16x16x32 ring
-# variant, in its data-parallel, split-K and stream-K forms (forced plans),
-# with ragged M, strided rows, ldc and alpha / beta. No packed copy: the
-# workspace is the plan's own.
+# Operands given transposed (B as N rows of K values, A as K rows of M
+# values, or both) read straight by every 16x16x32 ring variant, in its
+# data-parallel, split-K and stream-K forms (forced plans), with ragged M,
+# strided rows, ldc and alpha / beta. No packed copy: the workspace is the
+# plan's own.
 RING16_B16 = [v for v in range(sam.variant_count())
               if sam.variant_info(v)["name"].startswith("r") and "_b16" in sam.variant_info(v)["name"]]
 NT_SHAPES = [(300, 520, 264), (1000, 776, 1032)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)], ids=["NT", "TN", "TT"])
 @pytest.mark.parametrize("vid", RING16_B16)
-def test_ex_transposed_b_read_straight(dtype, vid):
+def test_ex_transposed_operands_read_straight(dtype, ta, tb, vid):
     ran = 0
     for (M, N, K) in NT_SHAPES:
         for split in (1, 2, -1):
@@ -239,37 +241,43 @@ def test_ex_transposed_b_read_straight(dtype, vid):
             except sam.SamError:
                 continue
             alpha, beta = 0.5, -1.0
-            Av, Bv, C0, lda, ldb, ldc = _fused_case(dtype, M, N, K, False, True, 8, 8, 4, alpha, beta,
-                                                    M + N + vid + 3 * split)
-            assert sam.ex_workspace_bytes(M, N, K, False, True, lda, ldb, ldc, alpha, beta, dtype, variant=vid,
+            pa = (8 - M % 8) if ta else 8          # transposed A: rows of lda % 8 == 0 values
+            Av, Bv, C0, lda, ldb, ldc = _fused_case(dtype, M, N, K, ta, tb, pa, 8, 4, alpha, beta,
+                                                    M + N + vid + 3 * split + 5 * ta)
+            assert sam.ex_workspace_bytes(M, N, K, ta, tb, lda, ldb, ldc, alpha, beta, dtype, variant=vid,
                                           split=split) == p["workspace_bytes"]
-            print(f"[nt] variant {vid} {dtype} {(M, N, K)} split {split}", flush=True)
+            print(f"[tr] variant {vid} {dtype} {'T' if ta else 'N'}{'T' if tb else 'N'} {(M, N, K)} split {split}",
+                  flush=True)
+            ca, cb = (M if ta else K), (K if tb else N)
             Cd = torch.from_numpy(C0.copy()).cuda()
-            sam.gemm_ex(_dev(dtype, _enc(dtype, Av))[:, :K], _dev(dtype, _enc(dtype, Bv))[:, :K], Cd[:, :N],
-                        trans_b=True, alpha=alpha, beta=beta, variant=vid, split=split)
+            sam.gemm_ex(_dev(dtype, _enc(dtype, Av))[:, :ca], _dev(dtype, _enc(dtype, Bv))[:, :cb], Cd[:, :N],
+                        trans_a=ta, trans_b=tb, alpha=alpha, beta=beta, variant=vid, split=split)
             torch.cuda.synchronize()
             got = Cd.cpu().numpy()
-            ref = orc().gemm_ex(dtype, M, N, K, _enc(dtype, Av), lda, _enc(dtype, Bv), ldb, False, True, alpha, beta,
+            ref = orc().gemm_ex(dtype, M, N, K, _enc(dtype, Av), lda, _enc(dtype, Bv), ldb, ta, tb, alpha, beta,
                                 np.ascontiguousarray(C0[:, :N]), nthreads=orc().max_threads())
-            assert bitexact_mismatches(got[:, :N], ref) == 0, (vid, dtype, (M, N, K), split)
+            assert bitexact_mismatches(got[:, :N], ref) == 0, (vid, dtype, ta, tb, (M, N, K), split)
             assert np.all(got[:, N:] == 12345.0)
             ran += 1
     assert ran > 0
 
 
-def test_ex_transposed_b_random_repeatable():
-    """Random bf16 operands through the transposed-B form of the dispatcher's
-    plan: rel_rms within 1e-5 of the oracle (exact products, FP32 sums), and
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)], ids=["NT", "TN", "TT"])
+def test_ex_transposed_random_repeatable(ta, tb):
+    """Random bf16 operands given transposed through the dispatcher's plan:
+    rel_rms within 1e-5 of the oracle (exact products, FP32 sums), and
     bitwise the same twice."""
     M, N, K = 2560, 3072, 256
     assert sam.plan(M, N, K, "bf16")["name"].startswith("bf16_r256x256")
-    rng = np.random.default_rng(11)
+    assert sam.ex_workspace_bytes(M, N, K, ta, tb, M if ta else K, K if tb else N, N, 1.0, 0.0, "bf16") == 0
+    rng = np.random.default_rng(11 + 2 * ta + tb)
     A = si.normal16(rng, (M, K), "bf16")
-    Bt = si.normal16(rng, (N, K), "bf16")
-    dA, dBt = _dev("bf16", A), _dev("bf16", Bt)
-    C1 = sam.gemm_ex(dA, dBt, trans_b=True)
-    C2 = sam.gemm_ex(dA, dBt, trans_b=True)
+    B = si.normal16(rng, (K, N), "bf16")
+    dA = _dev("bf16", np.ascontiguousarray(A.T) if ta else A)
+    dB = _dev("bf16", np.ascontiguousarray(B.T) if tb else B)
+    C1 = sam.gemm_ex(dA, dB, trans_a=ta, trans_b=tb)
+    C2 = sam.gemm_ex(dA, dB, trans_a=ta, trans_b=tb)
     torch.cuda.synchronize()
     assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
-    ref = orc().gemm("bf16", A, np.ascontiguousarray(Bt.T), nthreads=orc().max_threads())
+    ref = orc().gemm("bf16", A, B, nthreads=orc().max_threads())
     assert rel_rms(C1.cpu().numpy(), ref) <= 1e-5   # exact products, FP32 accumulation
