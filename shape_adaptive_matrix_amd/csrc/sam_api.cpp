@@ -381,6 +381,16 @@ sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long l
         L->total = L->plan.ws_bytes;
         return SAM_OK;
     }
+    // A 16-bit ring plan that has to read C (beta != 0) takes the operand-swap
+    // form of its variant when there is one: the same tile and schedule, with
+    // C read and written 16 bytes per lane instead of 4.
+    if (!f && L->product && beta != 0.0f && L->plan.kind == sam::KIND_DMA && !L->plan.swap) {
+        const int twin = sam::swap_twin(L->plan.variant_id);
+        sam::Plan q{};
+        if (twin >= 0 && sam::plan_for_variant(twin, M, N, K, dtype, L->plan.sk ? -1 : L->plan.split, &q,
+                                               L->plan.raster_n))
+            L->plan = q;
+    }
     L->direct_a = L->product && !ta && lda != K && reads_strided(L->plan, true, lda);
     L->direct_b = L->product && !tb && ldb != N && reads_strided(L->plan, false, ldb);
     // Transposed operands read straight where the plan can (both, else B

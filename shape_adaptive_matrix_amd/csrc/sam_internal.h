@@ -134,6 +134,9 @@ bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out);
 bool plan_model(long long M, long long N, long long K, int dtype, Plan* out);
 void plan_name(const Plan& p, char* buf, int n);
 int k_stage(const Variant& v, int dtype);   // K per LDS stage
+// The operand-swap form of a variant (same tile and schedule, 16-byte
+// stores and loads of C), or -1.
+int swap_twin(int id);
 
 // Kernel launchers (sam_kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s);

@@ -76,6 +76,17 @@ const Variant* variant_get(int id)
     return (id >= 0 && id < kVariantCount) ? &kVariants[id] : nullptr;
 }
 
+int swap_twin(int id)
+{
+    const Variant* v = variant_get(id);
+    if (!v || v->swap) return -1;
+    char want[96];
+    snprintf(want, sizeof want, "%s_sw", v->name);
+    for (int i = 0; i < kVariantCount; ++i)
+        if (strcmp(kVariants[i].name, want) == 0) return i;
+    return -1;
+}
+
 int k_stage(const Variant& v, int dtype)
 {
     if (v.kind == KIND_MX8 && dtype == DT_MX4) return 2 * v.bk;   // E2M1: twice the values per LDS row

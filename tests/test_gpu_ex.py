@@ -156,6 +156,9 @@ FUSED = [
     ("bf16", (640, 1792, 256), False, False, 8, 8, 4, 0.5, -1.0, "bf16_r", "s1"),
     ("bf16", (256, 384, 3072), True, False, 0, 0, 8, 1.0, 1.0, "bf16_r", "s12"),
     ("f16", (640, 1792, 256), False, True, 0, 0, 4, -2.0, 0.5, "f16_r", "s1"),
+    # beta != 0 on a 16x16x32 plan: its operand-swap form reads and writes C
+    ("bf16", (2560, 3072, 256), False, False, 8, 8, 4, 0.5, 1.0, "bf16_r256x256", "s1"),
+    ("f16", (2560, 3072, 256), True, True, 0, 0, 4, -1.0, 0.25, "f16_r256x256", "s1"),
 ]
 
 
