@@ -39,9 +39,9 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "mxfp8": 5000.0, "mx
 PEAK_HBM_GBS = 8000.0
 
 
-KERNEL_SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_kernels_stream.hip", "sam_kernels_f32ring.hip",
-                  "sam_kernels_mx.hip", "sam_kernels_kq.hip", "sam_kernels_kp.hip", "sam_dma.h", "sam_internal.h",
-                  "sam_variants.h", "sam_variants_mx.h"]
+KERNEL_SOURCES = ["sam_kernels.hip", "sam_kernels_dma.hip", "sam_kernels_dma_t.hip", "sam_ring16.h", "sam_sk.h",
+                  "sam_kernels_stream.hip", "sam_kernels_f32ring.hip", "sam_kernels_mx.hip", "sam_kernels_kq.hip",
+                  "sam_kernels_kp.hip", "sam_dma.h", "sam_internal.h", "sam_variants.h", "sam_variants_mx.h"]
 
 # Kernel function of a plan, by the leading letters of its variant name.
 KERNEL_OF = {"t": "sam::gemm_kernel", "r": "sam::gemm16_dma_kernel", "q": "sam::gemm16_dma_kernel",
@@ -55,11 +55,25 @@ def kernel_name(plan) -> str:
     return KERNEL_OF.get(variant[:2], KERNEL_OF.get(variant[0], "?"))
 
 
-def src_digest() -> str:
-    """Hash of the kernel sources: a stored counter reading is only reported
-    while the kernels it was taken on are unchanged."""
+# The sources a kernel family is built from: a stored counter reading of one
+# of its kernels stays valid while these are unchanged.
+SOURCES_OF_KERNEL = {
+    "sam::gemm_f32_ring_kernel": ["sam_kernels_f32ring.hip", "sam_dma.h", "sam_sk.h", "sam_internal.h",
+                                  "sam_variants.h"],
+    "sam::gemm16_dma_kernel": ["sam_ring16.h", "sam_kernels_dma.hip", "sam_dma.h", "sam_sk.h", "sam_internal.h",
+                               "sam_variants.h"],
+    "sam::gemm_mx8_kernel": ["sam_kernels_mx.hip", "sam_dma.h", "sam_internal.h", "sam_variants.h",
+                             "sam_variants_mx.h"],
+}
+
+
+def src_digest(plan=None) -> str:
+    """Hash of the sources of the plan's kernel (of every kernel source
+    without a plan): a stored counter reading is only reported while the
+    kernel it was taken on is unchanged."""
+    names = SOURCES_OF_KERNEL.get(kernel_name(plan), KERNEL_SOURCES) if plan is not None else KERNEL_SOURCES
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names:
         p = ROOT / "shape_adaptive_matrix_amd" / "csrc" / name
         h.update(name.encode())
         h.update(p.read_bytes())
@@ -193,7 +207,7 @@ def profile_kernel_avg_us(workload: str, kernel: str):
     return None
 
 
-def roofline_of(w, t_ms: float, plan, digest: str) -> dict:
+def roofline_of(w, t_ms: float, plan) -> dict:
     """Roofline record of one timed workload: MFMA-bound for the dense
     shapes (2MNK FLOP against the dtype's peak), HBM-bound for the skinny ones
     (algorithmic bytes against 8 TB/s)."""
@@ -207,7 +221,7 @@ def roofline_of(w, t_ms: float, plan, digest: str) -> dict:
         achieved = w.flops / t_ms / 1e9
         rec = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
                "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4)}
-    rec["traffic"] = None if split else load_traffic(w.name, digest)
+    rec["traffic"] = None if split else load_traffic(w.name, src_digest(plan))
     rec["kernel"] = kernel_name(plan) + (" + sam::splitk_reduce_kernel" if split else "") + \
         (" + sam::sk_fixup_kernel" if plan["split_k"] == -1 else "")
     if plan["split_k"] == 1:
@@ -233,7 +247,7 @@ def time_steps(torch, step, steps: int) -> float:
     return s.elapsed_time(e)
 
 
-def sweep(torch, sam, si, digest: str, rounds: int = 5):
+def sweep(torch, sam, si, rounds: int = 5):
     """Every workload: median over rounds of the per-launch time of a batch
     lasting >= 20 ms; cold-cache single launches for the skinny shapes."""
     out = []
@@ -258,7 +272,7 @@ def sweep(torch, sam, si, digest: str, rounds: int = 5):
             "tflops": round(w.flops / t_ms / 1e9, 2),
             "pct_mfma_peak": round(100 * w.flops / t_ms / 1e9 / PEAK_TFLOPS[w.dtype], 1),
             "alg_gbs": round(w.alg_bytes / t_ms / 1e6, 1),
-            "roofline": roofline_of(w, t_ms, g["plan"], digest),
+            "roofline": roofline_of(w, t_ms, g["plan"]),
         }
         if min(w.M, w.N) <= 16:
             # Evict the operands by reading 1 GiB: a read leaves clean lines,
@@ -402,12 +416,12 @@ def main():
     else:
         g = prepare(w, torch, sam, si, args.variant, args.split)
     step = g["step"]
-    digest = src_digest()
+    digest = src_digest(g["plan"])
     # The sweep runs first: after it the clock has settled under load, so a
     # short timed region measures the kernel rather than the clock ramp.
     sweep_rec = None
     if not args.no_sweep:
-        sweep_rec = sweep(torch, sam, si, digest)
+        sweep_rec = sweep(torch, sam, si)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -15,7 +15,8 @@
 //  * A sits in LDS K-contiguous (64-byte rows, 16-byte chunks XOR-swizzled
 //    by row >> 2) and is read as one 128-bit fragment per MFMA block.
 //  * B sits in LDS in its natural N-contiguous layout (16-byte chunks
-//    XOR-swizzled by 4 (k & 3)) and is read with the transposing LDS load:
+//    XOR-swizzled by K row, nsw below) and is read with the transposing LDS
+//    load:
 //    within each 16-lane group, lane d receives, for k = kbase..kbase+3,
 //    the value at column (4 (source lane % 4) + d % 4) of the row that source
 //    lane 4 i + d / 4 points at. Two such loads give the eight consecutive K
@@ -89,6 +90,14 @@ template <int DT> struct Mf<DT, 16> {
 };
 
 }  // namespace dma
+
+// Chunk swizzle of a row of K-row-major data in LDS (B in the plain layout,
+// A given transposed): LDS slot c of row `row` holds logical 16-byte chunk
+// c ^ nsw(row). The transposing fragment reads of one pass (32 lanes: two
+// groups of 16 reading rows 8 apart, four rows x four column pairs each)
+// then fall on 32 distinct bank pairs: bits 2-3 separate the four rows of a
+// group, bit 1 the two groups.
+__device__ __forceinline__ int nsw(int row) { return (4 * (row & 3)) ^ (2 * ((row >> 3) & 1)); }
 
 // MODE 0: loads write LDS directly (ring of NBUF stages).
 // MODE 1: loads go to registers and are written to LDS with ds_write_b128
@@ -205,7 +214,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
             // A^T rows k0 + row (M-contiguous), placed and swizzled as B's in MODE 0.
             const int I = wave + q * NW;
             const int row = I * RPIA + lane / CPRA;
-            const int c = (lane % CPRA) ^ (4 * (row & 3));
+            const int c = (lane % CPRA) ^ nsw(row);
             const bool ok = k0 + row < kend && m0 + c * 8 < M;
             const long long abase = ((long long)k0 * lda + m0) * 2;
             const i4 rAt = rsrc_words(static_cast<const char*>(args.A) + abase, a_bytes - abase);
@@ -234,7 +243,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
         } else {
             const int I = wave + (q - A_PW) * NW;
             const int row = I * RPI + lane / CPR;
-            const int c = (lane % CPR) ^ (4 * (row & 3));
+            const int c = (lane % CPR) ^ nsw(row);
             const bool ok = k0 + row < kend && n0 + c * 8 < N;
             const long long bbase = ((long long)k0 * ldb + n0) * 2;
             const int off = ok ? (row * ldb + c * 8) * 2 : kOOB;
@@ -320,7 +329,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
             for (int half = 0; half < 2; ++half) {
                 const int col = wm0 + BLK * r + (lrow & ~15) + 4 * (s16 & 3);
                 const int row = MF::KSTEP * t + 8 * lgrp + 4 * half + (s16 >> 2);
-                const int c = (col >> 3) ^ (4 * (row & 3));
+                const int c = (col >> 3) ^ nsw(row);
                 const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     SAM_LDS4S(buf + row * A_ROW_T + c * 16 + (col & 7) * 2));
                 h[half] = __builtin_bit_cast(u2, v);
@@ -341,7 +350,7 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
             const int j = (r - TM) >> 1, half = (r - TM) & 1;
             const int col = wn0 + BLK * j + (lrow & ~15) + 4 * (s16 & 3);
             const int row = MF::KSTEP * t + 8 * lgrp + 4 * half + (s16 >> 2);
-            const int c = (col >> 3) ^ (4 * (row & 3));
+            const int c = (col >> 3) ^ nsw(row);
             const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 SAM_LDS4S(buf + A_BYTES + row * B_ROW + c * 16 + (col & 7) * 2));
             fb[j][half] = __builtin_bit_cast(u2, v);
