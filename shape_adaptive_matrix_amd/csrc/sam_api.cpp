@@ -165,6 +165,7 @@ struct ExTail {
     long long lda, ldb, ldc;
     float alpha, beta;
     int tr;    // operands given transposed, read straight: bit 0 B (N rows of K), bit 1 A (K rows of M)
+    bool ct;   // the product (M x N here) goes to C transposed: C is N rows of M values with stride ldc
 };
 
 // Whether a plan can take A rows with stride lda != K in place: a 16-bit
@@ -210,10 +211,12 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
     if (blockscaled != (mx != nullptr)) return fail(SAM_ERR_INTERNAL, "scale arguments mismatch");
     const int tr = x ? x->tr : 0;
     const bool at = tr & 2, bt = tr & 1;
+    const bool ct = x && x->ct;
     const long long lda = x ? x->lda : (at ? M : K), ldb = x ? x->ldb : (bt ? K : N), ldc = x ? x->ldc : N;
     const float alpha = x ? x->alpha : 1.0f, beta = x ? x->beta : 0.0f;
     const bool gen = alpha != 1.0f || beta != 0.0f;
-    if (x && (K == 0 || lda < (at ? M : K) || ldb < (bt ? K : N) || ldc < N ||
+    if (x && (K == 0 || lda < (at ? M : K) || ldb < (bt ? K : N) || ldc < (ct ? M : N) ||
+              (ct && (p.kind != sam::KIND_F32RING || tr || ldc % 4)) ||
               (tr && !reads_transposed(p, tr, lda, ldb)) || (!at && lda != K && !reads_strided(p, true, lda)) ||
               (!bt && ldb != N && !reads_strided(p, false, ldb)) || ((ldc != N || gen) && !writes_general_c(p, ldc))))
         return fail(SAM_ERR_INTERNAL, "strides, transposed operands or alpha / beta on a plan that cannot take them");
@@ -229,7 +232,7 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
     if (mx && K > 0 && (!mx->sa || !mx->sb)) return fail(SAM_ERR_INVALID_ARG, "a scale array is null");
     if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))) || (ws && !aligned16(ws)))
         return fail(SAM_ERR_MISALIGNED, "A, B, C and workspace must be 16-byte aligned");
-    const unsigned long long cbytes = (unsigned long long)((M - 1) * ldc + N) * 4ull;
+    const unsigned long long cbytes = (unsigned long long)(ct ? (N - 1) * ldc + M : (M - 1) * ldc + N) * 4ull;
     const unsigned long long abytes =
         K ? (unsigned long long)(at ? (K - 1) * lda + M : (M - 1) * lda + K) * es / half : 0;
     const unsigned long long bbytes =
@@ -277,6 +280,7 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         a.out = p.split > 1 ? static_cast<float*>(ws) : C;
         a.ldc = (int)(p.split > 1 ? N : ldc);   // split-K: the reduce pass writes C
         a.epi = p.split > 1 ? 0 : (int)gen;
+        a.ct = p.split > 1 ? 0 : (int)ct;
         a.alpha = alpha;
         a.beta = beta;
         a.M = (int)M;
@@ -306,8 +310,9 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         q.tr = tr;
         e = sam::launch_gemm(q, a, s);
         if (e == hipSuccess && p.split > 1)
-            e = ldc != N || gen
-                    ? sam::launch_reduce_ex(static_cast<const float*>(ws), p.split, M * N, C, M, N, ldc, alpha, beta, s)
+            e = ldc != N || gen || ct
+                    ? sam::launch_reduce_ex(static_cast<const float*>(ws), p.split, M * N, C, M, N, ldc, alpha, beta,
+                                            (int)ct, s)
                     : sam::launch_reduce(static_cast<const float*>(ws), p.split, M * N, C, M * N, s);
         if (e == hipSuccess && p.sk) e = sam::launch_sk_fixup(p, a, s);
     }
@@ -335,6 +340,7 @@ struct ExLayout {
     bool direct_a, direct_b;  // strided A / B read in place by a ring plan
     bool fused_c;         // a ring plan stores C itself (stride ldc, alpha / beta)
     int tr;               // operands given transposed read straight by a 16-bit ring plan (bit 0 B, bit 1 A)
+    bool ct;              // FP32 A^T B^T as (B A)^T: a ring plan for N x M x K storing C transposed
     bool use_t;           // product into a temporary, then C = alpha T + beta C
     unsigned long long off_a, off_b, off_t, off_w, total;
     sam::Plan plan;
@@ -380,6 +386,21 @@ sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long l
     if (L->fast) {
         L->total = L->plan.ws_bytes;
         return SAM_OK;
+    }
+    // Both operands given transposed on the FP32 path: A^T B^T = (B A)^T, a
+    // plain product of the operands as stored (B as N rows of K, A as K rows
+    // of M) whose ring plan stores C transposed, with no copies.
+    if (!f && L->product && ta && tb && dtype == SAM_F32 && ldc % 4 == 0) {
+        sam::Plan q{};
+        if (sam::plan_auto(N, M, K, dtype, &q) && q.kind == sam::KIND_F32RING &&
+            (ldb == K || reads_strided(q, true, ldb)) && (lda == M || reads_strided(q, false, lda))) {
+            L->ct = true;
+            L->fused_c = true;
+            L->plan = q;
+            L->off_a = L->off_b = L->off_t = L->off_w = 0;
+            L->total = q.ws_bytes;
+            return SAM_OK;
+        }
     }
     // A 16-bit ring plan that has to read C (beta != 0) takes the operand-swap
     // form of its variant when there is one: the same tile and schedule, with
@@ -459,9 +480,13 @@ sam_status gemm_ex_run(const ExLayout& L, sam_dtype dtype, sam_op trans_a, sam_o
             b = ws + L.off_b;
         }
         if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+        if (L.ct) {   // (B A)^T: B as the N x K left operand, A as the K x M right one
+            const ExTail y{ldb, lda, ldc, alpha, beta, 0, true};
+            return run(L.plan, B, A, C, N, M, K, L.plan.ws_bytes ? ws : nullptr, L.plan.ws_bytes, stream, nullptr, &y);
+        }
         float* out = L.use_t ? reinterpret_cast<float*>(ws + L.off_t) : C;
         const ExTail x{(L.direct_a || (L.tr & 2)) ? lda : K, (L.direct_b || (L.tr & 1)) ? ldb : N,
-                       L.fused_c ? ldc : N, L.fused_c ? alpha : 1.0f, L.fused_c ? beta : 0.0f, L.tr};
+                       L.fused_c ? ldc : N, L.fused_c ? alpha : 1.0f, L.fused_c ? beta : 0.0f, L.tr, false};
         st = run(L.plan, a, b, out, M, N, K, L.plan.ws_bytes ? ws + L.off_w : nullptr, L.plan.ws_bytes, stream,
                  nullptr, &x);
         if (st != SAM_OK) return st;

@@ -84,6 +84,10 @@ struct GemmArgs {
     int ldc;
     int epi;
     float alpha, beta;
+    // FP32 ring kernels, their stream-K fix-up and the general split-K
+    // reduce: the product D (M x N here) is stored transposed, D[i][j] at
+    // C[j * ldc + i] (the general entry point's A^T B^T, computed as B A).
+    int ct;
     const unsigned char* sa;   // block-scaled operands: scale codes of A (M x K/32)
     const unsigned char* sb;   // ... and of B (N x K/32); B is then N rows of K codes
     int fmt_a, fmt_b;    // element formats: 0 E4M3, 1 E5M2
@@ -156,9 +160,9 @@ hipError_t launch_kp(const Plan& p, const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const float* parts, int split, long long part_stride,
                          float* C, long long count, hipStream_t s);
 // Split-K sum into C with row stride ldc through the general entry point's
-// epilogue (alpha t + beta C).
+// epilogue (alpha t + beta C), transposed when ct.
 hipError_t launch_reduce_ex(const float* parts, int split, long long part_stride, float* C, long long M, long long N,
-                            long long ldc, float alpha, float beta, hipStream_t s);
+                            long long ldc, float alpha, float beta, int ct, hipStream_t s);
 hipError_t launch_zero(float* C, long long count, hipStream_t s);
 // General entry point (sam_kernels_ex.hip): pack an operand (transposing
 // when `trans`) into compact rows, and C = alpha T + beta C.

@@ -472,14 +472,14 @@ splitk_reduce_kernel(const float* __restrict__ P, int S, long long stride,
 // evaluated as fmaf(alpha, t, beta c), C read only when beta != 0.
 __global__ void __launch_bounds__(256)
 splitk_reduce_ex_kernel(const float* __restrict__ P, int S, long long stride, float* C, long long M, long long N,
-                        long long ldc, float alpha, float beta)
+                        long long ldc, float alpha, float beta, int ct)
 {
     const long long step = (long long)gridDim.x * blockDim.x, count = M * N;
     for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += step) {
         float t = P[e];
         for (int s = 1; s < S; ++s) t = t + P[s * stride + e];
         const long long i = e / N, j = e - i * N;
-        float* c = C + i * ldc + j;
+        float* c = ct ? C + j * ldc + i : C + i * ldc + j;   // ct: the product goes to C transposed
         *c = beta != 0.0f ? __fmaf_rn(alpha, t, beta * *c) : alpha * t;
     }
 }
@@ -561,13 +561,13 @@ hipError_t launch_reduce(const float* parts, int split, long long part_stride,
 }
 
 hipError_t launch_reduce_ex(const float* parts, int split, long long part_stride, float* C, long long M, long long N,
-                            long long ldc, float alpha, float beta, hipStream_t s)
+                            long long ldc, float alpha, float beta, int ct, hipStream_t s)
 {
     long long blocks = (M * N + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(splitk_reduce_ex_kernel, dim3((unsigned)blocks), dim3(256), 0, s, parts, split, part_stride, C,
-                       M, N, ldc, alpha, beta);
+                       M, N, ldc, alpha, beta, ct);
     return hipGetLastError();
 }
 

@@ -321,14 +321,19 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
     // split `ostride`'s partial slice, at (m0, n0) with row stride ldc (N
     // for partials). Formed here rather than by the caller, so it is not live
     // through the K loop.
+    // ct: the tile goes to C transposed, element (row, col) at C[col][row].
+    const bool ct = to_c && args.ct;
     if constexpr (!SEG) {
-        outp = args.out + (long long)ostride * args.part_stride + (long long)m0 * args.ldc + n0;
+        outp = args.out + (long long)ostride * args.part_stride +
+               (ct ? (long long)n0 * args.ldc + m0 : (long long)m0 * args.ldc + n0);
         orows = M - m0;
         ocols = N - n0;
         ostride = args.ldc;
     }
     const __amdgpu_buffer_rsrc_t rC =
-        make_rsrc(outp, orows > 0 && ocols > 0 ? ((long long)(orows - 1) * ostride + ocols) * 4 : 0);
+        make_rsrc(outp, orows > 0 && ocols > 0
+                            ? (ct ? (long long)(ocols - 1) * ostride + orows : (long long)(orows - 1) * ostride + ocols) * 4
+                            : 0);
     const bool gen = to_c && args.epi;       // the general entry point's alpha / beta
     auto finish = [&](auto hc) {
         constexpr int H = decltype(hc)::value;
@@ -406,10 +411,49 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
                     }
                 }
         };
-        if (gen)
+        // Transposed: rows 4 q .. 4 q + 3 of a block are consecutive for
+        // every lane, so each of its V columns is stored as four adjacent
+        // values of one row of C (one 16-byte store; value by value where
+        // the four cross the tile's last row).
+        auto store_all_t = [&](auto genc) {
+            constexpr bool GEN = decltype(genc)::value;
+#pragma unroll
+            for (int ii = 0; ii < I0; ++ii)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int col = wn0 + CG * j + V * lrow;
+#pragma unroll
+                    for (int v = 0; v < V; ++v)
+#pragma unroll
+                        for (int r4 = 0; r4 < MF::N / 4; ++r4) {
+                            const int row0 = wm0 + BLK * (IB + ii) + MF::row(lane, 4 * r4);
+                            const acc_t& a = acc[IB + ii][j][v];
+                            if (row0 + 3 < orows) {
+                                const u4 x = {__float_as_uint(a[4 * r4]), __float_as_uint(a[4 * r4 + 1]),
+                                              __float_as_uint(a[4 * r4 + 2]), __float_as_uint(a[4 * r4 + 3])};
+                                StoreC<4>::run(x, rC, col + v < ocols ? ((col + v) * ostride + row0) * 4 : kOOB, args,
+                                               GEN);
+                            } else {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q)
+                                    StoreC<1>::run(__float_as_uint(a[4 * r4 + q]), rC,
+                                                   row0 + q < orows && col + v < ocols
+                                                       ? ((col + v) * ostride + row0 + q) * 4 : kOOB,
+                                                   args, GEN);
+                            }
+                        }
+                }
+        };
+        if (ct) {
+            if (gen)
+                store_all_t(std::true_type{});
+            else
+                store_all_t(std::false_type{});
+        } else if (gen) {
             store_all(std::true_type{});
-        else
+        } else {
             store_all(std::false_type{});
+        }
     };
     if (KS == 1 || half == 0)
         finish(std::integral_constant<int, 0>{});
@@ -469,7 +513,7 @@ gemm_f32_ring_sk_kernel(GemmArgs args)
         if (!first) dma::barrier();   // the previous segment's last LDS reads are done
         const int kbeg = k0 * BK, kend = min(args.K, k1 * BK);
         const bool whole = k0 == 0 && k1 == I;
-        float* outp = whole ? args.out + (long long)m0 * args.ldc + n0
+        float* outp = whole ? args.out + (args.ct ? (long long)n0 * args.ldc + m0 : (long long)m0 * args.ldc + n0)
                             : args.ws + (2 * g + (first ? 0 : 1)) * (long long)(BM * BN);
         ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, true>(
             args, tm, tn, kbeg, kend, outp, whole ? args.ldc : BN, whole ? args.M - m0 : BM,

@@ -58,11 +58,14 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(GemmArgs args)
         sum[2] = sum[2] + x[2];
         sum[3] = sum[3] + x[3];
     }
-    float* crow = args.out + (long long)(m0 + r) * args.ldc + n0 + c;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        if (n0 + c + q < args.N)
-            crow[q] = args.epi ? dma::epi_value(sum[q], args.beta != 0.0f ? crow[q] : 0.0f, args) : sum[q];
+        if (n0 + c + q < args.N) {
+            // args.ct: the product is stored transposed, (row, col) at C[col][row].
+            float* cp = args.ct ? args.out + (long long)(n0 + c + q) * args.ldc + (m0 + r)
+                                : args.out + (long long)(m0 + r) * args.ldc + n0 + c + q;
+            *cp = args.epi ? dma::epi_value(sum[q], args.beta != 0.0f ? *cp : 0.0f, args) : sum[q];
+        }
 }
 
 }  // namespace sam

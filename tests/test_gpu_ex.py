@@ -284,3 +284,33 @@ def test_ex_transposed_random_repeatable(ta, tb):
     assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
     ref = orc().gemm("bf16", A, B, nthreads=orc().max_threads())
     assert rel_rms(C1.cpu().numpy(), ref) <= 1e-5   # exact products, FP32 accumulation
+
+
+# FP32 with both operands given transposed: C = A^T B^T computed as the
+# plain product B A of the operands as stored, whose ring plan (for N x M x K)
+# stores C transposed, in the kernel, the split-K reduce or the stream-K
+# fix-up; element forms where rows are not 16-byte pieces, and a tile edge
+# inside a group of four rows of the product (N odd).
+TT_F32 = [((1792, 1792, 256), "s1"), ((1536, 256, 3072), "s8"), ((2560, 2304, 1536), "sk"),
+          ((4097, 2049, 1025), "s3_ua_ub"), ((3000, 3000, 3001), "_ua")]
+
+
+@pytest.mark.parametrize("case", TT_F32, ids=lambda c: "x".join(map(str, c[0])))
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (0.5, -1.0)])
+def test_ex_f32_both_transposed_as_transposed_store(case, alpha, beta):
+    (M, N, K), form = case
+    q = sam.plan(N, M, K, "f32")
+    assert q["name"].startswith("f32_f") and form in q["name"], q["name"]
+    pc = 4 - N % 4 if N % 4 else 4
+    Av, Bv, C0, lda, ldb, ldc = _fused_case("f32", M, N, K, True, True, 4, 4, pc, alpha, beta, M + 3 * N + K)
+    assert sam.ex_workspace_bytes(M, N, K, True, True, lda, ldb, ldc, alpha, beta, "f32") == q["workspace_bytes"]
+    print(f"[tt] {(M, N, K)} {q['name']} alpha {alpha} beta {beta}", flush=True)
+    Cd = torch.from_numpy(C0.copy()).cuda()
+    sam.gemm_ex(_dev("f32", Av)[:, :M], _dev("f32", Bv)[:, :K], Cd[:, :N], trans_a=True, trans_b=True, alpha=alpha,
+                beta=beta)
+    torch.cuda.synchronize()
+    got = Cd.cpu().numpy()
+    ref = orc().gemm_ex("f32", M, N, K, Av, lda, Bv, ldb, True, True, alpha, beta, np.ascontiguousarray(C0[:, :N]),
+                        nthreads=orc().max_threads())
+    assert bitexact_mismatches(got[:, :N], ref) == 0
+    assert np.all(got[:, N:] == 12345.0)
