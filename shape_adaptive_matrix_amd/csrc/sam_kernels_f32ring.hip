@@ -288,7 +288,13 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
     for (int r = 0; r < NRD; ++r) read_one(lds, tbase, r, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int k = 0; k < nk; ++k) {
+    // One stage of the K loop. REFILL: its last chunk step refills the slot
+    // the stage leaves with stage k + NBUF. With two stages the loop's wait
+    // is for every load issued, so the last two stages, whose refill would
+    // lie past the end, run without it (a separate copy of the loop, not a
+    // branch inside it); with more the wait's count assumes every refill.
+    auto stage = [&](int k, auto refill) {
+        constexpr bool REFILL = decltype(refill)::value;
         const unsigned char* cur = lds + (k % NBUF) * STAGE;
         const unsigned char* nxt = lds + ((k + 1) % NBUF) * STAGE;
 #pragma unroll
@@ -300,7 +306,7 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
         // Last chunk step of stage k: read this wave's first step of stage k+1
         // and refill the slot stage k leaves with stage k + NBUF.
         constexpr int L = (KH - 1) & 1;
-        kstep(fa[L], fb[L], nxt, tbase, fa[L ^ 1], fb[L ^ 1], k + NBUF);
+        kstep(fa[L], fb[L], nxt, tbase, fa[L ^ 1], fb[L ^ 1], REFILL ? k + NBUF : -1);
         if constexpr (L == 0) {   // odd number of chunk steps: next stage starts in set 1
 #pragma unroll
             for (int i = 0; i < TM; ++i) fa[0][i] = fa[1][i];
@@ -309,7 +315,13 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
 #pragma unroll
                 for (int e = 0; e < 4; ++e) fb[0][j][e] = fb[1][j][e];
         }
-    }
+    };
+    constexpr bool TRIM = NBUF == 2;
+    const int nk_refill = TRIM ? (nk > NBUF ? nk - NBUF : 0) : nk;
+    int k = 0;
+    for (; k < nk_refill; ++k) stage(k, std::true_type{});
+    if constexpr (TRIM)
+        for (; k < nk; ++k) stage(k, std::false_type{});
     wait_cnt<0, 0>();   // no LDS load may still be in flight when the workgroup ends
 
     // K split: the half-0 wave of a position keeps row blocks [0, TM/2) and

@@ -473,7 +473,13 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
     for (int r = 0; r < NRD; ++r) read_one(lds, 0, r, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int k = 0; k < nk; ++k) {
+    // One stage of the K loop. REFILL: its last k-step refills the LDS slot
+    // the stage leaves. With two stages the loop's wait is for every load
+    // issued, so the last two stages, whose refill would lie past the end,
+    // run without it (a separate copy of the loop, not a branch inside it);
+    // with more stages the wait's count assumes every refill is issued.
+    auto stage = [&](int k, auto refill) {
+        constexpr bool REFILL = decltype(refill)::value;
         const unsigned char* cur = lds + (k % NBUF) * STAGE;
         const unsigned char* nxt = lds + ((k + 1) % NBUF) * STAGE;
         // k-steps 0 .. KSTEPS-2 of stage k, each reading the next k-step.
@@ -501,14 +507,21 @@ __device__ __forceinline__ void ring16_segment(const GemmArgs& args, int tm, int
         // LDS slot stage k leaves (MODE 0: whole stage k + NBUF; MODE 2: A of
         // stage k + 2).
         constexpr int L = (KSTEPS - 1) & 1;
-        kstep(fa[L & FA], fb[L], nxt, 0, fa[(L ^ 1) & FA], fb[L ^ 1], DIRECT ? k + NBUF : (MODE == 2 ? k + 2 : -1), -1);
+        kstep(fa[L & FA], fb[L], nxt, 0, fa[(L ^ 1) & FA], fb[L ^ 1],
+              REFILL ? (DIRECT ? k + NBUF : (MODE == 2 ? k + 2 : -1)) : -1, -1);
         if constexpr (L == 0) {   // odd number of k-steps: next stage starts in set 1
 #pragma unroll
             for (int i = 0; i < TM; ++i) fa[0][i] = fa[FA][i];
 #pragma unroll
             for (int j = 0; j < TN; ++j) { fb[0][j][0] = fb[1][j][0]; fb[0][j][1] = fb[1][j][1]; }
         }
-    }
+    };
+    constexpr bool TRIM = DIRECT && NBUF == 2 && !SEG;   // stream-K segments keep one loop (registers)
+    const int nk_refill = TRIM ? (nk > NBUF ? nk - NBUF : 0) : nk;
+    int k = 0;
+    for (; k < nk_refill; ++k) stage(k, std::true_type{});
+    if constexpr (TRIM)
+        for (; k < nk; ++k) stage(k, std::false_type{});
     wait_cnt<0, 0>();   // no LDS load may still be in flight when the segment ends
 
     // The data-parallel form stores to C or to split `ostride`'s partial
