@@ -110,6 +110,21 @@ def _copy_values(pmc_dir, counter: str) -> list[float]:
     return vals
 
 
+def mfma_row(pmc_dir, workload: str, kernel: str, event_us=None) -> dict:
+    """MFMA utilisation of one kernel from the SQ_VALU_MFMA_BUSY_CYCLES /
+    SQ_INSTS_VALU_MFMA_MOPS_* / GRBM_GUI_ACTIVE run: MFMA-busy SIMD-cycles
+    over (1024 SIMDs x kernel cycles), kernel cycles = GRBM_GUI_ACTIVE / 8
+    XCDs, and the clock those cycles imply at the event-timed duration."""
+    m = counter_means(pmc_dir, kernel)
+    cyc = m["GRBM_GUI_ACTIVE"]["mean"] / 8
+    mops = sum(m[c]["mean"] for c in m if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+    row = {"workload": workload, "kernel": kernel_full_name(pmc_dir, kernel), "kernel_cycles": cyc,
+           "mops_x512": mops * 512, "mfma_util": m["SQ_VALU_MFMA_BUSY_CYCLES"]["mean"] / (1024 * cyc)}
+    if event_us:
+        row["clock_ghz"] = cyc / (event_us * 1e3)
+    return row
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
