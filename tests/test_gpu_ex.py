@@ -202,8 +202,11 @@ def test_ex_fused_epilogue_on_ring_plans(case):
 # The 16-bit stream-K and operand-swap forms at the sizes that take them:
 # the product against the oracle's plain GEMM of the compact operands,
 # then alpha P + beta C0 (exact here: small integers, dyadic alpha / beta).
+# Both calls read C (beta != 0), so the 16x16x32 plans run as their
+# operand-swap twins: stream-K with the fix-up at 6144^3, data-parallel with
+# K = 11008.
 @pytest.mark.parametrize("dtype,shape,form", [("bf16", (6144, 6144, 6144), "_sk"),
-                                              ("f16", (4096, 4096, 11008), "_sw_")])
+                                              ("f16", (4096, 4096, 11008), "_r256x256_")])
 def test_ex_fused_epilogue_16bit_stream_k_and_swap(dtype, shape, form):
     M, N, K = shape
     plan = sam.plan(M, N, K, dtype)
