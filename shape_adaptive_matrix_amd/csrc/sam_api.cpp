@@ -261,14 +261,14 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
         // 16-bit operands whose rows are not whole 16-byte pieces: padded
         // copies in front of the plan's own workspace.
         char* wsb = static_cast<char*>(ws);
-        if (p.pad_a) {
-            e = sam::launch_pad16(A, lda, wsb, p.lda, M, K, s);
-            A = wsb;
-        }
-        if (e == hipSuccess && p.pad_b) {
+        if (p.pad_a || p.pad_b) {
+            sam::Pad16 pa{}, pb{};
             char* bb = wsb + (p.pad_a ? ((unsigned long long)(M * p.lda) * 2ull + 255ull) & ~255ull : 0ull);
-            e = sam::launch_pad16(B, ldb, bb, p.ldb, K, N, s);
-            B = bb;
+            if (p.pad_a) pa = {A, lda, wsb, p.lda, M, K};
+            if (p.pad_b) pb = {B, ldb, bb, p.ldb, K, N};
+            e = sam::launch_pad16(pa, pb, s);
+            if (p.pad_a) A = wsb;
+            if (p.pad_b) B = bb;
         }
         if (e != hipSuccess) return fail(SAM_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
         ws = p.ws_bytes > 0 ? wsb + p.ws_inner : ws;

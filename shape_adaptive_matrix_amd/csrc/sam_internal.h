@@ -172,8 +172,15 @@ hipError_t launch_axpby(const float* T, long long ldt, float* C, long long ldc, 
                         float beta, hipStream_t s);
 // 16-bit rows x cols (row stride lds elements) into dst with row stride ldd
 // (a multiple of 8, dst 16-byte aligned), zeros in columns cols .. ldd - 1.
-hipError_t launch_pad16(const void* src, long long lds, void* dst, long long ldd, long long rows, long long cols,
-                        hipStream_t s);
+// One padded copy of a 16-bit operand: rows x cols values with row stride lds
+// into rows of ldd (a multiple of 8) values, zeros past cols.
+struct Pad16 {
+    const void* src;
+    long long lds;
+    void* dst;
+    long long ldd, rows, cols;
+};
+hipError_t launch_pad16(const Pad16& a, const Pad16& b, hipStream_t s);
 // A representative kernel symbol for loadability checks.
 const void* probe_kernel();
 
