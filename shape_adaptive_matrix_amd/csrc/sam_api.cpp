@@ -402,6 +402,18 @@ sam_status ex_layout(int dtype, int ta, int tb, long long M, long long N, long l
             return SAM_OK;
         }
     }
+    // A 16-bit ring tile with no form for A given transposed (192 rows: an
+    // A^T row is not whole 1 KB loads) gives way to the same schedule on
+    // 256-row tiles, which reads A^T straight instead of packing it.
+    if (!f && L->product && ta && L->plan.kind == sam::KIND_DMA &&
+        !sam::dma_has_layout(L->plan.variant_id, tb ? 3 : 2, dtype)) {
+        const int twin = sam::tile256_twin(L->plan.variant_id);
+        sam::Plan q{};
+        if (twin >= 0 && (sam::plan_for_variant(twin, M, N, K, dtype, L->plan.sk ? -1 : L->plan.split, &q,
+                                                L->plan.raster_n) ||
+                          sam::plan_for_variant(twin, M, N, K, dtype, 0, &q, L->plan.raster_n)))
+            L->plan = q;
+    }
     // A 16-bit ring plan that has to read C (beta != 0) takes the operand-swap
     // form of its variant when there is one: the same tile and schedule, with
     // C read and written 16 bytes per lane instead of 4.

@@ -141,6 +141,9 @@ int k_stage(const Variant& v, int dtype);   // K per LDS stage
 // The operand-swap form of a variant (same tile and schedule, 16-byte
 // stores and loads of C), or -1.
 int swap_twin(int id);
+// The 16-bit ring variant with the same schedule on 256-row tiles (for a
+// tile that has no A-given-transposed form), or -1.
+int tile256_twin(int id);
 
 // Kernel launchers (sam_kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s);

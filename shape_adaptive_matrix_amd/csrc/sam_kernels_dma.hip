@@ -35,7 +35,8 @@ constexpr KernelFn ring16_sk()
     SAM_DMA_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, 0, gm, xr, ms, e16)
 
 static const DmaKernels kDmaTable[] = {SAM_DMA_VARIANTS(SAM_DMA_ENTRY0) SAM_DMA16_VARIANTS(SAM_DMA_ENTRY0)
-                                           SAM_DMA16S_VARIANTS(SAM_DMA_ENTRY)};
+                                           SAM_DMA16S_VARIANTS(SAM_DMA_ENTRY)
+                                               SAM_DMA16M_VARIANTS(SAM_DMA_ENTRY)};
 
 static const DmaKernels* dma_entry(int id)
 {

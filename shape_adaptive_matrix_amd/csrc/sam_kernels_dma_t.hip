@@ -18,7 +18,8 @@ struct DmaTKernels {
 template <int DT, int BM, int BN, int WM, int WN, int BK, int NBUF, int MODE, int BLK, int SWAP, bool SK>
 constexpr KernelFn ring16_t()
 {
-    if constexpr (BLK == 16) {
+    constexpr bool ATR = MODE == 4 || MODE == 5;   // A^T rows: BM must be whole 1 KB loads
+    if constexpr (BLK == 16 && (!ATR || BM == 128 || BM == 256)) {
         if constexpr (SK)
             return gemm16_dma_sk_kernel<DT, BM, BN, WM, WN, BK, NBUF, MODE, BLK, SWAP>;
         else
@@ -45,7 +46,8 @@ constexpr KernelFn ring16_t()
 #define SAM_DMA_T_IF16(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, gm, xr, ms, e16) \
     SAM_DMA_T_ENTRY0(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, gm, xr, ms, e16)
 
-const DmaTKernels kDmaTTable[] = {SAM_DMA16_VARIANTS(SAM_DMA_T_IF16) SAM_DMA16S_VARIANTS(SAM_DMA_T_ENTRY)};
+const DmaTKernels kDmaTTable[] = {SAM_DMA16_VARIANTS(SAM_DMA_T_IF16) SAM_DMA16S_VARIANTS(SAM_DMA_T_ENTRY)
+                                      SAM_DMA16M_VARIANTS(SAM_DMA_T_ENTRY)};
 
 }  // namespace
 

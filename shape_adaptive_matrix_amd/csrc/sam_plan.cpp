@@ -65,7 +65,8 @@ static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_
                                         SAM_STREAM_VARIANTS(SAM_STREAM_ROW) SAM_F32RING_VARIANTS(SAM_F32RING_ROW)
                                             SAM_MX8_VARIANTS(SAM_MX8_ROW) SAM_DMA16_VARIANTS(SAM_DMA_ROW)
                                                 SAM_KQ_VARIANTS(SAM_KQ_ROW) SAM_KP_VARIANTS(SAM_KP_ROW)
-                                                    SAM_KQ8_VARIANTS(SAM_KQ_ROW) SAM_DMA16S_VARIANTS(SAM_DMA_ROWS)};
+                                                    SAM_KQ8_VARIANTS(SAM_KQ_ROW) SAM_DMA16S_VARIANTS(SAM_DMA_ROWS)
+                                                        SAM_DMA16M_VARIANTS(SAM_DMA_ROWS)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -84,6 +85,19 @@ int swap_twin(int id)
     snprintf(want, sizeof want, "%s_sw", v->name);
     for (int i = 0; i < kVariantCount; ++i)
         if (strcmp(kVariants[i].name, want) == 0) return i;
+    return -1;
+}
+
+int tile256_twin(int id)
+{
+    const Variant* v = variant_get(id);
+    if (!v || v->kind != KIND_DMA) return -1;
+    for (int i = 0; i < kVariantCount; ++i) {
+        const Variant& w = kVariants[i];
+        if (w.kind == KIND_DMA && w.bm == 256 && w.bn == v->bn && w.wm == v->wm && w.wn == v->wn && w.bk == v->bk &&
+            w.nbuf == v->nbuf && w.blk == v->blk && w.swap == v->swap)
+            return i;
+    }
     return -1;
 }
 

@@ -118,3 +118,13 @@
     D(56, "r256x256_w2x4_k64n2_b16_sw", 256, 256, 2, 4, 64, 2, 0, 16, 1, 8, 1, 8, 0.575)  \
     D(57, "r256x256_w4x2_k64n2_b16_sw", 256, 256, 4, 2, 64, 2, 0, 16, 1, 8, 1, 8, 0.57)  \
     D(58, "r128x128_w2x2_k64n2_b16_sw", 128, 128, 2, 2, 64, 2, 0, 16, 1, 8, 1, 16, 0.34)
+
+// 192-row tiles of the 16x16x32 ring (same list format as SAM_DMA16S_VARIANTS):
+// for shapes whose 256-row tile count leaves a large part of the CUs idle or
+// adds a partial round (M = 2049: nine 256-row tiles, the last holding one
+// row; M = 6144: 32 row tiles instead of 24), three quarters of the work per
+// workgroup in more workgroups. A 192-row tile is not a power of two, so it
+// has no transposed-A form (its A^T rows would not be whole 1 KB loads).
+#define SAM_DMA16M_VARIANTS(D)                                                           \
+    D(59, "r192x256_w2x4_k64n2_b16", 192, 256, 2, 4, 64, 2, 0, 16, 0, 8, 1, 8, 0.55)    \
+    D(60, "r192x256_w2x4_k64n2_b16_sw", 192, 256, 2, 4, 64, 2, 0, 16, 1, 8, 1, 8, 0.545)

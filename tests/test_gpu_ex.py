@@ -157,8 +157,8 @@ FUSED = [
     ("bf16", (256, 384, 3072), True, False, 0, 0, 8, 1.0, 1.0, "bf16_r", "s12"),
     ("f16", (640, 1792, 256), False, True, 0, 0, 4, -2.0, 0.5, "f16_r", "s1"),
     # beta != 0 on a 16x16x32 plan: its operand-swap form reads and writes C
-    ("bf16", (2560, 3072, 256), False, False, 8, 8, 4, 0.5, 1.0, "bf16_r256x256", "s1"),
-    ("f16", (2560, 3072, 256), True, True, 0, 0, 4, -1.0, 0.25, "f16_r256x256", "s1"),
+    ("bf16", (2560, 3072, 256), False, False, 8, 8, 4, 0.5, 1.0, "bf16_r", "b16_s1"),
+    ("f16", (2560, 3072, 256), True, True, 0, 0, 4, -1.0, 0.25, "f16_r", "b16_s1"),
 ]
 
 
@@ -199,23 +199,22 @@ def test_ex_fused_epilogue_on_ring_plans(case):
     assert np.all(got[:, N:] == 12345.0)
 
 
-# The 16-bit stream-K and operand-swap forms at the sizes that take them:
-# the product against the oracle's plain GEMM of the compact operands,
-# then alpha P + beta C0 (exact here: small integers, dyadic alpha / beta).
-# Both calls read C (beta != 0), so the 16x16x32 plans run as their
-# operand-swap twins: stream-K with the fix-up at 6144^3, data-parallel with
-# K = 11008.
-@pytest.mark.parametrize("dtype,shape,form", [("bf16", (6144, 6144, 6144), "_sk"),
-                                              ("f16", (4096, 4096, 11008), "_r256x256_")])
-def test_ex_fused_epilogue_16bit_stream_k_and_swap(dtype, shape, form):
+# The operand-swap forms of the 16-bit ring (the ones a call that reads C
+# runs) at full size, in their stream-K form with the fix-up at 6144^3 and
+# data-parallel with K = 11008: the product against the oracle's plain GEMM
+# of the compact operands, then alpha P + beta C0 (exact here: small
+# integers, dyadic alpha / beta).
+@pytest.mark.parametrize("dtype,shape,split", [("bf16", (6144, 6144, 6144), -1), ("f16", (4096, 4096, 11008), 1)])
+def test_ex_fused_epilogue_16bit_stream_k_and_swap(dtype, shape, split):
     M, N, K = shape
-    plan = sam.plan(M, N, K, dtype)
-    assert form in plan["name"], plan["name"]
+    vid = next(v for v in range(sam.variant_count()) if sam.variant_info(v)["name"] == "r256x256_w2x4_k64n2_b16_sw")
+    plan = sam.variant_plan(vid, M, N, K, dtype, split)
+    assert plan["operand_swap"] == 1 and (plan["name"].endswith("_sk") if split < 0 else "_s1" in plan["name"])
     alpha, beta = 0.5, -1.0
     Av, Bv, C0, lda, ldb, ldc = _fused_case(dtype, M, N, K, False, False, 8, 16, 4, alpha, beta, 5)
     Cd = torch.from_numpy(C0.copy()).cuda()
     sam.gemm_ex(_dev(dtype, _enc(dtype, Av))[:, :K], _dev(dtype, _enc(dtype, Bv))[:, :N], Cd[:, :N],
-                alpha=alpha, beta=beta)
+                alpha=alpha, beta=beta, variant=vid, split=split)
     torch.cuda.synchronize()
     got = Cd.cpu().numpy()
     P = orc().gemm(dtype, np.ascontiguousarray(_enc(dtype, Av)[:, :K]), np.ascontiguousarray(_enc(dtype, Bv)[:, :N]),
@@ -229,7 +228,7 @@ def test_ex_fused_epilogue_16bit_stream_k_and_swap(dtype, shape, form):
 # values, or both) read straight by every 16x16x32 ring variant, in its
 # data-parallel, split-K and stream-K forms (forced plans), with ragged M,
 # strided rows, ldc and alpha / beta. No packed copy: the workspace is the
-# plan's own.
+# plan's own (192-row tiles read a transposed B straight and pack A^T).
 RING16_B16 = [v for v in range(sam.variant_count())
               if sam.variant_info(v)["name"].startswith("r") and "_b16" in sam.variant_info(v)["name"]]
 NT_SHAPES = [(300, 520, 264), (1000, 776, 1032)]
@@ -250,8 +249,11 @@ def test_ex_transposed_operands_read_straight(dtype, ta, tb, vid):
             pa = (8 - M % 8) if ta else 8          # transposed A: rows of lda % 8 == 0 values
             Av, Bv, C0, lda, ldb, ldc = _fused_case(dtype, M, N, K, ta, tb, pa, 8, 4, alpha, beta,
                                                     M + N + vid + 3 * split + 5 * ta)
-            assert sam.ex_workspace_bytes(M, N, K, ta, tb, lda, ldb, ldc, alpha, beta, dtype, variant=vid,
-                                          split=split) == p["workspace_bytes"]
+            ws = sam.ex_workspace_bytes(M, N, K, ta, tb, lda, ldb, ldc, alpha, beta, dtype, variant=vid, split=split)
+            if ta and sam.variant_info(vid)["tile_m"] not in (128, 256):
+                assert ws > p["workspace_bytes"]   # no A^T form for this tile: A is packed first
+            else:
+                assert ws == p["workspace_bytes"]
             print(f"[tr] variant {vid} {dtype} {'T' if ta else 'N'}{'T' if tb else 'N'} {(M, N, K)} split {split}",
                   flush=True)
             ca, cb = (M if ta else K), (K if tb else N)
@@ -274,7 +276,7 @@ def test_ex_transposed_random_repeatable(ta, tb):
     rel_rms within 1e-5 of the oracle (exact products, FP32 sums), and
     bitwise the same twice."""
     M, N, K = 2560, 3072, 256
-    assert sam.plan(M, N, K, "bf16")["name"].startswith("bf16_r256x256")
+    assert sam.plan(M, N, K, "bf16")["name"].startswith("bf16_r")
     assert sam.ex_workspace_bytes(M, N, K, ta, tb, M if ta else K, K if tb else N, N, 1.0, 0.0, "bf16") == 0
     rng = np.random.default_rng(11 + 2 * ta + tb)
     A = si.normal16(rng, (M, K), "bf16")
