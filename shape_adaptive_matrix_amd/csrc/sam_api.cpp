@@ -168,14 +168,15 @@ struct ExTail {
     bool ct;   // the product (M x N here) goes to C transposed: C is N rows of M values with stride ldc
 };
 
-// Whether a plan can take A rows with stride lda != K in place: a 16-bit
-// ring plan whose rows stay 16-byte pieces or which copies A into padded
-// rows anyway (the copy reads any stride); an FP32 ring plan whose rows stay
-// 16-byte pieces or which reads A one value at a time. Likewise B.
+// Whether a plan can take A rows with stride lda != K in place: a ring plan
+// whose rows stay 16-byte pieces or which copies A into padded rows anyway
+// (the copy reads any stride), or an FP32 ring plan which reads A one value
+// at a time. Likewise B.
 bool reads_strided(const sam::Plan& p, bool a_side, long long ld)
 {
     if (p.kind == sam::KIND_DMA) return (a_side ? p.pad_a : p.pad_b) || ld % 8 == 0;
-    if (p.kind == sam::KIND_F32RING) return !(a_side ? p.a_vec : p.b_vec) || ld % 4 == 0;
+    if (p.kind == sam::KIND_F32RING)
+        return (a_side ? p.pad_a : p.pad_b) || !(a_side ? p.a_vec : p.b_vec) || ld % 4 == 0;
     return false;
 }
 
@@ -258,15 +259,16 @@ sam_status run(const sam::Plan& p, const void* A, const void* B, float* C, long 
     if (K == 0) {
         e = sam::launch_zero(C, M * N, s);
     } else {
-        // 16-bit operands whose rows are not whole 16-byte pieces: padded
-        // copies in front of the plan's own workspace.
+        // Operands whose rows are not whole 16-byte pieces, on a plan that
+        // pads them (16-bit ring plans always, FP32 ring plans of a padding
+        // variant): padded copies in front of the plan's own workspace.
         char* wsb = static_cast<char*>(ws);
         if (p.pad_a || p.pad_b) {
-            sam::Pad16 pa{}, pb{};
-            char* bb = wsb + (p.pad_a ? ((unsigned long long)(M * p.lda) * 2ull + 255ull) & ~255ull : 0ull);
+            sam::PadCopy pa{}, pb{};
+            char* bb = wsb + (p.pad_a ? ((unsigned long long)(M * p.lda) * es + 255ull) & ~255ull : 0ull);
             if (p.pad_a) pa = {A, lda, wsb, p.lda, M, K};
             if (p.pad_b) pb = {B, ldb, bb, p.ldb, K, N};
-            e = sam::launch_pad16(pa, pb, s);
+            e = sam::launch_pad(pa, pb, (int)es, s);
             if (p.pad_a) A = wsb;
             if (p.pad_b) B = bb;
         }

@@ -53,6 +53,7 @@ struct Variant {
     double eff_h16;
     double eff_mx8;      // block-scaled 8-bit variants
     double eff_mx4;      // ... running E2M1 elements
+    int pad;             // FP32 ring: takes rows that are not whole 16-byte pieces through padded copies
 };
 
 int variant_count();
@@ -105,6 +106,7 @@ struct Plan {
     int group_m;
     int xcd_remap;
     int a_vec, b_vec;
+    int c_vec;           // FP32 ring: C rows are whole 16-byte pieces (N % 4 == 0), stored 16 bytes at a time
     int tiles_m, tiles_n;
     long long grid;
     unsigned long long ws_bytes;
@@ -175,15 +177,17 @@ hipError_t launch_axpby(const float* T, long long ldt, float* C, long long ldc, 
                         float beta, hipStream_t s);
 // 16-bit rows x cols (row stride lds elements) into dst with row stride ldd
 // (a multiple of 8, dst 16-byte aligned), zeros in columns cols .. ldd - 1.
-// One padded copy of a 16-bit operand: rows x cols values with row stride lds
-// into rows of ldd (a multiple of 8) values, zeros past cols.
-struct Pad16 {
+// One padded copy of an operand: rows x cols values of es bytes (2 or 4)
+// with row stride lds into rows of ldd values (ldd es a multiple of 16),
+// zeros past cols.
+struct PadCopy {
     const void* src;
     long long lds;
     void* dst;
     long long ldd, rows, cols;
 };
-hipError_t launch_pad16(const Pad16& a, const Pad16& b, hipStream_t s);
+// Both operands' copies in one launch; a copy with no rows is skipped.
+hipError_t launch_pad(const PadCopy& a, const PadCopy& b, int es, hipStream_t s);
 // A representative kernel symbol for loadability checks.
 const void* probe_kernel();
 

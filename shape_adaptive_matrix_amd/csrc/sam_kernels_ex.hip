@@ -43,29 +43,32 @@ pack_kernel(const T* __restrict__ in, long long ld, T* __restrict__ out, long lo
     }
 }
 
-// dst[r][c] = c < cols ? src[r][c] : 0 for 16-bit values, c < ldd: the
-// copy of an operand whose rows are not whole 16-byte pieces into rows that
-// are (ldd a multiple of 8, dst 16-byte aligned), so the ring kernel can load
-// it 16 bytes at a time. One thread per 16-byte piece of dst. The source
-// piece starts at any 2-byte boundary: the thread reads the two aligned
-// 16-byte blocks around it (the second only while it starts inside the
-// source; src is 16-byte aligned) and shifts the 16 bytes out of them.
+// dst[r][c] = c < cols ? src[r][c] : 0 for c < ldd, values of ES bytes (2
+// or 4): the copy of an operand whose rows are not whole 16-byte pieces into
+// rows that are (ldd ES a multiple of 16, dst 16-byte aligned), so the ring
+// kernels can load it 16 bytes at a time. One thread per 16-byte piece of
+// dst. The source piece starts at any ES-byte boundary: the thread reads the
+// two aligned 16-byte blocks around it (the second only while it starts
+// inside the source; src is 16-byte aligned) and shifts the 16 bytes out of
+// them.
 __device__ __forceinline__ unsigned pick4(int d, unsigned a, unsigned b, unsigned c, unsigned e)
 {
     return d == 0 ? a : (d == 1 ? b : (d == 2 ? c : e));
 }
 
-__device__ __forceinline__ void pad16_piece(const Pad16& p, long long e)
+template <int ES>
+__device__ __forceinline__ void pad_piece(const PadCopy& p, long long e)
 {
     typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    const long long per_row = p.ldd / 8;
-    const long long ext = ((p.rows - 1) * p.lds + p.cols) * 2;   // bytes of src that belong to the operand
+    constexpr int PER = 16 / ES;   // values per 16-byte piece
+    const long long per_row = p.ldd / PER;
+    const long long ext = ((p.rows - 1) * p.lds + p.cols) * ES;   // bytes of src that belong to the operand
     const char* sb = static_cast<const char*>(p.src);
-    const long long r = e / per_row, c0 = (e - r * per_row) * 8;
+    const long long r = e / per_row, c0 = (e - r * per_row) * PER;
     u4 out = {0u, 0u, 0u, 0u};
     if (c0 < p.cols) {
-        const long long b = (r * p.lds + c0) * 2, a = b & ~15ll;
-        const int sh = (int)(b & 15);   // even
+        const long long b = (r * p.lds + c0) * ES, a = b & ~15ll;
+        const int sh = (int)(b & 15);   // a multiple of ES
         const u4 w0 = *reinterpret_cast<const u4*>(sb + a);
         const u4 w1 = a + 16 < ext ? *reinterpret_cast<const u4*>(sb + a + 16) : u4{0u, 0u, 0u, 0u};
         const unsigned W[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
@@ -73,30 +76,39 @@ __device__ __forceinline__ void pad16_piece(const Pad16& p, long long e)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const unsigned lo = pick4(d, W[q], W[q + 1], W[q + 2], W[q + 3]);
-            const unsigned hi = pick4(d, W[q + 1], W[q + 2], W[q + 3], W[q + 4]);
-            out[q] = (sh & 2) ? (lo >> 16) | (hi << 16) : lo;
+            if constexpr (ES == 2) {
+                const unsigned hi = pick4(d, W[q + 1], W[q + 2], W[q + 3], W[q + 4]);
+                out[q] = (sh & 2) ? (lo >> 16) | (hi << 16) : lo;
+            } else {
+                out[q] = lo;
+            }
         }
-        if (c0 + 8 > p.cols) {   // the row's last piece: values past cols are zero
+        if (c0 + PER > p.cols) {   // the row's last piece: values past cols are zero
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (c0 + 2 * q >= p.cols) out[q] = 0u;
-                else if (c0 + 2 * q + 1 >= p.cols) out[q] &= 0xFFFFu;
+                if constexpr (ES == 2) {
+                    if (c0 + 2 * q >= p.cols) out[q] = 0u;
+                    else if (c0 + 2 * q + 1 >= p.cols) out[q] &= 0xFFFFu;
+                } else {
+                    if (c0 + q >= p.cols) out[q] = 0u;
+                }
             }
         }
     }
-    *reinterpret_cast<u4*>(static_cast<unsigned short*>(p.dst) + r * p.ldd + c0) = out;
+    *reinterpret_cast<u4*>(static_cast<char*>(p.dst) + (r * p.ldd + c0) * ES) = out;
 }
 
-// Both operands' copies in one launch (a job with no rows is skipped).
-__global__ void __launch_bounds__(256) pad16_kernel(Pad16 a, Pad16 b)
+template <int ES>
+__global__ void __launch_bounds__(256) pad_kernel(PadCopy a, PadCopy b)
 {
-    const long long ta = a.rows * (a.ldd / 8), total = ta + b.rows * (b.ldd / 8);
+    constexpr int PER = 16 / ES;
+    const long long ta = a.rows * (a.ldd / PER), total = ta + b.rows * (b.ldd / PER);
     const long long step = (long long)gridDim.x * blockDim.x;
     for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += step) {
         if (e < ta)
-            pad16_piece(a, e);
+            pad_piece<ES>(a, e);
         else
-            pad16_piece(b, e - ta);
+            pad_piece<ES>(b, e - ta);
     }
 }
 
@@ -122,13 +134,18 @@ axpby_kernel(const float* T, long long ldt, float* C, long long ldc, long long M
 
 }  // namespace
 
-hipError_t launch_pad16(const Pad16& a, const Pad16& b, hipStream_t s)
+hipError_t launch_pad(const PadCopy& a, const PadCopy& b, int es, hipStream_t s)
 {
-    const long long total = a.rows * (a.ldd / 8) + b.rows * (b.ldd / 8);
+    if (es != 2 && es != 4) return hipErrorInvalidValue;
+    const int per = 16 / es;
+    const long long total = a.rows * (a.ldd / per) + b.rows * (b.ldd / per);
     long long blocks = (total + 255) / 256;
     if (blocks > 16384) blocks = 16384;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(pad16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, b);
+    if (es == 2)
+        hipLaunchKernelGGL(pad_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, a, b);
+    else
+        hipLaunchKernelGGL(pad_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, a, b);
     return hipGetLastError();
 }
 

@@ -84,7 +84,8 @@ constexpr int ring_lds_bytes() { return NBUF * (BM + BN) * BK * 4; }
 // direct-to-LDS loads address it without a generic-to-LDS conversion. SEG: the tile's result goes to `outp` (row
 // stride `ostride` floats), of which `orows` x `ocols` are stored; otherwise
 // to C or to the partial slice of split `ostride`.
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool SEG>
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC,
+          bool SEG>
 __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int tn, int kbeg, int kend, float* outp,
                                              int ostride, int orows, int ocols, bool to_c)
 {
@@ -397,7 +398,7 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
 #pragma unroll
                     for (int r = 0; r < MF::N; ++r) {
                         const int row = wm0 + BLK * (IB + ii) + MF::row(lane, r);
-                        if constexpr (ELB) {
+                        if constexpr (ELB || ELC) {
                             // Rows need not be 16-byte pieces: one float per
                             // store, each column checked against N.
 #pragma unroll
@@ -475,7 +476,7 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
 
 // Data-parallel form: one workgroup per (tile, split); split s covers K
 // values [s k_chunk, (s + 1) k_chunk) and writes C or its partial slice.
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB>
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC>
 __global__ void __launch_bounds__(WM * WN * KS * 64)
 __attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / ring_lds_bytes<BM, BN, BK, NBUF>()) * WM * WN * KS + 3) / 4)))
 gemm_f32_ring_kernel(GemmArgs args)
@@ -485,7 +486,8 @@ gemm_f32_ring_kernel(GemmArgs args)
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = s * args.k_chunk;
     const int kend = min(args.K, kbeg + args.k_chunk);
-    ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, false>(args, tm, tn, kbeg, kend, nullptr, s, 0, 0,
+    ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false>(args, tm, tn, kbeg, kend, nullptr, s, 0,
+                                                                            0,
                                                                        true);
 }
 
@@ -501,7 +503,7 @@ gemm_f32_ring_kernel(GemmArgs args)
 // range order. Ranges are numbered by logical workgroup (each XCD holds
 // consecutive ranges). The split points depend only on the plan, so the
 // result does not depend on timing.
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB>
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC>
 __global__ void __launch_bounds__(WM * WN * KS * 64)
 __attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / ring_lds_bytes<BM, BN, BK, NBUF>()) * WM * WN * KS + 3) / 4)))
 gemm_f32_ring_sk_kernel(GemmArgs args)
@@ -527,7 +529,7 @@ gemm_f32_ring_sk_kernel(GemmArgs args)
         const bool whole = k0 == 0 && k1 == I;
         float* outp = whole ? args.out + (args.ct ? (long long)n0 * args.ldc + m0 : (long long)m0 * args.ldc + n0)
                             : args.ws + (2 * g + (first ? 0 : 1)) * (long long)(BM * BN);
-        ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, true>(
+        ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, true>(
             args, tm, tn, kbeg, kend, outp, whole ? args.ldc : BN, whole ? args.M - m0 : BM,
             whole ? args.N - n0 : BN, whole);
         it += k1 - k0;
@@ -541,19 +543,24 @@ typedef void (*F32RingFn)(GemmArgs);
 constexpr int kSkMaxTile = 128 * 256;
 
 // A kernel of the table: data-parallel or stream-K (SK), each operand in
-// 16-byte or element form. The element forms exist only for variants that
-// have them (EL = 1 in the table): they need four times the loads in flight,
-// and their address arithmetic costs registers that the largest tiles do not
-// have to spare.
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, int EL, bool ELA, bool ELB, bool SK>
+// 16-byte or element form, C stored 16 bytes or one value at a time (ELC:
+// its rows are not 16-byte pieces; always so with an element-form B, whose
+// rows are C's length). The element forms exist only for variants that have
+// them (EL = 1 in the table): they need four times the loads in flight, and
+// their address arithmetic costs registers that the largest tiles do not
+// have to spare. The padding forms (EL = 2) load both operands 16 bytes at a
+// time (from padded copies where need be) and store C either way.
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, int EL, bool ELA, bool ELB, bool ELC,
+          bool SK>
 constexpr F32RingFn ring_kernel() {
-    if constexpr ((EL != 0 || (!ELA && !ELB)) && (!SK || BM * BN <= kSkMaxTile)) {
+    constexpr bool form = EL == 2 ? (!ELA && !ELB) : (ELC == ELB && (EL != 0 || (!ELA && !ELB)));
+    if constexpr (form && (!SK || BM * BN <= kSkMaxTile)) {
         static_assert((NBUF - 1) * (((BM + BN) * BK * 4 / 1024) / (WM * WN * KS) * (ELA || ELB ? 4 : 1)) < 64,
                       "loads in flight must stay countable");
         if constexpr (SK)
-            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB>;
+            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC>;
         else
-            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB>;
+            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC>;
     } else {
         return nullptr;
     }
@@ -561,32 +568,39 @@ constexpr F32RingFn ring_kernel() {
 
 struct F32RingKernel {
     int id;
-    F32RingFn fn[2][2][2];   // [stream-K][a_vec][b_vec]: 16-byte loads for an operand whose rows are 16-byte pieces
+    F32RingFn fn[2][2][2][2];   // [stream-K][a_vec][b_vec][c_vec]: 16-byte pieces (1) or one value at a time (0)
     F32RingFn fixup;
     int fixup_wgs;   // fix-up workgroups per tile
     int threads;
 };
 
+#define SAM_F32RING_CSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, A, B, SK)            \
+    {ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, A, B, true, SK>(),             \
+     ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, A, B, false, SK>()}
 #define SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, SK)                              \
-    {{ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, true, SK>(),                     \
-      ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, false, SK>()},                   \
-     {ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false, true, SK>(),                    \
-      ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false, false, SK>()}}
+    {{SAM_F32RING_CSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, true, SK),                  \
+      SAM_F32RING_CSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true, false, SK)},                \
+     {SAM_F32RING_CSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false, true, SK),                 \
+      SAM_F32RING_CSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false, false, SK)}}
 
 #define SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32)      \
     {id,                                                                                         \
      {SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false),                          \
       SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true)},                          \
      sk_fixup_kernel<BM, BN>, sk_fixup_wgs<BM, BN>(), WM * WN * KS * 64},
+// The padding forms: the same kernels, EL 2.
+#define SAM_F32PAD_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32) \
+    SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, 2, gm, xr, ms, e32)
 
-static const F32RingKernel kF32RingTable[] = {SAM_F32RING_VARIANTS(SAM_F32RING_ENTRY)};
+static const F32RingKernel kF32RingTable[] = {SAM_F32RING_VARIANTS(SAM_F32RING_ENTRY)
+                                                  SAM_F32PAD_VARIANTS(SAM_F32PAD_ENTRY)};
 
 hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s)
 {
     for (const F32RingKernel& k : kF32RingTable) {
         if (k.id != p.variant_id) continue;
         if (p.dtype != DT_F32) return hipErrorInvalidDeviceFunction;
-        const F32RingFn fn = k.fn[p.sk ? 1 : 0][p.a_vec ? 1 : 0][p.b_vec ? 1 : 0];
+        const F32RingFn fn = k.fn[p.sk ? 1 : 0][p.a_vec ? 1 : 0][p.b_vec ? 1 : 0][p.c_vec ? 1 : 0];
         if (!fn) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(k.threads), 0, s, a);
         return hipGetLastError();

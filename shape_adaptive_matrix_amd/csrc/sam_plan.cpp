@@ -52,6 +52,10 @@ namespace sam {
 #define SAM_F32RING_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32) \
     {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, BLK, NBUF, BK, gm, xr, ms, EL, 0, e32, 0.0},
 
+#define SAM_F32PAD_ROW(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32)                   \
+    {id, name, KIND_F32RING, (1 << DT_F32), BM, BN, WM, WN * KS, BLK, NBUF, BK, gm, xr, ms, 0, 0, e32, 0.0, 0.0, 0.0, \
+     1},
+
 #define SAM_MX8_ROW(id, name, BM, BN, WM, WN, BK, SD, gm, xr, ms, e8, e4) \
     {id, name, KIND_MX8, (1 << DT_MX8) | (1 << DT_MX4), BM, BN, WM, WN, 32, 2, BK, gm, xr, ms, 0, 0, 0.0, 0.0, e8, e4},
 
@@ -66,7 +70,8 @@ static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_
                                             SAM_MX8_VARIANTS(SAM_MX8_ROW) SAM_DMA16_VARIANTS(SAM_DMA_ROW)
                                                 SAM_KQ_VARIANTS(SAM_KQ_ROW) SAM_KP_VARIANTS(SAM_KP_ROW)
                                                     SAM_KQ8_VARIANTS(SAM_KQ_ROW) SAM_DMA16S_VARIANTS(SAM_DMA_ROWS)
-                                                        SAM_DMA16M_VARIANTS(SAM_DMA_ROWS)};
+                                                        SAM_DMA16M_VARIANTS(SAM_DMA_ROWS)
+                                                            SAM_F32PAD_VARIANTS(SAM_F32PAD_ROW)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -238,34 +243,38 @@ static bool split_admissible(const Variant& v, long long K, int dtype, int split
 
 static unsigned long long align256(unsigned long long x) { return (x + 255ull) & ~255ull; }
 
-// The 16-bit ring kernels load whole 16-byte pieces of A and B rows. When K
-// (A's rows) or N (B's rows) is not a multiple of 8, that operand is first
-// copied into the workspace with its row stride rounded up to a multiple of
-// 8 and zeros in the gap; the kernel reads the copy, whose K and N tails it
-// masks as always. C is written in place. p->ws_bytes holds the plan's own
-// workspace on entry; the copies go in front of it.
+// The 16-bit ring kernels, and the FP32 ring kernels of the padding forms,
+// load whole 16-byte pieces of A and B rows. When K (A's rows) or N (B's
+// rows) is not a multiple of 8 (16-bit) or 4 (FP32), that operand is first
+// copied into the workspace with its row stride rounded up to such a
+// multiple and zeros in the gap; the kernel reads the copy, whose K and N
+// tails it masks as always. C is written in place. p->ws_bytes holds the
+// plan's own workspace on entry; the copies go in front of it.
 static void apply_pad(const Variant& v, long long M, long long N, long long K, Plan* p)
 {
     p->pad_a = p->pad_b = 0;
     p->lda = K;
     p->ldb = N;
     p->ws_inner = 0;
-    if (v.kind != KIND_DMA || (K % 8 == 0 && N % 8 == 0)) return;
-    p->pad_a = K % 8 != 0;
-    p->pad_b = N % 8 != 0;
-    p->lda = p->pad_a ? (K + 7) / 8 * 8 : K;
-    p->ldb = p->pad_b ? (N + 7) / 8 * 8 : N;
+    if (v.kind != KIND_DMA && !v.pad) return;
+    const long long q = v.kind == KIND_DMA ? 8 : 4;          // values per 16-byte piece
+    const unsigned long long es = v.kind == KIND_DMA ? 2 : 4;
+    if (K % q == 0 && N % q == 0) return;
+    p->pad_a = K % q != 0;
+    p->pad_b = N % q != 0;
+    p->lda = p->pad_a ? (K + q - 1) / q * q : K;
+    p->ldb = p->pad_b ? (N + q - 1) / q * q : N;
     unsigned long long off = 0;
-    if (p->pad_a) off = align256((unsigned long long)(M * p->lda) * 2ull);
-    if (p->pad_b) off = align256(off + (unsigned long long)(K * p->ldb) * 2ull);
+    if (p->pad_a) off = align256((unsigned long long)(M * p->lda) * es);
+    if (p->pad_b) off = align256(off + (unsigned long long)(K * p->ldb) * es);
     p->ws_inner = off;
     p->ws_bytes += off;
-    // The copies read the operand one value at a time (about half the
-    // streaming rate) and write it 16 bytes at a time; one launch each.
+    // One launch reads each copied operand once and writes its copy, 16
+    // bytes at a time, at about half the streaming rate of a plain copy.
     const double mb = 1e-6;
-    const double bytes_a = p->pad_a ? 2.0 * M * K + 2.0 * M * p->lda : 0.0;
-    const double bytes_b = p->pad_b ? 2.0 * K * N + 2.0 * K * p->ldb : 0.0;
-    p->est_us += (bytes_a + bytes_b) * mb / (0.5 * kDev.hbm_gbs) * 1e3 + (p->pad_a + p->pad_b) * kDev.launch_us;
+    const double bytes_a = p->pad_a ? (double)es * (M * K + M * p->lda) : 0.0;
+    const double bytes_b = p->pad_b ? (double)es * (K * N + K * p->ldb) : 0.0;
+    p->est_us += (bytes_a + bytes_b) * mb / (0.5 * kDev.hbm_gbs) * 1e3 + kDev.launch_us;
 }
 
 static void fill_plan(const Variant& v, long long M, long long N, long long K, int dtype, int split,
@@ -307,7 +316,9 @@ static void fill_plan(const Variant& v, long long M, long long N, long long K, i
     p->sk = 0;
     p->sk_dp = 0;
     p->sk_g = 0;
-    if (v.kind == KIND_DMA) p->a_vec = p->b_vec = 1;   // always 16-byte pieces (of a padded copy if need be)
+    // Always 16-byte pieces (of a padded copy if need be).
+    if (v.kind == KIND_DMA || v.pad) p->a_vec = p->b_vec = 1;
+    p->c_vec = p->b_vec && N % 4 == 0;
     p->est_us = estimate_us(v, M, N, K, dtype, split, p->a_vec, p->b_vec, raster_n);
     apply_pad(v, M, N, K, p);
 }
@@ -433,8 +444,10 @@ bool plan_for_variant(int vid, long long M, long long N, long long K, int dtype,
     // rows must be whole 16-byte pieces.
     if (v->kind == KIND_DMA && v->swap && N % 4 != 0) return false;
     // FP32 ring kernels take rows that are not 16-byte pieces only in their
-    // element-load form, which not every variant has.
-    if (v->kind == KIND_F32RING && (K % 4 != 0 || N % 4 != 0) && !v->elem_loads) return false;
+    // element-load form, which not every variant has, or through padded
+    // copies (the padding forms, which are only for such shapes).
+    if (v->kind == KIND_F32RING && (K % 4 != 0 || N % 4 != 0) && !v->elem_loads && !v->pad) return false;
+    if (v->kind == KIND_F32RING && v->pad && K % 4 == 0 && N % 4 == 0) return false;
     // The single-launch small-tile kernels split K inside the workgroup only,
     // and address A's tile rows and all of B with 32-bit byte offsets.
     // Prefetches run up to 48 values of K past a wave's range (the plan's

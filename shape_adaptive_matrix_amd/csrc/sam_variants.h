@@ -128,3 +128,15 @@
 #define SAM_DMA16M_VARIANTS(D)                                                           \
     D(59, "r192x256_w2x4_k64n2_b16", 192, 256, 2, 4, 64, 2, 0, 16, 0, 8, 1, 8, 0.55)    \
     D(60, "r192x256_w2x4_k64n2_b16_sw", 192, 256, 2, 4, 64, 2, 0, 16, 1, 8, 1, 8, 0.545)
+
+// Padding forms of FP32 ring variants (same list format as
+// SAM_F32RING_VARIANTS; EL 0): for K or N not a multiple of 4 they copy the
+// operand whose rows are not whole 16-byte pieces into the workspace with
+// its rows padded to a multiple of 4 values (zeros in the gap), and run the
+// 16-byte-load kernel on the copy instead of the element-load form. Not
+// admitted when K and N are multiples of 4 (then they are their base
+// variant).
+#define SAM_F32PAD_VARIANTS(F)                                                           \
+    F(61, "f128x128_w4x2_k32n2_b16_pad",   128, 128, 4, 2, 32, 2, 4, 1, 16, 0, 8, 1, 16, 0.88)   \
+    F(62, "f256x256_w4x2_k32n2_b16_pad",   256, 256, 4, 2, 32, 2, 4, 1, 16, 0, 8, 1,  8, 0.95)   \
+    F(63, "f128x128_w2x2s2_k64n2_b16_pad", 128, 128, 2, 2, 64, 2, 4, 2, 16, 0, 8, 1, 16, 0.91)

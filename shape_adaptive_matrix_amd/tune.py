@@ -76,7 +76,8 @@ def candidates(sam, dt, M, N, K):
     own split and raster choice and its stream-K form (split -1) where it has
     one; for the four variants the cost model ranks best, the other raster
     order (M-major 0 / N-major 1) too, and, when their tile count leaves CUs
-    idle, the other admissible splits."""
+    idle (fewer tiles than CUs, or a last round of tiles less than 90% full),
+    the other admissible splits."""
     own = []
     for vid in range(sam.variant_count()):
         try:
@@ -98,7 +99,8 @@ def candidates(sam, dt, M, N, K):
                 out.add((p["variant_id"], p["split_k"], 1 - p["raster_n"]))
             except sam.SamError:
                 pass
-        if p["grid_wgs"] // max(p["split_k"], 1) >= 256:
+        tiles = -(-M // p["tile_m"]) * -(-N // p["tile_n"])
+        if tiles >= 256 and tiles / (256 * -(-tiles // 256)) >= 0.9:
             continue
         for s in SPLITS:
             try:

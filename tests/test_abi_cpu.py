@@ -86,14 +86,20 @@ def _a256(x):
 
 
 def expected_workspace(p, M, N, K, dtype):
-    """Padded 16-bit operand copies (ring kernels with K or N not a multiple
-    of 8), then split-K partials or stream-K slots."""
+    """Padded operand copies (16-bit ring kernels with K or N not a multiple
+    of 8, FP32 padding forms with K or N not a multiple of 4), then split-K
+    partials or stream-K slots."""
     pad = 0
+    q, es = 0, 0
     if dtype in ("bf16", "f16") and p["name"].split("_", 1)[1][0] in "rqh":
-        if K % 8:
-            pad = _a256(M * ((K + 7) // 8 * 8) * 2)
-        if N % 8:
-            pad = _a256(pad + K * ((N + 7) // 8 * 8) * 2)
+        q, es = 8, 2
+    elif dtype == "f32" and "_pad" in p["name"]:
+        q, es = 4, 4
+    if q:
+        if K % q:
+            pad = _a256(M * ((K + q - 1) // q * q) * es)
+        if N % q:
+            pad = _a256(pad + K * ((N + q - 1) // q * q) * es)
     if p["split_k"] > 1:
         return pad + p["split_k"] * M * N * 4
     if p["split_k"] == -1:
@@ -111,10 +117,19 @@ def test_large_d_picks_other_tile_than_2048():
 
 
 def test_alignment_routes():
-    assert sam.plan(4097, 3071, 8191, "f32")["a_vector"] == 0
-    assert sam.plan(4097, 3071, 8191, "f32")["b_vector"] == 0
+    # FP32 ring variants with an element-load form: rows that are not 16-byte
+    # pieces are read one value at a time.
+    p = sam.variant_plan(39, 4097, 3071, 8191, "f32", 4)
+    assert p["a_vector"] == 0 and p["b_vector"] == 0 and p["workspace_bytes"] == 4 * 4097 * 3071 * 4
+    p = sam.variant_plan(38, 8191, 8193, 4096, "f32", 1)
+    assert p["a_vector"] == 1 and p["b_vector"] == 0 and p["workspace_bytes"] == 0
+    # Their padding forms (the measured choice at these sizes) load 16 bytes
+    # at a time from copies with rows padded to multiples of 4 values.
+    p = sam.plan(4097, 3071, 8191, "f32")
+    assert p["name"].startswith("f32_f128x128_w4x2_k32n2_b16_pad_")
+    assert p["a_vector"] == 1 and p["b_vector"] == 1
     p = sam.plan(8191, 8193, 4096, "f32")
-    assert p["a_vector"] == 1 and p["b_vector"] == 0
+    assert "_pad_" in p["name"] and p["workspace_bytes"] == _a256(4096 * 8196 * 4)
     p = sam.plan(64, 64, 68, "bf16")
     assert p["a_vector"] == 0 and p["b_vector"] == 1
 

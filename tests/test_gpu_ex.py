@@ -152,7 +152,7 @@ FUSED = [
     ("f32", (1792, 1792, 256), True, True, 0, 0, 4, 2.0, 0.0, "f32_f", "s1"),
     ("f32", (256, 1536, 3072), False, False, 0, 0, 12, -1.0, 0.25, "f32_f", "s8"),
     ("f32", (2304, 2560, 1536), False, False, 4, 4, 4, 0.5, 2.0, "f32_f", "sk"),
-    ("f32", (2049, 4097, 1025), False, False, 3, 1, 3, 1.0, 1.0, "f32_f", "s3_ua_ub"),
+    ("f32", (2049, 4097, 1025), False, False, 3, 1, 3, 1.0, 1.0, "f32_f", "pad_s3"),
     ("bf16", (640, 1792, 256), False, False, 8, 8, 4, 0.5, -1.0, "bf16_r", "s1"),
     ("bf16", (256, 384, 3072), True, False, 0, 0, 8, 1.0, 1.0, "bf16_r", "s12"),
     ("f16", (640, 1792, 256), False, True, 0, 0, 4, -2.0, 0.5, "f16_r", "s1"),
@@ -195,6 +195,30 @@ def test_ex_fused_epilogue_on_ring_plans(case):
     got = Cd.cpu().numpy()
     ref = orc().gemm_ex(dtype, M, N, K, _enc(dtype, Av), lda, _enc(dtype, Bv), ldb, ta, tb, alpha, beta,
                         np.ascontiguousarray(C0[:, :N]), nthreads=orc().max_threads())
+    assert bitexact_mismatches(got[:, :N], ref) == 0
+    assert np.all(got[:, N:] == 12345.0)
+
+
+# The FP32 ring's element-load forms (rows that are not 16-byte pieces read
+# one value at a time, C stored one value at a time) under the fused
+# epilogue, forced: the dispatcher prefers the padding forms at this size.
+@pytest.mark.parametrize("split", [1, 3, -1])
+def test_ex_fused_epilogue_on_element_forms(split):
+    M, N, K = 2049, 4097, 1025
+    vid = next(v for v in range(sam.variant_count()) if sam.variant_info(v)["name"] == "f128x128_w4x2_k32n2")
+    p = sam.variant_plan(vid, M, N, K, "f32", split)
+    assert p["a_vector"] == 0 and p["b_vector"] == 0, p["name"]
+    alpha, beta = 1.0, 1.0
+    Av, Bv, C0, lda, ldb, ldc = _fused_case("f32", M, N, K, False, False, 3, 1, 3, alpha, beta, 17 + split)
+    assert sam.ex_workspace_bytes(M, N, K, False, False, lda, ldb, ldc, alpha, beta, "f32", variant=vid,
+                                  split=split) == p["workspace_bytes"]
+    Cd = torch.from_numpy(C0.copy()).cuda()
+    sam.gemm_ex(_dev("f32", Av)[:, :K], _dev("f32", Bv)[:, :N], Cd[:, :N], alpha=alpha, beta=beta, variant=vid,
+                split=split)
+    torch.cuda.synchronize()
+    got = Cd.cpu().numpy()
+    ref = orc().gemm_ex("f32", M, N, K, Av, lda, Bv, ldb, False, False, alpha, beta, np.ascontiguousarray(C0[:, :N]),
+                        nthreads=orc().max_threads())
     assert bitexact_mismatches(got[:, :N], ref) == 0
     assert np.all(got[:, N:] == 12345.0)
 
@@ -297,7 +321,7 @@ def test_ex_transposed_random_repeatable(ta, tb):
 # fix-up; element forms where rows are not 16-byte pieces, and a tile edge
 # inside a group of four rows of the product (N odd).
 TT_F32 = [((1792, 1792, 256), "s1"), ((1536, 256, 3072), "s8"), ((2560, 2304, 1536), "sk"),
-          ((4097, 2049, 1025), "s3_ua_ub"), ((3000, 3000, 3001), "_ua")]
+          ((4097, 2049, 1025), "pad_s3"), ((3000, 3000, 3001), "_ua")]
 
 
 @pytest.mark.parametrize("case", TT_F32, ids=lambda c: "x".join(map(str, c[0])))

@@ -77,6 +77,8 @@ def test_every_variant_dyadic_ragged(vid, dtype):
 def test_every_variant_random(vid, dtype):
     M, N, K = 150, 176, 336
     if not _supported(vid, M, N, K, dtype):
+        M, N, K = 150, 174, 333   # rows that are not 16-byte pieces (the padding forms' domain)
+    if not _supported(vid, M, N, K, dtype):
         pytest.skip(f"variant {vid} does not take {dtype}")
     rng = np.random.default_rng(vid + 40)
     if dtype == "f32":

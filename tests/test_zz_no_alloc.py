@@ -22,7 +22,8 @@ pytestmark = pytest.mark.gpu
 # (M, N, K, dtype): split-K and stream-K plans, each pair larger then smaller.
 PAIRS = [
     [(8192, 16, 8192, "f32"), (2048, 16, 8192, "f32")],          # split-K partials, 4 MiB then 1.5 MiB
-    [(2200, 1900, 4095, "f32"), (1500, 3000, 2047, "f32")],      # stream-K slots, 32 MiB each, the second problem smaller
+    [(2200, 1900, 4092, "f32"), (1500, 3000, 2047, "f32")],      # stream-K slots (32 MiB), then a smaller problem
+                                                                 # whose padded copies sit in front of its slots
     [(512, 512, 8192, "bf16"), (64, 1024, 8192, "bf16")],        # 16-bit split-K
     [(64, 1024, 8192, "f16"), (16, 8192, 8192, "f32")],
 ]
