@@ -207,6 +207,16 @@ def profile_kernel_avg_us(workload: str, kernel: str):
     return None
 
 
+def pads(w, plan) -> bool:
+    """Whether the plan copies an operand into padded rows first (16-bit ring
+    plans with K or N not a multiple of 8, FP32 padding forms with K or N not
+    a multiple of 4)."""
+    form = plan["name"].split("_", 1)[1]
+    if w.dtype in ("bf16", "f16") and form[0] in "rqh":
+        return w.K % 8 != 0 or w.N % 8 != 0
+    return "_pad" in form and (w.K % 4 != 0 or w.N % 4 != 0)
+
+
 def roofline_of(w, t_ms: float, plan) -> dict:
     """Roofline record of one timed workload: MFMA-bound for the dense
     shapes (2MNK FLOP against the dtype's peak), HBM-bound for the skinny ones
@@ -223,7 +233,7 @@ def roofline_of(w, t_ms: float, plan) -> dict:
                "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4)}
     rec["traffic"] = None if split else load_traffic(w.name, src_digest(plan))
     rec["kernel"] = kernel_name(plan) + (" + sam::splitk_reduce_kernel" if split else "") + \
-        (" + sam::sk_fixup_kernel" if plan["split_k"] == -1 else "")
+        (" + sam::sk_fixup_kernel" if plan["split_k"] == -1 else "") + (" + sam::pad_kernel" if pads(w, plan) else "")
     if plan["split_k"] == 1:
         prof = profile_kernel_avg_us(w.name, kernel_name(plan))
         if prof is not None:

@@ -59,22 +59,27 @@ def kernel_full_name(pmc_dir, kernel: str) -> str:
 
 def trace_text(kt_dir, workload: str, kernel: str, command: str, bench_json=None) -> str:
     header, rows = kernel_stats(kt_dir)
-    mine = [r for r in rows if kernel in next(csv.reader([r]))[0]]
-    if not mine:
+    cells_of = [next(csv.reader([r])) for r in rows]
+    dom = [c for c in cells_of if kernel in c[0]]
+    if not dom:
         raise KeyError(f"{kernel} not in the kernel trace")
-    cells = next(csv.reader([mine[0]]))
+    cells = dom[0]
+    lib = [(r, c) for r, c in zip(rows, cells_of) if "sam::" in c[0]]   # every kernel of the library's plan
     avg_us = float(cells[3]) / 1e3
+    per_call_us = sum(float(c[2]) for _, c in lib) / float(cells[1]) / 1e3
     short = kernel.rstrip("<").split("::")[-1]
     out = [f"# {short}, {workload} -- kernel trace", "",
            "Command (run from the repository root on one MI355X, ROCm 7.2):", "", f"    {command}", "",
-           "kernel_stats.csv, the rows of this workload's kernels:", "", header, *mine, "",
+           "kernel_stats.csv, the rows of the library's kernels:", "", header, *[r for r, _ in lib], "",
            f"Average duration of {short} under the profiler: {avg_us:.1f} us over {cells[1]} dispatches."]
+    if len(lib) > 1:
+        out.append(f"All of the plan's kernels together: {per_call_us:.1f} us per call.")
     if bench_json:
         d = json.loads(Path(bench_json).read_text().strip().splitlines()[-1])
         ev_us = d["ms_per_step"] * 1e3
         out += [f"The same command without the profiler, HIP events on the launch stream: {ev_us:.1f} us per "
                 f"call ({d['value']:.1f} {d['unit']}, plan {d['config'].get('plan', '?')}).",
-                f"The two differ by {100 * (avg_us - ev_us) / ev_us:+.1f}%."]
+                f"The two differ by {100 * (per_call_us - ev_us) / ev_us:+.1f}%."]
     return "\n".join(out) + "\n"
 
 
