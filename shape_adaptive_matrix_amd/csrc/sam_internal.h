@@ -146,6 +146,9 @@ int swap_twin(int id);
 // The 16-bit ring variant with the same schedule on 256-row tiles (for a
 // tile that has no A-given-transposed form), or -1.
 int tile256_twin(int id);
+// Whether an FP32 ring variant has the form that reads B given transposed
+// (N rows of K values) straight, in its data-parallel or stream-K form.
+bool f32_has_bt(int variant_id, bool stream_k);
 
 // Kernel launchers (sam_kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s);

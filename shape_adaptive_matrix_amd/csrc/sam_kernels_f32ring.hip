@@ -19,6 +19,10 @@
 //    four consecutive K values of one row.
 //  * B sits in LDS in its natural N-contiguous layout and is read V = 4 (or
 //    2) consecutive columns of one K row at a time (128- or 64-bit reads).
+//    B given transposed (BT: N rows of K values, as the general entry point
+//    takes op(B) = B^T) sits K-contiguous like A and is read four
+//    consecutive K values of one column at a time, one read per column of
+//    the V: the same values reach the same MFMAs, gathered the other way.
 //    The 32x32x2 MFMA takes one B value per lane (column lane % 32), so the V
 //    columns feed V MFMAs that each cover every V-th column of a 32 V-column
 //    group: MFMA v produces columns n + V j + v, j < 32. Only the output
@@ -85,7 +89,7 @@ constexpr int ring_lds_bytes() { return NBUF * (BM + BN) * BK * 4; }
 // stride `ostride` floats), of which `orows` x `ocols` are stored; otherwise
 // to C or to the partial slice of split `ostride`.
 template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC,
-          bool SEG>
+          bool SEG, bool BT>
 __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int tn, int kbeg, int kend, float* outp,
                                              int ostride, int orows, int ocols, bool to_c)
 {
@@ -122,6 +126,12 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
     static_assert(KS == 1 || KS == 2, "intra-workgroup K split");
     static_assert(KH >= 2, "the barrier sits before each wave's last chunk step");
     static_assert(KS == 1 || TM % 2 == 0, "K-split halves exchange half of the row blocks");
+    static_assert(!BT || (V == 4 && !ELA && !ELB), "B given transposed: 16-byte loads, four-column reads");
+    // BT: B rows are columns of op(B), BK values each, placed like A's rows;
+    // RPB of them per 1 KB load. Column n's logical chunk c sits in physical
+    // row bt_row(n) at chunk slot c ^ bt_swz(n): the 16 lanes of one read
+    // (columns 4 l + v, l < 16, one chunk) then cover all 64 banks.
+    constexpr int RPB = 1024 / A_ROW;
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * STAGE];
 
@@ -144,6 +154,8 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
     const i4 rA = rsrc_words(reinterpret_cast<const char*>(args.A) + (long long)m0 * lda * 4,
                              (long long)(M - m0) * lda * 4);
     const long long b_bytes = (long long)K * ldb * 4;
+    auto bt_row = [](int n) { return RSW == 2 ? n ^ ((n >> 2) & 1) : n; };   // an involution
+    auto bt_swz = [](int n) { return (RSW == 2 ? n >> 3 : n >> 2) & (CPA - 1); };
 
     // Wave load q of stage `st`: the first A_PW LA loads fetch A rows into
     // 1 KB blocks (RPA rows per block, chunks placed swizzled: physical chunk
@@ -198,6 +210,17 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
             const int gk = k0 + 4 * c;
             const bool ok = m0 + row < M && gk < kend;
             lds_load16(rA, lds_addr(buf + I * 1024), ok ? (row * lda + gk) * 4 : kOOB);
+        } else if constexpr (BT) {
+            // Physical row / slot of this lane -> column n and its chunk c.
+            const int I = wave + (q - A_PW) * NW;
+            const int prow = I * RPB + lane / CPA;
+            const int n = bt_row(prow);
+            const int c = (lane % CPA) ^ bt_swz(n);
+            const int gk = k0 + 4 * c;
+            const bool ok = n0 + n < N && gk < kend;
+            const i4 rBt = rsrc_words(reinterpret_cast<const char*>(args.B) + (long long)n0 * ldb * 4,
+                                      (long long)(N - n0) * ldb * 4);
+            lds_load16(rBt, lds_addr(buf + A_BYTES + I * 1024), ok ? (n * ldb + gk) * 4 : kOOB);
         } else {
             const int I = wave + (q - A_PW) * NW;
             const int byte = I * 1024 + 16 * lane;
@@ -220,6 +243,12 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
             const int row = wm0 + BLK * r + lrow;
             const int c = (G * t + g) ^ ((row / RSW) % CPA);
             fa[r] = *reinterpret_cast<const u4*>(buf + row * A_ROW + c * 16);
+        } else if constexpr (BT) {
+            // Read (j, v): column wn0 + CG j + V lrow + v, K values 4 (G t + g) .. + 3,
+            // held as fb[j][v] (element e is K value e).
+            const int j = (r - TM) >> 2, v = (r - TM) & 3;
+            const int n = wn0 + CG * j + V * lrow + v;
+            fb[j][v] = *reinterpret_cast<const u4*>(buf + A_BYTES + bt_row(n) * A_ROW + ((G * t + g) ^ bt_swz(n)) * 16);
         } else {
             const int j = (r - TM) >> 2, e = (r - TM) & 3;
             const int row = 4 * (G * t + g) + e;
@@ -251,7 +280,7 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
         const int e = m / (V * TM * TN);
         const int rest = m % (V * TM * TN);
         const int i = rest / (V * TN), j = (rest / V) % TN, v = rest % V;
-        MF::mfma(acc[i][j][v], fa[i][e], fb[j][e][v]);
+        MF::mfma(acc[i][j][v], fa[i][e], BT ? fb[j][v][e] : fb[j][e][v]);
     };
 
     constexpr int RPS = (NRD + NMF - 1) / NMF;   // reads per MFMA slot
@@ -476,7 +505,8 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
 
 // Data-parallel form: one workgroup per (tile, split); split s covers K
 // values [s k_chunk, (s + 1) k_chunk) and writes C or its partial slice.
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC>
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC,
+          bool BT>
 __global__ void __launch_bounds__(WM * WN * KS * 64)
 __attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / ring_lds_bytes<BM, BN, BK, NBUF>()) * WM * WN * KS + 3) / 4)))
 gemm_f32_ring_kernel(GemmArgs args)
@@ -486,9 +516,8 @@ gemm_f32_ring_kernel(GemmArgs args)
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = s * args.k_chunk;
     const int kend = min(args.K, kbeg + args.k_chunk);
-    ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false>(args, tm, tn, kbeg, kend, nullptr, s, 0,
-                                                                            0,
-                                                                       true);
+    ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false, BT>(args, tm, tn, kbeg, kend, nullptr, s,
+                                                                                0, 0, true);
 }
 
 // Stream-K form (page "fix(fp4_gemm autotune) SM107 kernel family excluded
@@ -503,7 +532,8 @@ gemm_f32_ring_kernel(GemmArgs args)
 // range order. Ranges are numbered by logical workgroup (each XCD holds
 // consecutive ranges). The split points depend only on the plan, so the
 // result does not depend on timing.
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC>
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC,
+          bool BT>
 __global__ void __launch_bounds__(WM * WN * KS * 64)
 __attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / ring_lds_bytes<BM, BN, BK, NBUF>()) * WM * WN * KS + 3) / 4)))
 gemm_f32_ring_sk_kernel(GemmArgs args)
@@ -529,7 +559,7 @@ gemm_f32_ring_sk_kernel(GemmArgs args)
         const bool whole = k0 == 0 && k1 == I;
         float* outp = whole ? args.out + (args.ct ? (long long)n0 * args.ldc + m0 : (long long)m0 * args.ldc + n0)
                             : args.ws + (2 * g + (first ? 0 : 1)) * (long long)(BM * BN);
-        ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, true>(
+        ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, true, BT>(
             args, tm, tn, kbeg, kend, outp, whole ? args.ldc : BN, whole ? args.M - m0 : BM,
             whole ? args.N - n0 : BN, whole);
         it += k1 - k0;
@@ -558,9 +588,9 @@ constexpr F32RingFn ring_kernel() {
         static_assert((NBUF - 1) * (((BM + BN) * BK * 4 / 1024) / (WM * WN * KS) * (ELA || ELB ? 4 : 1)) < 64,
                       "loads in flight must stay countable");
         if constexpr (SK)
-            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC>;
+            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false>;
         else
-            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC>;
+            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false>;
     } else {
         return nullptr;
     }
@@ -572,7 +602,24 @@ struct F32RingKernel {
     F32RingFn fixup;
     int fixup_wgs;   // fix-up workgroups per tile
     int threads;
+    F32RingFn bt[2][2];         // B given transposed: [stream-K][c_vec] (16-byte loads of A and B)
 };
+
+// B-given-transposed forms: for the 16x16x4 variants that read four columns
+// at a time, with tiles of at most 128 x 256 (each of the read addresses of
+// a column group is formed per lane, and the 256 x 256 tile has no
+// registers to spare for them).
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELC, bool SK>
+constexpr F32RingFn ring_bt_kernel() {
+    if constexpr (V == 4 && BLK == 16 && BM * BN <= kSkMaxTile) {
+        if constexpr (SK)
+            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false, ELC, true>;
+        else
+            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false, ELC, true>;
+    } else {
+        return nullptr;
+    }
+}
 
 #define SAM_F32RING_CSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, A, B, SK)            \
     {ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, A, B, true, SK>(),             \
@@ -587,10 +634,18 @@ struct F32RingKernel {
     {id,                                                                                         \
      {SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, false),                          \
       SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, true)},                          \
-     sk_fixup_kernel<BM, BN>, sk_fixup_wgs<BM, BN>(), WM * WN * KS * 64},
-// The padding forms: the same kernels, EL 2.
-#define SAM_F32PAD_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32) \
-    SAM_F32RING_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, 2, gm, xr, ms, e32)
+     sk_fixup_kernel<BM, BN>, sk_fixup_wgs<BM, BN>(), WM * WN * KS * 64,                          \
+     {{ring_bt_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, true, false>(),                        \
+       ring_bt_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false>()},                      \
+      {ring_bt_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, true, true>(),                         \
+       ring_bt_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, true>()}}},
+// The padding forms: the same kernels, EL 2, and no B-given-transposed form
+// (a padded copy is made in the plain layout).
+#define SAM_F32PAD_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32)     \
+    {id,                                                                                         \
+     {SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, 2, false),                           \
+      SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, 2, true)},                           \
+     sk_fixup_kernel<BM, BN>, sk_fixup_wgs<BM, BN>(), WM * WN * KS * 64, {{nullptr, nullptr}, {nullptr, nullptr}}},
 
 static const F32RingKernel kF32RingTable[] = {SAM_F32RING_VARIANTS(SAM_F32RING_ENTRY)
                                                   SAM_F32PAD_VARIANTS(SAM_F32PAD_ENTRY)};
@@ -600,12 +655,20 @@ hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s)
     for (const F32RingKernel& k : kF32RingTable) {
         if (k.id != p.variant_id) continue;
         if (p.dtype != DT_F32) return hipErrorInvalidDeviceFunction;
-        const F32RingFn fn = k.fn[p.sk ? 1 : 0][p.a_vec ? 1 : 0][p.b_vec ? 1 : 0][p.c_vec ? 1 : 0];
+        const F32RingFn fn = (p.tr & 1) ? (p.a_vec ? k.bt[p.sk ? 1 : 0][p.c_vec ? 1 : 0] : nullptr)
+                                        : k.fn[p.sk ? 1 : 0][p.a_vec ? 1 : 0][p.b_vec ? 1 : 0][p.c_vec ? 1 : 0];
         if (!fn) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(k.threads), 0, s, a);
         return hipGetLastError();
     }
     return hipErrorInvalidDeviceFunction;
+}
+
+bool f32_has_bt(int variant_id, bool stream_k)
+{
+    for (const F32RingKernel& k : kF32RingTable)
+        if (k.id == variant_id) return k.bt[stream_k ? 1 : 0][0] != nullptr && k.bt[stream_k ? 1 : 0][1] != nullptr;
+    return false;
 }
 
 hipError_t launch_sk_fixup(const Plan& p, const GemmArgs& a, hipStream_t s)

@@ -279,6 +279,23 @@ def test_ex_on_a_ring_plan_writes_c_itself():
     assert sam.ex_workspace_bytes(256, 256, 256, False, False, 256, 256, 264, 0.5, -1.0, "f32") >= 256 * 256 * 4
 
 
+def test_ex_f32_transposed_b_read_straight_where_the_variant_can():
+    """FP32 with B given transposed: a ring plan with the transposed-B form
+    (tiles up to 128 x 256) reads it in place, K % 4 == 0 and 16-byte rows of
+    B^T; the 256 x 256 tile, K % 4 != 0 and misaligned rows still pack B."""
+    M = N = K = 2048
+    p = sam.plan(M, N, K, "f32")
+    assert p["name"].startswith("f32_f128x128")
+    ws = lambda M, N, K, ldb: sam.ex_workspace_bytes(M, N, K, False, True, K, ldb, N, 1.0, 0.0, "f32")
+    assert ws(M, N, K, K) == p["workspace_bytes"] == 0
+    assert ws(M, N, K, K + 4) == 0
+    assert ws(M, N, K, K + 2) >= K * N * 4                               # rows of B^T not 16-byte pieces
+    q = sam.plan(4096, 4096, 4096, "f32")
+    assert q["name"].startswith("f32_f256x256")
+    assert ws(4096, 4096, 4096, 4096) >= 4096 * 4096 * 4                 # no transposed-B form: packed
+    assert ws(1000, 776, 1030, 1030) >= 1030 * 776 * 4                   # K % 4 != 0: packed
+
+
 def test_mxfp8_plans_and_rejections_before_any_device_call():
     """Block-scaled plans come from the block-scaled variants only; K not a
     multiple of 32, bad formats, a negative split, null scales and the plain

@@ -315,6 +315,64 @@ def test_ex_transposed_random_repeatable(ta, tb):
     assert rel_rms(C1.cpu().numpy(), ref) <= 1e-5   # exact products, FP32 accumulation
 
 
+# FP32 with B given transposed (N rows of K values) read straight by the
+# ring variants that have that form (B placed K-contiguous like A, four K
+# values of one column per read), data-parallel, split-K and stream-K, with
+# strided rows, ldc, alpha / beta, ragged M and N (C rows not 16-byte pieces
+# too): no copy, the workspace is the plan's own.
+F32_BT = [v for v in range(sam.variant_count())
+          if sam.variant_info(v)["name"] in ("f128x128_w2x2s2_k64n2_b16", "f128x128_w4x2_k64n2_b16",
+                                             "f128x128_w4x2_k32n2_b16")]
+F32_BT_SHAPES = [(300, 518, 264), (1000, 776, 1032), (129, 130, 512)]
+
+
+@pytest.mark.parametrize("vid", F32_BT)
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (0.5, -1.0)])
+def test_ex_f32_transposed_b_read_straight(vid, alpha, beta):
+    ran = 0
+    for (M, N, K) in F32_BT_SHAPES:
+        for split in (1, 2, -1):
+            try:
+                p = sam.variant_plan(vid, M, N, K, "f32", split)
+            except sam.SamError:
+                continue
+            pc = 4 - N % 4 if N % 4 else 4
+            Av, Bv, C0, lda, ldb, ldc = _fused_case("f32", M, N, K, False, True, 4, 4, pc, alpha, beta,
+                                                    M + N + vid + 3 * split)
+            assert sam.ex_workspace_bytes(M, N, K, False, True, lda, ldb, ldc, alpha, beta, "f32", variant=vid,
+                                          split=split) == p["workspace_bytes"]
+            print(f"[bt] variant {vid} {(M, N, K)} split {split} alpha {alpha} beta {beta}", flush=True)
+            Cd = torch.from_numpy(C0.copy()).cuda()
+            sam.gemm_ex(_dev("f32", Av)[:, :K], _dev("f32", Bv)[:, :K], Cd[:, :N], trans_b=True, alpha=alpha,
+                        beta=beta, variant=vid, split=split)
+            torch.cuda.synchronize()
+            got = Cd.cpu().numpy()
+            ref = orc().gemm_ex("f32", M, N, K, Av, lda, Bv, ldb, False, True, alpha, beta,
+                                np.ascontiguousarray(C0[:, :N]), nthreads=orc().max_threads())
+            assert bitexact_mismatches(got[:, :N], ref) == 0, (vid, (M, N, K), split)
+            assert np.all(got[:, N:] == 12345.0)
+            ran += 1
+    assert ran > 0
+
+
+def test_ex_f32_transposed_b_random_repeatable():
+    """FP32 2048^3 with B given transposed through the dispatcher's plan: no
+    copy, rel_rms within 1e-5 of the oracle, bitwise the same twice."""
+    M = N = K = 2048
+    assert sam.ex_workspace_bytes(M, N, K, False, True, K, K, N, 1.0, 0.0, "f32") == 0
+    rng = np.random.default_rng(29)
+    A = si.uniform_pm1(rng, (M, K))
+    B = si.uniform_pm1(rng, (K, N))
+    dA = torch.from_numpy(A).cuda()
+    dBt = torch.from_numpy(np.ascontiguousarray(B.T)).cuda()
+    C1 = sam.gemm_ex(dA, dBt, trans_b=True)
+    C2 = sam.gemm_ex(dA, dBt, trans_b=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
+    ref = orc().gemm("f32", A, B, nthreads=orc().max_threads())
+    assert rel_rms(C1.cpu().numpy(), ref) <= 1e-5
+
+
 # FP32 with both operands given transposed: C = A^T B^T computed as the
 # plain product B A of the operands as stored, whose ring plan (for N x M x K)
 # stores C transposed, in the kernel, the split-K reduce or the stream-K
