@@ -215,8 +215,13 @@ typedef enum { SAM_OP_N = 0, SAM_OP_T = 1 } sam_op;
  *    padded rows anyway), and store C themselves with row stride ldc (a
  *    multiple of 4) and alpha / beta applied where C is written: in the
  *    kernel, the split-K reduce or the stream-K fix-up. 16-bit 16x16x32 ring
- *    plans also read a transposed B (SAM_OP_T) straight, when K, N and ldb
- *    are multiples of 8;
+ *    plans also read transposed operands (SAM_OP_T) straight, when K, N and
+ *    the transposed operand's leading dimension are multiples of 8 (a
+ *    192-row tile hands a transposed A to its 256-row twin); FP32 ring plans
+ *    with tiles up to 128 x 256 read a transposed B straight when K and ldb
+ *    are multiples of 4; FP32 with both operands transposed runs as the
+ *    plain product B A of the operands as stored, whose ring plan stores C
+ *    transposed;
  *  - whatever remains (a transposed operand the plan cannot read, other
  *    strides, other plan kinds) is copied into compact rows in the
  *    workspace first, the product goes to a workspace temporary unless the
