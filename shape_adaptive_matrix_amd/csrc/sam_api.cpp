@@ -184,12 +184,17 @@ bool reads_strided(const sam::Plan& p, bool a_side, long long ld)
 // 0 B as N rows of K values, bit 1 A as K rows of M values): its variant has
 // the kernels of that layout, neither operand needs a padded copy (16-bit: K
 // and N multiples of 8) and each transposed operand's rows are whole 16-byte
-// pieces. FP32 ring plans read B given transposed only, with A's rows whole
-// 16-byte pieces (K % 4 == 0).
+// pieces. FP32 ring plans read one operand given transposed: B with A's
+// rows whole 16-byte pieces (K % 4 == 0), or A with B's and C's rows whole
+// 16-byte pieces (N % 4 == 0).
 bool reads_transposed(const sam::Plan& p, int tr, long long lda, long long ldb)
 {
-    if (p.kind == sam::KIND_F32RING)
-        return tr == 1 && p.a_vec && !p.pad_a && !p.pad_b && ldb % 4 == 0 && sam::f32_has_bt(p.variant_id, p.sk != 0);
+    if (p.kind == sam::KIND_F32RING) {
+        if (p.pad_a || p.pad_b) return false;
+        if (tr == 1) return p.a_vec && ldb % 4 == 0 && sam::f32_has_bt(p.variant_id, p.sk != 0);
+        if (tr == 2) return p.b_vec && p.c_vec && lda % 4 == 0 && sam::f32_has_at(p.variant_id, p.sk != 0);
+        return false;
+    }
     return p.kind == sam::KIND_DMA && !p.pad_a && !p.pad_b && (!(tr & 1) || ldb % 8 == 0) &&
            (!(tr & 2) || lda % 8 == 0) && sam::dma_has_layout(p.variant_id, tr, p.dtype);
 }

@@ -149,6 +149,9 @@ int tile256_twin(int id);
 // Whether an FP32 ring variant has the form that reads B given transposed
 // (N rows of K values) straight, in its data-parallel or stream-K form.
 bool f32_has_bt(int variant_id, bool stream_k);
+// Whether it has the form that reads A given transposed (K rows of M
+// values) straight, with B's and C's rows whole 16-byte pieces.
+bool f32_has_at(int variant_id, bool stream_k);
 
 // Kernel launchers (sam_kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t s);

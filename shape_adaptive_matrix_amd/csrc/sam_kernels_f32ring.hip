@@ -23,6 +23,11 @@
 //    takes op(B) = B^T) sits K-contiguous like A and is read four
 //    consecutive K values of one column at a time, one read per column of
 //    the V: the same values reach the same MFMAs, gathered the other way.
+//  * A given transposed (AT: K rows of M values) sits M-contiguous like B
+//    and is read VA = 4 (or 2) adjacent rows of one K row at a time: lane l
+//    of a group of VA row blocks holds rows VA l .. VA l + VA - 1, so block
+//    u of the group covers every VA-th row (rows VA l + u). Only the output
+//    row order is permuted, and the store undoes it.
 //    The 32x32x2 MFMA takes one B value per lane (column lane % 32), so the V
 //    columns feed V MFMAs that each cover every V-th column of a 32 V-column
 //    group: MFMA v produces columns n + V j + v, j < 32. Only the output
@@ -89,7 +94,7 @@ constexpr int ring_lds_bytes() { return NBUF * (BM + BN) * BK * 4; }
 // stride `ostride` floats), of which `orows` x `ocols` are stored; otherwise
 // to C or to the partial slice of split `ostride`.
 template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC,
-          bool SEG, bool BT>
+          bool SEG, bool BT, bool AT>
 __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int tn, int kbeg, int kend, float* outp,
                                              int ostride, int orows, int ocols, bool to_c)
 {
@@ -132,6 +137,12 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
     // row bt_row(n) at chunk slot c ^ bt_swz(n): the 16 lanes of one read
     // (columns 4 l + v, l < 16, one chunk) then cover all 64 banks.
     constexpr int RPB = 1024 / A_ROW;
+    // AT: A rows are K values of op(A), BM values each (A_ROW_T bytes); VA
+    // row blocks form a group read VA rows at a time (NRA reads per step).
+    constexpr int VA = AT ? (TM % 4 == 0 ? 4 : 2) : 1;
+    constexpr int A_ROW_T = BM * 4;
+    constexpr int NRA = AT ? (TM / VA) * 4 : TM;
+    static_assert(!AT || (TM % VA == 0 && !ELA && !BT && BLK == 16), "A given transposed: groups of VA row blocks");
 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * STAGE];
 
@@ -154,6 +165,7 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
     const i4 rA = rsrc_words(reinterpret_cast<const char*>(args.A) + (long long)m0 * lda * 4,
                              (long long)(M - m0) * lda * 4);
     const long long b_bytes = (long long)K * ldb * 4;
+    const long long a_bytes_t = (long long)K * lda * 4;   // A given transposed: K rows of lda values
     auto bt_row = [](int n) { return RSW == 2 ? n ^ ((n >> 2) & 1) : n; };   // an involution
     auto bt_swz = [](int n) { return (RSW == 2 ? n >> 3 : n >> 2) & (CPA - 1); };
 
@@ -203,7 +215,16 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
         if constexpr (SEG) asm volatile("" : "+v"(lane));
         const int k0 = kbeg + st * BK;
         unsigned char* buf = lds + (st % NBUF) * STAGE;
-        if (q < A_PW) {
+        if (AT && q < A_PW) {
+            // A^T rows k0 + row, M-contiguous, in their natural order (as B's).
+            const int I = wave + q * NW;
+            const int byte = I * 1024 + 16 * lane;
+            const int row = byte / A_ROW_T, col = (byte % A_ROW_T) / 4;
+            const bool ok = k0 + row < kend && m0 + col < M;
+            const long long abase = ((long long)k0 * lda + m0) * 4;
+            const i4 rAt = rsrc_words(reinterpret_cast<const char*>(args.A) + abase, a_bytes_t - abase);
+            lds_load16(rAt, lds_addr(buf + I * 1024), ok ? (row * lda + col) * 4 : kOOB);
+        } else if (q < A_PW) {
             const int I = wave + q * NW;
             const int row = I * RPA + lane / CPA;
             const int c = (lane % CPA) ^ ((row / RSW) % CPA);
@@ -235,22 +256,37 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
     const int lrow = lane % BLK;
     const int g = lane / BLK;
     // Fragment read r of chunk step t: r < TM is A block r (row wm0 + BLK r +
-    // lrow, chunk G t + g); then B reads (j, e) = ((r - TM) / 4, (r - TM) % 4):
+    // lrow, chunk G t + g) (AT: the NRA reads of its row-block groups); then
+    // B reads (j, e) = ((r - NRA) / 4, (r - NRA) % 4):
     // row 4 (G t + g) + e, columns wn0 + CG j + V lrow .. + V - 1.
-    constexpr int NRD = TM + 4 * TN;
+    constexpr int NRD = NRA + 4 * TN;
     auto read_one = [&](const unsigned char* buf, int t, int r, u4 (&fa)[TM], u4 (&fb)[TN][4]) {
-        if (r < TM) {
+        if (AT && r < NRA) {
+            // Read (I, e): rows wm0 + BLK VA I + VA lrow .. + VA - 1 at K row
+            // 4 (G t + g) + e; value (I, e, u) is kept at flat index
+            // 4 VA I + VA e + u of fa.
+            const int I = r >> 2, e = r & 3;
+            const unsigned char* p = buf + (4 * (G * t + g) + e) * A_ROW_T + (wm0 + BLK * VA * I + VA * lrow) * 4;
+            if constexpr (VA == 4) {
+                fa[4 * I + e] = *reinterpret_cast<const u4*>(p);
+            } else {
+                typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+                const u2 x = *reinterpret_cast<const u2*>(p);
+                fa[2 * I + (e >> 1)][2 * (e & 1)] = x[0];
+                fa[2 * I + (e >> 1)][2 * (e & 1) + 1] = x[1];
+            }
+        } else if (r < TM) {
             const int row = wm0 + BLK * r + lrow;
             const int c = (G * t + g) ^ ((row / RSW) % CPA);
             fa[r] = *reinterpret_cast<const u4*>(buf + row * A_ROW + c * 16);
         } else if constexpr (BT) {
             // Read (j, v): column wn0 + CG j + V lrow + v, K values 4 (G t + g) .. + 3,
             // held as fb[j][v] (element e is K value e).
-            const int j = (r - TM) >> 2, v = (r - TM) & 3;
+            const int j = (r - NRA) >> 2, v = (r - NRA) & 3;
             const int n = wn0 + CG * j + V * lrow + v;
             fb[j][v] = *reinterpret_cast<const u4*>(buf + A_BYTES + bt_row(n) * A_ROW + ((G * t + g) ^ bt_swz(n)) * 16);
         } else {
-            const int j = (r - TM) >> 2, e = (r - TM) & 3;
+            const int j = (r - NRA) >> 2, e = (r - NRA) & 3;
             const int row = 4 * (G * t + g) + e;
             const unsigned char* p = buf + A_BYTES + row * B_ROW + (wn0 + CG * j + V * lrow) * 4;
             if constexpr (V == 4) {
@@ -280,7 +316,10 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
         const int e = m / (V * TM * TN);
         const int rest = m % (V * TM * TN);
         const int i = rest / (V * TN), j = (rest / V) % TN, v = rest % V;
-        MF::mfma(acc[i][j][v], fa[i][e], BT ? fb[j][v][e] : fb[j][e][v]);
+        // AT: block i is u = i % VA of group i / VA, its value at flat index
+        // 4 VA (i / VA) + VA e + u.
+        const unsigned a = AT ? fa[(4 * VA * (i / VA) + VA * e + i % VA) / 4][(VA * e + i % VA) % 4] : fa[i][e];
+        MF::mfma(acc[i][j][v], a, BT ? fb[j][v][e] : fb[j][e][v]);
     };
 
     constexpr int RPS = (NRD + NMF - 1) / NMF;   // reads per MFMA slot
@@ -426,7 +465,9 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
                     const int col = wn0 + CG * j + V * lrow;
 #pragma unroll
                     for (int r = 0; r < MF::N; ++r) {
-                        const int row = wm0 + BLK * (IB + ii) + MF::row(lane, r);
+                        const int ib = IB + ii;   // AT: block u = ib % VA of group ib / VA holds every VA-th row
+                        const int row = AT ? wm0 + BLK * VA * (ib / VA) + VA * MF::row(lane, r) + ib % VA
+                                           : wm0 + BLK * ib + MF::row(lane, r);
                         if constexpr (ELB || ELC) {
                             // Rows need not be 16-byte pieces: one float per
                             // store, each column checked against N.
@@ -486,7 +527,7 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
                         }
                 }
         };
-        if (ct) {
+        if (!AT && ct) {   // the transposed store takes four adjacent rows: not with AT's row order
             if (gen)
                 store_all_t(std::true_type{});
             else
@@ -506,7 +547,7 @@ __device__ __forceinline__ void ring_segment(const GemmArgs& args, int tm, int t
 // Data-parallel form: one workgroup per (tile, split); split s covers K
 // values [s k_chunk, (s + 1) k_chunk) and writes C or its partial slice.
 template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC,
-          bool BT>
+          bool BT, bool AT>
 __global__ void __launch_bounds__(WM * WN * KS * 64)
 __attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / ring_lds_bytes<BM, BN, BK, NBUF>()) * WM * WN * KS + 3) / 4)))
 gemm_f32_ring_kernel(GemmArgs args)
@@ -516,8 +557,8 @@ gemm_f32_ring_kernel(GemmArgs args)
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = s * args.k_chunk;
     const int kend = min(args.K, kbeg + args.k_chunk);
-    ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false, BT>(args, tm, tn, kbeg, kend, nullptr, s,
-                                                                                0, 0, true);
+    ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false, BT, AT>(args, tm, tn, kbeg, kend, nullptr,
+                                                                                    s, 0, 0, true);
 }
 
 // Stream-K form (page "fix(fp4_gemm autotune) SM107 kernel family excluded
@@ -533,7 +574,7 @@ gemm_f32_ring_kernel(GemmArgs args)
 // consecutive ranges). The split points depend only on the plan, so the
 // result does not depend on timing.
 template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool ELA, bool ELB, bool ELC,
-          bool BT>
+          bool BT, bool AT>
 __global__ void __launch_bounds__(WM * WN * KS * 64)
 __attribute__((amdgpu_waves_per_eu(1, ((160 * 1024 / ring_lds_bytes<BM, BN, BK, NBUF>()) * WM * WN * KS + 3) / 4)))
 gemm_f32_ring_sk_kernel(GemmArgs args)
@@ -559,7 +600,7 @@ gemm_f32_ring_sk_kernel(GemmArgs args)
         const bool whole = k0 == 0 && k1 == I;
         float* outp = whole ? args.out + (args.ct ? (long long)n0 * args.ldc + m0 : (long long)m0 * args.ldc + n0)
                             : args.ws + (2 * g + (first ? 0 : 1)) * (long long)(BM * BN);
-        ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, true, BT>(
+        ring_segment<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, true, BT, AT>(
             args, tm, tn, kbeg, kend, outp, whole ? args.ldc : BN, whole ? args.M - m0 : BM,
             whole ? args.N - n0 : BN, whole);
         it += k1 - k0;
@@ -588,9 +629,23 @@ constexpr F32RingFn ring_kernel() {
         static_assert((NBUF - 1) * (((BM + BN) * BK * 4 / 1024) / (WM * WN * KS) * (ELA || ELB ? 4 : 1)) < 64,
                       "loads in flight must stay countable");
         if constexpr (SK)
-            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false>;
+            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false, false>;
         else
-            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false>;
+            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, ELA, ELB, ELC, false, false>;
+    } else {
+        return nullptr;
+    }
+}
+
+// A-given-transposed forms (B in its plain layout, N % 4 == 0): the same
+// variants, whose wave tiles hold whole groups of two or four row blocks.
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool SK>
+constexpr F32RingFn ring_at_kernel() {
+    if constexpr (V == 4 && BLK == 16 && BM * BN <= kSkMaxTile && (BM / WM / BLK) % 2 == 0) {
+        if constexpr (SK)
+            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false, false, false, true>;
+        else
+            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false, false, false, true>;
     } else {
         return nullptr;
     }
@@ -603,6 +658,7 @@ struct F32RingKernel {
     int fixup_wgs;   // fix-up workgroups per tile
     int threads;
     F32RingFn bt[2][2];         // B given transposed: [stream-K][c_vec] (16-byte loads of A and B)
+    F32RingFn at[2];            // A given transposed: [stream-K] (B rows and C rows 16-byte pieces)
 };
 
 // B-given-transposed forms: for the 16x16x4 variants that read four columns
@@ -613,9 +669,9 @@ template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int B
 constexpr F32RingFn ring_bt_kernel() {
     if constexpr (V == 4 && BLK == 16 && BM * BN <= kSkMaxTile) {
         if constexpr (SK)
-            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false, ELC, true>;
+            return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false, ELC, true, false>;
         else
-            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false, ELC, true>;
+            return gemm_f32_ring_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false, ELC, true, false>;
     } else {
         return nullptr;
     }
@@ -638,14 +694,17 @@ constexpr F32RingFn ring_bt_kernel() {
      {{ring_bt_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, true, false>(),                        \
        ring_bt_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false>()},                      \
       {ring_bt_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, true, true>(),                         \
-       ring_bt_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, true>()}}},
+       ring_bt_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, true>()}},                      \
+     {ring_at_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false>(),                               \
+      ring_at_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, true>()}},
 // The padding forms: the same kernels, EL 2, and no B-given-transposed form
 // (a padded copy is made in the plain layout).
 #define SAM_F32PAD_ENTRY(id, name, BM, BN, WM, WN, BK, NBUF, V, KS, BLK, EL, gm, xr, ms, e32)     \
     {id,                                                                                         \
      {SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, 2, false),                           \
       SAM_F32RING_KSET(BM, BN, WM, WN, BK, NBUF, V, KS, BLK, 2, true)},                           \
-     sk_fixup_kernel<BM, BN>, sk_fixup_wgs<BM, BN>(), WM * WN * KS * 64, {{nullptr, nullptr}, {nullptr, nullptr}}},
+     sk_fixup_kernel<BM, BN>, sk_fixup_wgs<BM, BN>(), WM * WN * KS * 64, {{nullptr, nullptr}, {nullptr, nullptr}},     \
+     {nullptr, nullptr}},
 
 static const F32RingKernel kF32RingTable[] = {SAM_F32RING_VARIANTS(SAM_F32RING_ENTRY)
                                                   SAM_F32PAD_VARIANTS(SAM_F32PAD_ENTRY)};
@@ -655,13 +714,22 @@ hipError_t launch_f32_ring(const Plan& p, const GemmArgs& a, hipStream_t s)
     for (const F32RingKernel& k : kF32RingTable) {
         if (k.id != p.variant_id) continue;
         if (p.dtype != DT_F32) return hipErrorInvalidDeviceFunction;
-        const F32RingFn fn = (p.tr & 1) ? (p.a_vec ? k.bt[p.sk ? 1 : 0][p.c_vec ? 1 : 0] : nullptr)
-                                        : k.fn[p.sk ? 1 : 0][p.a_vec ? 1 : 0][p.b_vec ? 1 : 0][p.c_vec ? 1 : 0];
+        const int sk = p.sk ? 1 : 0;
+        const F32RingFn fn = (p.tr & 2)   ? (p.tr == 2 && p.b_vec && p.c_vec ? k.at[sk] : nullptr)
+                             : (p.tr & 1) ? (p.a_vec ? k.bt[sk][p.c_vec ? 1 : 0] : nullptr)
+                                          : k.fn[sk][p.a_vec ? 1 : 0][p.b_vec ? 1 : 0][p.c_vec ? 1 : 0];
         if (!fn) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(fn, dim3((unsigned)p.grid), dim3(k.threads), 0, s, a);
         return hipGetLastError();
     }
     return hipErrorInvalidDeviceFunction;
+}
+
+bool f32_has_at(int variant_id, bool stream_k)
+{
+    for (const F32RingKernel& k : kF32RingTable)
+        if (k.id == variant_id) return k.at[stream_k ? 1 : 0] != nullptr;
+    return false;
 }
 
 bool f32_has_bt(int variant_id, bool stream_k)

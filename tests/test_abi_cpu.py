@@ -296,6 +296,17 @@ def test_ex_f32_transposed_b_read_straight_where_the_variant_can():
     assert ws(1000, 776, 1030, 1030) >= 1030 * 776 * 4                   # K % 4 != 0: packed
 
 
+def test_ex_f32_transposed_a_read_straight_where_the_variant_can():
+    """FP32 with A given transposed: the same variants read it in place when
+    B's and C's rows are 16-byte pieces (any K) and A^T's rows are too."""
+    ws = lambda M, N, K, lda: sam.ex_workspace_bytes(M, N, K, True, False, lda, N, N, 1.0, 0.0, "f32")
+    assert ws(2048, 2048, 2048, 2048) == 0
+    assert ws(2048, 2048, 2048, 2052) == 0
+    assert ws(2048, 2048, 2048, 2050) >= 2048 * 2048 * 4                 # rows of A^T not 16-byte pieces
+    assert ws(4096, 4096, 4096, 4096) >= 4096 * 4096 * 4                 # 256 x 256 plan: packed
+    assert sam.ex_workspace_bytes(2048, 2046, 2048, True, False, 2048, 2046, 2048, 1.0, 0.0, "f32") > 0
+
+
 def test_mxfp8_plans_and_rejections_before_any_device_call():
     """Block-scaled plans come from the block-scaled variants only; K not a
     multiple of 32, bad formats, a negative split, null scales and the plain

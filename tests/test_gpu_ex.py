@@ -355,6 +355,61 @@ def test_ex_f32_transposed_b_read_straight(vid, alpha, beta):
     assert ran > 0
 
 
+# FP32 with A given transposed (K rows of M values) read straight: A^T rows
+# placed M-contiguous like B's and read two or four rows at a time, the row
+# order inside each group of row blocks undone at the store; B's and C's
+# rows whole 16-byte pieces (N % 4 == 0), any K, ragged M with Inf in the
+# padding of A^T's rows (it reaches only rows of C that are never stored).
+F32_AT_SHAPES = [(300, 520, 264), (1000, 776, 1030), (129, 136, 512)]
+
+
+@pytest.mark.parametrize("vid", F32_BT)
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (0.5, -1.0)])
+def test_ex_f32_transposed_a_read_straight(vid, alpha, beta):
+    ran = 0
+    for (M, N, K) in F32_AT_SHAPES:
+        for split in (1, 2, -1):
+            try:
+                p = sam.variant_plan(vid, M, N, K, "f32", split)
+            except sam.SamError:
+                continue
+            pa = 4 - M % 4 if M % 4 else 4
+            Av, Bv, C0, lda, ldb, ldc = _fused_case("f32", M, N, K, True, False, pa, 4, 4, alpha, beta,
+                                                    M + 2 * N + vid + 3 * split)
+            assert sam.ex_workspace_bytes(M, N, K, True, False, lda, ldb, ldc, alpha, beta, "f32", variant=vid,
+                                          split=split) == p["workspace_bytes"]
+            print(f"[at] variant {vid} {(M, N, K)} split {split} alpha {alpha} beta {beta}", flush=True)
+            Cd = torch.from_numpy(C0.copy()).cuda()
+            sam.gemm_ex(_dev("f32", Av)[:, :M], _dev("f32", Bv)[:, :N], Cd[:, :N], trans_a=True, alpha=alpha,
+                        beta=beta, variant=vid, split=split)
+            torch.cuda.synchronize()
+            got = Cd.cpu().numpy()
+            ref = orc().gemm_ex("f32", M, N, K, Av, lda, Bv, ldb, True, False, alpha, beta,
+                                np.ascontiguousarray(C0[:, :N]), nthreads=orc().max_threads())
+            assert bitexact_mismatches(got[:, :N], ref) == 0, (vid, (M, N, K), split)
+            assert np.all(got[:, N:] == 12345.0)
+            ran += 1
+    assert ran > 0
+
+
+def test_ex_f32_transposed_a_random_repeatable():
+    """FP32 2048^3 with A given transposed through the dispatcher's plan: no
+    copy, rel_rms within 1e-5 of the oracle, bitwise the same twice."""
+    M = N = K = 2048
+    assert sam.ex_workspace_bytes(M, N, K, True, False, M, N, N, 1.0, 0.0, "f32") == 0
+    rng = np.random.default_rng(31)
+    A = si.uniform_pm1(rng, (M, K))
+    B = si.uniform_pm1(rng, (K, N))
+    dAt = torch.from_numpy(np.ascontiguousarray(A.T)).cuda()
+    dB = torch.from_numpy(B).cuda()
+    C1 = sam.gemm_ex(dAt, dB, trans_a=True)
+    C2 = sam.gemm_ex(dAt, dB, trans_a=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32))
+    ref = orc().gemm("f32", A, B, nthreads=orc().max_threads())
+    assert rel_rms(C1.cpu().numpy(), ref) <= 1e-5
+
+
 def test_ex_f32_transposed_b_random_repeatable():
     """FP32 2048^3 with B given transposed through the dispatcher's plan: no
     copy, rel_rms within 1e-5 of the oracle, bitwise the same twice."""
