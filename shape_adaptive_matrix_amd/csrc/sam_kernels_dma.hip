@@ -36,7 +36,7 @@ constexpr KernelFn ring16_sk()
 
 static const DmaKernels kDmaTable[] = {SAM_DMA_VARIANTS(SAM_DMA_ENTRY0) SAM_DMA16_VARIANTS(SAM_DMA_ENTRY0)
                                            SAM_DMA16S_VARIANTS(SAM_DMA_ENTRY)
-                                               SAM_DMA16M_VARIANTS(SAM_DMA_ENTRY)};
+                                               SAM_DMA16M_VARIANTS(SAM_DMA_ENTRY) SAM_DMA16D_VARIANTS(SAM_DMA_ENTRY)};
 
 static const DmaKernels* dma_entry(int id)
 {

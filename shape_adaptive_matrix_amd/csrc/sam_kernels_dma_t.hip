@@ -47,7 +47,7 @@ constexpr KernelFn ring16_t()
     SAM_DMA_T_ENTRY0(id, name, BM, BN, WM, WN, BK, NBUF, MODE, BLK, gm, xr, ms, e16)
 
 const DmaTKernels kDmaTTable[] = {SAM_DMA16_VARIANTS(SAM_DMA_T_IF16) SAM_DMA16S_VARIANTS(SAM_DMA_T_ENTRY)
-                                      SAM_DMA16M_VARIANTS(SAM_DMA_T_ENTRY)};
+                                      SAM_DMA16M_VARIANTS(SAM_DMA_T_ENTRY) SAM_DMA16D_VARIANTS(SAM_DMA_T_ENTRY)};
 
 }  // namespace
 

@@ -71,7 +71,8 @@ static const Variant kVariants[] = {SAM_STAGED_VARIANTS(SAM_STAGED_ROW) SAM_DMA_
                                                 SAM_KQ_VARIANTS(SAM_KQ_ROW) SAM_KP_VARIANTS(SAM_KP_ROW)
                                                     SAM_KQ8_VARIANTS(SAM_KQ_ROW) SAM_DMA16S_VARIANTS(SAM_DMA_ROWS)
                                                         SAM_DMA16M_VARIANTS(SAM_DMA_ROWS)
-                                                            SAM_F32PAD_VARIANTS(SAM_F32PAD_ROW)};
+                                                            SAM_F32PAD_VARIANTS(SAM_F32PAD_ROW)
+                                                                SAM_DMA16D_VARIANTS(SAM_DMA_ROWS)};
 
 static const int kVariantCount = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 

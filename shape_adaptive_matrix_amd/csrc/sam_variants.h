@@ -140,3 +140,11 @@
     F(61, "f128x128_w4x2_k32n2_b16_pad",   128, 128, 4, 2, 32, 2, 4, 1, 16, 0, 8, 1, 16, 0.88)   \
     F(62, "f256x256_w4x2_k32n2_b16_pad",   256, 256, 4, 2, 32, 2, 4, 1, 16, 0, 8, 1,  8, 0.95)   \
     F(63, "f128x128_w2x2s2_k64n2_b16_pad", 128, 128, 2, 2, 64, 2, 4, 2, 16, 0, 8, 1, 16, 0.91)
+
+// A deeper ring for 128 x 128 16-bit tiles (same list format as
+// SAM_DMA16S_VARIANTS): such a tile moves half the bytes per stage of a
+// 256 x 256 one, so four stages (three in flight) fit where two do there,
+// and eight waves of 64 x 32 keep enough loads and MFMAs in flight per CU
+// for shapes whose tile counts leave no room for larger tiles.
+#define SAM_DMA16D_VARIANTS(D)                                                           \
+    D(64, "r128x128_w2x4_k64n4_b16", 128, 128, 2, 4, 64, 4, 0, 16, 0, 8, 1, 16, 0.40)

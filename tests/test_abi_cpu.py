@@ -253,7 +253,11 @@ def test_ex_strided_rows_on_a_16bit_ring_plan_need_no_packed_copy(dtype):
     ws = lambda ta, tb, lda, ldb: sam.ex_workspace_bytes(M, N, K, ta, tb, lda, ldb, N, 1.0, 0.0, dtype)
     assert ws(False, False, K + 8, N + 16) == p["workspace_bytes"]
     assert ws(False, False, K + 3, N) >= M * K * 2                      # misaligned rows: packed
-    assert ws(True, False, M, N) >= M * K * 2                           # transposed: packed
+    if "_b16" in p["name"]:                                             # 16x16x32 ring: A^T read straight
+        assert ws(True, False, M, N) == p["workspace_bytes"]
+    else:                                                               # 32x32x16 ring: transposed is packed
+        assert ws(True, False, M, N) >= M * K * 2
+    assert ws(True, False, M + 4, N) >= M * K * 2                       # rows of A^T not 16-byte pieces: packed
     q = sam.plan(2049, 4097, 1025, dtype)                               # plan pads both operands
     assert q["name"].startswith(dtype + "_r") and q["workspace_bytes"] > 0
     assert sam.ex_workspace_bytes(2049, 4097, 1025, False, False, 1028, 4102, 4097, 1.0, 0.0,
