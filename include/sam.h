@@ -219,8 +219,9 @@ typedef enum { SAM_OP_N = 0, SAM_OP_T = 1 } sam_op;
  *    the transposed operand's leading dimension are multiples of 8 (a
  *    192-row tile hands a transposed A to its 256-row twin); FP32 ring plans
  *    with tiles up to 128 x 256 read a transposed B straight when K and ldb
- *    are multiples of 4, and a transposed A when N and lda are multiples of
- *    4; FP32 with both operands transposed runs as the
+ *    are multiples of 4, and those and the 256 x 256 tile a transposed A
+ *    when N and lda are multiples of 4; FP32 with both operands transposed
+ *    runs as the
  *    plain product B A of the operands as stored, whose ring plan stores C
  *    transposed;
  *  - whatever remains (a transposed operand the plan cannot read, other

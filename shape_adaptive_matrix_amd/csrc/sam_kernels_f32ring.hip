@@ -637,11 +637,13 @@ constexpr F32RingFn ring_kernel() {
     }
 }
 
-// A-given-transposed forms (B in its plain layout, N % 4 == 0): the same
-// variants, whose wave tiles hold whole groups of two or four row blocks.
+// A-given-transposed forms (B in its plain layout, N % 4 == 0): the 16x16x4
+// variants that read four columns at a time and whose wave tiles hold whole
+// groups of two or four row blocks, the 256 x 256 tile included (its reads
+// of A^T share one address per group); stream-K forms as for the others.
 template <int BM, int BN, int WM, int WN, int BK, int NBUF, int V, int KS, int BLK, bool SK>
 constexpr F32RingFn ring_at_kernel() {
-    if constexpr (V == 4 && BLK == 16 && BM * BN <= kSkMaxTile && (BM / WM / BLK) % 2 == 0) {
+    if constexpr (V == 4 && BLK == 16 && (!SK || BM * BN <= kSkMaxTile) && (BM / WM / BLK) % 2 == 0) {
         if constexpr (SK)
             return gemm_f32_ring_sk_kernel<BM, BN, WM, WN, BK, NBUF, V, KS, BLK, false, false, false, false, true>;
         else

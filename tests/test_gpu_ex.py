@@ -363,7 +363,10 @@ def test_ex_f32_transposed_b_read_straight(vid, alpha, beta):
 F32_AT_SHAPES = [(300, 520, 264), (1000, 776, 1030), (129, 136, 512)]
 
 
-@pytest.mark.parametrize("vid", F32_BT)
+F32_AT = F32_BT + [v for v in range(sam.variant_count()) if sam.variant_info(v)["name"] == "f256x256_w4x2_k32n2_b16"]
+
+
+@pytest.mark.parametrize("vid", F32_AT)
 @pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (0.5, -1.0)])
 def test_ex_f32_transposed_a_read_straight(vid, alpha, beta):
     ran = 0
