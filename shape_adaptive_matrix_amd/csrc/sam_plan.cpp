@@ -549,8 +549,10 @@ bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out)
     }
     // 2. A measured shape in the same half-octave bucket in M, N and K (the
     //    nearest one, ties to the earlier table row): its variant and raster
-    //    order, with its split when that is admissible here and otherwise
-    //    the variant's own choice. The bucketed fallback of page
+    //    order. Its split too when the variant gives this shape the same
+    //    number of tiles (and the split is admissible here); otherwise the
+    //    variant's own split or stream-K choice, since how a split fills the
+    //    CUs depends on the tile count. The bucketed fallback of page
     //    "fix(fp4_gemm autotune) SM107 kernel family excluded from autotune
     //    candidates and heuristics update - #4856", description item 4.
     if (M > 0 && N > 0 && K > 0) {
@@ -570,7 +572,10 @@ bool plan_auto(long long M, long long N, long long K, int dtype, Plan* out)
         }
         if (near) {
             Plan p{};
-            if (!plan_for_variant(near->variant, M, N, K, dtype, near->split, &p, near->raster))
+            const Variant* v = variant_get(near->variant);
+            const bool same_tiles =
+                cdiv(M, v->bm) * cdiv(N, v->bn) == cdiv(near->M, v->bm) * cdiv(near->N, v->bn);
+            if (!same_tiles || !plan_for_variant(near->variant, M, N, K, dtype, near->split, &p, near->raster))
                 plan_for_variant(near->variant, M, N, K, dtype, 0, &p, near->raster);
             p.tuned = 2;
             *out = p;
