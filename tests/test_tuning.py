@@ -58,6 +58,18 @@ def test_shape_in_a_measured_bucket_takes_its_plan():
     assert sam.plan(2040, 2056, 2064, "f32") == p   # pure function of the shape
 
 
+def test_bucket_split_is_replanned_when_the_tile_count_differs():
+    """A bucket shape takes the measured split only when its tile count is the
+    measured shape's; otherwise the variant's own split or stream-K choice
+    (2040 x 2056 x 2064: 272 tiles of 128 x 128 against 2048^3's 256)."""
+    p = sam.plan(2040, 2056, 2064, "f32")
+    own = sam.variant_plan(p["variant_id"], 2040, 2056, 2064, "f32", 0, p["raster_n"])
+    assert p["tuned"] == 2 and (p["split_k"], p["grid_wgs"]) == (own["split_k"], own["grid_wgs"])
+    q = sam.plan(3000, 3000, 2990, "f32")                  # 3000^3's tiles: its split kept
+    ref = sam.plan(3000, 3000, 3000, "f32")
+    assert q["tuned"] == 2 and q["variant_id"] == ref["variant_id"] and q["split_k"] == ref["split_k"]
+
+
 def test_shape_outside_every_bucket_uses_the_cost_model():
     p = sam.plan(2040, 2056, 700, "f32")
     assert p["tuned"] == 0 and not p["name"].endswith(("_tuned", "_bucket"))
