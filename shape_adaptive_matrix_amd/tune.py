@@ -39,10 +39,12 @@ EXTRA = {
     "f32": [(512, 512, 512), (1024, 1024, 1024), (1536, 1536, 1536), (3072, 3072, 3072),
             (6144, 6144, 6144), (1000, 1000, 1000), (3000, 3000, 3000), (2048, 2048, 512),
             (2048, 2048, 8192), (4096, 4096, 1024), (64, 4096, 4096), (4096, 64, 4096),
-            (32, 8192, 8192), (256, 11008, 4096), (4096, 4096, 11008), (2049, 4097, 1025)],
+            (32, 8192, 8192), (256, 11008, 4096), (4096, 4096, 11008), (2049, 4097, 1025),
+            (5000, 5000, 5000), (7168, 7168, 7168)],
     "bf16": [(1024, 1024, 1024), (2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144),
              (4096, 4096, 1024), (2048, 8192, 2048), (256, 11008, 4096), (4096, 4096, 11008),
-             (2049, 4097, 1025), (5120, 5120, 5120), (8192, 8192, 8190)],
+             (2049, 4097, 1025), (5120, 5120, 5120), (8192, 8192, 8190), (1536, 1536, 1536),
+             (2560, 2560, 2560), (3584, 3584, 3584), (7168, 7168, 7168)],
     "f16": [(2048, 2048, 2048), (6144, 6144, 6144), (4096, 4096, 11008), (256, 11008, 4096), (2049, 4097, 1025)],
     "mxfp8": [(2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144), (4096, 4096, 1024),
               (256, 11008, 4096), (4096, 4096, 11008), (2048, 8192, 2048)],
