@@ -318,8 +318,8 @@ sam_status sam_gemm_variant(int32_t id, sam_dtype dtype, int32_t split_k,
  * SAM_F32, SAM_BF16 or SAM_F16; the same plan, kernels and bits) without a
  * caller workspace and without any allocation: for callers that cannot
  * allocate device memory (code under graph capture, tight serving loops,
- * harnesses that forbid hipMalloc). Split-K partials and stream-K slots go to
- * a file-scope device array of SAM_SCRATCH_BYTES that each GPU holds from
+ * harnesses that forbid hipMalloc). The plan's workspace (padded operand
+ * copies, split-K partials, stream-K slots) goes to a file-scope device array of SAM_SCRATCH_BYTES that each GPU holds from
  * its first such call until the process ends. A plan whose workspace_bytes
  * exceeds SAM_SCRATCH_BYTES is refused with SAM_ERR_WORKSPACE (use
  * sam_gemm_<dtype> with a workspace for it). Nothing in the array needs to
